@@ -1,0 +1,170 @@
+/*
+ * tkg -- tiled dense GEMM for AMD MI355X (gfx950): the C ABI.
+ *
+ * Every entry point computes one matrix product
+ *
+ *     C = s * A * B          (A: M x K, B: K x N, C: M x N)
+ *
+ * with fp32 accumulation on the matrix cores and a bf16 result, as defined
+ * on page "ThunderKittens: Simple, Fast, and Adorable AI Kernels", section
+ * 3.4, "Integration: How the Three Levels Compose into a Complete Kernel"
+ * (C = A x B, A is M x K, B is K x N), with A row-major and B column-major
+ * as the tensor-core layout rule of page "ThunderKittens: 16x16 Tiles, the
+ * Load-Compute-Store-Finish Template, and Why 40 Lines Can Match cuBLAS",
+ * section "Warp level: tiles are the only data structure", requires.
+ *
+ * Common conventions
+ * ------------------
+ * - All matrix pointers are DEVICE pointers owned by the caller; the
+ *   library never allocates, frees or keeps them.
+ * - A is row-major M x K (leading dimension K). B is column-major K x N,
+ *   i.e. stored as an N x K row-major array (leading dimension K): both
+ *   operands are contiguous along K. C is row-major M x N bf16 (leading
+ *   dimension N) and is overwritten.
+ * - Every matrix pointer must be 16-byte aligned.
+ * - `stream` is a hipStream_t (NULL = the default stream). The call only
+ *   enqueues work and returns; the product is complete when the stream
+ *   reaches that point. Calls on one stream run in order; separate calls may
+ *   run concurrently on different streams as long as their C do not overlap.
+ * - The bf16 result is round-to-nearest-even of the fp32 accumulator times
+ *   the scale. The summation order over K is unspecified.
+ * - M == 0 or N == 0 is an empty product: nothing is launched, TKG_OK is
+ *   returned and no pointer is read. K == 0 writes zeros to C.
+ * - Return value: TKG_OK (0) once the kernel is enqueued, or a negative
+ *   tkg_status. On any error nothing is enqueued and C is untouched.
+ *   tkg_status_string() names every status.
+ * - The library holds no mutable state besides a per-device cache of the
+ *   compute-unit count; all entry points are thread-safe.
+ */
+#ifndef TKG_H
+#define TKG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tkg_status {
+  TKG_OK = 0,
+  TKG_ERR_NULL = -1,   /* a required pointer is NULL                        */
+  TKG_ERR_SHAPE = -2,  /* negative size, unsupported multiple or too large  */
+  TKG_ERR_ALIGN = -3,  /* a matrix pointer is not 16-byte aligned           */
+  TKG_ERR_LAUNCH = -4, /* the HIP runtime rejected the launch               */
+  TKG_ERR_DEVICE = -5  /* no usable HIP device / device query failed        */
+} tkg_status;
+
+/*
+ * bf16 x bf16 -> bf16, s = 1.
+ *   A: M x K bf16, B: N x K bf16 (B column-major), C: M x N bf16.
+ *   Requires K % 8 == 0 (16-byte rows) and K <= 4194303.
+ * The operand type and fp32 accumulation: page "ThunderKittens: Simple,
+ * Fast, and Adorable AI Kernels", section 3.4, "Warp-Level: Tile
+ * Operations".
+ */
+int gemm_bf16(int64_t M, int64_t N, int64_t K, const void *A, const void *B,
+              void *C, void *stream);
+
+/*
+ * fp8 x fp8 -> bf16 with per-tensor scales, s = scale_a * scale_b.
+ *   A: M x K bytes, B: N x K bytes, both OCP FP8 e4m3 (largest finite 448;
+ *   0x7F/0xFF are NaN). scale_a, scale_b: fp32 dequantization scales, so
+ *   A_real = scale_a * A and B_real = scale_b * B. Their product is formed
+ *   in fp32 and multiplies the fp32 accumulator before rounding to bf16.
+ *   Requires K % 16 == 0 and K <= 8388607.
+ * FP8 operands: page "ThunderKittens reaches 22.4 PFLOPS on NVIDIA Rubin"
+ * (FP8 GEMM); the 16 x 32 fp8 base tile: page "ThunderKittens DSL for GPU
+ * kernels" (tile abstractions).
+ */
+int gemm_fp8(int64_t M, int64_t N, int64_t K, const void *A, float scale_a,
+             const void *B, float scale_b, void *C, void *stream);
+
+/*
+ * Block-scaled 4-bit x block-scaled 4-bit -> bf16, s = a_scale * b_scale.
+ *   A: M x K/2 bytes of packed e2m1 values, element 2t of a row in the LOW
+ *      nibble of byte t (sign bit 3, 2 exponent bits with bias 1, 1 mantissa
+ *      bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6).
+ *   A_scales: M x K/16 bytes, OCP e4m3 scale of each block of 16 consecutive
+ *      K-elements of a row.
+ *   a_scale: fp32 per-tensor scale. A_real[i][k] =
+ *      a_scale * e4m3(A_scales[i][k/16]) * e2m1(A[i][k]).
+ *   B, B_scales, b_scale: the same for B in column-major order (N x K/2
+ *      values, N x K/16 scales).
+ *   Each e2m1 value times its block scale is exact in bf16, so the product
+ *   runs as an exact bf16 GEMM with fp32 accumulation; a_scale * b_scale
+ *   (fp32) multiplies the accumulator before rounding to bf16.
+ *   Requires K % 64 == 0 and K <= 16777215. All five pointers 16-byte
+ *   aligned.
+ * The block-scaled 4-bit format with scale factors kept next to the
+ * values: page "ThunderKittens reaches 22.4 PFLOPS on NVIDIA Rubin",
+ * sections "Rubin widens the data path" and "Feeding the faster tensor
+ * cores".
+ */
+int gemm_fp4_blockscaled(int64_t M, int64_t N, int64_t K, const void *A,
+                         const void *A_scales, float a_scale, const void *B,
+                         const void *B_scales, float b_scale, void *C,
+                         void *stream);
+
+/* Static, human-readable name of a tkg_status value (never NULL). */
+const char *tkg_status_string(int status);
+
+/*
+ * Launch options for measurement and ablation. tkg_gemm_ex() runs the same
+ * kernels as the three entry points above with these knobs exposed:
+ *   grid     -- workgroups to launch; 0 = one per compute unit (persistent),
+ *               a value >= the number of output tiles gives one workgroup
+ *               per tile (non-persistent).
+ *   group_m  -- tile rows per band of the grouped tile order; 0 = default
+ *               (8), 1 = plain row-major tile order.
+ *   xcd_remap -- 1 (default when grid is a multiple of 8) gives each XCD a
+ *               contiguous range of tiles; 0 leaves the hardware's
+ *               round-robin order.
+ * Page "ThunderKittens: Simple, Fast, and Adorable AI Kernels", section
+ * 3.4, "Persistent Grid Launch" (Table 2) and "Block Launch Order and L2
+ * Cache Reuse" (Table 3), measure these choices.
+ */
+typedef struct tkg_opts {
+  int32_t grid;
+  int32_t group_m;
+  int32_t xcd_remap;
+  int32_t reserved;
+} tkg_opts;
+
+enum { TKG_DTYPE_BF16 = 0, TKG_DTYPE_FP8 = 1, TKG_DTYPE_FP4_BLOCKSCALED = 2 };
+
+/*
+ * dtype: TKG_DTYPE_*. Arguments that a dtype does not use (A_scales,
+ * B_scales for bf16/fp8; the scales for bf16) are ignored. opts may be NULL
+ * (defaults). Same contract and errors as the typed entry points.
+ */
+int tkg_gemm_ex(int dtype, int64_t M, int64_t N, int64_t K, const void *A,
+                const void *A_scales, float a_scale, const void *B,
+                const void *B_scales, float b_scale, void *C, void *stream,
+                const tkg_opts *opts);
+
+/*
+ * LDS layout introspection for the CPU bank-conflict model (no GPU work).
+ * Writes the 64 per-lane LDS byte offsets (relative to the operand tile)
+ * of one ds_read_b128 fragment read of the staged operand tiles:
+ *   dtype  -- TKG_DTYPE_*;
+ *   step   -- MFMA k-step inside a stage (0 .. steps-1);
+ *   part   -- 0 or 1, which 16-byte half of a 32-byte fp8 operand
+ *             (0 for bf16 and for the 4-bit values);
+ *   frag   -- 32-row fragment index inside the workgroup tile (0 .. 7).
+ * Returns the number of k-steps per stage for the dtype, or a negative
+ * tkg_status for an invalid argument.
+ */
+int tkg_lds_fragment_offsets(int dtype, int step, int part, int frag,
+                             uint32_t *out64);
+
+/*
+ * Row length in bytes of the staged operand tiles for dtype (the unit the
+ * swizzle works on), or a negative tkg_status.
+ */
+int tkg_lds_row_bytes(int dtype);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TKG_H */

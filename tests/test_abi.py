@@ -1,0 +1,83 @@
+"""The C-ABI library: loads without a GPU, exports every function that
+include/tkg.h declares, and rejects invalid arguments with the documented
+status before touching any device (these calls never reach the GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tiled_dense_gemm_amd as tkg
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "tkg.h")
+S = tkg.STATUS
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) -
+                  {"defined"})
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("gemm_bf16", "gemm_fp8", "gemm_fp4_blockscaled",
+              "tkg_status_string", "tkg_gemm_ex"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function():
+    lib = ctypes.CDLL(tkg.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for name, v in S.items():
+        assert tkg.tkg_status_string(v).startswith(name)
+    assert "unknown" in tkg.tkg_status_string(12345)
+
+
+A16, B16, C16 = 4096, 8192, 12288   # 16-byte aligned fake addresses
+L = tkg.lib
+
+
+@pytest.mark.parametrize("call,want", [
+    # negative or unsupported sizes
+    (lambda: L.gemm_bf16(-1, 8, 8, A16, B16, C16, None), S["TKG_ERR_SHAPE"]),
+    (lambda: L.gemm_bf16(8, -1, 8, A16, B16, C16, None), S["TKG_ERR_SHAPE"]),
+    (lambda: L.gemm_bf16(8, 8, -8, A16, B16, C16, None), S["TKG_ERR_SHAPE"]),
+    (lambda: L.gemm_bf16(8, 8, 12, A16, B16, C16, None), S["TKG_ERR_SHAPE"]),
+    (lambda: L.gemm_bf16(8, 8, 1 << 23, A16, B16, C16, None), S["TKG_ERR_SHAPE"]),
+    (lambda: L.gemm_bf16(1 << 31, 8, 8, A16, B16, C16, None), S["TKG_ERR_SHAPE"]),
+    (lambda: L.gemm_fp8(8, 8, 24, A16, 1.0, B16, 1.0, C16, None), S["TKG_ERR_SHAPE"]),
+    (lambda: L.gemm_fp4_blockscaled(8, 8, 96, A16, A16, 1.0, B16, B16, 1.0, C16, None), S["TKG_ERR_SHAPE"]),
+    (lambda: L.tkg_gemm_ex(7, 8, 8, 8, A16, None, 1.0, B16, None, 1.0, C16, None, None), S["TKG_ERR_SHAPE"]),
+    # null pointers
+    (lambda: L.gemm_bf16(8, 8, 8, None, B16, C16, None), S["TKG_ERR_NULL"]),
+    (lambda: L.gemm_bf16(8, 8, 8, A16, None, C16, None), S["TKG_ERR_NULL"]),
+    (lambda: L.gemm_bf16(8, 8, 8, A16, B16, None, None), S["TKG_ERR_NULL"]),
+    (lambda: L.gemm_fp8(8, 8, 16, A16, 1.0, None, 1.0, C16, None), S["TKG_ERR_NULL"]),
+    (lambda: L.gemm_fp4_blockscaled(8, 8, 64, A16, None, 1.0, B16, B16, 1.0, C16, None), S["TKG_ERR_NULL"]),
+    (lambda: L.gemm_fp4_blockscaled(8, 8, 64, A16, A16, 1.0, B16, None, 1.0, C16, None), S["TKG_ERR_NULL"]),
+    # misaligned pointers
+    (lambda: L.gemm_bf16(8, 8, 8, A16 + 2, B16, C16, None), S["TKG_ERR_ALIGN"]),
+    (lambda: L.gemm_bf16(8, 8, 8, A16, B16 + 8, C16, None), S["TKG_ERR_ALIGN"]),
+    (lambda: L.gemm_bf16(8, 8, 8, A16, B16, C16 + 4, None), S["TKG_ERR_ALIGN"]),
+    (lambda: L.gemm_fp8(8, 8, 16, A16 + 1, 1.0, B16, 1.0, C16, None), S["TKG_ERR_ALIGN"]),
+    (lambda: L.gemm_fp4_blockscaled(8, 8, 64, A16, A16 + 4, 1.0, B16, B16, 1.0, C16, None), S["TKG_ERR_ALIGN"]),
+    # empty products succeed without reading any pointer
+    (lambda: L.gemm_bf16(0, 8, 8, None, None, None, None), S["TKG_OK"]),
+    (lambda: L.gemm_fp8(8, 0, 16, None, 1.0, None, 1.0, None, None), S["TKG_OK"]),
+    (lambda: L.gemm_fp4_blockscaled(0, 0, 64, None, None, 1.0, None, None, 1.0, None, None), S["TKG_OK"]),
+])
+def test_argument_errors(call, want):
+    assert call() == want
+
+
+def test_lds_introspection_errors():
+    buf = (ctypes.c_uint32 * 64)()
+    assert L.tkg_lds_fragment_offsets(0, 99, 0, 0, buf) == S["TKG_ERR_SHAPE"]
+    assert L.tkg_lds_fragment_offsets(0, 0, 0, 0, None) == S["TKG_ERR_NULL"]
+    assert L.tkg_lds_row_bytes(9) == S["TKG_ERR_SHAPE"]

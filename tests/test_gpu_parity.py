@@ -1,0 +1,301 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the CPU oracle.
+
+Tolerances:
+* bf16: relative Frobenius error <= 1e-3 against the oracle rounded to bf16
+  (rounding the exact product to bf16 alone costs ~1.7e-3 against the
+  unrounded one, so the bound applies to the rounded reference), and per
+  element |G - C| <= 1e-2 * (|A||B|)_ij + 1e-3 against the unrounded oracle.
+* fp8 and block-scaled 4-bit: relative Frobenius error <= 2e-2 against the
+  oracle on the same dequantized inputs.
+* Integer-valued and structured inputs (identity, permutation, small
+  integers) make fp32 accumulation exact, so there the result must equal the
+  oracle rounded to bf16 bit for bit.
+Large shapes are checked on 64x64 output tiles (corners, tiles straddling
+workgroup-tile boundaries, random ones), each tile on its own.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import gemm_inputs as gi
+import gemm_inputs.device  # noqa: F401  (gi.device)
+import oracle
+import tiled_dense_gemm_amd as tkg
+from oracle.formats import decode_bf16, decode_e4m3, round_to_bf16
+from tests.parity import relfro, sample_tiles, to_numpy_u16, to_numpy_u8
+
+pytestmark = pytest.mark.gpu
+
+BF16_RELFRO = 1e-3
+BF16_ELEM_REL, BF16_ELEM_ABS = 1e-2, 1e-3
+LOWP_RELFRO = 2e-2
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU parity tests need the HIP device"
+    return torch.device("cuda:0")
+
+
+def _up(a, dev, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    return t if dtype is None else t.view(dtype)
+
+
+def _bf16_result(C):
+    return decode_bf16(to_numpy_u16(C))
+
+
+def check_bf16(G, A64, Bt64, what=""):
+    R = oracle.gemm_f64(A64, Bt64)
+    err = relfro(G, round_to_bf16(R))
+    assert err <= BF16_RELFRO, (what, err)
+    bound = BF16_ELEM_REL * oracle.abs_gemm_f64(A64, Bt64) + BF16_ELEM_ABS
+    assert np.all(np.abs(G - R) <= bound), (what, float(np.max(np.abs(G - R) - bound)))
+    return err
+
+
+# ----------------------------------------------------------------- bf16
+
+def test_bf16_identity_bit_exact(dev):
+    M, K = 300, 512
+    A = gi.bf16_operand(1, M, K)
+    C = tkg.gemm_bf16(_up(A, dev, torch.bfloat16),
+                      _up(gi.identity_bits_bf16(K), dev, torch.bfloat16))
+    assert np.array_equal(to_numpy_u16(C), A)
+
+
+def test_bf16_permutation_bit_exact(dev):
+    M, K = 256, 768
+    A = gi.bf16_operand(2, M, K)
+    perm = gi.permutation(3, K)
+    Bt = np.zeros((K, K), np.uint16)
+    Bt[np.arange(K), perm] = 0x3F80              # B[perm[j], j] = 1
+    C = tkg.gemm_bf16(_up(A, dev, torch.bfloat16), _up(Bt, dev, torch.bfloat16))
+    assert np.array_equal(to_numpy_u16(C), A[:, perm])
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 512, 512), (300, 260, 136),
+                                   (1, 1, 8), (257, 255, 1032)])
+def test_bf16_integers_bit_exact(dev, M, N, K):
+    A = gi.small_integers(4, M, K)
+    Bt = gi.small_integers(5, N, K)
+    C = tkg.gemm_bf16(_up(gi.bf16_bits(A), dev, torch.bfloat16),
+                      _up(gi.bf16_bits(Bt), dev, torch.bfloat16))
+    assert np.array_equal(_bf16_result(C), round_to_bf16(oracle.gemm_f64(A, Bt)))
+
+
+def test_bf16_rank_one_bit_exact(dev):
+    # A[i,k] = a_i u_k, B[k,j] = v_k b_j with powers of two: C is exact
+    M, N, K = 320, 288, 256
+    g = np.random.default_rng(7)
+    a = 2.0 ** g.integers(-3, 4, M); u = 2.0 ** g.integers(-3, 4, K)
+    b = 2.0 ** g.integers(-3, 4, N); v = g.choice([-1.0, 1.0], K)
+    A, Bt = np.outer(a, u), np.outer(b, v)
+    C = tkg.gemm_bf16(_up(gi.bf16_bits(A), dev, torch.bfloat16),
+                      _up(gi.bf16_bits(Bt), dev, torch.bfloat16))
+    assert np.array_equal(_bf16_result(C), round_to_bf16(np.outer(a, b) * float(u @ v)))
+
+
+def test_bf16_normal_256(dev):
+    # the small configuration: 256^3, entries N(0, 1)
+    A = gi.bf16_operand(0, 256, 256)
+    Bt = gi.bf16_operand(1, 256, 256)
+    C = tkg.gemm_bf16(_up(A, dev, torch.bfloat16), _up(Bt, dev, torch.bfloat16))
+    G = _bf16_result(C)
+    check_bf16(G, decode_bf16(A), decode_bf16(Bt), "256^3")
+    # statistical pin: against the unrounded product the error is the bf16
+    # output rounding, ~1.7e-3; much more would mean accumulation damage
+    R = oracle.gemm_bf16(A, Bt)
+    assert relfro(G, R) < 2.5e-3
+
+
+@pytest.mark.parametrize("M,N,K", [(17, 33, 72), (300, 260, 136),
+                                   (513, 1000, 1032), (256, 256, 8),
+                                   (64, 2048, 520), (1500, 96, 200)])
+def test_bf16_ragged(dev, M, N, K):
+    A = gi.bf16_operand(10, M, K, std=K ** -0.5)
+    Bt = gi.bf16_operand(11, N, K, std=K ** -0.5)
+    C = tkg.gemm_bf16(_up(A, dev, torch.bfloat16), _up(Bt, dev, torch.bfloat16))
+    check_bf16(_bf16_result(C), decode_bf16(A), decode_bf16(Bt), (M, N, K))
+
+
+def test_bf16_k_zero_writes_zeros(dev):
+    C = torch.full((40, 300), 7.0, dtype=torch.bfloat16, device=dev)
+    A = torch.empty((40, 0), dtype=torch.bfloat16, device=dev)
+    Bt = torch.empty((300, 0), dtype=torch.bfloat16, device=dev)
+    tkg.gemm_bf16(A, Bt, out=C)
+    assert not C.float().abs().sum().item()
+
+
+def test_bf16_empty_output(dev):
+    A = torch.zeros((0, 64), dtype=torch.bfloat16, device=dev)
+    Bt = torch.zeros((32, 64), dtype=torch.bfloat16, device=dev)
+    assert tkg.gemm_bf16(A, Bt).shape == (0, 32)
+
+
+def _sampled_bf16(dev, M, N, K, seed):
+    A = gi.device.bf16_operand(seed, M, K, std=K ** -0.5, device=dev)
+    Bt = gi.device.bf16_operand(seed + 1, N, K, std=K ** -0.5, device=dev)
+    C = tkg.gemm_bf16(A, Bt)
+    torch.cuda.synchronize()
+    for (i0, j0) in sample_tiles(M, N, seed):
+        a = decode_bf16(to_numpy_u16(A[i0:i0 + 64]))
+        b = decode_bf16(to_numpy_u16(Bt[j0:j0 + 64]))
+        G = _bf16_result(C[i0:i0 + 64, j0:j0 + 64])
+        check_bf16(G, a, b, (M, N, K, i0, j0))
+
+
+@pytest.mark.parametrize("M,N,K", [(1024, 1024, 1024), (2048, 2048, 2048),
+                                   (4096, 4096, 4096), (8192, 8192, 8192),
+                                   (8192, 14336, 4096), (8192, 4096, 14336),
+                                   (16384, 16384, 16384)])
+def test_bf16_config_shapes_sampled(dev, M, N, K):
+    _sampled_bf16(dev, M, N, K, seed=100 + M % 997 + K % 13)
+
+
+def test_bf16_launch_options_agree(dev):
+    # persistent vs one-workgroup-per-tile, grouped vs row-major order,
+    # XCD remap on/off: every output is computed by the same instruction
+    # sequence, so results are identical bit for bit.
+    M, N, K = 2048, 1536, 1024
+    A = gi.device.bf16_operand(7, M, K, std=K ** -0.5, device=dev)
+    Bt = gi.device.bf16_operand(8, N, K, std=K ** -0.5, device=dev)
+    ref = tkg.gemm_bf16(A, Bt)
+    for grid, gm, xr in [(10000, 0, 1), (0, 1, 1), (0, 3, 0), (64, 16, 1), (7, 8, 1)]:
+        C = torch.empty_like(ref)
+        st = tkg.tkg_gemm_ex(tkg.DTYPE_BF16, M, N, K, A, None, 1.0, Bt, None,
+                             1.0, C, grid=grid, group_m=gm, xcd_remap=xr)
+        assert st == 0
+        assert torch.equal(C.view(torch.int16), ref.view(torch.int16)), (grid, gm, xr)
+
+
+def test_bf16_side_stream(dev):
+    M = N = K = 512
+    A = gi.bf16_operand(1, M, K)
+    Bt = gi.bf16_operand(2, N, K)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        Ad, Bd = _up(A, dev, torch.bfloat16), _up(Bt, dev, torch.bfloat16)
+        C = tkg.gemm_bf16(Ad, Bd)
+    s.synchronize()
+    check_bf16(_bf16_result(C), decode_bf16(A), decode_bf16(Bt), "stream")
+
+
+# ------------------------------------------------------------------ fp8
+
+def test_fp8_identity_bit_exact(dev):
+    M, K = 260, 256
+    codes = gi.e4m3_codes(gi.normal(3, M, K) * 40)
+    eye = np.zeros((K, K), np.uint8)
+    np.fill_diagonal(eye, 0x38)                      # 1.0
+    C = tkg.gemm_fp8(_up(codes, dev), 1.0, _up(eye, dev), 1.0)
+    # every e4m3 value is exact in bf16 (incl. 448 = 0x7E, subnormals)
+    assert np.array_equal(_bf16_result(C), decode_e4m3(codes))
+
+
+def test_fp8_all_codes_decode(dev):
+    # each of the 254 finite codes, once per row, against the identity
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    K = 256
+    A = np.zeros((codes.size, K), np.uint8)
+    A[np.arange(codes.size), np.arange(codes.size) % K] = codes
+    eye = np.zeros((K, K), np.uint8)
+    np.fill_diagonal(eye, 0x38)
+    C = tkg.gemm_fp8(_up(A, dev), 1.0, _up(eye, dev), 1.0)
+    G = _bf16_result(C)
+    assert np.array_equal(G[np.arange(codes.size), np.arange(codes.size) % K],
+                          decode_e4m3(codes))
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 512, 512), (300, 260, 144)])
+def test_fp8_integers_bit_exact(dev, M, N, K):
+    A = gi.e4m3_codes(gi.small_integers(6, M, K))
+    Bt = gi.e4m3_codes(gi.small_integers(7, N, K))
+    C = tkg.gemm_fp8(_up(A, dev), 1.0, _up(Bt, dev), 1.0)
+    ref = round_to_bf16(oracle.gemm_fp8(A, 1.0, Bt, 1.0))
+    assert np.array_equal(_bf16_result(C), ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (300, 260, 144),
+                                   (1000, 513, 1040)])
+def test_fp8_normal(dev, M, N, K):
+    A, sa = gi.fp8_operand(20, M, K)
+    Bt, sb = gi.fp8_operand(21, N, K)
+    C = tkg.gemm_fp8(_up(A, dev), sa, _up(Bt, dev), sb)
+    R = oracle.gemm_fp8(A, sa, Bt, sb)
+    assert relfro(_bf16_result(C), R) <= LOWP_RELFRO
+
+
+@pytest.mark.parametrize("n", [8192, 16384])
+def test_fp8_config_shapes_sampled(dev, n):
+    A, sa = gi.device.fp8_operand(30, n, n, device=dev)
+    Bt, sb = gi.device.fp8_operand(31, n, n, device=dev)
+    C = tkg.gemm_fp8(A, sa, Bt, sb)
+    torch.cuda.synchronize()
+    for (i0, j0) in sample_tiles(n, n, n):
+        R = oracle.gemm_fp8(to_numpy_u8(A[i0:i0 + 64]), sa,
+                            to_numpy_u8(Bt[j0:j0 + 64]), sb)
+        G = _bf16_result(C[i0:i0 + 64, j0:j0 + 64])
+        assert relfro(G, R) <= LOWP_RELFRO, (n, i0, j0)
+
+
+# ----------------------------------------------------- block-scaled 4-bit
+
+def _fp4_identity(K):
+    codes = np.zeros((K, K), np.uint8)
+    np.fill_diagonal(codes, 0x2)                     # 1.0
+    return gi.pack_nibbles(codes), np.full((K, K // 16), 0x38, np.uint8)
+
+
+def test_fp4_identity_bit_exact(dev):
+    M, K = 272, 256
+    Ap, As, _ = gi.fp4_quantize(gi.normal(40, M, K))
+    Ip, Is = _fp4_identity(K)
+    C = tkg.gemm_fp4_blockscaled(_up(Ap, dev), _up(As, dev), 1.0,
+                                 _up(Ip, dev), _up(Is, dev), 1.0)
+    # value x block scale is exact in bf16 (at most 6 significant bits)
+    assert np.array_equal(_bf16_result(C), oracle.dequant_fp4_blockscaled(Ap, As))
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (300, 260, 192),
+                                   (513, 700, 1088)])
+def test_fp4_normal(dev, M, N, K):
+    Ap, As, ta = gi.fp4_operand(41, M, K)
+    Bp, Bs, tb = gi.fp4_operand(42, N, K)
+    C = tkg.gemm_fp4_blockscaled(_up(Ap, dev), _up(As, dev), ta,
+                                 _up(Bp, dev), _up(Bs, dev), tb)
+    R = oracle.gemm_fp4_blockscaled(Ap, As, ta, Bp, Bs, tb)
+    assert relfro(_bf16_result(C), R) <= LOWP_RELFRO
+
+
+def test_fp4_integers_bit_exact(dev):
+    # power-of-two block scales and tensor scales 1: exact accumulation
+    M, N, K = 320, 288, 512
+    g = np.random.default_rng(9)
+    Ac = g.integers(0, 16, (M, K)).astype(np.uint8)
+    Bc = g.integers(0, 16, (N, K)).astype(np.uint8)
+    As = g.choice(np.array([0x30, 0x38, 0x40], np.uint8), (M, K // 16))
+    Bs = g.choice(np.array([0x30, 0x38, 0x40], np.uint8), (N, K // 16))
+    Ap, Bp = gi.pack_nibbles(Ac), gi.pack_nibbles(Bc)
+    C = tkg.gemm_fp4_blockscaled(_up(Ap, dev), _up(As, dev), 1.0,
+                                 _up(Bp, dev), _up(Bs, dev), 1.0)
+    ref = round_to_bf16(oracle.gemm_fp4_blockscaled(Ap, As, 1.0, Bp, Bs, 1.0))
+    assert np.array_equal(_bf16_result(C), ref)
+
+
+@pytest.mark.parametrize("n", [16384, 65536])
+def test_fp4_config_shapes_sampled(dev, n):
+    Ap, As, ta = gi.device.fp4_operand(50, n, n, device=dev)
+    Bp, Bs, tb = gi.device.fp4_operand(51, n, n, device=dev)
+    C = tkg.gemm_fp4_blockscaled(Ap, As, ta, Bp, Bs, tb)
+    torch.cuda.synchronize()
+    tiles = sample_tiles(n, n, n, n_random=4 if n > 20000 else 8)
+    for (i0, j0) in tiles:
+        R = oracle.gemm_fp4_blockscaled(
+            to_numpy_u8(Ap[i0:i0 + 64]), to_numpy_u8(As[i0:i0 + 64]), ta,
+            to_numpy_u8(Bp[j0:j0 + 64]), to_numpy_u8(Bs[j0:j0 + 64]), tb)
+        G = _bf16_result(C[i0:i0 + 64, j0:j0 + 64])
+        assert relfro(G, R) <= LOWP_RELFRO, (n, i0, j0)
+    del C

@@ -1,0 +1,212 @@
+"""Python binding of the tkg C ABI (``include/tkg.h``): tiled dense GEMM on
+AMD MI355X (gfx950).
+
+Argument marshalling only: every step of the product runs in the HIP
+kernels of ``libtkg.so``. torch supplies device memory and the current
+stream. Names match the C entry points: ``gemm_bf16``, ``gemm_fp8``,
+``gemm_fp4_blockscaled``, ``tkg_gemm_ex`` and ``tkg_status_string``.
+
+Operand layouts: ``A`` is M x K row-major; ``B`` is passed column-major,
+i.e. as an N x K row-major tensor ``Bt``; the result is an M x N row-major
+bf16 tensor. There is no CPU fallback: importing works without a GPU (the
+library loads), but every product needs the HIP device.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "gemm_bf16", "gemm_fp8", "gemm_fp4_blockscaled", "tkg_gemm_ex",
+    "tkg_status_string", "lds_fragment_offsets", "lds_row_bytes", "lib",
+    "TkgError", "DTYPE_BF16", "DTYPE_FP8", "DTYPE_FP4_BLOCKSCALED",
+    "STATUS", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtkg.so")
+
+DTYPE_BF16, DTYPE_FP8, DTYPE_FP4_BLOCKSCALED = 0, 1, 2
+STATUS = {"TKG_OK": 0, "TKG_ERR_NULL": -1, "TKG_ERR_SHAPE": -2,
+          "TKG_ERR_ALIGN": -3, "TKG_ERR_LAUNCH": -4, "TKG_ERR_DEVICE": -5}
+
+
+class TkgError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = int(status)
+        super().__init__("%s%s" % (what + ": " if what else "",
+                                   tkg_status_string(status)))
+
+
+class TkgOpts(ctypes.Structure):
+    _fields_ = [("grid", ctypes.c_int32), ("group_m", ctypes.c_int32),
+                ("xcd_remap", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            "libtkg.so is not built (%s); run `python -m "
+            "tiled_dense_gemm_amd._build`" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    i64, vp, f32, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
+    L.gemm_bf16.argtypes = [i64, i64, i64, vp, vp, vp, vp]
+    L.gemm_bf16.restype = i32
+    L.gemm_fp8.argtypes = [i64, i64, i64, vp, f32, vp, f32, vp, vp]
+    L.gemm_fp8.restype = i32
+    L.gemm_fp4_blockscaled.argtypes = [i64, i64, i64, vp, vp, f32, vp, vp,
+                                       f32, vp, vp]
+    L.gemm_fp4_blockscaled.restype = i32
+    L.tkg_gemm_ex.argtypes = [i32, i64, i64, i64, vp, vp, f32, vp, vp, f32,
+                              vp, vp, ctypes.POINTER(TkgOpts)]
+    L.tkg_gemm_ex.restype = i32
+    L.tkg_status_string.argtypes = [i32]
+    L.tkg_status_string.restype = ctypes.c_char_p
+    L.tkg_lds_fragment_offsets.argtypes = [i32, i32, i32, i32,
+                                           ctypes.POINTER(ctypes.c_uint32)]
+    L.tkg_lds_fragment_offsets.restype = i32
+    L.tkg_lds_row_bytes.argtypes = [i32]
+    L.tkg_lds_row_bytes.restype = i32
+    return L
+
+
+lib = _load()
+
+
+def tkg_status_string(status: int) -> str:
+    return lib.tkg_status_string(int(status)).decode()
+
+
+def lds_row_bytes(dtype: int) -> int:
+    r = lib.tkg_lds_row_bytes(int(dtype))
+    if r < 0:
+        raise TkgError(r, "tkg_lds_row_bytes")
+    return r
+
+
+def lds_fragment_offsets(dtype: int, step: int, part: int, frag: int):
+    """The 64 per-lane LDS byte offsets of one fragment read (see tkg.h)."""
+    buf = (ctypes.c_uint32 * 64)()
+    r = lib.tkg_lds_fragment_offsets(int(dtype), int(step), int(part),
+                                     int(frag), buf)
+    if r < 0:
+        raise TkgError(r, "tkg_lds_fragment_offsets")
+    return list(buf)
+
+
+# ------------------------------------------------------------ torch layer
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check_mat(x, name, rows, cols, dtypes, device):
+    torch = _torch()
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if x.dtype not in dtypes:
+        raise TypeError("%s has dtype %s, expected one of %s"
+                        % (name, x.dtype, dtypes))
+    if x.dim() != 2 or tuple(x.shape) != (rows, cols):
+        raise ValueError("%s has shape %s, expected (%d, %d)"
+                         % (name, tuple(x.shape), rows, cols))
+    if not x.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if x.device.type != "cuda" or (device is not None and x.device != device):
+        raise ValueError("%s must be on the GPU (%s)" % (name, device))
+
+
+def _out(out, M, N, device):
+    torch = _torch()
+    if out is None:
+        return torch.empty((M, N), dtype=torch.bfloat16, device=device)
+    _check_mat(out, "out", M, N, (torch.bfloat16,), device)
+    return out
+
+
+def _raise(st, what):
+    if st != 0:
+        raise TkgError(st, what)
+
+
+def gemm_bf16(A, Bt, out=None, stream=None):
+    """out (M x N bf16) = A (M x K bf16) @ B, with B given as Bt (N x K)."""
+    torch = _torch()
+    M, K = A.shape
+    N = Bt.shape[0]
+    dt = (torch.bfloat16, torch.int16, torch.uint16)
+    _check_mat(A, "A", M, K, dt, None)
+    _check_mat(Bt, "Bt", N, K, dt, A.device)
+    out = _out(out, M, N, A.device)
+    with torch.cuda.device(A.device):
+        st = lib.gemm_bf16(M, N, K, A.data_ptr(), Bt.data_ptr(),
+                           out.data_ptr(), _stream_ptr(stream))
+    _raise(st, "gemm_bf16")
+    return out
+
+
+def _fp8_types():
+    torch = _torch()
+    return tuple(t for t in (torch.uint8, getattr(torch, "float8_e4m3fn", None))
+                 if t is not None)
+
+
+def gemm_fp8(A, scale_a, Bt, scale_b, out=None, stream=None):
+    """out = (scale_a * A) @ (scale_b * B); A: M x K e4m3, Bt: N x K e4m3
+    (uint8 or float8_e4m3fn tensors), fp32 scales."""
+    torch = _torch()
+    M, K = A.shape
+    N = Bt.shape[0]
+    _check_mat(A, "A", M, K, _fp8_types(), None)
+    _check_mat(Bt, "Bt", N, K, _fp8_types(), A.device)
+    out = _out(out, M, N, A.device)
+    with torch.cuda.device(A.device):
+        st = lib.gemm_fp8(M, N, K, A.data_ptr(), float(scale_a),
+                          Bt.data_ptr(), float(scale_b), out.data_ptr(),
+                          _stream_ptr(stream))
+    _raise(st, "gemm_fp8")
+    return out
+
+
+def gemm_fp4_blockscaled(A, A_scales, a_scale, Bt, B_scales, b_scale,
+                         out=None, stream=None):
+    """Block-scaled 4-bit product. A: M x K/2 packed e2m1 (uint8),
+    A_scales: M x K/16 e4m3 (uint8), a_scale: fp32; Bt, B_scales, b_scale
+    likewise for B in column-major order (N rows)."""
+    torch = _torch()
+    M, Kh = A.shape
+    K = 2 * Kh
+    N = Bt.shape[0]
+    u8 = (torch.uint8,)
+    _check_mat(A, "A", M, Kh, u8, None)
+    _check_mat(Bt, "Bt", N, Kh, u8, A.device)
+    _check_mat(A_scales, "A_scales", M, K // 16, _fp8_types(), A.device)
+    _check_mat(B_scales, "B_scales", N, K // 16, _fp8_types(), A.device)
+    out = _out(out, M, N, A.device)
+    with torch.cuda.device(A.device):
+        st = lib.gemm_fp4_blockscaled(
+            M, N, K, A.data_ptr(), A_scales.data_ptr(), float(a_scale),
+            Bt.data_ptr(), B_scales.data_ptr(), float(b_scale),
+            out.data_ptr(), _stream_ptr(stream))
+    _raise(st, "gemm_fp4_blockscaled")
+    return out
+
+
+def tkg_gemm_ex(dtype, M, N, K, A, A_scales, a_scale, Bt, B_scales, b_scale,
+                out, stream=None, grid=0, group_m=0, xcd_remap=1):
+    """Raw entry point with launch options (see tkg.h). Tensors or None for
+    unused operands; returns the tkg status instead of raising."""
+    torch = _torch()
+    ptr = lambda t: None if t is None else t.data_ptr()
+    o = TkgOpts(int(grid), int(group_m), int(xcd_remap), 0)
+    with torch.cuda.device(out.device):
+        return lib.tkg_gemm_ex(int(dtype), int(M), int(N), int(K), ptr(A),
+                               ptr(A_scales), float(a_scale), ptr(Bt),
+                               ptr(B_scales), float(b_scale), ptr(out),
+                               _stream_ptr(stream), ctypes.byref(o))

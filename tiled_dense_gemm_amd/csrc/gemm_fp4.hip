@@ -1,0 +1,340 @@
+// Block-scaled 4-bit tiled GEMM for gfx950 (MI355X).
+//
+// Format (page "ThunderKittens reaches 22.4 PFLOPS on NVIDIA Rubin": NVFP4,
+// a block-scaled 4-bit float whose block-scaling factors travel with the
+// values, "Feeding the faster tensor cores"): e2m1 values, one e4m3 scale
+// per 16 consecutive K-elements of a row, one fp32 scale per tensor.
+//
+// gfx950's block-scaled MFMA takes power-of-two (E8M0) scales per 32
+// elements, which cannot express an e4m3 scale per 16. Each e2m1 value
+// times its e4m3 block scale has at most 6 significant bits and lies in
+// [2^-10, 2688], so it is exact in fp16: the kernel dequantizes in
+// registers, right after the LDS read, and multiplies on the fp16 matrix
+// cores with fp32 accumulation. The product is therefore exact up to fp32
+// summation, at the 16-bit MFMA rate.
+//
+// Structure as in gemm_dense.hip (256x256 workgroup tile of 2x2 wave tiles
+// of 4x4 32x32 accumulators, persistent grouped grid with XCD remap, LDS
+// ring fed by direct global->LDS loads), with a 4-deep ring: one stage holds
+// 128 K-elements per row, i.e. 64 bytes of packed values (swizzled as in
+// tkg_layout.hpp) and 8 bytes of block scales.
+#include "tkg_device.hpp"
+#include "tkg_kernels.hpp"
+#include "tkg_layout.hpp"
+
+#include <type_traits>
+
+namespace tkg {
+namespace {
+
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int BM = kBM, BN = kBN;
+constexpr int VB = 64;                    // value bytes per row per stage
+constexpr int SB = 8;                     // scale bytes per row per stage
+constexpr int STAGES = 4;
+constexpr int TILE_V = BM * VB;           // 16 KiB
+constexpr int TILE_S = BM * SB;           // 2 KiB
+constexpr int OFF_BV = TILE_V;
+constexpr int OFF_AS = 2 * TILE_V;
+constexpr int OFF_BS = 2 * TILE_V + TILE_S;
+constexpr int STAGE_BYTES = 2 * TILE_V + 2 * TILE_S;  // 36 KiB
+constexpr int WAVES = kThreads / 64;
+constexpr int WM = 128, WN = 128;
+constexpr int FM = WM / 32, FN = WN / 32;
+constexpr int VDMA = TILE_V / 1024 / WAVES;  // 4 b128 loads per wave per operand
+constexpr int SDMA = TILE_S / 256 / WAVES;   // 2 b32 loads per wave per operand
+constexpr int DMA_PER_STAGE = 2 * VDMA + 2 * SDMA;  // per lane
+
+static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS budget");
+
+// 1: v_cvt_scalef32_pk_f16_fp4 multiplies by the whole fp32 scale.
+// 0: it only applies the scale's power of two; the remaining mantissa
+//    factor is applied with a packed fp16 multiply (exact either way).
+#ifndef TKG_FP4_CVT_FULL_SCALE
+#define TKG_FP4_CVT_FULL_SCALE 0
+#endif
+
+struct TileState {
+  int m0, n0;
+  __amdgpu_buffer_rsrc_t rav, rbv, ras, rbs;
+};
+
+__device__ __forceinline__ TileState tile_state(const Fp4Args& p, int t) {
+  TileState s;
+  if (t >= p.num_tiles) {
+    s.m0 = s.n0 = 0;
+    s.rav = make_rsrc(p.A, 0);
+    s.rbv = make_rsrc(p.B, 0);
+    s.ras = make_rsrc(p.As, 0);
+    s.rbs = make_rsrc(p.Bs, 0);
+    return s;
+  }
+  int pm, pn;
+  grouped_tile(t, p.tiles_m, p.tiles_n, p.group_m, pm, pn);
+  s.m0 = pm * BM;
+  s.n0 = pn * BN;
+  const uint32_t ra = (uint32_t)min(p.M - s.m0, BM);
+  const uint32_t rb = (uint32_t)min(p.N - s.n0, BN);
+  s.rav = make_rsrc(p.A + (size_t)s.m0 * p.vbytes, ra * p.vbytes);
+  s.rbv = make_rsrc(p.B + (size_t)s.n0 * p.vbytes, rb * p.vbytes);
+  s.ras = make_rsrc(p.As + (size_t)s.m0 * p.sbytes, ra * p.sbytes);
+  s.rbs = make_rsrc(p.Bs + (size_t)s.n0 * p.sbytes, rb * p.sbytes);
+  return s;
+}
+
+// Eight e2m1 values (one dword, element 2t in the low nibble of byte t)
+// times a block scale -> eight exact fp16 values.
+__device__ __forceinline__ f16x8_t dequant8(uint32_t packed, float scale,
+                                            f16x2_t mant) {
+  f16x2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, scale, 0);
+  f16x2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, scale, 1);
+  f16x2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, scale, 2);
+  f16x2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, scale, 3);
+#if !TKG_FP4_CVT_FULL_SCALE
+  h0 = h0 * mant;
+  h1 = h1 * mant;
+  h2 = h2 * mant;
+  h3 = h3 * mant;
+#endif
+  return f16x8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+}
+
+// Block scale (byte BYTE of `word`, OCP e4m3) -> the scale operand of the
+// convert and the fp16 mantissa factor still to apply.
+template <int BYTE>
+__device__ __forceinline__ void split_scale(uint32_t word, float& s,
+                                            f16x2_t& mant) {
+  const float f = __builtin_amdgcn_cvt_f32_fp8((int)word, BYTE);
+#if TKG_FP4_CVT_FULL_SCALE
+  s = f;
+  mant = f16x2_t{(_Float16)1.0f, (_Float16)1.0f};
+#else
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  s = __builtin_bit_cast(float, u & 0xFF800000u);  // sign, power of two
+  const _Float16 m =
+      (_Float16)__builtin_bit_cast(float, (u & 0x007FFFFFu) | 0x3F800000u);
+  mant = f16x2_t{m, m};  // in [1, 2), exact in fp16 (3 mantissa bits)
+#endif
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_fp4_kernel(Fp4Args p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[STAGES * STAGE_BYTES];
+  TKG_LDS uint8_t* smem = (TKG_LDS uint8_t*)smem_raw;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int G = gridDim.x;
+  int t = xcd_virtual_id(blockIdx.x, G, p.xcd_remap);
+  if (t >= p.num_tiles) return;
+
+  // ---- staging offsets ---------------------------------------------------
+  uint32_t voff[VDMA], vkb[VDMA];
+#pragma unroll
+  for (int i = 0; i < VDMA; ++i) {
+    const uint32_t q = wave * VDMA + i;
+    const uint32_t row = dma_row(VB, q, lane);
+    const uint32_t chunk = dma_chunk(VB, q, lane);
+    voff[i] = row * p.vbytes + chunk * 16u;
+    vkb[i] = chunk * 16u;
+  }
+  // scales: one wave b32 load covers 32 rows x 8 bytes
+  uint32_t soff[SDMA];
+  const uint32_t skb = (lane & 1) * 4u;
+#pragma unroll
+  for (int i = 0; i < SDMA; ++i) {
+    const uint32_t q = wave * SDMA + i;
+    soff[i] = (q * 32u + (lane >> 1)) * p.sbytes + skb;
+  }
+
+  auto issue = [&](const TileState& ts, uint32_t kt, int buf) {
+    const uint32_t k0 = kt * VB;       // value byte offset
+    const uint32_t s0 = kt * SB;       // scale byte offset
+    const bool full = k0 + VB <= p.vbytes;
+    TKG_LDS uint8_t* st = smem + buf * STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < VDMA; ++i) {
+      uint32_t off = voff[i] + k0;
+      if (!full && k0 + vkb[i] >= p.vbytes) off = kOobOffset;
+      const uint32_t q = wave * VDMA + i;
+      dma_b128(ts.rav, st + q * 1024, off);
+      dma_b128(ts.rbv, st + OFF_BV + q * 1024, off);
+    }
+#pragma unroll
+    for (int i = 0; i < SDMA; ++i) {
+      uint32_t off = soff[i] + s0;
+      if (!full && s0 + skb >= p.sbytes) off = kOobOffset;
+      const uint32_t q = wave * SDMA + i;
+      dma_b32(ts.ras, st + OFF_AS + q * 256, off);
+      dma_b32(ts.rbs, st + OFF_BS + q * 256, off);
+    }
+  };
+
+  // ---- fragment reads ------------------------------------------------------
+  // Lane l works on row l%32 of each 32-row fragment. Per stage it reads two
+  // 16-byte chunks of packed values, chunk 2s + l/32 for s = 0, 1 (32
+  // K-elements each, 4 MFMA k-steps of 8), and the row's 8 scale bytes
+  // (one 8-byte read: 32 consecutive rows fill the banks without conflict).
+  // The same K order is used for A and B, so the MFMA's reduction is over
+  // the same K-elements on both sides.
+  const uint32_t frow = lane & 31;
+  const uint32_t khalf = lane >> 5;
+  uint32_t roff[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) roff[s] = swz_offset(VB, frow, 2 * s + khalf);
+  const uint32_t av_base = wm * WM * VB, bv_base = OFF_BV + wn * WN * VB;
+  const uint32_t as_base = OFF_AS + (wm * WM + frow) * SB;
+  const uint32_t bs_base = OFF_BS + (wn * WN + frow) * SB;
+
+  struct Raw {
+    i32x4_t a[FM], b[FN];  // packed values of one chunk
+    uint32_t sa[FM], sb[FN];  // this lane's 2 block scales of the chunk
+  };
+  auto read_raw = [&](int buf, int s, Raw& r) {
+    const TKG_LDS uint8_t* st = smem + buf * STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      r.a[i] = lds_read<i32x4_t>(st, av_base + i * 32 * VB + roff[s]);
+      r.sa[i] = lds_read<u32x2_t>(st, as_base + i * 32 * SB)[s] >> (16 * khalf);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      r.b[j] = lds_read<i32x4_t>(st, bv_base + j * 32 * VB + roff[s]);
+      r.sb[j] = lds_read<u32x2_t>(st, bs_base + j * 32 * SB)[s] >> (16 * khalf);
+    }
+  };
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
+
+  // 4 MFMA k-steps out of one chunk: k-step q uses dword q of the chunk,
+  // whose block (16 elements) is 2*(2s + khalf) + q/2, i.e. byte q/2 of the
+  // lane's pre-shifted scale word.
+  auto mma_kstep = [&](const Raw& r, auto qc) {
+    constexpr int q = decltype(qc)::value;
+    f16x8_t a[FM], b[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      float s; f16x2_t m;
+      split_scale<q / 2>(r.sa[i], s, m);
+      a[i] = dequant8((uint32_t)r.a[i][q], s, m);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      float s; f16x2_t m;
+      split_scale<q / 2>(r.sb[j], s, m);
+      b[j] = dequant8((uint32_t)r.b[j][q], s, m);
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[j], a[i], acc[i][j], 0, 0, 0);
+  };
+  auto mma_chunk = [&](const Raw& r) {
+    mma_kstep(r, std::integral_constant<int, 0>{});
+    mma_kstep(r, std::integral_constant<int, 1>{});
+    mma_kstep(r, std::integral_constant<int, 2>{});
+    mma_kstep(r, std::integral_constant<int, 3>{});
+  };
+
+  // ---- prologue ------------------------------------------------------------
+  TileState cur = tile_state(p, t);
+  TileState lts = cur;
+  int lt = t;
+  uint32_t lkt = 0;
+  auto advance_load = [&]() {
+    if (++lkt == p.nk) {
+      lkt = 0;
+      lt += G;
+      lts = tile_state(p, lt);
+    }
+  };
+#pragma unroll
+  for (int b = 0; b < STAGES; ++b) {
+    issue(lts, lkt, b);
+    advance_load();
+  }
+  wait_vmcnt<(STAGES - 1) * DMA_PER_STAGE>();
+  __syncthreads();
+
+  Raw raw[2];
+  read_raw(0, 0, raw[0]);
+
+  int buf = 0;
+  for (;;) {
+    for (uint32_t kt = 0; kt < p.nk; ++kt) {
+      // chunk s = 0 of this stage is in raw[0]; fetch chunk 1, multiply 0
+      read_raw(buf, 1, raw[1]);
+      mma_chunk(raw[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      // stage boundary: the next stage must have landed; this one is free
+      wait_vmcnt<(STAGES - 2) * DMA_PER_STAGE>();
+      __syncthreads();
+      issue(lts, lkt, buf);
+      advance_load();
+      const int nbuf = (buf + 1 == STAGES) ? 0 : buf + 1;
+      read_raw(nbuf, 0, raw[0]);
+      mma_chunk(raw[1]);
+      __builtin_amdgcn_sched_barrier(0);
+      buf = nbuf;
+    }
+
+    // ---- finish (as in gemm_dense.hip) -----------------------------------
+    const bool vec_ok = (p.N & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int m = cur.m0 + wm * WM + i * 32 + (int)frow;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = cur.n0 + wn * WN + j * 32 + 8 * g + 4 * (int)khalf;
+          const uint2 pk = pack_bf16x4(acc[i][j][4 * g + 0] * p.scale,
+                                       acc[i][j][4 * g + 1] * p.scale,
+                                       acc[i][j][4 * g + 2] * p.scale,
+                                       acc[i][j][4 * g + 3] * p.scale);
+          if (m < p.M) {
+            uint16_t* cp = p.C + (size_t)m * (size_t)p.N + n;
+            if (vec_ok && n + 3 < p.N) {
+              *reinterpret_cast<uint2*>(cp) = pk;
+            } else {
+              const uint16_t e[4] = {(uint16_t)(pk.x & 0xFFFF), (uint16_t)(pk.x >> 16),
+                                     (uint16_t)(pk.y & 0xFFFF), (uint16_t)(pk.y >> 16)};
+#pragma unroll
+              for (int u = 0; u < 4; ++u)
+                if (n + u < p.N) cp[u] = e[u];
+            }
+          }
+        }
+        acc[i][j] = f32x16_t{};
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    t += G;
+    if (t >= p.num_tiles) break;
+    cur = tile_state(p, t);
+  }
+  // The load cursor ran ahead into empty resources; let those LDS writes
+  // land before the workgroup's LDS is released.
+  wait_vmcnt<0>();
+}
+
+}  // namespace
+
+uint32_t fp4_stage_vbytes() { return VB; }
+
+hipError_t launch_fp4(const Fp4Args& a, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(gemm_fp4_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace tkg

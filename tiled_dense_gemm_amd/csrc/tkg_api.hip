@@ -1,0 +1,240 @@
+// C-ABI entry points: argument checks, launch configuration, kernel launch.
+// Declared and documented in include/tkg.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <stdint.h>
+
+#include "tkg.h"
+#include "tkg_kernels.hpp"
+#include "tkg_layout.hpp"
+
+namespace {
+
+using tkg::kBM;
+using tkg::kBN;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];  // 0 = not queried yet
+
+// Compute units of the current device (cached per device).
+int cu_count(int* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return TKG_ERR_DEVICE;
+  if (dev < kMaxDevices) {
+    const int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *out = c;
+      return TKG_OK;
+    }
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+          hipSuccess ||
+      n <= 0)
+    return TKG_ERR_DEVICE;
+  if (dev < kMaxDevices) g_cu_count[dev].store(n, std::memory_order_relaxed);
+  *out = n;
+  return TKG_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Plan {
+  int32_t tiles_m, tiles_n, num_tiles, group_m, xcd_remap, grid;
+};
+
+int make_plan(int64_t M, int64_t N, const tkg_opts* o, Plan* pl) {
+  pl->tiles_m = (int32_t)((M + kBM - 1) / kBM);
+  pl->tiles_n = (int32_t)((N + kBN - 1) / kBN);
+  const int64_t tiles = (int64_t)pl->tiles_m * pl->tiles_n;
+  if (tiles > INT32_MAX / 2) return TKG_ERR_SHAPE;
+  pl->num_tiles = (int32_t)tiles;
+  int cus = 0;
+  const int st = cu_count(&cus);
+  if (st != TKG_OK) return st;
+  int grid = (o && o->grid > 0) ? o->grid : cus;
+  if (grid > pl->num_tiles) grid = pl->num_tiles;
+  pl->grid = grid;
+  int gm = (o && o->group_m > 0) ? o->group_m : 8;
+  if (gm > pl->tiles_m) gm = pl->tiles_m;
+  pl->group_m = gm;
+  pl->xcd_remap = (o == nullptr || o->xcd_remap != 0) ? 1 : 0;
+  return TKG_OK;
+}
+
+// Checks shared by every dtype. `kmult` is the required multiple of K and
+// `kbytes_per_elem_x2` twice the bytes of one K-element of the staged rows.
+int check_common(int64_t M, int64_t N, int64_t K, int64_t kmult,
+                 int64_t kmax) {
+  if (M < 0 || N < 0 || K < 0) return TKG_ERR_SHAPE;
+  if (M > INT32_MAX || N > INT32_MAX || K > kmax) return TKG_ERR_SHAPE;
+  if (K % kmult != 0) return TKG_ERR_SHAPE;
+  return TKG_OK;
+}
+
+int run_dense(tkg::DenseType dt, int64_t M, int64_t N, int64_t K,
+              const void* A, const void* B, void* C, float scale,
+              void* stream, const tkg_opts* opts) {
+  const int64_t eb = 1 + (dt == tkg::kBf16);
+  const int64_t kmult = (dt == tkg::kBf16) ? 8 : 16;
+  // 256 rows of K*eb bytes must stay below 2^31 (one buffer resource).
+  const int64_t kmax = (dt == tkg::kBf16) ? 4194303 : 8388607;
+  int st = check_common(M, N, K, kmult, kmax);
+  if (st != TKG_OK) return st;
+  if (M == 0 || N == 0) return TKG_OK;
+  if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr)))
+    return TKG_ERR_NULL;
+  if (!aligned16(C) || (K > 0 && (!aligned16(A) || !aligned16(B))))
+    return TKG_ERR_ALIGN;
+  Plan pl;
+  st = make_plan(M, N, opts, &pl);
+  if (st != TKG_OK) return st;
+  tkg::DenseArgs a;
+  a.A = static_cast<const uint8_t*>(A);
+  a.B = static_cast<const uint8_t*>(B);
+  a.C = static_cast<uint16_t*>(C);
+  a.M = (int32_t)M;
+  a.N = (int32_t)N;
+  a.kbytes = (uint32_t)(K * eb);
+  const uint32_t sk = tkg::dense_stage_kbytes();
+  a.nk = (a.kbytes + sk - 1) / sk;
+  a.scale = scale;
+  a.tiles_m = pl.tiles_m;
+  a.tiles_n = pl.tiles_n;
+  a.num_tiles = pl.num_tiles;
+  a.group_m = pl.group_m;
+  a.xcd_remap = pl.xcd_remap;
+  if (K == 0) {  // empty reduction: the kernel's zero accumulators are C
+    a.A = a.B = static_cast<const uint8_t*>(C);
+  }
+  const hipError_t e =
+      tkg::launch_dense(dt, a, pl.grid, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TKG_OK : TKG_ERR_LAUNCH;
+}
+
+int run_fp4(int64_t M, int64_t N, int64_t K, const void* A, const void* As,
+            float sa, const void* B, const void* Bs, float sb, void* C,
+            void* stream, const tkg_opts* opts) {
+  int st = check_common(M, N, K, 64, 16777215);
+  if (st != TKG_OK) return st;
+  if (M == 0 || N == 0) return TKG_OK;
+  if (C == nullptr ||
+      (K > 0 && (A == nullptr || B == nullptr || As == nullptr || Bs == nullptr)))
+    return TKG_ERR_NULL;
+  if (!aligned16(C) || (K > 0 && (!aligned16(A) || !aligned16(B) ||
+                                  !aligned16(As) || !aligned16(Bs))))
+    return TKG_ERR_ALIGN;
+  Plan pl;
+  st = make_plan(M, N, opts, &pl);
+  if (st != TKG_OK) return st;
+  tkg::Fp4Args a;
+  a.A = static_cast<const uint8_t*>(A);
+  a.As = static_cast<const uint8_t*>(As);
+  a.B = static_cast<const uint8_t*>(B);
+  a.Bs = static_cast<const uint8_t*>(Bs);
+  a.C = static_cast<uint16_t*>(C);
+  a.M = (int32_t)M;
+  a.N = (int32_t)N;
+  a.vbytes = (uint32_t)(K / 2);
+  a.sbytes = (uint32_t)(K / 16);
+  const uint32_t sk = tkg::fp4_stage_vbytes();
+  a.nk = (a.vbytes + sk - 1) / sk;
+  a.scale = sa * sb;
+  a.tiles_m = pl.tiles_m;
+  a.tiles_n = pl.tiles_n;
+  a.num_tiles = pl.num_tiles;
+  a.group_m = pl.group_m;
+  a.xcd_remap = pl.xcd_remap;
+  if (K == 0) {
+    a.A = a.B = a.As = a.Bs = static_cast<const uint8_t*>(C);
+  }
+  const hipError_t e = tkg::launch_fp4(a, pl.grid, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TKG_OK : TKG_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
+              void* C, void* stream) {
+  return run_dense(tkg::kBf16, M, N, K, A, B, C, 1.0f, stream, nullptr);
+}
+
+int gemm_fp8(int64_t M, int64_t N, int64_t K, const void* A, float scale_a,
+             const void* B, float scale_b, void* C, void* stream) {
+  return run_dense(tkg::kFp8, M, N, K, A, B, C, scale_a * scale_b, stream,
+                   nullptr);
+}
+
+int gemm_fp4_blockscaled(int64_t M, int64_t N, int64_t K, const void* A,
+                         const void* A_scales, float a_scale, const void* B,
+                         const void* B_scales, float b_scale, void* C,
+                         void* stream) {
+  return run_fp4(M, N, K, A, A_scales, a_scale, B, B_scales, b_scale, C,
+                 stream, nullptr);
+}
+
+int tkg_gemm_ex(int dtype, int64_t M, int64_t N, int64_t K, const void* A,
+                const void* A_scales, float a_scale, const void* B,
+                const void* B_scales, float b_scale, void* C, void* stream,
+                const tkg_opts* opts) {
+  switch (dtype) {
+    case TKG_DTYPE_BF16:
+      return run_dense(tkg::kBf16, M, N, K, A, B, C, 1.0f, stream, opts);
+    case TKG_DTYPE_FP8:
+      return run_dense(tkg::kFp8, M, N, K, A, B, C, a_scale * b_scale, stream,
+                       opts);
+    case TKG_DTYPE_FP4_BLOCKSCALED:
+      return run_fp4(M, N, K, A, A_scales, a_scale, B, B_scales, b_scale, C,
+                     stream, opts);
+    default:
+      return TKG_ERR_SHAPE;
+  }
+}
+
+const char* tkg_status_string(int status) {
+  switch (status) {
+    case TKG_OK: return "TKG_OK: success";
+    case TKG_ERR_NULL: return "TKG_ERR_NULL: a required pointer is NULL";
+    case TKG_ERR_SHAPE: return "TKG_ERR_SHAPE: unsupported or invalid shape";
+    case TKG_ERR_ALIGN: return "TKG_ERR_ALIGN: pointer not 16-byte aligned";
+    case TKG_ERR_LAUNCH: return "TKG_ERR_LAUNCH: kernel launch failed";
+    case TKG_ERR_DEVICE: return "TKG_ERR_DEVICE: no usable HIP device";
+    default: return "unknown tkg status";
+  }
+}
+
+int tkg_lds_row_bytes(int dtype) {
+  switch (dtype) {
+    case TKG_DTYPE_BF16:
+    case TKG_DTYPE_FP8: return (int)tkg::dense_stage_kbytes();
+    case TKG_DTYPE_FP4_BLOCKSCALED: return (int)tkg::fp4_stage_vbytes();
+    default: return TKG_ERR_SHAPE;
+  }
+}
+
+int tkg_lds_fragment_offsets(int dtype, int step, int part, int frag,
+                             uint32_t* out64) {
+  if (out64 == nullptr) return TKG_ERR_NULL;
+  const int rb = tkg_lds_row_bytes(dtype);
+  if (rb < 0) return rb;
+  // k-steps per stage and 16-byte chunks read per lane per k-step
+  int steps, parts;
+  if (dtype == TKG_DTYPE_BF16) { steps = rb / 32; parts = 1; }       // 16 k x 2 B
+  else if (dtype == TKG_DTYPE_FP8) { steps = rb / 64; parts = 2; }   // 64 k x 1 B
+  else { steps = rb / 32; parts = 1; }  // 4-bit: one 16-byte chunk per lane
+  if (step < 0 || step >= steps || part < 0 || part >= parts || frag < 0 ||
+      frag >= kBM / 32)
+    return TKG_ERR_SHAPE;
+  for (uint32_t lane = 0; lane < 64; ++lane) {
+    const uint32_t row = (uint32_t)frag * 32u + (lane & 31u);
+    const uint32_t half = lane >> 5;
+    const uint32_t chunk = (uint32_t)(step * 2 * parts) + half * parts + (uint32_t)part;
+    out64[lane] = tkg::swz_offset((uint32_t)rb, row, chunk);
+  }
+  return steps;
+}
+
+}  // extern "C"

@@ -1,0 +1,110 @@
+// Device-side building blocks for the gfx950 GEMM kernels: vector types,
+// buffer resources for bounds-checked global->LDS staging, explicit wait
+// counters, and the MFMA instructions the 16x16-based tile grid is built of.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define TKG_LDS __attribute__((address_space(3)))
+
+namespace tkg {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Offset that lies outside every resource this library builds (their
+// num_records never exceeds 2^31 - 1): a load there returns zeros.
+constexpr uint32_t kOobOffset = 0x80000000u;
+
+// Raw buffer resource over [base, base + nbytes): loads past nbytes return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
+                                                            uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)nbytes, 0x00020000);
+}
+
+// 16 bytes per lane straight from global memory into LDS: the wave writes
+// 1 KiB at `lds` (wave-uniform), lane l at byte 16*l.
+__device__ __forceinline__ void dma_b128(__amdgpu_buffer_rsrc_t r,
+                                         TKG_LDS void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, 0, 0, 0);
+}
+// 4 bytes per lane: the wave writes 256 bytes at `lds`, lane l at byte 4*l.
+__device__ __forceinline__ void dma_b32(__amdgpu_buffer_rsrc_t r,
+                                        TKG_LDS void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 4, voff, 0, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) |
+                             (0xF << 8));
+}
+
+template <typename T>
+__device__ __forceinline__ T lds_read(const TKG_LDS uint8_t* base,
+                                      uint32_t off) {
+  return *reinterpret_cast<const TKG_LDS T*>(base + off);
+}
+
+// D(32x32, fp32) += A(32x16, bf16) * B(16x32, bf16). Lane l supplies row
+// l%32 of A and column l%32 of B, 8 consecutive k each (k-half l/32); it
+// receives column l%32 of D, rows 8*(r/4) + 4*(l/32) + r%4 in element r.
+__device__ __forceinline__ f32x16_t mfma_bf16(bf16x8_t a, bf16x8_t b,
+                                              f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// D(32x32, fp32) += A(32x64, OCP e4m3) * B(64x32, OCP e4m3); 32 k per lane.
+__device__ __forceinline__ f32x16_t mfma_fp8(i32x8_t a, i32x8_t b,
+                                             f32x16_t c) {
+  // format 0 = fp8 e4m3 for both operands, no block scaling
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0,
+                                                         0, 0);
+}
+
+// Four fp32 -> four bf16 (round to nearest even), packed in 8 bytes.
+__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c,
+                                             float d) {
+  bf16x2_t lo = {(__bf16)a, (__bf16)b};
+  bf16x2_t hi = {(__bf16)c, (__bf16)d};
+  uint2 r;
+  r.x = __builtin_bit_cast(uint32_t, lo);
+  r.y = __builtin_bit_cast(uint32_t, hi);
+  return r;
+}
+
+// Persistent-grid tile order. Workgroups are dispatched round-robin over the
+// 8 XCDs (workgroup w runs on XCD w % 8), each XCD with its own L2. The
+// virtual id gives every XCD a contiguous range of G/8 ids, so the tiles an
+// XCD runs at the same time are neighbours in the grouped order below and
+// share operand panels in that XCD's L2.
+__device__ __forceinline__ int xcd_virtual_id(int w, int G, int remap) {
+  return (remap && G % 8 == 0) ? (w % 8) * (G / 8) + (w / 8) : w;
+}
+
+// Grouped order: tiles are walked in bands of `group_m` tile rows; inside a
+// band, column by column. Consecutive tiles then reuse the same few A row
+// panels and B column panels (the pages' {8, N, M/8} block order).
+__device__ __forceinline__ void grouped_tile(int t, int tiles_m, int tiles_n,
+                                             int group_m, int& pm, int& pn) {
+  const int per_group = group_m * tiles_n;
+  const int g = t / per_group;
+  const int first = g * group_m;
+  const int rows = min(tiles_m - first, group_m);
+  const int r = t - g * per_group;
+  pm = first + r % rows;
+  pn = r / rows;
+}
+
+}  // namespace tkg

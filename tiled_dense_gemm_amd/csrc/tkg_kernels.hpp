@@ -1,0 +1,55 @@
+// Launch interface between the C-ABI entry points and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tkg {
+
+enum DenseType { kBf16 = 0, kFp8 = 1 };
+
+// One dense problem: C (M x N, bf16, row-major) = scale * A (M x K) * B,
+// with A row-major and B given as an N x K row-major array; both operands
+// hold `kbytes` bytes per row.
+struct DenseArgs {
+  const uint8_t* A;
+  const uint8_t* B;
+  uint16_t* C;
+  int32_t M, N;
+  uint32_t kbytes;  // bytes of K per operand row
+  uint32_t nk;      // number of K steps of the staging ring
+  float scale;
+  int32_t tiles_m, tiles_n, num_tiles, group_m;
+  int32_t xcd_remap;  // 1: give each XCD a contiguous range of tiles
+};
+
+// Block-scaled 4-bit problem: values packed two per byte (K/2 bytes per row)
+// and one e4m3 scale per 16 K-elements (K/16 bytes per row).
+struct Fp4Args {
+  const uint8_t* A;
+  const uint8_t* As;
+  const uint8_t* B;
+  const uint8_t* Bs;
+  uint16_t* C;
+  int32_t M, N;
+  uint32_t vbytes;  // K/2
+  uint32_t sbytes;  // K/16
+  uint32_t nk;
+  float scale;
+  int32_t tiles_m, tiles_n, num_tiles, group_m;
+  int32_t xcd_remap;
+};
+
+// Tile shape shared by the kernels and the host-side argument checks.
+constexpr int kBM = 256;
+constexpr int kBN = 256;
+constexpr int kThreads = 256;
+
+hipError_t launch_dense(DenseType dt, const DenseArgs& a, int grid,
+                        hipStream_t stream);
+hipError_t launch_fp4(const Fp4Args& a, int grid, hipStream_t stream);
+
+// K bytes per stage row of each kernel family (for the host).
+uint32_t dense_stage_kbytes();
+uint32_t fp4_stage_vbytes();
+
+}  // namespace tkg

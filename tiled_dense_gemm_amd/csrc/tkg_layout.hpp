@@ -1,0 +1,64 @@
+// LDS layout of the staged operand tiles: the XOR swizzle and the byte
+// offsets every lane reads. Host- and device-side (constexpr), so the host
+// library can report the exact addresses the kernels use.
+//
+// The pages' swizzle (page "ThunderKittens: Simple, Fast, and Adorable AI
+// Kernels", section 3.4, "Shared Memory Tiles: Automated Swizzling to
+// Eliminate Bank Conflicts"; page "ThunderKittens: 16x16 Tiles, ...",
+// section "Warp level: tiles are the only data structure") XORs the 16-byte
+// chunk index of an address with bits of its row so that the rows a tensor
+// core load touches together land in different banks. The same idea is
+// re-derived here for how a gfx950 wave reads LDS:
+//
+// * An operand tile is stored row by row, one row per M (or N) index, with
+//   ROW_BYTES bytes of K per row (both A and the column-major B are
+//   K-contiguous). A row holds ROW_BYTES / 16 chunks of 16 bytes.
+// * A fragment read is ds_read_b128: lane l reads 16 bytes of row
+//   (l mod 32) at one chunk, lanes 32..63 at another chunk.
+// * Whether LDS serves a b128 read in phases of 8 lanes over 32 banks or of
+//   16 lanes over 64 banks, the rows read in one phase must map their chunk
+//   onto distinct 16-byte bank groups. The permutation below satisfies both
+//   geometries (proved by the CPU bank model in lds_bank_model.py and
+//   checked with the SQ_LDS_BANK_CONFLICT counter).
+//
+// For 128-byte rows (8 chunks): chunk' = chunk ^ ((r & 7) ^ ((r >> 3) & 1))
+// For  64-byte rows (4 chunks): chunk' = chunk ^ (((r >> 1) ^ (r >> 3)) & 3)
+#pragma once
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define TKG_HD __host__ __device__
+#else
+#define TKG_HD
+#endif
+
+namespace tkg {
+
+// XOR mask applied to the chunk index of row `r` in a tile whose rows are
+// `row_bytes` long (64 or 128).
+TKG_HD constexpr uint32_t swz_mask(uint32_t row_bytes, uint32_t r) {
+  return row_bytes == 128 ? ((r & 7u) ^ ((r >> 3) & 1u))
+                          : (((r >> 1) ^ (r >> 3)) & 3u);
+}
+
+// Byte offset, inside a tile of `row_bytes`-long rows, of logical chunk
+// `chunk` (16 bytes) of row `r`.
+TKG_HD constexpr uint32_t swz_offset(uint32_t row_bytes, uint32_t r,
+                                     uint32_t chunk) {
+  return r * row_bytes + ((chunk ^ swz_mask(row_bytes, r)) << 4);
+}
+
+// Direct global->LDS staging: one wave instruction writes 1 KiB of LDS, lane
+// l at byte 16*l. Writing in storage order means lane l fills physical chunk
+// slot (l mod S) of row (l / S), S = row_bytes/16; it must therefore fetch
+// the logical chunk that the swizzle stores there (XOR is an involution).
+TKG_HD constexpr uint32_t dma_row(uint32_t row_bytes, uint32_t instr,
+                                  uint32_t lane) {
+  return instr * (1024u / row_bytes) + lane / (row_bytes / 16u);
+}
+TKG_HD constexpr uint32_t dma_chunk(uint32_t row_bytes, uint32_t instr,
+                                    uint32_t lane) {
+  return (lane % (row_bytes / 16u)) ^ swz_mask(row_bytes, dma_row(row_bytes, instr, lane));
+}
+
+}  // namespace tkg
