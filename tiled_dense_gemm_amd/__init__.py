@@ -43,6 +43,13 @@ class TkgOpts(ctypes.Structure):
 
 
 def _load() -> ctypes.CDLL:
+    # torch ships its own HIP runtime (same soname as ROCm's). Loading torch
+    # first makes libtkg bind to that one, so the library and torch share
+    # one runtime (devices, streams, memory) in the process.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             "libtkg.so is not built (%s); run `python -m "
