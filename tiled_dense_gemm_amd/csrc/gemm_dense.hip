@@ -12,11 +12,12 @@
 //   operands are K-contiguous, the layout the matrix cores take.
 // * Load-compute-store-finish (page 2, section 3.4 "The LCSF Template" and
 //   "Multi-Stage Buffer: The Pipeline Depth Parameter", Table 1): every wave
-//   streams its share of the next K step straight from global memory into a
-//   ring of LDS stages while all waves run MFMAs on the current stage;
-//   s_waitcnt + s_barrier play the part of arrive/expect. The finish step
-//   converts the fp32 accumulators (times the fp8 scale) to bf16 and stores
-//   them while the next tile's first stage is already loading.
+//   streams its share of a K step straight from global memory into a ring of
+//   STAGES LDS buffers, STAGES - 1 steps ahead of the MFMAs; s_waitcnt +
+//   s_barrier play the part of arrive/expect. The loads of a step are issued
+//   between the MFMAs of the current one. The finish step converts the fp32
+//   accumulators (times the fp8 scale) to bf16 and stores them while the
+//   next tile's first stages are already loading.
 // * Swizzled LDS (page 2, section 3.4 "Shared Memory Tiles: Automated
 //   Swizzling to Eliminate Bank Conflicts"): see tkg_layout.hpp.
 // * Persistent grid and block order (page 2, section 3.4 "Persistent Grid
@@ -24,7 +25,8 @@
 //   one workgroup per CU loops over output tiles in grouped order, with the
 //   workgroup id remapped so each XCD works on neighbouring tiles.
 //
-// A stage holds 128 bytes of K per row: 64 bf16 or 128 fp8 elements.
+// A stage holds 64 bytes of K per row: 32 bf16 (two 32x32x16 MFMA k-steps)
+// or 64 fp8 (one 32x32x64 k-step).
 #include "tkg_device.hpp"
 #include "tkg_kernels.hpp"
 #include "tkg_layout.hpp"
@@ -35,17 +37,15 @@ namespace tkg {
 namespace {
 
 constexpr int BM = kBM, BN = kBN;
-constexpr int BKB = 128;                 // K bytes per row per stage
-constexpr int STAGES = 2;
-constexpr int TILE_A = BM * BKB;         // 32 KiB
-constexpr int TILE_B = BN * BKB;         // 32 KiB
-constexpr int STAGE_BYTES = TILE_A + TILE_B;
+constexpr int BKB = 64;                  // K bytes per row per stage
+constexpr int TILE = BM * BKB;           // 16 KiB per operand per stage
+constexpr int STAGE_BYTES = 2 * TILE;    // A then B
 constexpr int WAVES = kThreads / 64;     // 4, as 2 x 2
 constexpr int WM = 128, WN = 128;        // wave tile
 constexpr int FM = WM / 32, FN = WN / 32;  // 32x32 accumulators per wave
-constexpr int DMA_PER_WAVE = TILE_A / 1024 / WAVES;  // 8 KiB per wave per operand
-
-static_assert(TILE_A == TILE_B, "A and B stage tiles share offsets");
+constexpr int DMA = TILE / 1024 / WAVES;   // b128 loads per wave per operand
+constexpr int STAGES = 5;
+static_assert(BM == BN, "A and B stage tiles share offsets");
 static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS budget");
 
 struct TileState {
@@ -80,6 +80,10 @@ void gemm_dense_kernel(DenseArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[STAGES * STAGE_BYTES];
   TKG_LDS uint8_t* smem = (TKG_LDS uint8_t*)smem_raw;
 
+  // MFMA k-steps per stage and 16-byte reads per operand fragment
+  constexpr int KSTEPS = (DT == kBf16) ? 2 : 1;
+  constexpr int PARTS = (DT == kBf16) ? 1 : 2;
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -88,84 +92,94 @@ void gemm_dense_kernel(DenseArgs p) {
   int t = xcd_virtual_id(blockIdx.x, G, p.xcd_remap);
   if (t >= p.num_tiles) return;
 
+  // Number of K stages per tile. fp8 walks two stages per loop trip, so its
+  // count is rounded up to even; the extra stage reads zeros.
+  const uint32_t nk = (KSTEPS == 1) ? (p.nk + (p.nk & 1)) : p.nk;
+
   // ---- per-lane staging offsets (tile independent) -----------------------
-  // DMA instruction i of this wave fills stage rows dma_row(q), q = wave*8+i.
-  uint32_t dma_off[DMA_PER_WAVE];
-  uint32_t dma_kb[2];  // chunk byte offset for even / odd q (row bit 3)
+  // DMA instruction i of this wave fills rows dma_row(q), q = wave*DMA + i;
+  // with 64-byte rows the fetched chunk depends on the lane only.
+  uint32_t dma_off[DMA];
 #pragma unroll
-  for (int i = 0; i < DMA_PER_WAVE; ++i) {
-    const uint32_t q = wave * DMA_PER_WAVE + i;
-    const uint32_t row = dma_row(BKB, q, lane);
-    const uint32_t chunk = dma_chunk(BKB, q, lane);
-    dma_off[i] = row * p.kbytes + chunk * 16u;
-    if (i < 2) dma_kb[i] = chunk * 16u;
+  for (int i = 0; i < DMA; ++i) {
+    const uint32_t q = wave * DMA + i;
+    dma_off[i] = dma_row(BKB, q, lane) * p.kbytes + dma_chunk(BKB, q, lane) * 16u;
   }
+  const uint32_t dma_kb = dma_chunk(BKB, wave * DMA, lane) * 16u;
 
   // ---- per-lane fragment read offsets ------------------------------------
-  // Rows of the wave's fragments are (multiple of 32) + lane%32, so their
-  // swizzle mask depends on lane%16 only.
+  // Fragment rows are (multiple of 32) + lane%32, so the swizzle mask only
+  // depends on the lane. k-step s of a stage reads chunk 2s + lane/32 (bf16)
+  // or chunks 2*(lane/32) and 2*(lane/32) + 1 (fp8): the same K order for A
+  // and B, so the MFMA reduces over matching elements.
   const uint32_t frow = lane & 31;
   const uint32_t khalf = lane >> 5;
-  constexpr int SUBS = (DT == kBf16) ? 4 : 2;  // MFMA k-steps per stage
-  uint32_t roff[SUBS][DT == kBf16 ? 1 : 2];
+  uint32_t roff[KSTEPS][PARTS];
 #pragma unroll
-  for (int s = 0; s < SUBS; ++s) {
-    if (DT == kBf16) {
-      roff[s][0] = swz_offset(BKB, frow, 2 * s + khalf);
-    } else {
-      roff[s][0] = swz_offset(BKB, frow, 4 * s + 2 * khalf);
-      roff[s][DT == kBf16 ? 0 : 1] = swz_offset(BKB, frow, 4 * s + 2 * khalf + 1);
-    }
-  }
-  const uint32_t a_base = wm * WM * BKB;           // within the A tile
-  const uint32_t b_base = TILE_A + wn * WN * BKB;  // within the stage
+  for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+    for (int q = 0; q < PARTS; ++q)
+      roff[s][q] = swz_offset(BKB, frow, (DT == kBf16) ? 2 * s + khalf : 2 * khalf + q);
+  const uint32_t a_base = wm * WM * BKB;
+  const uint32_t b_base = TILE + wn * WN * BKB;
 
-  auto issue = [&](const TileState& ts, uint32_t kt, int buf) {
-    const uint32_t k0 = kt * BKB;
-    const bool full = k0 + BKB <= p.kbytes;
+  // ---- load cursor: (tile lt, stage lkt), STAGES stages ahead -------------
+  TileState cur = tile_state(p, t);
+  TileState lts = cur;
+  int lt = t;
+  uint32_t lkt = 0;
+  auto advance_load = [&]() {
+    if (++lkt == nk) {
+      lkt = 0;
+      lt += G;
+      lts = tile_state(p, lt);
+    }
+  };
+  // Loads of stage (lts, lkt) into buffer `buf`; stages past K read zeros.
+  auto issue = [&](int buf) {
+    const uint32_t k0 = lkt * BKB;
     TKG_LDS uint8_t* st = smem + buf * STAGE_BYTES;
+    const bool kok = k0 + dma_kb < p.kbytes;  // this lane's chunk exists
 #pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i) {
-      uint32_t off = dma_off[i] + k0;
-      if (!full && k0 + dma_kb[i & 1] >= p.kbytes) off = kOobOffset;
-      const uint32_t q = wave * DMA_PER_WAVE + i;
-      dma_b128(ts.ra, st + q * 1024, off);
-      dma_b128(ts.rb, st + TILE_A + q * 1024, off);
+    for (int i = 0; i < DMA; ++i) {
+      const uint32_t off = kok ? dma_off[i] + k0 : kOobOffset;
+      const uint32_t q = wave * DMA + i;
+      dma_b128(lts.ra, st + q * 1024, off);
+      dma_b128(lts.rb, st + TILE + q * 1024, off);
     }
   };
 
-  // Operand fragments of one MFMA k-step: FM rows of A and FN rows of B
-  // (32 rows each). Two sets: the step being multiplied and the next one.
   using Frag = typename std::conditional<DT == kBf16, bf16x8_t, i32x8_t>::type;
   Frag fa[2][FM], fb[2][FN];
   auto read_frags = [&](int buf, int s, Frag (&a)[FM], Frag (&b)[FN]) {
     const TKG_LDS uint8_t* st = smem + buf * STAGE_BYTES;
-    if constexpr (DT == kBf16) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
+      if constexpr (DT == kBf16) {
         a[i] = lds_read<bf16x8_t>(st, a_base + i * 32 * BKB + roff[s][0]);
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        b[j] = lds_read<bf16x8_t>(st, b_base + j * 32 * BKB + roff[s][0]);
-    } else {
-      constexpr int H = DT == kBf16 ? 0 : 1;
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
+      } else {
         const i32x4_t lo = lds_read<i32x4_t>(st, a_base + i * 32 * BKB + roff[s][0]);
-        const i32x4_t hi = lds_read<i32x4_t>(st, a_base + i * 32 * BKB + roff[s][H]);
+        const i32x4_t hi = lds_read<i32x4_t>(st, a_base + i * 32 * BKB + roff[s][PARTS - 1]);
         a[i] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
+    }
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
+    for (int j = 0; j < FN; ++j) {
+      if constexpr (DT == kBf16) {
+        b[j] = lds_read<bf16x8_t>(st, b_base + j * 32 * BKB + roff[s][0]);
+      } else {
         const i32x4_t lo = lds_read<i32x4_t>(st, b_base + j * 32 * BKB + roff[s][0]);
-        const i32x4_t hi = lds_read<i32x4_t>(st, b_base + j * 32 * BKB + roff[s][H]);
+        const i32x4_t hi = lds_read<i32x4_t>(st, b_base + j * 32 * BKB + roff[s][PARTS - 1]);
         b[j] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
     }
   };
 
-  constexpr int LDS_READS = (DT == kBf16) ? 1 : 2;  // ds_read_b128 per fragment
   f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
   auto mma_step = [&](const Frag (&a)[FM], const Frag (&b)[FN]) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -179,73 +193,65 @@ void gemm_dense_kernel(DenseArgs p) {
       }
   };
 
+  // ---- prologue: the first STAGES stages in flight ------------------------
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
-
-  // ---- prologue: stages for the first two K steps in flight --------------
-  // The load cursor (lt, lkt) walks the same (tile, K step) sequence as the
-  // computation, two steps ahead; past the end it loads zeros from an empty
-  // resource, which keeps the main loop free of branches.
-  TileState cur = tile_state(p, t);
-  TileState lts = cur;
-  int lt = t;
-  uint32_t lkt = 0;
-  auto advance_load = [&]() {
-    if (++lkt == p.nk) {
-      lkt = 0;
-      lt += G;
-      lts = tile_state(p, lt);
-    }
-  };
-  issue(lts, lkt, 0);
-  advance_load();
-  issue(lts, lkt, 1);
-  advance_load();
-  wait_vmcnt<2 * DMA_PER_WAVE>();  // the first stage has landed
+  for (int b = 0; b < STAGES; ++b) {
+    issue(b);
+    advance_load();
+  }
+  wait_vmcnt<(STAGES - 1) * 2 * DMA>();  // stage 0 has landed
   __syncthreads();
   read_frags(0, 0, fa[0], fb[0]);
 
+  // One MFMA k-step. Register set c holds its fragments; the next k-step's
+  // fragments go to set c ^ 1. At the last k-step of a stage the next stage
+  // must have landed (wait + barrier); after the barrier every wave has read
+  // the current stage, so its buffer is refilled STAGES stages ahead.
   int buf = 0;
-  for (;;) {
-    for (uint32_t kt = 0; kt < p.nk; ++kt) {
+  bool fresh_tile = false;  // finish stores are in flight
+  auto kstep = [&](int c, int s, bool last) {
+    if (!last) {
+      read_frags(buf, s + 1, fa[c ^ 1], fb[c ^ 1]);
+      mma_step(fa[c], fb[c]);
 #pragma unroll
-      for (int s = 0; s < SUBS; ++s) {
-        const int c = s & 1;
-        if (s + 1 < SUBS) {
-          // fragments of the next k-step interleaved with this one's MFMAs
-          read_frags(buf, s + 1, fa[c ^ 1], fb[c ^ 1]);
-          mma_step(fa[c], fb[c]);
-#pragma unroll
-          for (int q = 0; q < FM + FN; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, LDS_READS, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
-          __builtin_amdgcn_sched_barrier(0);
-        } else {
-          // Stage boundary. After the wait and the barrier every wave holds
-          // the last fragments of stage `buf` in registers and the next
-          // stage has landed: refill `buf` two K steps ahead (load), read
-          // the next stage (compute) and multiply the last k-step.
-          wait_vmcnt<0>();
-          __syncthreads();
-          issue(lts, lkt, buf);
-          advance_load();
-          read_frags(buf ^ 1, 0, fa[c ^ 1], fb[c ^ 1]);
-          mma_step(fa[c], fb[c]);
-#pragma unroll
-          for (int q = 0; q < FM + FN; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // DMA
-            __builtin_amdgcn_sched_group_barrier(0x100, LDS_READS, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+      for (int q = 0; q < FM + FN; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, PARTS, 0);      // ds_read
       }
-      buf ^= 1;
+      __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      if (fresh_tile) wait_vmcnt<0>();
+      else wait_vmcnt<(STAGES - 2) * 2 * DMA>();
+      fresh_tile = false;
+      lds_barrier();
+      issue(buf);
+      const int nbuf = (buf + 1 == STAGES) ? 0 : buf + 1;
+      read_frags(nbuf, 0, fa[c ^ 1], fb[c ^ 1]);
+      mma_step(fa[c], fb[c]);
+#pragma unroll
+      for (int q = 0; q < FM + FN; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);          // DMA
+        __builtin_amdgcn_sched_group_barrier(0x100, PARTS, 0);      // ds_read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+      __builtin_amdgcn_sched_barrier(0);
+      buf = nbuf;
+      advance_load();
+    }
+  };
+
+  for (;;) {
+    // two k-steps per trip: one bf16 stage, or two fp8 stages
+    for (uint32_t kt = 0; kt < nk; kt += 2 / KSTEPS) {
+      if constexpr (KSTEPS == 2) {
+        kstep(0, 0, false);
+        kstep(1, 1, true);
+      } else {
+        kstep(0, 0, true);
+        kstep(1, 0, true);
+      }
     }
 
     // ---- finish: C[m][n .. n+3] from accumulator rows 4g .. 4g+3 ----------
@@ -284,6 +290,7 @@ void gemm_dense_kernel(DenseArgs p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    fresh_tile = true;
 
     t += G;
     if (t >= p.num_tiles) break;

@@ -269,6 +269,7 @@ void gemm_fp4_kernel(Fp4Args p) {
   read_raw(0, 0, raw[0]);
 
   int buf = 0;
+  bool fresh_tile = false;  // finish stores are in flight
   for (;;) {
     for (uint32_t kt = 0; kt < p.nk; ++kt) {
       // chunk s = 0 of this stage is in raw[0]; fetch chunk 1, multiply 0
@@ -276,8 +277,11 @@ void gemm_fp4_kernel(Fp4Args p) {
       mma_chunk(raw[0]);
       __builtin_amdgcn_sched_barrier(0);
       // stage boundary: the next stage must have landed; this one is free
-      wait_vmcnt<(STAGES - 2) * DMA_PER_STAGE>();
-      __syncthreads();
+      // (right after a finish, its stores are in flight too: wait for all)
+      if (fresh_tile) wait_vmcnt<0>();
+      else wait_vmcnt<(STAGES - 2) * DMA_PER_STAGE>();
+      fresh_tile = false;
+      lds_barrier();
       issue(lts, lkt, buf);
       advance_load();
       const int nbuf = (buf + 1 == STAGES) ? 0 : buf + 1;
@@ -318,6 +322,7 @@ void gemm_fp4_kernel(Fp4Args p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    fresh_tile = true;
 
     t += G;
     if (t >= p.num_tiles) break;

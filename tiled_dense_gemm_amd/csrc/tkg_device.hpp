@@ -51,6 +51,15 @@ __device__ __forceinline__ void wait_vmcnt() {
                              (0xF << 8));
 }
 
+// Workgroup barrier for the LDS ring: waits for this wave's own LDS reads,
+// then s_barrier. Unlike __syncthreads() it does not wait for outstanding
+// global loads (that fence would drain the whole ring at every stage); the
+// caller waits with wait_vmcnt for exactly the stage it needs. The asm
+// clobber keeps memory operations from moving across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <typename T>
 __device__ __forceinline__ T lds_read(const TKG_LDS uint8_t* base,
                                       uint32_t off) {
