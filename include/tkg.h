@@ -119,6 +119,13 @@ const char *tkg_status_string(int status);
  *   xcd_remap -- 1 (default when grid is a multiple of 8) gives each XCD a
  *               contiguous range of tiles; 0 leaves the hardware's
  *               round-robin order.
+ *   variant  -- bf16/fp8 only: kernel configuration, as (K bytes per row
+ *               of an LDS slab, operand slabs in the LDS ring, waves per
+ *               workgroup): 0 = (128, 4, 8) default, 1 = (128, 5, 8),
+ *               2 = (64, 10, 8), 3 = (128, 5, 4), 4 = (128, 4, 4),
+ *               5 = (64, 10, 4), 6 = (64, 8, 4); TKG_ERR_SHAPE outside
+ *               0..6. Must be 0 for the 4-bit product. Every variant
+ *               computes the same result.
  * Page "ThunderKittens: Simple, Fast, and Adorable AI Kernels", section
  * 3.4, "Persistent Grid Launch" (Table 2) and "Block Launch Order and L2
  * Cache Reuse" (Table 3), measure these choices.
@@ -127,7 +134,7 @@ typedef struct tkg_opts {
   int32_t grid;
   int32_t group_m;
   int32_t xcd_remap;
-  int32_t reserved;
+  int32_t variant;
 } tkg_opts;
 
 enum { TKG_DTYPE_BF16 = 0, TKG_DTYPE_FP8 = 1, TKG_DTYPE_FP4_BLOCKSCALED = 2 };

@@ -171,6 +171,36 @@ def test_bf16_launch_options_agree(dev):
         assert torch.equal(C.view(torch.int16), ref.view(torch.int16)), (grid, gm, xr)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_kernel_variants_agree(dev, dtype):
+    # every compiled kernel configuration (LDS ring shape, waves per
+    # workgroup) computes the same bits, including ragged edges
+    M, N, K = 1300, 700, 1088
+    if dtype == "bf16":
+        A = gi.device.bf16_operand(3, M, K, std=K ** -0.5, device=dev)
+        Bt = gi.device.bf16_operand(4, N, K, std=K ** -0.5, device=dev)
+        d, sa, sb = tkg.DTYPE_BF16, 1.0, 1.0
+    else:
+        A, sa = gi.device.fp8_operand(3, M, K, device=dev)
+        Bt, sb = gi.device.fp8_operand(4, N, K, device=dev)
+        d = tkg.DTYPE_FP8
+    outs = []
+    for v in range(7):
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        assert tkg.tkg_gemm_ex(d, M, N, K, A, None, sa, Bt, None, sb, C, variant=v) == 0
+        outs.append(C)
+    for v in range(1, 7):
+        assert torch.equal(outs[v].view(torch.int16), outs[0].view(torch.int16)), v
+    a = A.view(torch.int16).cpu().numpy().view(np.uint16) if dtype == "bf16" else to_numpy_u8(A)
+    b = Bt.view(torch.int16).cpu().numpy().view(np.uint16) if dtype == "bf16" else to_numpy_u8(Bt)
+    G = _bf16_result(outs[0])
+    if dtype == "bf16":
+        check_bf16(G, decode_bf16(a), decode_bf16(b), "variants")
+    else:
+        assert relfro(G, oracle.gemm_fp8(a, sa, b, sb)) <= LOWP_RELFRO
+    assert tkg.tkg_gemm_ex(d, M, N, K, A, None, sa, Bt, None, sb, outs[0], variant=7) == -2
+
+
 def test_bf16_side_stream(dev):
     M = N = K = 512
     A = gi.bf16_operand(1, M, K)

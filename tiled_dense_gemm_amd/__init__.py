@@ -39,7 +39,7 @@ class TkgError(RuntimeError):
 
 class TkgOpts(ctypes.Structure):
     _fields_ = [("grid", ctypes.c_int32), ("group_m", ctypes.c_int32),
-                ("xcd_remap", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("xcd_remap", ctypes.c_int32), ("variant", ctypes.c_int32)]
 
 
 def _load() -> ctypes.CDLL:
@@ -206,12 +206,12 @@ def gemm_fp4_blockscaled(A, A_scales, a_scale, Bt, B_scales, b_scale,
 
 
 def tkg_gemm_ex(dtype, M, N, K, A, A_scales, a_scale, Bt, B_scales, b_scale,
-                out, stream=None, grid=0, group_m=0, xcd_remap=1):
+                out, stream=None, grid=0, group_m=0, xcd_remap=1, variant=0):
     """Raw entry point with launch options (see tkg.h). Tensors or None for
     unused operands; returns the tkg status instead of raising."""
     torch = _torch()
     ptr = lambda t: None if t is None else t.data_ptr()
-    o = TkgOpts(int(grid), int(group_m), int(xcd_remap), 0)
+    o = TkgOpts(int(grid), int(group_m), int(xcd_remap), int(variant))
     with torch.cuda.device(out.device):
         return lib.tkg_gemm_ex(int(dtype), int(M), int(N), int(K), ptr(A),
                                ptr(A_scales), float(a_scale), ptr(Bt),

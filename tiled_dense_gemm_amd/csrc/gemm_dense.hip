@@ -6,16 +6,17 @@
 // * Tiles (page "ThunderKittens: 16x16 Tiles, ...", section "Warp level:
 //   tiles are the only data structure"; page "ThunderKittens: Simple, Fast,
 //   and Adorable AI Kernels", section 3.4 "The Warp-Level Tile
-//   Abstraction"): the 256x256 workgroup tile is a 2x2 grid of 128x128 wave
-//   tiles, each a 4x4 grid of 32x32 MFMA accumulators (2x2 blocks of the
-//   16x16 base tile). A is read row-major and B column-major, so both
+//   Abstraction"): the 256x256 workgroup tile is a 2x4 grid of 128x64 wave
+//   tiles (two waves per SIMD; a 2x2 grid of 128x128 tiles is the one-wave
+//   configuration), each a grid of 32x32 MFMA accumulators (2x2 blocks of
+//   the 16x16 base tile). A is read row-major and B column-major, so both
 //   operands are K-contiguous, the layout the matrix cores take.
 // * Load-compute-store-finish (page 2, section 3.4 "The LCSF Template" and
 //   "Multi-Stage Buffer: The Pipeline Depth Parameter", Table 1): every wave
 //   streams its share of a K step straight from global memory into a ring of
-//   STAGES LDS buffers, STAGES - 1 steps ahead of the MFMAs; s_waitcnt +
-//   s_barrier play the part of arrive/expect. The loads of a step are issued
-//   between the MFMAs of the current one. The finish step converts the fp32
+//   LDS slots (one operand slab each, see kRings), several K steps ahead of
+//   the MFMAs; s_waitcnt + s_barrier play the part of arrive/expect. The
+//   loads are issued between the MFMAs of the current K step. The finish step converts the fp32
 //   accumulators (times the fp8 scale) to bf16 and stores them while the
 //   next tile's first stages are already loading.
 // * Swizzled LDS (page 2, section 3.4 "Shared Memory Tiles: Automated
@@ -25,8 +26,8 @@
 //   one workgroup per CU loops over output tiles in grouped order, with the
 //   workgroup id remapped so each XCD works on neighbouring tiles.
 //
-// A stage holds 64 bytes of K per row: 32 bf16 (two 32x32x16 MFMA k-steps)
-// or 64 fp8 (one 32x32x64 k-step).
+// A K stage holds BKB bytes of K per row: BKB/2 bf16 (BKB/32 MFMA k-steps of
+// 32x32x16) or BKB fp8 (BKB/64 k-steps of 32x32x64).
 #include "tkg_device.hpp"
 #include "tkg_kernels.hpp"
 #include "tkg_layout.hpp"
@@ -37,16 +38,21 @@ namespace tkg {
 namespace {
 
 constexpr int BM = kBM, BN = kBN;
-constexpr int BKB = 64;                  // K bytes per row per stage
-constexpr int TILE = BM * BKB;           // 16 KiB per operand per stage
-constexpr int STAGE_BYTES = 2 * TILE;    // A then B
-constexpr int WAVES = kThreads / 64;     // 4, as 2 x 2
-constexpr int WM = 128, WN = 128;        // wave tile
-constexpr int FM = WM / 32, FN = WN / 32;  // 32x32 accumulators per wave
-constexpr int DMA = TILE / 1024 / WAVES;   // b128 loads per wave per operand
-constexpr int STAGES = 5;
-static_assert(BM == BN, "A and B stage tiles share offsets");
-static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS budget");
+static_assert(BM == BN, "A and B slabs share offsets");
+
+// Ring shapes. The LDS ring holds SLOTS operand slabs; a slab is one
+// operand's 256 rows x BKB bytes of K, and a K stage is an A slab and a B
+// slab. Slab j (stage j/2, operand j%2) lives in slot j % SLOTS, so an odd
+// slot count lets the loads of a stage's A slab start a stage earlier than
+// its B slab, keeping more bytes in flight than whole-stage buffers allow.
+// WAVES_N: the 2 x WAVES_N wave grid of the workgroup tile; 4 gives 8 waves
+// (two per SIMD) of 128 x 64 each, 2 gives 4 waves of 128 x 128.
+struct Ring {
+  int bkb, slots, waves_n;
+};
+constexpr Ring kRings[] = {{128, 4, 4}, {128, 5, 4}, {64, 10, 4}, {128, 5, 2},
+                           {128, 4, 2}, {64, 10, 2}, {64, 8, 2}};
+constexpr int kNumRings = sizeof(kRings) / sizeof(kRings[0]);
 
 struct TileState {
   int m0, n0;
@@ -74,44 +80,78 @@ __device__ __forceinline__ TileState tile_state(const DenseArgs& p, int t) {
   return s;
 }
 
-template <int DT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// Evenly spread `total` instructions over `slots` MFMA slots: the count
+// placed after MFMA number q.
+constexpr int spread(int total, int slots, int q) {
+  return (q + 1) * total / slots - q * total / slots;
+}
+
+// Scheduling recipe for one k-step: each MFMA followed by its share of the
+// slab loads (NDMA) and fragment reads (NREAD).
+template <int NMMA, int NDMA, int NREAD, int Q = 0>
+__device__ __forceinline__ void interleave() {
+  if constexpr (Q < NMMA) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    if constexpr (spread(NDMA, NMMA, Q) > 0)
+      __builtin_amdgcn_sched_group_barrier(0x020, spread(NDMA, NMMA, Q), 0);
+    if constexpr (spread(NREAD, NMMA, Q) > 0)
+      __builtin_amdgcn_sched_group_barrier(0x100, spread(NREAD, NMMA, Q), 0);
+    interleave<NMMA, NDMA, NREAD, Q + 1>();
+  }
+}
+
+template <int DT, int BKB, int SLOTS, int WAVES_N>
+__global__ __launch_bounds__(128 * WAVES_N)
+__attribute__((amdgpu_waves_per_eu(WAVES_N / 2, WAVES_N / 2)))
 void gemm_dense_kernel(DenseArgs p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[STAGES * STAGE_BYTES];
+  constexpr int WAVES = 2 * WAVES_N;
+  constexpr int WM = BM / 2, WN = BN / WAVES_N;   // wave tile
+  constexpr int FM = WM / 32, FN = WN / 32;       // 32x32 accumulators
+  constexpr int NMMA = FM * FN;                   // MFMAs per k-step
+  constexpr int SLAB = BM * BKB;           // bytes of one operand slab
+  constexpr int DMA = SLAB / 1024 / WAVES; // b128 loads per wave per slab
+  static_assert(SLOTS >= 4, "two stages at least");
+  static_assert(SLOTS * SLAB <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[SLOTS * SLAB];
   TKG_LDS uint8_t* smem = (TKG_LDS uint8_t*)smem_raw;
 
-  // MFMA k-steps per stage and 16-byte reads per operand fragment
-  constexpr int KSTEPS = (DT == kBf16) ? 2 : 1;
+  // MFMA k-steps per stage (16 bf16 or 64 fp8 of K each) and 16-byte reads
+  // per operand fragment. The loop body runs an even number of k-steps (the
+  // fragment registers alternate between two sets): one stage, or two
+  // stages when a stage is a single k-step.
+  constexpr int KSTEPS = (DT == kBf16) ? BKB / 32 : BKB / 64;
   constexpr int PARTS = (DT == kBf16) ? 1 : 2;
+  constexpr int TRIP_STAGES = (KSTEPS >= 2) ? 1 : 2;
+  static_assert(KSTEPS % 2 == 0 || KSTEPS == 1, "k-steps per trip must be even");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int G = gridDim.x;
   int t = xcd_virtual_id(blockIdx.x, G, p.xcd_remap);
   if (t >= p.num_tiles) return;
 
-  // Number of K stages per tile. fp8 walks two stages per loop trip, so its
-  // count is rounded up to even; the extra stage reads zeros.
-  const uint32_t nk = (KSTEPS == 1) ? (p.nk + (p.nk & 1)) : p.nk;
+  // Number of K stages per tile, rounded up to whole loop trips; the extra
+  // stage reads zeros.
+  const uint32_t nk_raw = (p.kbytes + BKB - 1) / BKB;
+  const uint32_t nk = (TRIP_STAGES == 2) ? (nk_raw + (nk_raw & 1)) : nk_raw;
 
   // ---- per-lane staging offsets (tile independent) -----------------------
-  // DMA instruction i of this wave fills rows dma_row(q), q = wave*DMA + i;
-  // with 64-byte rows the fetched chunk depends on the lane only.
-  uint32_t dma_off[DMA];
+  // DMA instruction i of this wave fills rows dma_row(q), q = wave*DMA + i.
+  uint32_t dma_off[DMA], dma_kb[DMA];
 #pragma unroll
   for (int i = 0; i < DMA; ++i) {
     const uint32_t q = wave * DMA + i;
-    dma_off[i] = dma_row(BKB, q, lane) * p.kbytes + dma_chunk(BKB, q, lane) * 16u;
+    dma_kb[i] = dma_chunk(BKB, q, lane) * 16u;
+    dma_off[i] = dma_row(BKB, q, lane) * p.kbytes + dma_kb[i];
   }
-  const uint32_t dma_kb = dma_chunk(BKB, wave * DMA, lane) * 16u;
 
   // ---- per-lane fragment read offsets ------------------------------------
   // Fragment rows are (multiple of 32) + lane%32, so the swizzle mask only
   // depends on the lane. k-step s of a stage reads chunk 2s + lane/32 (bf16)
-  // or chunks 2*(lane/32) and 2*(lane/32) + 1 (fp8): the same K order for A
-  // and B, so the MFMA reduces over matching elements.
+  // or chunks 4s + 2*(lane/32) and 4s + 2*(lane/32) + 1 (fp8): the same K
+  // order for A and B, so the MFMA reduces over matching elements.
   const uint32_t frow = lane & 31;
   const uint32_t khalf = lane >> 5;
   uint32_t roff[KSTEPS][PARTS];
@@ -119,57 +159,74 @@ void gemm_dense_kernel(DenseArgs p) {
   for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
     for (int q = 0; q < PARTS; ++q)
-      roff[s][q] = swz_offset(BKB, frow, (DT == kBf16) ? 2 * s + khalf : 2 * khalf + q);
-  const uint32_t a_base = wm * WM * BKB;
-  const uint32_t b_base = TILE + wn * WN * BKB;
+      roff[s][q] = swz_offset(BKB, frow, (DT == kBf16) ? 2 * s + khalf : 4 * s + 2 * khalf + q);
+  const uint32_t a_base = wm * WM * BKB;   // within an A slab
+  const uint32_t b_base = wn * WN * BKB;   // within a B slab
 
-  // ---- load cursor: (tile lt, stage lkt), STAGES stages ahead -------------
+  // ---- load cursor: slab (tile lt, stage lkt, operand lop) ----------------
   TileState cur = tile_state(p, t);
   TileState lts = cur;
   int lt = t;
-  uint32_t lkt = 0;
+  uint32_t lkt = 0, lop = 0, lslot = 0;
   auto advance_load = [&]() {
-    if (++lkt == nk) {
-      lkt = 0;
-      lt += G;
-      lts = tile_state(p, lt);
+    lslot = (lslot + 1 == SLOTS) ? 0 : lslot + 1;
+    if (lop == 0) {
+      lop = 1;
+    } else {
+      lop = 0;
+      if (++lkt == nk) {
+        lkt = 0;
+        lt += G;
+        lts = tile_state(p, lt);
+      }
     }
   };
-  // Loads of stage (lts, lkt) into buffer `buf`; stages past K read zeros.
-  auto issue = [&](int buf) {
-    const uint32_t k0 = lkt * BKB;
-    TKG_LDS uint8_t* st = smem + buf * STAGE_BYTES;
-    const bool kok = k0 + dma_kb < p.kbytes;  // this lane's chunk exists
+  // The cursor's next slab: its resource, slot and K offset (then advance).
+  struct SlabLoad {
+    __amdgpu_buffer_rsrc_t r;
+    uint32_t slot, k0;
+  };
+  auto next_slab = [&]() {
+    SlabLoad s;
+    s.r = lop ? lts.rb : lts.ra;
+    s.slot = lslot;
+    s.k0 = lkt * BKB;
+    advance_load();
+    return s;
+  };
+  // Branch-free loads of one slab; chunks past K read zeros.
+  auto issue = [&](const SlabLoad& s) {
+    TKG_LDS uint8_t* st = smem + s.slot * SLAB;
 #pragma unroll
     for (int i = 0; i < DMA; ++i) {
-      const uint32_t off = kok ? dma_off[i] + k0 : kOobOffset;
-      const uint32_t q = wave * DMA + i;
-      dma_b128(lts.ra, st + q * 1024, off);
-      dma_b128(lts.rb, st + TILE + q * 1024, off);
+      const uint32_t off = (s.k0 + dma_kb[i] < p.kbytes) ? dma_off[i] + s.k0 : kOobOffset;
+      dma_b128(s.r, st + (wave * DMA + i) * 1024, off);
     }
   };
 
   using Frag = typename std::conditional<DT == kBf16, bf16x8_t, i32x8_t>::type;
   Frag fa[2][FM], fb[2][FN];
-  auto read_frags = [&](int buf, int s, Frag (&a)[FM], Frag (&b)[FN]) {
-    const TKG_LDS uint8_t* st = smem + buf * STAGE_BYTES;
+  // A and B slots of the stage being read
+  auto read_frags = [&](int aslot, int bslot, int s, Frag (&a)[FM], Frag (&b)[FN]) {
+    const TKG_LDS uint8_t* sa = smem + aslot * SLAB;
+    const TKG_LDS uint8_t* sb = smem + bslot * SLAB;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       if constexpr (DT == kBf16) {
-        a[i] = lds_read<bf16x8_t>(st, a_base + i * 32 * BKB + roff[s][0]);
+        a[i] = lds_read<bf16x8_t>(sa, a_base + i * 32 * BKB + roff[s][0]);
       } else {
-        const i32x4_t lo = lds_read<i32x4_t>(st, a_base + i * 32 * BKB + roff[s][0]);
-        const i32x4_t hi = lds_read<i32x4_t>(st, a_base + i * 32 * BKB + roff[s][PARTS - 1]);
+        const i32x4_t lo = lds_read<i32x4_t>(sa, a_base + i * 32 * BKB + roff[s][0]);
+        const i32x4_t hi = lds_read<i32x4_t>(sa, a_base + i * 32 * BKB + roff[s][PARTS - 1]);
         a[i] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       if constexpr (DT == kBf16) {
-        b[j] = lds_read<bf16x8_t>(st, b_base + j * 32 * BKB + roff[s][0]);
+        b[j] = lds_read<bf16x8_t>(sb, b_base + j * 32 * BKB + roff[s][0]);
       } else {
-        const i32x4_t lo = lds_read<i32x4_t>(st, b_base + j * 32 * BKB + roff[s][0]);
-        const i32x4_t hi = lds_read<i32x4_t>(st, b_base + j * 32 * BKB + roff[s][PARTS - 1]);
+        const i32x4_t lo = lds_read<i32x4_t>(sb, b_base + j * 32 * BKB + roff[s][0]);
+        const i32x4_t hi = lds_read<i32x4_t>(sb, b_base + j * 32 * BKB + roff[s][PARTS - 1]);
         b[j] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
     }
@@ -193,65 +250,52 @@ void gemm_dense_kernel(DenseArgs p) {
       }
   };
 
-  // ---- prologue: the first STAGES stages in flight ------------------------
+  // ---- prologue: the first SLOTS slabs in flight -------------------------
 #pragma unroll
-  for (int b = 0; b < STAGES; ++b) {
-    issue(b);
-    advance_load();
-  }
-  wait_vmcnt<(STAGES - 1) * 2 * DMA>();  // stage 0 has landed
+  for (int b = 0; b < SLOTS; ++b) issue(next_slab());
+  wait_vmcnt<(SLOTS - 2) * DMA>();  // slabs 0 and 1 (stage 0) have landed
   __syncthreads();
-  read_frags(0, 0, fa[0], fb[0]);
+  int aslot = 0, bslot = 1;         // slots of the stage being computed
+  read_frags(aslot, bslot, 0, fa[0], fb[0]);
 
   // One MFMA k-step. Register set c holds its fragments; the next k-step's
   // fragments go to set c ^ 1. At the last k-step of a stage the next stage
-  // must have landed (wait + barrier); after the barrier every wave has read
-  // the current stage, so its buffer is refilled STAGES stages ahead.
-  int buf = 0;
+  // must have landed (wait + barrier): SLOTS slabs were issued before stage
+  // k's end, so at most SLOTS - 4 slabs may still be loading. After the
+  // barrier every wave has read the current stage, so its two slots are
+  // refilled with the next two slabs of the cursor.
   bool fresh_tile = false;  // finish stores are in flight
+  constexpr int NREAD = (FM + FN) * PARTS;   // ds_read_b128 per k-step
+  constexpr int NDMA = 2 * DMA;              // slab loads per stage boundary
   auto kstep = [&](int c, int s, bool last) {
     if (!last) {
-      read_frags(buf, s + 1, fa[c ^ 1], fb[c ^ 1]);
+      read_frags(aslot, bslot, s + 1, fa[c ^ 1], fb[c ^ 1]);
       mma_step(fa[c], fb[c]);
-#pragma unroll
-      for (int q = 0; q < FM + FN; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, PARTS, 0);      // ds_read
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+      interleave<NMMA, 0, NREAD>();
       __builtin_amdgcn_sched_barrier(0);
     } else {
+      const SlabLoad l0 = next_slab();
+      const SlabLoad l1 = next_slab();
       if (fresh_tile) wait_vmcnt<0>();
-      else wait_vmcnt<(STAGES - 2) * 2 * DMA>();
+      else wait_vmcnt<(SLOTS - 4) * DMA>();
       fresh_tile = false;
       lds_barrier();
-      issue(buf);
-      const int nbuf = (buf + 1 == STAGES) ? 0 : buf + 1;
-      read_frags(nbuf, 0, fa[c ^ 1], fb[c ^ 1]);
+      issue(l0);
+      issue(l1);
+      aslot = (aslot + 2) % SLOTS;
+      bslot = (bslot + 2) % SLOTS;
+      read_frags(aslot, bslot, 0, fa[c ^ 1], fb[c ^ 1]);
       mma_step(fa[c], fb[c]);
-#pragma unroll
-      for (int q = 0; q < FM + FN; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);          // DMA
-        __builtin_amdgcn_sched_group_barrier(0x100, PARTS, 0);      // ds_read
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - (FM + FN), 0);
+      interleave<NMMA, NDMA, NREAD>();
       __builtin_amdgcn_sched_barrier(0);
-      buf = nbuf;
-      advance_load();
     }
   };
 
   for (;;) {
-    // two k-steps per trip: one bf16 stage, or two fp8 stages
-    for (uint32_t kt = 0; kt < nk; kt += 2 / KSTEPS) {
-      if constexpr (KSTEPS == 2) {
-        kstep(0, 0, false);
-        kstep(1, 1, true);
-      } else {
-        kstep(0, 0, true);
-        kstep(1, 0, true);
-      }
+    for (uint32_t kt = 0; kt < nk; kt += TRIP_STAGES) {
+#pragma unroll
+      for (int u = 0; u < TRIP_STAGES * KSTEPS; ++u)
+        kstep(u & 1, u % KSTEPS, u % KSTEPS == KSTEPS - 1);
     }
 
     // ---- finish: C[m][n .. n+3] from accumulator rows 4g .. 4g+3 ----------
@@ -303,16 +347,35 @@ void gemm_dense_kernel(DenseArgs p) {
 
 }  // namespace
 
-uint32_t dense_stage_kbytes() { return BKB; }
+template <int DT, int R>
+void launch_ring(const DenseArgs& a, int grid, hipStream_t stream) {
+  constexpr Ring r = kRings[R];
+  hipLaunchKernelGGL((gemm_dense_kernel<DT, r.bkb, r.slots, r.waves_n>),
+                     dim3(grid), dim3(128 * r.waves_n), 0, stream, a);
+}
 
-hipError_t launch_dense(DenseType dt, const DenseArgs& a, int grid,
+template <int DT>
+void launch_variant(int v, const DenseArgs& a, int grid, hipStream_t stream) {
+  switch (v) {
+    case 1: launch_ring<DT, 1>(a, grid, stream); break;
+    case 2: launch_ring<DT, 2>(a, grid, stream); break;
+    case 3: launch_ring<DT, 3>(a, grid, stream); break;
+    case 4: launch_ring<DT, 4>(a, grid, stream); break;
+    case 5: launch_ring<DT, 5>(a, grid, stream); break;
+    case 6: launch_ring<DT, 6>(a, grid, stream); break;
+    default: launch_ring<DT, 0>(a, grid, stream); break;
+  }
+}
+
+uint32_t dense_stage_kbytes() { return kRings[0].bkb; }
+int dense_num_variants() { return kNumRings; }
+
+hipError_t launch_dense(DenseType dt, const DenseArgs& a, int grid, int variant,
                         hipStream_t stream) {
   if (dt == kBf16)
-    hipLaunchKernelGGL(gemm_dense_kernel<kBf16>, dim3(grid), dim3(kThreads), 0,
-                       stream, a);
+    launch_variant<kBf16>(variant, a, grid, stream);
   else
-    hipLaunchKernelGGL(gemm_dense_kernel<kFp8>, dim3(grid), dim3(kThreads), 0,
-                       stream, a);
+    launch_variant<kFp8>(variant, a, grid, stream);
   return hipGetLastError();
 }
 

@@ -97,8 +97,6 @@ int run_dense(tkg::DenseType dt, int64_t M, int64_t N, int64_t K,
   a.M = (int32_t)M;
   a.N = (int32_t)N;
   a.kbytes = (uint32_t)(K * eb);
-  const uint32_t sk = tkg::dense_stage_kbytes();
-  a.nk = (a.kbytes + sk - 1) / sk;
   a.scale = scale;
   a.tiles_m = pl.tiles_m;
   a.tiles_n = pl.tiles_n;
@@ -108,8 +106,10 @@ int run_dense(tkg::DenseType dt, int64_t M, int64_t N, int64_t K,
   if (K == 0) {  // empty reduction: the kernel's zero accumulators are C
     a.A = a.B = static_cast<const uint8_t*>(C);
   }
-  const hipError_t e =
-      tkg::launch_dense(dt, a, pl.grid, static_cast<hipStream_t>(stream));
+  const int variant = opts ? opts->variant : 0;
+  if (variant < 0 || variant >= tkg::dense_num_variants()) return TKG_ERR_SHAPE;
+  const hipError_t e = tkg::launch_dense(dt, a, pl.grid, variant,
+                                         static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TKG_OK : TKG_ERR_LAUNCH;
 }
 
@@ -118,6 +118,7 @@ int run_fp4(int64_t M, int64_t N, int64_t K, const void* A, const void* As,
             void* stream, const tkg_opts* opts) {
   int st = check_common(M, N, K, 64, 16777215);
   if (st != TKG_OK) return st;
+  if (opts && opts->variant != 0) return TKG_ERR_SHAPE;
   if (M == 0 || N == 0) return TKG_OK;
   if (C == nullptr ||
       (K > 0 && (A == nullptr || B == nullptr || As == nullptr || Bs == nullptr)))

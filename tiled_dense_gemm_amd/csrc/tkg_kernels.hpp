@@ -16,7 +16,6 @@ struct DenseArgs {
   uint16_t* C;
   int32_t M, N;
   uint32_t kbytes;  // bytes of K per operand row
-  uint32_t nk;      // number of K steps of the staging ring
   float scale;
   int32_t tiles_m, tiles_n, num_tiles, group_m;
   int32_t xcd_remap;  // 1: give each XCD a contiguous range of tiles
@@ -44,8 +43,10 @@ constexpr int kBM = 256;
 constexpr int kBN = 256;
 constexpr int kThreads = 256;
 
-hipError_t launch_dense(DenseType dt, const DenseArgs& a, int grid,
+// variant: index of a compiled ring shape (0 = default; out of range = 0).
+hipError_t launch_dense(DenseType dt, const DenseArgs& a, int grid, int variant,
                         hipStream_t stream);
+int dense_num_variants();
 hipError_t launch_fp4(const Fp4Args& a, int grid, hipStream_t stream);
 
 // K bytes per stage row of each kernel family (for the host).
