@@ -119,12 +119,13 @@ const char *tkg_status_string(int status);
  *   xcd_remap -- 1 (default when grid is a multiple of 8) gives each XCD a
  *               contiguous range of tiles; 0 leaves the hardware's
  *               round-robin order.
- *   variant  -- bf16/fp8 only: kernel configuration, as (K bytes per row
+ *   variant  -- bf16/fp8: kernel configuration, as (K bytes per row
  *               of an LDS slab, operand slabs in the LDS ring, waves per
  *               workgroup): 0 = (128, 4, 8) default, 1 = (128, 5, 8),
  *               2 = (64, 10, 8), 3 = (128, 5, 4), 4 = (128, 4, 4),
  *               5 = (64, 10, 4), 6 = (64, 8, 4); TKG_ERR_SHAPE outside
- *               0..6. Must be 0 for the 4-bit product. Every variant
+ *               0..6. 4-bit product: 0 = 4 waves (default), 1 = 8 waves;
+ *               TKG_ERR_SHAPE outside 0..1. Every variant of a product
  *               computes the same result.
  * Page "ThunderKittens: Simple, Fast, and Adorable AI Kernels", section
  * 3.4, "Persistent Grid Launch" (Table 2) and "Block Launch Order and L2

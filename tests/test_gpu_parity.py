@@ -315,6 +315,23 @@ def test_fp4_integers_bit_exact(dev):
     assert np.array_equal(_bf16_result(C), ref)
 
 
+def test_fp4_variants_agree(dev):
+    M, N, K = 700, 1300, 1088
+    Ap, As, ta = gi.fp4_operand(60, M, K)
+    Bp, Bs, tb = gi.fp4_operand(61, N, K)
+    args = [_up(Ap, dev), _up(As, dev), ta, _up(Bp, dev), _up(Bs, dev), tb]
+    outs = []
+    for v in range(2):
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        st = tkg.tkg_gemm_ex(tkg.DTYPE_FP4_BLOCKSCALED, M, N, K, args[0], args[1],
+                             ta, args[3], args[4], tb, C, variant=v)
+        assert st == 0
+        outs.append(C)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    R = oracle.gemm_fp4_blockscaled(Ap, As, ta, Bp, Bs, tb)
+    assert relfro(_bf16_result(outs[0]), R) <= LOWP_RELFRO
+
+
 @pytest.mark.parametrize("n", [16384, 65536])
 def test_fp4_config_shapes_sampled(dev, n):
     Ap, As, ta = gi.device.fp4_operand(50, n, n, device=dev)

@@ -14,10 +14,11 @@
 // summation, at the 16-bit MFMA rate.
 //
 // Structure as in gemm_dense.hip (256x256 workgroup tile of 2x2 wave tiles
-// of 4x4 32x32 accumulators, persistent grouped grid with XCD remap, LDS
-// ring fed by direct global->LDS loads), with a 4-deep ring: one stage holds
-// 128 K-elements per row, i.e. 64 bytes of packed values (swizzled as in
-// tkg_layout.hpp) and 8 bytes of block scales.
+// of 32x32 accumulators, one wave per SIMD, or 2x4 with two per SIMD;
+// persistent grouped grid with XCD remap; LDS ring fed by direct global->LDS
+// loads), with a 4-deep ring:
+// one stage holds 128 K-elements per row, i.e. 64 bytes of packed values
+// (swizzled as in tkg_layout.hpp) and 8 bytes of block scales.
 #include "tkg_device.hpp"
 #include "tkg_kernels.hpp"
 #include "tkg_layout.hpp"
@@ -40,18 +41,13 @@ constexpr int OFF_BV = TILE_V;
 constexpr int OFF_AS = 2 * TILE_V;
 constexpr int OFF_BS = 2 * TILE_V + TILE_S;
 constexpr int STAGE_BYTES = 2 * TILE_V + 2 * TILE_S;  // 36 KiB
-constexpr int WAVES = kThreads / 64;
-constexpr int WM = 128, WN = 128;
-constexpr int FM = WM / 32, FN = WN / 32;
-constexpr int VDMA = TILE_V / 1024 / WAVES;  // 4 b128 loads per wave per operand
-constexpr int SDMA = TILE_S / 256 / WAVES;   // 2 b32 loads per wave per operand
-constexpr int DMA_PER_STAGE = 2 * VDMA + 2 * SDMA;  // per lane
 
 static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS budget");
 
 // 1: v_cvt_scalef32_pk_f16_fp4 multiplies by the whole fp32 scale.
-// 0: it only applies the scale's power of two; the remaining mantissa
-//    factor is applied with a packed fp16 multiply (exact either way).
+// 0: it only applies the scale's power of two (the behaviour measured on
+//    gfx950); the remaining mantissa factor is applied with a packed fp16
+//    multiply (exact either way).
 #ifndef TKG_FP4_CVT_FULL_SCALE
 #define TKG_FP4_CVT_FULL_SCALE 0
 #endif
@@ -119,15 +115,25 @@ __device__ __forceinline__ void split_scale(uint32_t word, float& s,
 #endif
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int WAVES_N>
+__global__ __launch_bounds__(128 * WAVES_N)
+__attribute__((amdgpu_waves_per_eu(WAVES_N / 2, WAVES_N / 2)))
 void gemm_fp4_kernel(Fp4Args p) {
+  constexpr int WAVES = 2 * WAVES_N;
+  constexpr int WM = BM / 2, WN = BN / WAVES_N;
+  constexpr int FM = WM / 32, FN = WN / 32;
+  constexpr int VDMA = TILE_V / 1024 / WAVES;  // b128 loads per wave per operand
+  constexpr int SDMA = TILE_S / 256 / WAVES;   // b32 loads per wave per operand
+  constexpr int DMA_PER_STAGE = 2 * VDMA + 2 * SDMA;  // per lane
+  static_assert(SDMA >= 1, "scale staging needs a load per wave");
+
   __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[STAGES * STAGE_BYTES];
   TKG_LDS uint8_t* smem = (TKG_LDS uint8_t*)smem_raw;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int G = gridDim.x;
   int t = xcd_virtual_id(blockIdx.x, G, p.xcd_remap);
   if (t >= p.num_tiles) return;
@@ -137,10 +143,8 @@ void gemm_fp4_kernel(Fp4Args p) {
 #pragma unroll
   for (int i = 0; i < VDMA; ++i) {
     const uint32_t q = wave * VDMA + i;
-    const uint32_t row = dma_row(VB, q, lane);
-    const uint32_t chunk = dma_chunk(VB, q, lane);
-    voff[i] = row * p.vbytes + chunk * 16u;
-    vkb[i] = chunk * 16u;
+    vkb[i] = dma_chunk(VB, q, lane) * 16u;
+    voff[i] = dma_row(VB, q, lane) * p.vbytes + vkb[i];
   }
   // scales: one wave b32 load covers 32 rows x 8 bytes
   uint32_t soff[SDMA];
@@ -151,36 +155,50 @@ void gemm_fp4_kernel(Fp4Args p) {
     soff[i] = (q * 32u + (lane >> 1)) * p.sbytes + skb;
   }
 
-  auto issue = [&](const TileState& ts, uint32_t kt, int buf) {
-    const uint32_t k0 = kt * VB;       // value byte offset
-    const uint32_t s0 = kt * SB;       // scale byte offset
-    const bool full = k0 + VB <= p.vbytes;
+  // ---- load cursor (tile lt, stage lkt) ------------------------------------
+  TileState cur = tile_state(p, t);
+  TileState lts = cur;
+  int lt = t;
+  uint32_t lkt = 0;
+  struct StageLoad {
+    __amdgpu_buffer_rsrc_t rav, rbv, ras, rbs;
+    uint32_t k0, s0;
+  };
+  auto next_stage = [&]() {
+    StageLoad s{lts.rav, lts.rbv, lts.ras, lts.rbs, lkt * VB, lkt * SB};
+    if (++lkt == p.nk) {
+      lkt = 0;
+      lt += G;
+      lts = tile_state(p, lt);
+    }
+    return s;
+  };
+  // Branch-free loads of one stage into buffer `buf`; past K reads zeros.
+  auto issue = [&](const StageLoad& s, int buf) {
     TKG_LDS uint8_t* st = smem + buf * STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < VDMA; ++i) {
-      uint32_t off = voff[i] + k0;
-      if (!full && k0 + vkb[i] >= p.vbytes) off = kOobOffset;
+      const uint32_t off = (s.k0 + vkb[i] < p.vbytes) ? voff[i] + s.k0 : kOobOffset;
       const uint32_t q = wave * VDMA + i;
-      dma_b128(ts.rav, st + q * 1024, off);
-      dma_b128(ts.rbv, st + OFF_BV + q * 1024, off);
+      dma_b128(s.rav, st + q * 1024, off);
+      dma_b128(s.rbv, st + OFF_BV + q * 1024, off);
     }
 #pragma unroll
     for (int i = 0; i < SDMA; ++i) {
-      uint32_t off = soff[i] + s0;
-      if (!full && s0 + skb >= p.sbytes) off = kOobOffset;
+      const uint32_t off = (s.s0 + skb < p.sbytes) ? soff[i] + s.s0 : kOobOffset;
       const uint32_t q = wave * SDMA + i;
-      dma_b32(ts.ras, st + OFF_AS + q * 256, off);
-      dma_b32(ts.rbs, st + OFF_BS + q * 256, off);
+      dma_b32(s.ras, st + OFF_AS + q * 256, off);
+      dma_b32(s.rbs, st + OFF_BS + q * 256, off);
     }
   };
 
   // ---- fragment reads ------------------------------------------------------
   // Lane l works on row l%32 of each 32-row fragment. Per stage it reads two
   // 16-byte chunks of packed values, chunk 2s + l/32 for s = 0, 1 (32
-  // K-elements each, 4 MFMA k-steps of 8), and the row's 8 scale bytes
-  // (one 8-byte read: 32 consecutive rows fill the banks without conflict).
-  // The same K order is used for A and B, so the MFMA's reduction is over
-  // the same K-elements on both sides.
+  // K-elements each, 4 MFMA k-steps of 8), and, once per stage, the row's 8
+  // scale bytes (one 8-byte read: 32 consecutive rows fill the banks without
+  // conflict). The same K order is used for A and B, so the MFMA's reduction
+  // is over the same K-elements on both sides.
   const uint32_t frow = lane & 31;
   const uint32_t khalf = lane >> 5;
   uint32_t roff[2];
@@ -191,20 +209,21 @@ void gemm_fp4_kernel(Fp4Args p) {
   const uint32_t bs_base = OFF_BS + (wn * WN + frow) * SB;
 
   struct Raw {
-    i32x4_t a[FM], b[FN];  // packed values of one chunk
-    uint32_t sa[FM], sb[FN];  // this lane's 2 block scales of the chunk
+    i32x4_t a[FM], b[FN];     // packed values of one chunk
+    u32x2_t sa[FM], sb[FN];   // the row's 8 block scales of the stage
   };
-  auto read_raw = [&](int buf, int s, Raw& r) {
+  // chunk s of buffer `buf`; the scales are read with chunk 0 and carried
+  auto read_raw = [&](int buf, int s, Raw& r, const Raw& prev) {
     const TKG_LDS uint8_t* st = smem + buf * STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       r.a[i] = lds_read<i32x4_t>(st, av_base + i * 32 * VB + roff[s]);
-      r.sa[i] = lds_read<u32x2_t>(st, as_base + i * 32 * SB)[s] >> (16 * khalf);
+      r.sa[i] = (s == 0) ? lds_read<u32x2_t>(st, as_base + i * 32 * SB) : prev.sa[i];
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       r.b[j] = lds_read<i32x4_t>(st, bv_base + j * 32 * VB + roff[s]);
-      r.sb[j] = lds_read<u32x2_t>(st, bs_base + j * 32 * SB)[s] >> (16 * khalf);
+      r.sb[j] = (s == 0) ? lds_read<u32x2_t>(st, bs_base + j * 32 * SB) : prev.sb[j];
     }
   };
 
@@ -214,23 +233,23 @@ void gemm_fp4_kernel(Fp4Args p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
 
-  // 4 MFMA k-steps out of one chunk: k-step q uses dword q of the chunk,
-  // whose block (16 elements) is 2*(2s + khalf) + q/2, i.e. byte q/2 of the
-  // lane's pre-shifted scale word.
-  auto mma_kstep = [&](const Raw& r, auto qc) {
+  // 4 MFMA k-steps out of chunk s: k-step q uses dword q of the chunk, whose
+  // block (16 elements) is 2*(2s + khalf) + q/2 of the stage, i.e. byte
+  // 2*khalf + q/2 of scale word s.
+  auto mma_kstep = [&](const Raw& r, int s, auto qc) {
     constexpr int q = decltype(qc)::value;
     f16x8_t a[FM], b[FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      float s; f16x2_t m;
-      split_scale<q / 2>(r.sa[i], s, m);
-      a[i] = dequant8((uint32_t)r.a[i][q], s, m);
+      float sc; f16x2_t m;
+      split_scale<q / 2>(r.sa[i][s] >> (16 * khalf), sc, m);
+      a[i] = dequant8((uint32_t)r.a[i][q], sc, m);
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      float s; f16x2_t m;
-      split_scale<q / 2>(r.sb[j], s, m);
-      b[j] = dequant8((uint32_t)r.b[j][q], s, m);
+      float sc; f16x2_t m;
+      split_scale<q / 2>(r.sb[j][s] >> (16 * khalf), sc, m);
+      b[j] = dequant8((uint32_t)r.b[j][q], sc, m);
     }
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -238,55 +257,41 @@ void gemm_fp4_kernel(Fp4Args p) {
       for (int j = 0; j < FN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[j], a[i], acc[i][j], 0, 0, 0);
   };
-  auto mma_chunk = [&](const Raw& r) {
-    mma_kstep(r, std::integral_constant<int, 0>{});
-    mma_kstep(r, std::integral_constant<int, 1>{});
-    mma_kstep(r, std::integral_constant<int, 2>{});
-    mma_kstep(r, std::integral_constant<int, 3>{});
+  auto mma_chunk = [&](const Raw& r, int s) {
+    mma_kstep(r, s, std::integral_constant<int, 0>{});
+    mma_kstep(r, s, std::integral_constant<int, 1>{});
+    mma_kstep(r, s, std::integral_constant<int, 2>{});
+    mma_kstep(r, s, std::integral_constant<int, 3>{});
   };
 
   // ---- prologue ------------------------------------------------------------
-  TileState cur = tile_state(p, t);
-  TileState lts = cur;
-  int lt = t;
-  uint32_t lkt = 0;
-  auto advance_load = [&]() {
-    if (++lkt == p.nk) {
-      lkt = 0;
-      lt += G;
-      lts = tile_state(p, lt);
-    }
-  };
 #pragma unroll
-  for (int b = 0; b < STAGES; ++b) {
-    issue(lts, lkt, b);
-    advance_load();
-  }
+  for (int b = 0; b < STAGES; ++b) issue(next_stage(), b);
   wait_vmcnt<(STAGES - 1) * DMA_PER_STAGE>();
   __syncthreads();
 
   Raw raw[2];
-  read_raw(0, 0, raw[0]);
+  read_raw(0, 0, raw[0], raw[0]);
 
   int buf = 0;
   bool fresh_tile = false;  // finish stores are in flight
   for (;;) {
     for (uint32_t kt = 0; kt < p.nk; ++kt) {
-      // chunk s = 0 of this stage is in raw[0]; fetch chunk 1, multiply 0
-      read_raw(buf, 1, raw[1]);
-      mma_chunk(raw[0]);
+      // chunk 0 of this stage is in raw[0]; fetch chunk 1, multiply chunk 0
+      read_raw(buf, 1, raw[1], raw[0]);
+      mma_chunk(raw[0], 0);
       __builtin_amdgcn_sched_barrier(0);
       // stage boundary: the next stage must have landed; this one is free
       // (right after a finish, its stores are in flight too: wait for all)
+      const StageLoad nl = next_stage();
       if (fresh_tile) wait_vmcnt<0>();
       else wait_vmcnt<(STAGES - 2) * DMA_PER_STAGE>();
       fresh_tile = false;
       lds_barrier();
-      issue(lts, lkt, buf);
-      advance_load();
+      issue(nl, buf);
       const int nbuf = (buf + 1 == STAGES) ? 0 : buf + 1;
-      read_raw(nbuf, 0, raw[0]);
-      mma_chunk(raw[1]);
+      read_raw(nbuf, 0, raw[0], raw[0]);
+      mma_chunk(raw[1], 1);
       __builtin_amdgcn_sched_barrier(0);
       buf = nbuf;
     }
@@ -337,8 +342,16 @@ void gemm_fp4_kernel(Fp4Args p) {
 
 uint32_t fp4_stage_vbytes() { return VB; }
 
-hipError_t launch_fp4(const Fp4Args& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(gemm_fp4_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+int fp4_num_variants() { return 2; }
+
+// variant 0: 4 waves (one per SIMD, 128x128 wave tiles: each fragment is
+// dequantized by fewer waves); 1: 8 waves (two per SIMD, 128x64)
+hipError_t launch_fp4(const Fp4Args& a, int grid, int variant,
+                      hipStream_t stream) {
+  if (variant == 1)
+    hipLaunchKernelGGL(gemm_fp4_kernel<4>, dim3(grid), dim3(512), 0, stream, a);
+  else
+    hipLaunchKernelGGL(gemm_fp4_kernel<2>, dim3(grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

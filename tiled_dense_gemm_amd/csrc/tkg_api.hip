@@ -118,7 +118,8 @@ int run_fp4(int64_t M, int64_t N, int64_t K, const void* A, const void* As,
             void* stream, const tkg_opts* opts) {
   int st = check_common(M, N, K, 64, 16777215);
   if (st != TKG_OK) return st;
-  if (opts && opts->variant != 0) return TKG_ERR_SHAPE;
+  const int variant = opts ? opts->variant : 0;
+  if (variant < 0 || variant >= tkg::fp4_num_variants()) return TKG_ERR_SHAPE;
   if (M == 0 || N == 0) return TKG_OK;
   if (C == nullptr ||
       (K > 0 && (A == nullptr || B == nullptr || As == nullptr || Bs == nullptr)))
@@ -150,7 +151,8 @@ int run_fp4(int64_t M, int64_t N, int64_t K, const void* A, const void* As,
   if (K == 0) {
     a.A = a.B = a.As = a.Bs = static_cast<const uint8_t*>(C);
   }
-  const hipError_t e = tkg::launch_fp4(a, pl.grid, static_cast<hipStream_t>(stream));
+  const hipError_t e =
+      tkg::launch_fp4(a, pl.grid, variant, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TKG_OK : TKG_ERR_LAUNCH;
 }
 

@@ -41,13 +41,14 @@ struct Fp4Args {
 // Tile shape shared by the kernels and the host-side argument checks.
 constexpr int kBM = 256;
 constexpr int kBN = 256;
-constexpr int kThreads = 256;
 
 // variant: index of a compiled ring shape (0 = default; out of range = 0).
 hipError_t launch_dense(DenseType dt, const DenseArgs& a, int grid, int variant,
                         hipStream_t stream);
 int dense_num_variants();
-hipError_t launch_fp4(const Fp4Args& a, int grid, hipStream_t stream);
+hipError_t launch_fp4(const Fp4Args& a, int grid, int variant,
+                      hipStream_t stream);
+int fp4_num_variants();
 
 // K bytes per stage row of each kernel family (for the host).
 uint32_t dense_stage_kbytes();
