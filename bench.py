@@ -59,6 +59,139 @@ def measured_traffic(kernel: str):
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+KERNEL_KEYS = {"gemm_dense_kernel<0": "gemm_bf16", "gemm_dense_kernel<1": "gemm_fp8",
+               "gemm_fp4_kernel": "gemm_fp4_blockscaled"}
+
+
+def _kernel_key(name: str):
+    for frag, key in KERNEL_KEYS.items():
+        if frag in name:
+            return key
+    return None
+
+
+def summarize_profile(trace_dir: str, fetch_dir: str, write_dir: str,
+                      size: int, out_md: str, out_json: str, command: str) -> int:
+    """Turn rocprofv3 CSV output into the committed summaries.
+
+    trace_dir: --kernel-trace --stats run of the timed bench;
+    fetch_dir / write_dir: --pmc FETCH_SIZE / WRITE_SIZE runs of
+    `bench.py --profile` (which ends with three 1 GiB device copies that
+    calibrate the counters: bytes = counter * (1 GiB / counter_of_copy))."""
+    import csv
+    import glob
+    import statistics
+
+    def rows(d, pattern):
+        out = []
+        for f in glob.glob(os.path.join(d, "**", pattern), recursive=True):
+            out += list(csv.DictReader(open(f)))
+        return out
+
+    dur = {}
+    for r in rows(trace_dir, "*kernel_trace.csv"):
+        k = _kernel_key(r["Kernel_Name"])
+        if k:
+            dur.setdefault(k, []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+
+    def counter(d, cname):
+        per, cal = {}, []
+        for r in rows(d, "*counter_collection.csv"):
+            if r["Counter_Name"] != cname:
+                continue
+            v = float(r["Counter_Value"])
+            k = _kernel_key(r["Kernel_Name"])
+            if k:
+                per.setdefault(k, []).append(v)
+            elif "copy" in r["Kernel_Name"] and v > 512 * 1024:
+                cal.append(v)
+        return per, cal
+
+    fetch, fcal = counter(fetch_dir, "FETCH_SIZE")
+    write, wcal = counter(write_dir, "WRITE_SIZE")
+    gib_kib = 1024.0 * 1024.0
+    ff = gib_kib / statistics.mean(fcal) if fcal else None
+    fw = gib_kib / statistics.mean(wcal) if wcal else None
+    M = N = K = size
+    flops = 2.0 * M * N * K
+    algo = {"gemm_bf16": (2 * M * K + 2 * N * K + 2 * M * N),
+            "gemm_fp8": (M * K + N * K + 2 * M * N),
+            "gemm_fp4_blockscaled": (M * K // 2 + N * K // 2 + M * K // 16
+                                     + N * K // 16 + 2 * M * N)}
+    rec = {"kernel_source_hash": kernel_source_hash(), "size": size,
+           "copy_calibration": {"fetch_factor": ff, "write_factor": fw,
+                                "copy_bytes": 1 << 30},
+           "command": command, "kernels": {}}
+    lines = ["# GEMM kernels at M=N=K=%d on one MI355X (rocprofv3)" % size, "",
+             "Produced by:", "", "```", command, "```", "",
+             "| kernel | launches | mean us | min us | TFLOP/s (mean) | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes/launch (calibrated) | compulsory bytes | ratio |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    for k in ("gemm_bf16", "gemm_fp8", "gemm_fp4_blockscaled"):
+        d = dur.get(k, [])
+        fk = statistics.mean(fetch[k]) if fetch.get(k) else None
+        wk = statistics.mean(write[k]) if write.get(k) else None
+        hbm = (fk * 1024 * ff + wk * 1024 * fw) if (fk and wk and ff and fw) else None
+        mean_us = statistics.mean(d) if d else None
+        rec["kernels"][k] = {"launches": len(d), "mean_us": mean_us,
+                             "min_us": min(d) if d else None,
+                             "fetch_kib": fk, "write_kib": wk,
+                             "hbm_bytes_per_launch": hbm,
+                             "compulsory_bytes": algo[k]}
+        lines.append("| %s | %d | %s | %s | %s | %s | %s | %s | %d | %s |" % (
+            k, len(d), "%.1f" % mean_us if d else "-",
+            "%.1f" % min(d) if d else "-",
+            "%.1f" % (flops / (mean_us * 1e-6) / 1e12) if d else "-",
+            "%.0f" % fk if fk else "-", "%.0f" % wk if wk else "-",
+            "%.3g" % hbm if hbm else "-", algo[k],
+            "%.2f" % (hbm / algo[k]) if hbm else "-"))
+    lines += ["", "Copy calibration: FETCH_SIZE factor %s, WRITE_SIZE factor %s "
+              "(1 GiB copy / counter reading)." % (
+                  "%.4f" % ff if ff else "-", "%.4f" % fw if fw else "-"), ""]
+    # optional SQ/TCC counter passes: every other counter_collection.csv
+    # under the trace dir's parent that is not the FETCH/WRITE pass
+    extra = {}
+    parent = os.path.dirname(os.path.abspath(trace_dir))
+    for d in sorted(glob.glob(os.path.join(parent, "*"))):
+        if os.path.abspath(d) in (os.path.abspath(fetch_dir), os.path.abspath(write_dir)):
+            continue
+        for r in rows(d, "*counter_collection.csv"):
+            k = _kernel_key(r["Kernel_Name"])
+            if k:
+                extra.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(
+                    float(r["Counter_Value"]))
+    if extra:
+        names = sorted({c for k in extra for c in extra[k]})
+        lines += ["Other counters (mean per launch, summed over the device):", "",
+                  "| counter | " + " | ".join(sorted(extra)) + " |",
+                  "|---" * (len(extra) + 1) + "|"]
+        for c in names:
+            lines.append("| %s | " % c + " | ".join(
+                "%.4g" % statistics.mean(extra[k][c]) if c in extra[k] else "-"
+                for k in sorted(extra)) + " |")
+        for k in sorted(extra):
+            e = extra[k]
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in e and "GRBM_GUI_ACTIVE" in e:
+                # MFMA busy cycles per SIMD over GPU-active cycles per XCD
+                util = (statistics.mean(e["SQ_VALU_MFMA_BUSY_CYCLES"]) / 1024.0) / (
+                    statistics.mean(e["GRBM_GUI_ACTIVE"]) / 8.0)
+                rec["kernels"][k]["mfma_busy_fraction"] = util
+                lines.append("")
+                lines.append("%s: MFMA busy %.1f%% of active cycles (1024 SIMDs, 8 XCDs)" % (k, 100 * util))
+            if "SQ_LDS_BANK_CONFLICT" in e and "SQ_LDS_IDX_ACTIVE" in e:
+                rec["kernels"][k]["lds_bank_conflict_over_active"] = (
+                    statistics.mean(e["SQ_LDS_BANK_CONFLICT"]) /
+                    max(1.0, statistics.mean(e["SQ_LDS_IDX_ACTIVE"])))
+            if "TCC_HIT_sum" in e and "TCC_MISS_sum" in e:
+                h, m = statistics.mean(e["TCC_HIT_sum"]), statistics.mean(e["TCC_MISS_sum"])
+                rec["kernels"][k]["l2_hit_rate"] = h / (h + m)
+        lines.append("")
+    open(out_md, "w").write("\n".join(lines))
+    json.dump(rec, open(out_json, "w"), indent=1)
+    print("\n".join(lines))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -68,7 +201,18 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile", action="store_true")
+    ap.add_argument("--summarize-profile", nargs=3,
+                    metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--profile-command", default="")
     args = ap.parse_args()
+
+    if args.summarize_profile:
+        return summarize_profile(
+            *args.summarize_profile, args.size,
+            os.path.join(ROOT, "profiles", "gemm_kernels_%d.md" % args.size),
+            TRAFFIC_FILE if args.size == 8192 else
+            os.path.join(ROOT, "profiles", "traffic_%d.json" % args.size),
+            args.profile_command)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU "
@@ -119,7 +263,7 @@ def main() -> int:
                 calls[k]()
         torch.cuda.synchronize()
         # calibration copy: 1 GiB read + 1 GiB written
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)

@@ -1,6 +1,10 @@
-// LDS bank-geometry probe: one kernel per address pattern, each lane reading
-// in-bounds LDS addresses (< 16 KiB) repeatedly. Counters per dispatch tell
-// which lane bits share a phase for b128 / b64 / b32 reads.
+// LDS bank-geometry probe for gfx950: one kernel per address pattern, each
+// lane reading in-bounds LDS addresses (< 16 KiB) repeatedly. Counted per
+// dispatch with rocprofv3 (SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE), the
+// patterns show which lane bits share a phase for b128 / b64 / b32 reads and
+// how addresses map to banks; the results calibrate lds_bank_model.py.
+//
+// Build: hipcc --offload-arch=gfx950 -O2 -std=c++17 lds_bank_probe.hip -o lds_bank_probe
 #include <hip/hip_runtime.h>
 #include <cstdio>
 #define LDS_AS __attribute__((address_space(3)))
