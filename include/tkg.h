@@ -121,10 +121,12 @@ const char *tkg_status_string(int status);
  *               round-robin order.
  *   variant  -- bf16/fp8: kernel configuration, as (K bytes per row
  *               of an LDS slab, operand slabs in the LDS ring, waves per
- *               workgroup): 0 = (128, 4, 8) default, 1 = (128, 5, 8),
- *               2 = (64, 10, 8), 3 = (128, 5, 4), 4 = (128, 4, 4),
- *               5 = (64, 10, 4), 6 = (64, 8, 4); TKG_ERR_SHAPE outside
- *               0..6. 4-bit product: 0 = 4 waves (default), 1 = 8 waves;
+ *               workgroup, waves issuing the global loads):
+ *               0 = (128, 4, 8, 4) default, 1 = (128, 5, 8, 4),
+ *               2 = (128, 4, 8, 8), 3 = (128, 5, 8, 8), 4 = (64, 10, 8, 8),
+ *               5 = (128, 5, 4, 4), 6 = (128, 4, 4, 4), 7 = (64, 10, 4, 4),
+ *               8 = (64, 8, 4, 4); TKG_ERR_SHAPE outside 0..8.
+ *               4-bit product: 0 = 4 waves (default), 1 = 8 waves;
  *               TKG_ERR_SHAPE outside 0..1. Every variant of a product
  *               computes the same result.
  * Page "ThunderKittens: Simple, Fast, and Adorable AI Kernels", section

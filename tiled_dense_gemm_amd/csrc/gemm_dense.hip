@@ -47,11 +47,15 @@ static_assert(BM == BN, "A and B slabs share offsets");
 // its B slab, keeping more bytes in flight than whole-stage buffers allow.
 // WAVES_N: the 2 x WAVES_N wave grid of the workgroup tile; 4 gives 8 waves
 // (two per SIMD) of 128 x 64 each, 2 gives 4 waves of 128 x 128.
+// LOADERS: 1 = only the waves of the first wave row (one per SIMD) issue
+// the slab loads, so their partner wave on each SIMD keeps issuing MFMAs
+// while the loaders wait for the memory pipeline to accept loads.
 struct Ring {
-  int bkb, slots, waves_n;
+  int bkb, slots, waves_n, loaders;
 };
-constexpr Ring kRings[] = {{128, 4, 4}, {128, 5, 4}, {64, 10, 4}, {128, 5, 2},
-                           {128, 4, 2}, {64, 10, 2}, {64, 8, 2}};
+constexpr Ring kRings[] = {{128, 4, 4, 1}, {128, 5, 4, 1}, {128, 4, 4, 0},
+                           {128, 5, 4, 0}, {64, 10, 4, 0}, {128, 5, 2, 0},
+                           {128, 4, 2, 0}, {64, 10, 2, 0}, {64, 8, 2, 0}};
 constexpr int kNumRings = sizeof(kRings) / sizeof(kRings[0]);
 
 struct TileState {
@@ -86,21 +90,28 @@ constexpr int spread(int total, int slots, int q) {
   return (q + 1) * total / slots - q * total / slots;
 }
 
+// The first `total` items placed `per` at a time after the first MFMAs.
+constexpr int front(int total, int per, int q) {
+  return total - q * per >= per ? per : (total - q * per > 0 ? total - q * per : 0);
+}
+
 // Scheduling recipe for one k-step: each MFMA followed by its share of the
-// slab loads (NDMA) and fragment reads (NREAD).
+// slab loads (NDMA, spread evenly) and of the next k-step's fragment reads
+// (NREAD, three per MFMA from the first one on, so they have most of the
+// k-step to land).
 template <int NMMA, int NDMA, int NREAD, int Q = 0>
 __device__ __forceinline__ void interleave() {
   if constexpr (Q < NMMA) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     if constexpr (spread(NDMA, NMMA, Q) > 0)
       __builtin_amdgcn_sched_group_barrier(0x020, spread(NDMA, NMMA, Q), 0);
-    if constexpr (spread(NREAD, NMMA, Q) > 0)
-      __builtin_amdgcn_sched_group_barrier(0x100, spread(NREAD, NMMA, Q), 0);
+    if constexpr (front(NREAD, 3, Q) > 0)
+      __builtin_amdgcn_sched_group_barrier(0x100, front(NREAD, 3, Q), 0);
     interleave<NMMA, NDMA, NREAD, Q + 1>();
   }
 }
 
-template <int DT, int BKB, int SLOTS, int WAVES_N>
+template <int DT, int BKB, int SLOTS, int WAVES_N, int LOADERS>
 __global__ __launch_bounds__(128 * WAVES_N)
 __attribute__((amdgpu_waves_per_eu(WAVES_N / 2, WAVES_N / 2)))
 void gemm_dense_kernel(DenseArgs p) {
@@ -109,7 +120,9 @@ void gemm_dense_kernel(DenseArgs p) {
   constexpr int FM = WM / 32, FN = WN / 32;       // 32x32 accumulators
   constexpr int NMMA = FM * FN;                   // MFMAs per k-step
   constexpr int SLAB = BM * BKB;           // bytes of one operand slab
-  constexpr int DMA = SLAB / 1024 / WAVES; // b128 loads per wave per slab
+  // waves that issue slab loads, and b128 loads per such wave per slab
+  constexpr int LOAD_WAVES = LOADERS ? WAVES_N : WAVES;
+  constexpr int DMA = SLAB / 1024 / LOAD_WAVES;
   static_assert(SLOTS >= 4, "two stages at least");
   static_assert(SLOTS * SLAB <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[SLOTS * SLAB];
@@ -139,10 +152,13 @@ void gemm_dense_kernel(DenseArgs p) {
 
   // ---- per-lane staging offsets (tile independent) -----------------------
   // DMA instruction i of this wave fills rows dma_row(q), q = wave*DMA + i.
+  // loader index of this wave (waves with wm > 0 load nothing if LOADERS)
+  const int lw = LOADERS ? wn : wave;
+  const bool loader = !LOADERS || wm == 0;
   uint32_t dma_off[DMA], dma_kb[DMA];
 #pragma unroll
   for (int i = 0; i < DMA; ++i) {
-    const uint32_t q = wave * DMA + i;
+    const uint32_t q = lw * DMA + i;
     dma_kb[i] = dma_chunk(BKB, q, lane) * 16u;
     dma_off[i] = dma_row(BKB, q, lane) * p.kbytes + dma_kb[i];
   }
@@ -200,10 +216,14 @@ void gemm_dense_kernel(DenseArgs p) {
 #pragma unroll
     for (int i = 0; i < DMA; ++i) {
       const uint32_t off = (s.k0 + dma_kb[i] < p.kbytes) ? dma_off[i] + s.k0 : kOobOffset;
-      dma_b128(s.r, st + (wave * DMA + i) * 1024, off);
+      dma_b128(s.r, st + (lw * DMA + i) * 1024, off);
     }
   };
 
+  // The main loop, in two copies: waves that issue slab loads and (with
+  // LOADERS) waves that only compute. Both run the same barriers.
+  auto main_loop = [&](auto loader_tag) {
+  constexpr bool IS_LOADER = decltype(loader_tag)::value;
   using Frag = typename std::conditional<DT == kBf16, bf16x8_t, i32x8_t>::type;
   Frag fa[2][FM], fb[2][FN];
   // A and B slots of the stage being read
@@ -252,7 +272,10 @@ void gemm_dense_kernel(DenseArgs p) {
 
   // ---- prologue: the first SLOTS slabs in flight -------------------------
 #pragma unroll
-  for (int b = 0; b < SLOTS; ++b) issue(next_slab());
+  for (int b = 0; b < SLOTS; ++b) {
+    const SlabLoad l = next_slab();
+    if constexpr (IS_LOADER) issue(l);
+  }
   wait_vmcnt<(SLOTS - 2) * DMA>();  // slabs 0 and 1 (stage 0) have landed
   __syncthreads();
   int aslot = 0, bslot = 1;         // slots of the stage being computed
@@ -280,14 +303,17 @@ void gemm_dense_kernel(DenseArgs p) {
       else wait_vmcnt<(SLOTS - 4) * DMA>();
       fresh_tile = false;
       lds_barrier();
-      issue(l0);
-      issue(l1);
+      if constexpr (IS_LOADER) {
+        issue(l0);
+        issue(l1);
+      }
+      const int na = (aslot + 2) % SLOTS, nb = (bslot + 2) % SLOTS;
+      read_frags(na, nb, 0, fa[c ^ 1], fb[c ^ 1]);
+      mma_step(fa[c], fb[c]);
+      interleave<NMMA, IS_LOADER ? NDMA : 0, NREAD>();
+      __builtin_amdgcn_sched_barrier(0);
       aslot = (aslot + 2) % SLOTS;
       bslot = (bslot + 2) % SLOTS;
-      read_frags(aslot, bslot, 0, fa[c ^ 1], fb[c ^ 1]);
-      mma_step(fa[c], fb[c]);
-      interleave<NMMA, NDMA, NREAD>();
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -340,6 +366,11 @@ void gemm_dense_kernel(DenseArgs p) {
     if (t >= p.num_tiles) break;
     cur = tile_state(p, t);
   }
+  };
+  if (loader)
+    main_loop(std::true_type{});
+  else
+    main_loop(std::false_type{});
   // The load cursor ran ahead into empty resources; let those LDS writes
   // land before the workgroup's LDS is released.
   wait_vmcnt<0>();
@@ -350,7 +381,7 @@ void gemm_dense_kernel(DenseArgs p) {
 template <int DT, int R>
 void launch_ring(const DenseArgs& a, int grid, hipStream_t stream) {
   constexpr Ring r = kRings[R];
-  hipLaunchKernelGGL((gemm_dense_kernel<DT, r.bkb, r.slots, r.waves_n>),
+  hipLaunchKernelGGL((gemm_dense_kernel<DT, r.bkb, r.slots, r.waves_n, r.loaders>),
                      dim3(grid), dim3(128 * r.waves_n), 0, stream, a);
 }
 
@@ -363,6 +394,8 @@ void launch_variant(int v, const DenseArgs& a, int grid, hipStream_t stream) {
     case 4: launch_ring<DT, 4>(a, grid, stream); break;
     case 5: launch_ring<DT, 5>(a, grid, stream); break;
     case 6: launch_ring<DT, 6>(a, grid, stream); break;
+    case 7: launch_ring<DT, 7>(a, grid, stream); break;
+    case 8: launch_ring<DT, 8>(a, grid, stream); break;
     default: launch_ring<DT, 0>(a, grid, stream); break;
   }
 }
