@@ -315,6 +315,33 @@ def test_fp4_integers_bit_exact(dev):
     assert np.array_equal(_bf16_result(C), ref)
 
 
+def test_fp4_signed_subnormal_and_zero_block_scales(dev):
+    # Block scales of every kind the e4m3 format holds: negative (the sign
+    # must reach the product), subnormal, +0 and -0, non-power-of-two
+    # mantissas and the largest finite magnitude. Per-element bound: fp32
+    # summation plus one bf16 rounding, at most 2^-8 (|A||B|)_ij here.
+    M, N, K = 256, 320, 512
+    g = np.random.default_rng(21)
+    kinds = np.array([0x38, 0xB8, 0xBF, 0x3A, 0x01, 0x83, 0x07, 0x00, 0x80,
+                      0x7E, 0xFE, 0x44, 0xC9], np.uint8)
+    Ac = g.integers(0, 16, (M, K)).astype(np.uint8)
+    Bc = g.integers(0, 16, (N, K)).astype(np.uint8)
+    As = g.choice(kinds, (M, K // 16))
+    Bs = g.choice(kinds, (N, K // 16))
+    Ap, Bp = gi.pack_nibbles(Ac), gi.pack_nibbles(Bc)
+    ta, tb = 0.75, 2.0 ** -12
+    C = tkg.gemm_fp4_blockscaled(_up(Ap, dev), _up(As, dev), ta,
+                                 _up(Bp, dev), _up(Bs, dev), tb)
+    R = oracle.gemm_fp4_blockscaled(Ap, As, ta, Bp, Bs, tb)
+    Ad = oracle.dequant_fp4_blockscaled(Ap, As)
+    Bd = oracle.dequant_fp4_blockscaled(Bp, Bs)
+    bound = 2.0 ** -8 * ta * tb * oracle.abs_gemm_f64(Ad, Bd)
+    G = _bf16_result(C)
+    assert np.all(np.abs(G - R) <= bound), float(np.max(np.abs(G - R) - bound))
+    assert np.any(As & 0x80) and np.any(Bs & 0x80)
+    assert relfro(G, R) <= 1e-2
+
+
 def test_fp4_variants_agree(dev):
     M, N, K = 700, 1300, 1088
     Ap, As, ta = gi.fp4_operand(60, M, K)

@@ -44,14 +44,6 @@ constexpr int STAGE_BYTES = 2 * TILE_V + 2 * TILE_S;  // 36 KiB
 
 static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS budget");
 
-// 1: v_cvt_scalef32_pk_f16_fp4 multiplies by the whole fp32 scale.
-// 0: it only applies the scale's power of two (the behaviour measured on
-//    gfx950); the remaining mantissa factor is applied with a packed fp16
-//    multiply (exact either way).
-#ifndef TKG_FP4_CVT_FULL_SCALE
-#define TKG_FP4_CVT_FULL_SCALE 0
-#endif
-
 struct TileState {
   int m0, n0;
   __amdgpu_buffer_rsrc_t rav, rbv, ras, rbs;
@@ -88,31 +80,48 @@ __device__ __forceinline__ f16x8_t dequant8(uint32_t packed, float scale,
   f16x2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, scale, 1);
   f16x2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, scale, 2);
   f16x2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, scale, 3);
-#if !TKG_FP4_CVT_FULL_SCALE
   h0 = h0 * mant;
   h1 = h1 * mant;
   h2 = h2 * mant;
   h3 = h3 * mant;
-#endif
   return f16x8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
 
 // Block scale (byte BYTE of `word`, OCP e4m3) -> the scale operand of the
-// convert and the fp16 mantissa factor still to apply.
+// convert and the fp16 factor still to apply. The convert uses only the
+// magnitude of its scale's power of two (measured on gfx950: mantissa and
+// sign are ignored), so the scale is passed as decoded and the factor
+// carries the sign and the mantissa: +-(1 + m/8) for m in 0..7, exact in
+// fp16. Subnormal e4m3 scales decode to normal fp32 values, so they split
+// the same way; a zero scale gives a zero power of two (fp16 underflow).
 template <int BYTE>
 __device__ __forceinline__ void split_scale(uint32_t word, float& s,
                                             f16x2_t& mant) {
-  const float f = __builtin_amdgcn_cvt_f32_fp8((int)word, BYTE);
-#if TKG_FP4_CVT_FULL_SCALE
-  s = f;
-  mant = f16x2_t{(_Float16)1.0f, (_Float16)1.0f};
-#else
-  const uint32_t u = __builtin_bit_cast(uint32_t, f);
-  s = __builtin_bit_cast(float, u & 0xFF800000u);  // sign, power of two
+  s = __builtin_amdgcn_cvt_f32_fp8((int)word, BYTE);
+  const uint32_t u = __builtin_bit_cast(uint32_t, s);
   const _Float16 m =
-      (_Float16)__builtin_bit_cast(float, (u & 0x007FFFFFu) | 0x3F800000u);
-  mant = f16x2_t{m, m};  // in [1, 2), exact in fp16 (3 mantissa bits)
-#endif
+      (_Float16)__builtin_bit_cast(float, (u & 0x807FFFFFu) | 0x3F800000u);
+  mant = f16x2_t{m, m};
+}
+
+// VALU instructions placed after each MFMA (6 measured fastest among
+// 3, 4, 6, 8 and 12 at 8192^3).
+constexpr int kValuPerMfma = 6;
+
+// Scheduling recipe for one k-step of NMMA MFMAs: the LDS reads (NREAD,
+// three after each of the first MFMAs) and slab loads (NDMA, one after each
+// MFMA) are front-loaded; the dequantization VALU work of the next k-step is
+// spread over all MFMAs, so the matrix core is fed while the VALU converts.
+template <int NMMA, int NREAD, int NDMA, int Q = 0>
+__device__ __forceinline__ void interleave_fp4() {
+  if constexpr (Q < NMMA) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    constexpr int r = NREAD - 3 * Q >= 3 ? 3 : (NREAD - 3 * Q > 0 ? NREAD - 3 * Q : 0);
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+    if constexpr (Q < NDMA) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);  // VALU
+    interleave_fp4<NMMA, NREAD, NDMA, Q + 1>();
+  }
 }
 
 template <int WAVES_N>
@@ -233,36 +242,54 @@ void gemm_fp4_kernel(Fp4Args p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
 
-  // 4 MFMA k-steps out of chunk s: k-step q uses dword q of the chunk, whose
-  // block (16 elements) is 2*(2s + khalf) + q/2 of the stage, i.e. byte
-  // 2*khalf + q/2 of scale word s.
-  auto mma_kstep = [&](const Raw& r, int s, auto qc) {
-    constexpr int q = decltype(qc)::value;
+  // Dequantized fragments of one MFMA k-step (8 K-elements per lane). Two
+  // sets alternate: while the MFMAs consume one, the VALU fills the other
+  // with the next k-step, so conversion and matrix work overlap.
+  struct Deq {
     f16x8_t a[FM], b[FN];
+  };
+  // k-step q (0..3) of chunk s: dword q of the chunk, whose block (16
+  // elements) is 2*(2s + khalf) + q/2 of the stage, i.e. byte
+  // 2*khalf + q/2 of scale word s.
+  auto dequant = [&](const Raw& r, int s, auto qc, Deq& d) {
+    constexpr int q = decltype(qc)::value;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       float sc; f16x2_t m;
       split_scale<q / 2>(r.sa[i][s] >> (16 * khalf), sc, m);
-      a[i] = dequant8((uint32_t)r.a[i][q], sc, m);
+      d.a[i] = dequant8((uint32_t)r.a[i][q], sc, m);
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       float sc; f16x2_t m;
       split_scale<q / 2>(r.sb[j][s] >> (16 * khalf), sc, m);
-      b[j] = dequant8((uint32_t)r.b[j][q], sc, m);
+      d.b[j] = dequant8((uint32_t)r.b[j][q], sc, m);
     }
+  };
+  // Keeps the conversion of a k-step ahead of a block boundary: without it
+  // the compiler sinks the VALU work past the loop's branch, where it can no
+  // longer overlap the MFMAs.
+  auto pin = [&](Deq& d) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(d.a[i]));
+#pragma unroll
+    for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(d.b[j]));
+  };
+  auto mma = [&](const Deq& d) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[j], a[i], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(d.b[j], d.a[i], acc[i][j], 0, 0, 0);
   };
-  auto mma_chunk = [&](const Raw& r, int s) {
-    mma_kstep(r, s, std::integral_constant<int, 0>{});
-    mma_kstep(r, s, std::integral_constant<int, 1>{});
-    mma_kstep(r, s, std::integral_constant<int, 2>{});
-    mma_kstep(r, s, std::integral_constant<int, 3>{});
-  };
+  using Q0 = std::integral_constant<int, 0>;
+  using Q1 = std::integral_constant<int, 1>;
+  using Q2 = std::integral_constant<int, 2>;
+  using Q3 = std::integral_constant<int, 3>;
+  constexpr int NMMA = FM * FN;
+  constexpr int NREAD0 = 2 * (FM + FN);   // chunk 0: values + scales
+  constexpr int NREAD1 = FM + FN;         // chunk 1: values
+  constexpr int NDMA = 2 * VDMA + 2 * SDMA;
 
   // ---- prologue ------------------------------------------------------------
 #pragma unroll
@@ -271,19 +298,41 @@ void gemm_fp4_kernel(Fp4Args p) {
   __syncthreads();
 
   Raw raw[2];
+  Deq deq[2];
   read_raw(0, 0, raw[0], raw[0]);
+  dequant(raw[0], 0, Q0{}, deq[0]);
 
+  // Eight k-steps per stage (chunk s = u/4, k-step q = u%4). k-step u
+  // multiplies deq[u&1] while deq[(u+1)&1] is filled with k-step u+1; the
+  // last k-step converts chunk 0 of the next stage. Chunk 1 is read from LDS
+  // at u = 0; at u = 4 (all waves have read the stage) the next stage must
+  // have landed, the barrier frees this buffer for the cursor's next stage,
+  // and chunk 0 of the next stage is read.
   int buf = 0;
   bool fresh_tile = false;  // finish stores are in flight
   for (;;) {
     for (uint32_t kt = 0; kt < p.nk; ++kt) {
-      // chunk 0 of this stage is in raw[0]; fetch chunk 1, multiply chunk 0
-      read_raw(buf, 1, raw[1], raw[0]);
-      mma_chunk(raw[0], 0);
-      __builtin_amdgcn_sched_barrier(0);
-      // stage boundary: the next stage must have landed; this one is free
-      // (right after a finish, its stores are in flight too: wait for all)
+      // the cursor moves here so that no branch splits the stage's k-steps
       const StageLoad nl = next_stage();
+      read_raw(buf, 1, raw[1], raw[0]);
+      dequant(raw[0], 0, Q1{}, deq[1]);
+      mma(deq[0]);
+      interleave_fp4<NMMA, NREAD1, 0>();
+      __builtin_amdgcn_sched_barrier(0);
+      dequant(raw[0], 0, Q2{}, deq[0]);
+      mma(deq[1]);
+      interleave_fp4<NMMA, 0, 0>();
+      __builtin_amdgcn_sched_barrier(0);
+      dequant(raw[0], 0, Q3{}, deq[1]);
+      mma(deq[0]);
+      interleave_fp4<NMMA, 0, 0>();
+      __builtin_amdgcn_sched_barrier(0);
+      dequant(raw[1], 1, Q0{}, deq[0]);
+      mma(deq[1]);
+      interleave_fp4<NMMA, 0, 0>();
+      pin(deq[0]);
+      __builtin_amdgcn_sched_barrier(0);
+
       if (fresh_tile) wait_vmcnt<0>();
       else wait_vmcnt<(STAGES - 2) * DMA_PER_STAGE>();
       fresh_tile = false;
@@ -291,7 +340,22 @@ void gemm_fp4_kernel(Fp4Args p) {
       issue(nl, buf);
       const int nbuf = (buf + 1 == STAGES) ? 0 : buf + 1;
       read_raw(nbuf, 0, raw[0], raw[0]);
-      mma_chunk(raw[1], 1);
+      dequant(raw[1], 1, Q1{}, deq[1]);
+      mma(deq[0]);
+      interleave_fp4<NMMA, NREAD0, NDMA>();
+      __builtin_amdgcn_sched_barrier(0);
+      dequant(raw[1], 1, Q2{}, deq[0]);
+      mma(deq[1]);
+      interleave_fp4<NMMA, 0, 0>();
+      __builtin_amdgcn_sched_barrier(0);
+      dequant(raw[1], 1, Q3{}, deq[1]);
+      mma(deq[0]);
+      interleave_fp4<NMMA, 0, 0>();
+      __builtin_amdgcn_sched_barrier(0);
+      dequant(raw[0], 0, Q0{}, deq[0]);
+      mma(deq[1]);
+      interleave_fp4<NMMA, 0, 0>();
+      pin(deq[0]);
       __builtin_amdgcn_sched_barrier(0);
       buf = nbuf;
     }
