@@ -121,14 +121,16 @@ const char *tkg_status_string(int status);
  *               round-robin order.
  *   variant  -- bf16/fp8: kernel configuration, as (K bytes per row
  *               of an LDS slab, operand slabs in the LDS ring, waves per
- *               workgroup, waves issuing the global loads):
- *               0 = (128, 4, 8, 4) default, 1 = (128, 5, 8, 4),
- *               2 = (128, 4, 8, 8), 3 = (128, 5, 8, 8), 4 = (64, 10, 8, 8),
- *               5 = (128, 5, 4, 4), 6 = (128, 4, 4, 4), 7 = (64, 10, 4, 4),
- *               8 = (64, 8, 4, 4); TKG_ERR_SHAPE outside 0..8.
+ *               workgroup, waves issuing the global loads, MFMA block):
+ *               0 = (128, 4, 8, 4, 16) default, 1 = (128, 5, 8, 4, 16),
+ *               2 = (128, 4, 8, 4, 32), 3 = (128, 5, 8, 4, 32),
+ *               4 = (128, 4, 8, 8, 32), 5 = (128, 4, 4, 4, 32),
+ *               6 = (64, 10, 8, 8, 32); MFMA block 16 = 16x16x32 bf16
+ *               MFMAs, 32 = 32x32x16; fp8 always uses 32x32x64.
+ *               TKG_ERR_SHAPE outside 0..6.
  *               4-bit product: 0 = 4 waves (default), 1 = 8 waves;
  *               TKG_ERR_SHAPE outside 0..1. Every variant of a product
- *               computes the same result.
+ *               computes the same sums (the tests find them bit-identical).
  * Page "ThunderKittens: Simple, Fast, and Adorable AI Kernels", section
  * 3.4, "Persistent Grid Launch" (Table 2) and "Block Launch Order and L2
  * Cache Reuse" (Table 3), measure these choices.
@@ -160,12 +162,20 @@ int tkg_gemm_ex(int dtype, int64_t M, int64_t N, int64_t K, const void *A,
  *   step   -- MFMA k-step inside a stage (0 .. steps-1);
  *   part   -- 0 or 1, which 16-byte half of a 32-byte fp8 operand
  *             (0 for bf16 and for the 4-bit values);
- *   frag   -- 32-row fragment index inside the workgroup tile (0 .. 7).
+ *   frag   -- fragment index inside the 256-row workgroup tile
+ *             (0 .. 256/R - 1, R = tkg_lds_fragment_rows(dtype)).
+ * These are the reads of the default kernel configuration (variant 0).
  * Returns the number of k-steps per stage for the dtype, or a negative
  * tkg_status for an invalid argument.
  */
 int tkg_lds_fragment_offsets(int dtype, int step, int part, int frag,
                              uint32_t *out64);
+
+/*
+ * Rows R of one operand fragment of the default kernel for dtype (the MFMA
+ * block: 16 for the 16x16 blocks, 32 for 32x32), or a negative tkg_status.
+ */
+int tkg_lds_fragment_rows(int dtype);
 
 /*
  * Row length in bytes of the staged operand tiles for dtype (the unit the

@@ -81,3 +81,22 @@ def test_lds_introspection_errors():
     assert L.tkg_lds_fragment_offsets(0, 99, 0, 0, buf) == S["TKG_ERR_SHAPE"]
     assert L.tkg_lds_fragment_offsets(0, 0, 0, 0, None) == S["TKG_ERR_NULL"]
     assert L.tkg_lds_row_bytes(9) == S["TKG_ERR_SHAPE"]
+
+
+def test_build_script_loads_without_its_package():
+    # __graft_entry__.build() must work when libtkg.so is missing or stale,
+    # so the build script may not import the package (which loads the
+    # library on import).
+    import ast
+    import importlib.util
+    path = os.path.join(os.path.dirname(tkg.__file__), "_build.py")
+    tree = ast.parse(open(path).read())
+    for node in ast.walk(tree):
+        if isinstance(node, ast.ImportFrom):
+            assert node.level == 0 and not (node.module or "").startswith("tiled_dense_gemm_amd")
+        if isinstance(node, ast.Import):
+            assert all(not a.name.startswith("tiled_dense_gemm_amd") for a in node.names)
+    spec = importlib.util.spec_from_file_location("tkg_build_probe", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    assert callable(mod.build) and mod.LIB.endswith("libtkg.so")

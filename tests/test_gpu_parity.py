@@ -30,6 +30,7 @@ pytestmark = pytest.mark.gpu
 BF16_RELFRO = 1e-3
 BF16_ELEM_REL, BF16_ELEM_ABS = 1e-2, 1e-3
 LOWP_RELFRO = 2e-2
+DENSE_VARIANTS = 7   # kernel configurations selectable by tkg_opts.variant
 
 
 @pytest.fixture(scope="module")
@@ -185,11 +186,11 @@ def test_kernel_variants_agree(dev, dtype):
         Bt, sb = gi.device.fp8_operand(4, N, K, device=dev)
         d = tkg.DTYPE_FP8
     outs = []
-    for v in range(9):
+    for v in range(DENSE_VARIANTS):
         C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         assert tkg.tkg_gemm_ex(d, M, N, K, A, None, sa, Bt, None, sb, C, variant=v) == 0
         outs.append(C)
-    for v in range(1, 9):
+    for v in range(1, DENSE_VARIANTS):
         assert torch.equal(outs[v].view(torch.int16), outs[0].view(torch.int16)), v
     a = A.view(torch.int16).cpu().numpy().view(np.uint16) if dtype == "bf16" else to_numpy_u8(A)
     b = Bt.view(torch.int16).cpu().numpy().view(np.uint16) if dtype == "bf16" else to_numpy_u8(Bt)
@@ -198,7 +199,8 @@ def test_kernel_variants_agree(dev, dtype):
         check_bf16(G, decode_bf16(a), decode_bf16(b), "variants")
     else:
         assert relfro(G, oracle.gemm_fp8(a, sa, b, sb)) <= LOWP_RELFRO
-    assert tkg.tkg_gemm_ex(d, M, N, K, A, None, sa, Bt, None, sb, outs[0], variant=9) == -2
+    assert tkg.tkg_gemm_ex(d, M, N, K, A, None, sa, Bt, None, sb, outs[0],
+                           variant=DENSE_VARIANTS) == -2
 
 
 def test_bf16_side_stream(dev):

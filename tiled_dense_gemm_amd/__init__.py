@@ -18,7 +18,8 @@ import os
 
 __all__ = [
     "gemm_bf16", "gemm_fp8", "gemm_fp4_blockscaled", "tkg_gemm_ex",
-    "tkg_status_string", "lds_fragment_offsets", "lds_row_bytes", "lib",
+    "tkg_status_string", "lds_fragment_offsets", "lds_fragment_rows",
+    "lds_row_bytes", "lib",
     "TkgError", "DTYPE_BF16", "DTYPE_FP8", "DTYPE_FP4_BLOCKSCALED",
     "STATUS", "LIB_PATH",
 ]
@@ -52,8 +53,8 @@ def _load() -> ctypes.CDLL:
         pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            "libtkg.so is not built (%s); run `python -m "
-            "tiled_dense_gemm_amd._build`" % LIB_PATH)
+            "libtkg.so is not built (%s); run `python "
+            "tiled_dense_gemm_amd/_build.py`" % LIB_PATH)
     L = ctypes.CDLL(LIB_PATH)
     i64, vp, f32, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
     L.gemm_bf16.argtypes = [i64, i64, i64, vp, vp, vp, vp]
@@ -73,6 +74,8 @@ def _load() -> ctypes.CDLL:
     L.tkg_lds_fragment_offsets.restype = i32
     L.tkg_lds_row_bytes.argtypes = [i32]
     L.tkg_lds_row_bytes.restype = i32
+    L.tkg_lds_fragment_rows.argtypes = [i32]
+    L.tkg_lds_fragment_rows.restype = i32
     return L
 
 
@@ -87,6 +90,13 @@ def lds_row_bytes(dtype: int) -> int:
     r = lib.tkg_lds_row_bytes(int(dtype))
     if r < 0:
         raise TkgError(r, "tkg_lds_row_bytes")
+    return r
+
+
+def lds_fragment_rows(dtype: int) -> int:
+    r = lib.tkg_lds_fragment_rows(int(dtype))
+    if r < 0:
+        raise TkgError(r, "tkg_lds_fragment_rows")
     return r
 
 

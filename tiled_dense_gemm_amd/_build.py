@@ -1,8 +1,10 @@
 """Build step for the HIP library ``libtkg.so`` (gfx950).
 
-``python -m tiled_dense_gemm_amd._build`` compiles every ``csrc/*.hip`` file
+``python tiled_dense_gemm_amd/_build.py`` compiles every ``csrc/*.hip`` file
 for gfx950 with hipcc and links them into ``tiled_dense_gemm_amd/libtkg.so``
-in place. The build is always done from scratch (seconds per file).
+in place. The build is always done from scratch (seconds per file). The
+script imports nothing from its package, so it runs before the library
+exists (the package itself loads the library on import).
 """
 from __future__ import annotations
 

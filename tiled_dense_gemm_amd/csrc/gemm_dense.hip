@@ -50,12 +50,14 @@ static_assert(BM == BN, "A and B slabs share offsets");
 // LOADERS: 1 = only the waves of the first wave row (one per SIMD) issue
 // the slab loads, so their partner wave on each SIMD keeps issuing MFMAs
 // while the loaders wait for the memory pipeline to accept loads.
+// MI: the MFMA block, 32 (32x32x16 bf16 / 32x32x64 fp8) or 16 (16x16x32 /
+// 16x16x128).
 struct Ring {
-  int bkb, slots, waves_n, loaders;
+  int bkb, slots, waves_n, loaders, mi;
 };
-constexpr Ring kRings[] = {{128, 4, 4, 1}, {128, 5, 4, 1}, {128, 4, 4, 0},
-                           {128, 5, 4, 0}, {64, 10, 4, 0}, {128, 5, 2, 0},
-                           {128, 4, 2, 0}, {64, 10, 2, 0}, {64, 8, 2, 0}};
+constexpr Ring kRings[] = {{128, 4, 4, 1, 16}, {128, 5, 4, 1, 16}, {128, 4, 4, 1, 32},
+                           {128, 5, 4, 1, 32}, {128, 4, 4, 0, 32}, {128, 4, 2, 0, 32},
+                           {64, 10, 4, 0, 32}};
 constexpr int kNumRings = sizeof(kRings) / sizeof(kRings[0]);
 
 struct TileState {
@@ -84,40 +86,13 @@ __device__ __forceinline__ TileState tile_state(const DenseArgs& p, int t) {
   return s;
 }
 
-// Evenly spread `total` instructions over `slots` MFMA slots: the count
-// placed after MFMA number q.
-constexpr int spread(int total, int slots, int q) {
-  return (q + 1) * total / slots - q * total / slots;
-}
-
-// The first `total` items placed `per` at a time after the first MFMAs.
-constexpr int front(int total, int per, int q) {
-  return total - q * per >= per ? per : (total - q * per > 0 ? total - q * per : 0);
-}
-
-// Scheduling recipe for one k-step: each MFMA followed by its share of the
-// slab loads (NDMA, spread evenly) and of the next k-step's fragment reads
-// (NREAD, three per MFMA from the first one on, so they have most of the
-// k-step to land).
-template <int NMMA, int NDMA, int NREAD, int Q = 0>
-__device__ __forceinline__ void interleave() {
-  if constexpr (Q < NMMA) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    if constexpr (spread(NDMA, NMMA, Q) > 0)
-      __builtin_amdgcn_sched_group_barrier(0x020, spread(NDMA, NMMA, Q), 0);
-    if constexpr (front(NREAD, 3, Q) > 0)
-      __builtin_amdgcn_sched_group_barrier(0x100, front(NREAD, 3, Q), 0);
-    interleave<NMMA, NDMA, NREAD, Q + 1>();
-  }
-}
-
-template <int DT, int BKB, int SLOTS, int WAVES_N, int LOADERS>
+template <int DT, int BKB, int SLOTS, int WAVES_N, int LOADERS, int MI, bool KTAIL>
 __global__ __launch_bounds__(128 * WAVES_N)
 __attribute__((amdgpu_waves_per_eu(WAVES_N / 2, WAVES_N / 2)))
 void gemm_dense_kernel(DenseArgs p) {
   constexpr int WAVES = 2 * WAVES_N;
   constexpr int WM = BM / 2, WN = BN / WAVES_N;   // wave tile
-  constexpr int FM = WM / 32, FN = WN / 32;       // 32x32 accumulators
+  constexpr int FM = WM / MI, FN = WN / MI;       // MIxMI accumulators
   constexpr int NMMA = FM * FN;                   // MFMAs per k-step
   constexpr int SLAB = BM * BKB;           // bytes of one operand slab
   // waves that issue slab loads, and b128 loads per such wave per slab
@@ -128,13 +103,20 @@ void gemm_dense_kernel(DenseArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[SLOTS * SLAB];
   TKG_LDS uint8_t* smem = (TKG_LDS uint8_t*)smem_raw;
 
-  // MFMA k-steps per stage (16 bf16 or 64 fp8 of K each) and 16-byte reads
-  // per operand fragment. The loop body runs an even number of k-steps (the
-  // fragment registers alternate between two sets): one stage, or two
-  // stages when a stage is a single k-step.
-  constexpr int KSTEPS = (DT == kBf16) ? BKB / 32 : BKB / 64;
-  constexpr int PARTS = (DT == kBf16) ? 1 : 2;
+  // K bytes per row of one MFMA k-step, 16-byte chunks per k-step (CPK),
+  // lane groups sharing a row (P: lanes l, l+MI, ... read the same row at
+  // different chunks) and 16-byte reads per lane per fragment (PARTS). The
+  // loop body runs an even number of k-steps (the fragment registers
+  // alternate between two sets): one stage, or two when a stage is a single
+  // k-step.
+  constexpr int KSTEP_BYTES = (DT == kBf16 ? 32 : 64) * (32 / MI);
+  constexpr int KSTEPS = BKB / KSTEP_BYTES;
+  constexpr int CPK = KSTEP_BYTES / 16;
+  constexpr int P = 64 / MI;
+  constexpr int PARTS = CPK / P;
   constexpr int TRIP_STAGES = (KSTEPS >= 2) ? 1 : 2;
+  using Acc = typename std::conditional<MI == 32, f32x16_t, f32x4_t>::type;
+  constexpr int NE = MI * MI / 64;                // accumulator elements per lane
   static_assert(KSTEPS % 2 == 0 || KSTEPS == 1, "k-steps per trip must be even");
 
   const int tid = threadIdx.x;
@@ -151,31 +133,42 @@ void gemm_dense_kernel(DenseArgs p) {
   const uint32_t nk = (TRIP_STAGES == 2) ? (nk_raw + (nk_raw & 1)) : nk_raw;
 
   // ---- per-lane staging offsets (tile independent) -----------------------
-  // DMA instruction i of this wave fills rows dma_row(q), q = wave*DMA + i.
+  // DMA instruction i of this wave fills rows dma_row(q), q = lw*DMA + i.
   // loader index of this wave (waves with wm > 0 load nothing if LOADERS)
   const int lw = LOADERS ? wn : wave;
   const bool loader = !LOADERS || wm == 0;
-  uint32_t dma_off[DMA], dma_kb[DMA];
+  // Without a K tail the offset of load q is a uniform part (scalar) plus
+  // one of two per-lane values (dma_lane_offset); with a tail each load
+  // keeps its full per-lane offset and K chunk for the bounds test.
+  constexpr int NOFF = KTAIL ? DMA : 2;
+  uint32_t dma_off[NOFF], dma_kb[KTAIL ? DMA : 1];
+  if constexpr (KTAIL) {
 #pragma unroll
-  for (int i = 0; i < DMA; ++i) {
-    const uint32_t q = lw * DMA + i;
-    dma_kb[i] = dma_chunk(BKB, q, lane) * 16u;
-    dma_off[i] = dma_row(BKB, q, lane) * p.kbytes + dma_kb[i];
+    for (int i = 0; i < DMA; ++i) {
+      const uint32_t q = lw * DMA + i;
+      dma_kb[i] = dma_chunk(BKB, q, lane) * 16u;
+      dma_off[i] = dma_row(BKB, q, lane) * p.kbytes + dma_kb[i];
+    }
+  } else {
+    dma_kb[0] = 0;
+#pragma unroll
+    for (int par = 0; par < 2; ++par) dma_off[par] = dma_lane_offset(BKB, par, lane, p.kbytes);
   }
+  const uint32_t rows_step = dma_rows_per_instr(BKB) * p.kbytes;  // bytes per load q
 
   // ---- per-lane fragment read offsets ------------------------------------
-  // Fragment rows are (multiple of 32) + lane%32, so the swizzle mask only
-  // depends on the lane. k-step s of a stage reads chunk 2s + lane/32 (bf16)
-  // or chunks 4s + 2*(lane/32) and 4s + 2*(lane/32) + 1 (fp8): the same K
-  // order for A and B, so the MFMA reduces over matching elements.
-  const uint32_t frow = lane & 31;
-  const uint32_t khalf = lane >> 5;
+  // Fragment rows are (multiple of MI) + lane%MI, so the swizzle mask only
+  // depends on the lane. Lane l reads, at k-step s, the PARTS chunks from
+  // s*CPK + (l/MI)*PARTS on: the same K order for A and B, so the MFMA
+  // reduces over matching elements.
+  const uint32_t frow = lane % MI;
+  const uint32_t kpart = lane / MI;
   uint32_t roff[KSTEPS][PARTS];
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
     for (int q = 0; q < PARTS; ++q)
-      roff[s][q] = swz_offset(BKB, frow, (DT == kBf16) ? 2 * s + khalf : 4 * s + 2 * khalf + q);
+      roff[s][q] = swz_offset(BKB, frow, s * CPK + kpart * PARTS + q);
   const uint32_t a_base = wm * WM * BKB;   // within an A slab
   const uint32_t b_base = wn * WN * BKB;   // within a B slab
 
@@ -210,14 +203,22 @@ void gemm_dense_kernel(DenseArgs p) {
     advance_load();
     return s;
   };
-  // Branch-free loads of one slab; chunks past K read zeros.
-  auto issue = [&](const SlabLoad& s) {
-    TKG_LDS uint8_t* st = smem + s.slot * SLAB;
-#pragma unroll
-    for (int i = 0; i < DMA; ++i) {
+  // Load i of one slab. Without a K tail every chunk is inside K: the
+  // per-lane offset is loop invariant and the stage's K offset is the
+  // scalar offset. With a tail, chunks past K read zeros.
+  auto issue_one = [&](const SlabLoad& s, int i) {
+    TKG_LDS uint8_t* dst = smem + s.slot * SLAB + (lw * DMA + i) * 1024;
+    if constexpr (KTAIL) {
       const uint32_t off = (s.k0 + dma_kb[i] < p.kbytes) ? dma_off[i] + s.k0 : kOobOffset;
-      dma_b128(s.r, st + (lw * DMA + i) * 1024, off);
+      dma_b128(s.r, dst, off);
+    } else {
+      const uint32_t q = lw * DMA + i;
+      dma_b128_soff(s.r, dst, dma_off[q & 1], s.k0 + q * rows_step);
     }
+  };
+  auto issue = [&](const SlabLoad& s) {
+#pragma unroll
+    for (int i = 0; i < DMA; ++i) issue_one(s, i);
   };
 
   // The main loop, in two copies: waves that issue slab loads and (with
@@ -225,48 +226,67 @@ void gemm_dense_kernel(DenseArgs p) {
   auto main_loop = [&](auto loader_tag) {
   constexpr bool IS_LOADER = decltype(loader_tag)::value;
   using Frag = typename std::conditional<DT == kBf16, bf16x8_t, i32x8_t>::type;
-  Frag fa[2][FM], fb[2][FN];
-  // A and B slots of the stage being read
-  auto read_frags = [&](int aslot, int bslot, int s, Frag (&a)[FM], Frag (&b)[FN]) {
-    const TKG_LDS uint8_t* sa = smem + aslot * SLAB;
-    const TKG_LDS uint8_t* sb = smem + bslot * SLAB;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      if constexpr (DT == kBf16) {
-        a[i] = lds_read<bf16x8_t>(sa, a_base + i * 32 * BKB + roff[s][0]);
-      } else {
-        const i32x4_t lo = lds_read<i32x4_t>(sa, a_base + i * 32 * BKB + roff[s][0]);
-        const i32x4_t hi = lds_read<i32x4_t>(sa, a_base + i * 32 * BKB + roff[s][PARTS - 1]);
-        a[i] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      if constexpr (DT == kBf16) {
-        b[j] = lds_read<bf16x8_t>(sb, b_base + j * 32 * BKB + roff[s][0]);
-      } else {
-        const i32x4_t lo = lds_read<i32x4_t>(sb, b_base + j * 32 * BKB + roff[s][0]);
-        const i32x4_t hi = lds_read<i32x4_t>(sb, b_base + j * 32 * BKB + roff[s][PARTS - 1]);
-        b[j] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
+  // Fragment registers. A fragment i is last used by MFMA (i, FN-1) of a
+  // k-step, so the next k-step's A fragment i is read into the same
+  // registers right after it. B fragments are used until the k-step's last
+  // row of MFMAs: two sets, the next one read at the k-step's start, unless
+  // registers are short (fp8 16x16: one set, each B fragment re-read right
+  // after its last use, a few MFMAs before its next one).
+  constexpr bool B_SINGLE = (DT == kFp8 && MI == 16);
+  constexpr int BSETS = B_SINGLE ? 1 : 2;
+  Frag fa[FM], fb[BSETS][FN];
+  auto read_one = [&](const TKG_LDS uint8_t* base, uint32_t row0, int s, Frag& v) {
+    if constexpr (DT == kBf16) {
+      v = lds_read<bf16x8_t>(base, row0 + roff[s][0]);
+    } else {
+      const i32x4_t lo = lds_read<i32x4_t>(base, row0 + roff[s][0]);
+      const i32x4_t hi = lds_read<i32x4_t>(base, row0 + roff[s][PARTS - 1]);
+      v = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   };
+  auto read_a = [&](int aslot, int s, int i) {
+    read_one(smem + aslot * SLAB, a_base + i * MI * BKB, s, fa[i]);
+  };
+  auto read_b = [&](int bslot, int s, int j, Frag& v) {
+    read_one(smem + bslot * SLAB, b_base + j * MI * BKB, s, v);
+  };
 
-  f32x16_t acc[FM][FN];
+  Acc acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
-  auto mma_step = [&](const Frag (&a)[FM], const Frag (&b)[FN]) {
+    for (int j = 0; j < FN; ++j) acc[i][j] = Acc{};
+  auto mma = [&](const Frag& b, const Frag& a, Acc& c) {
+    if constexpr (MI == 32) {
+      if constexpr (DT == kBf16) c = mfma_bf16(b, a, c);
+      else c = mfma_fp8(b, a, c);
+    } else {
+      if constexpr (DT == kBf16) c = mfma16_bf16(b, a, c);
+      else c = mfma16_fp8(b, a, c);
+    }
+  };
+  // One k-step in program order: after MFMA (i, j) come the instructions of
+  // its slot, and a scheduling fence keeps that order, so loads and reads
+  // are spread over the MFMAs exactly as written. Fragment reads of the
+  // next k-step come from slots (ns_a, ns_b) at k-step ns.
+  auto kstep_body = [&](int c, int ns, int ns_a, int ns_b, auto&& extra) {
+    Frag (&b)[FN] = fb[B_SINGLE ? 0 : c];
+    Frag (&bn)[FN] = fb[B_SINGLE ? 0 : c ^ 1];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         // B first: the accumulator holds the transposed block (see finish)
-        if constexpr (DT == kBf16)
-          acc[i][j] = mfma_bf16(b[j], a[i], acc[i][j]);
-        else
-          acc[i][j] = mfma_fp8(b[j], a[i], acc[i][j]);
+        mma(b[j], fa[i], acc[i][j]);
+        const int q = i * FN + j;
+        if constexpr (B_SINGLE) {
+          if (i == FM - 1) read_b(ns_b, ns, j, bn[j]);
+        } else {
+          if (q < FN) read_b(ns_b, ns, q, bn[q]);
+        }
+        if (j == FN - 1) read_a(ns_a, ns, i);
+        extra(q);
+        __builtin_amdgcn_sched_barrier(0);
       }
   };
 
@@ -279,23 +299,22 @@ void gemm_dense_kernel(DenseArgs p) {
   wait_vmcnt<(SLOTS - 2) * DMA>();  // slabs 0 and 1 (stage 0) have landed
   __syncthreads();
   int aslot = 0, bslot = 1;         // slots of the stage being computed
-  read_frags(aslot, bslot, 0, fa[0], fb[0]);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) read_a(aslot, 0, i);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) read_b(bslot, 0, j, fb[0][j]);
 
-  // One MFMA k-step. Register set c holds its fragments; the next k-step's
-  // fragments go to set c ^ 1. At the last k-step of a stage the next stage
-  // must have landed (wait + barrier): SLOTS slabs were issued before stage
-  // k's end, so at most SLOTS - 4 slabs may still be loading. After the
-  // barrier every wave has read the current stage, so its two slots are
-  // refilled with the next two slabs of the cursor.
+  // One MFMA k-step; c selects the B register set. At the last k-step of a
+  // stage the next stage must have landed (wait + barrier): SLOTS slabs were
+  // issued before stage k's end, so at most SLOTS - 4 slabs may still be
+  // loading. After the barrier every wave has read the current stage, so
+  // its two slots are refilled with the next two slabs of the cursor, the
+  // loads spread over the MFMAs.
   bool fresh_tile = false;  // finish stores are in flight
-  constexpr int NREAD = (FM + FN) * PARTS;   // ds_read_b128 per k-step
-  constexpr int NDMA = 2 * DMA;              // slab loads per stage boundary
+  constexpr int NDMA = 2 * DMA;             // slab loads per stage boundary
   auto kstep = [&](int c, int s, bool last) {
     if (!last) {
-      read_frags(aslot, bslot, s + 1, fa[c ^ 1], fb[c ^ 1]);
-      mma_step(fa[c], fb[c]);
-      interleave<NMMA, 0, NREAD>();
-      __builtin_amdgcn_sched_barrier(0);
+      kstep_body(c, s + 1, aslot, bslot, [&](int) {});
     } else {
       const SlabLoad l0 = next_slab();
       const SlabLoad l1 = next_slab();
@@ -303,17 +322,18 @@ void gemm_dense_kernel(DenseArgs p) {
       else wait_vmcnt<(SLOTS - 4) * DMA>();
       fresh_tile = false;
       lds_barrier();
-      if constexpr (IS_LOADER) {
-        issue(l0);
-        issue(l1);
-      }
       const int na = (aslot + 2) % SLOTS, nb = (bslot + 2) % SLOTS;
-      read_frags(na, nb, 0, fa[c ^ 1], fb[c ^ 1]);
-      mma_step(fa[c], fb[c]);
-      interleave<NMMA, IS_LOADER ? NDMA : 0, NREAD>();
-      __builtin_amdgcn_sched_barrier(0);
-      aslot = (aslot + 2) % SLOTS;
-      bslot = (bslot + 2) % SLOTS;
+      kstep_body(c, 0, na, nb, [&](int q) {
+        if constexpr (IS_LOADER) {
+#pragma unroll
+          for (int d = q * NDMA / NMMA; d < (q + 1) * NDMA / NMMA; ++d) {
+            if (d < DMA) issue_one(l0, d);
+            else issue_one(l1, d - DMA);
+          }
+        }
+      });
+      aslot = na;
+      bslot = nb;
     }
   };
 
@@ -324,19 +344,19 @@ void gemm_dense_kernel(DenseArgs p) {
         kstep(u & 1, u % KSTEPS, u % KSTEPS == KSTEPS - 1);
     }
 
-    // ---- finish: C[m][n .. n+3] from accumulator rows 4g .. 4g+3 ----------
+    // ---- finish: C[m][n .. n+3] from accumulator elements 4g .. 4g+3 -----
     // The MFMA ran with B as its first operand, so accumulator (i, j) holds
-    // the transposed 32x32 block: lane l owns C row m = l%32 and, in element
-    // r, column 8*(r/4) + 4*(l/32) + r%4.
+    // the transposed MIxMI block: lane l owns C row m = l%MI and, in element
+    // r, column 4*P*(r/4) + 4*(l/MI) + r%4.
     const bool vec_ok = (p.N & 3) == 0;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int m = cur.m0 + wm * WM + i * 32 + (int)frow;
+      const int m = cur.m0 + wm * WM + i * MI + (int)frow;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = cur.n0 + wn * WN + j * 32 + 8 * g + 4 * (int)khalf;
+        for (int g = 0; g < NE / 4; ++g) {
+          const int n = cur.n0 + wn * WN + j * MI + 4 * P * g + 4 * (int)kpart;
           float v[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u)
@@ -355,7 +375,7 @@ void gemm_dense_kernel(DenseArgs p) {
             }
           }
         }
-        acc[i][j] = f32x16_t{};
+        acc[i][j] = Acc{};
         // keep the scheduler from hoisting every accumulator read at once
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -378,37 +398,45 @@ void gemm_dense_kernel(DenseArgs p) {
 
 }  // namespace
 
-template <int DT, int R>
+template <int DT, int R, bool KTAIL>
 void launch_ring(const DenseArgs& a, int grid, hipStream_t stream) {
   constexpr Ring r = kRings[R];
-  hipLaunchKernelGGL((gemm_dense_kernel<DT, r.bkb, r.slots, r.waves_n, r.loaders>),
+  // fp8 keeps the 32x32 block: the 16x16x128 fragments of a 128x64 wave
+  // tile (96 VGPRs) do not fit beside its accumulators at two waves per SIMD
+  constexpr int MI = (DT == kFp8) ? 32 : r.mi;
+  hipLaunchKernelGGL((gemm_dense_kernel<DT, r.bkb, r.slots, r.waves_n, r.loaders, MI, KTAIL>),
                      dim3(grid), dim3(128 * r.waves_n), 0, stream, a);
 }
 
-template <int DT>
+template <int DT, bool KTAIL>
 void launch_variant(int v, const DenseArgs& a, int grid, hipStream_t stream) {
   switch (v) {
-    case 1: launch_ring<DT, 1>(a, grid, stream); break;
-    case 2: launch_ring<DT, 2>(a, grid, stream); break;
-    case 3: launch_ring<DT, 3>(a, grid, stream); break;
-    case 4: launch_ring<DT, 4>(a, grid, stream); break;
-    case 5: launch_ring<DT, 5>(a, grid, stream); break;
-    case 6: launch_ring<DT, 6>(a, grid, stream); break;
-    case 7: launch_ring<DT, 7>(a, grid, stream); break;
-    case 8: launch_ring<DT, 8>(a, grid, stream); break;
-    default: launch_ring<DT, 0>(a, grid, stream); break;
+    case 1: launch_ring<DT, 1, KTAIL>(a, grid, stream); break;
+    case 2: launch_ring<DT, 2, KTAIL>(a, grid, stream); break;
+    case 3: launch_ring<DT, 3, KTAIL>(a, grid, stream); break;
+    case 4: launch_ring<DT, 4, KTAIL>(a, grid, stream); break;
+    case 5: launch_ring<DT, 5, KTAIL>(a, grid, stream); break;
+    case 6: launch_ring<DT, 6, KTAIL>(a, grid, stream); break;
+    default: launch_ring<DT, 0, KTAIL>(a, grid, stream); break;
   }
 }
 
 uint32_t dense_stage_kbytes() { return kRings[0].bkb; }
 int dense_num_variants() { return kNumRings; }
+int dense_default_mi(DenseType dt) { return dt == kFp8 ? 32 : kRings[0].mi; }
 
 hipError_t launch_dense(DenseType dt, const DenseArgs& a, int grid, int variant,
                         hipStream_t stream) {
-  if (dt == kBf16)
-    launch_variant<kBf16>(variant, a, grid, stream);
-  else
-    launch_variant<kFp8>(variant, a, grid, stream);
+  // Whether a stage can reach past K: a ragged last stage, or the zero
+  // stage that pads an odd stage count when a loop trip runs two stages.
+  const bool ktail = a.kbytes % (2 * kRings[variant].bkb) != 0;
+  if (dt == kBf16) {
+    if (ktail) launch_variant<kBf16, true>(variant, a, grid, stream);
+    else launch_variant<kBf16, false>(variant, a, grid, stream);
+  } else {
+    if (ktail) launch_variant<kFp8, true>(variant, a, grid, stream);
+    else launch_variant<kFp8, false>(variant, a, grid, stream);
+  }
   return hipGetLastError();
 }
 

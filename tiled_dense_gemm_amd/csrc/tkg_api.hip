@@ -218,23 +218,37 @@ int tkg_lds_row_bytes(int dtype) {
   }
 }
 
+int tkg_lds_fragment_rows(int dtype) {
+  switch (dtype) {
+    case TKG_DTYPE_BF16: return tkg::dense_default_mi(tkg::kBf16);
+    case TKG_DTYPE_FP8: return tkg::dense_default_mi(tkg::kFp8);
+    case TKG_DTYPE_FP4_BLOCKSCALED: return 32;
+    default: return TKG_ERR_SHAPE;
+  }
+}
+
 int tkg_lds_fragment_offsets(int dtype, int step, int part, int frag,
                              uint32_t* out64) {
   if (out64 == nullptr) return TKG_ERR_NULL;
   const int rb = tkg_lds_row_bytes(dtype);
   if (rb < 0) return rb;
-  // k-steps per stage and 16-byte chunks read per lane per k-step
-  int steps, parts;
-  if (dtype == TKG_DTYPE_BF16) { steps = rb / 32; parts = 1; }       // 16 k x 2 B
-  else if (dtype == TKG_DTYPE_FP8) { steps = rb / 64; parts = 2; }   // 64 k x 1 B
-  else { steps = rb / 32; parts = 1; }  // 4-bit: one 16-byte chunk per lane
+  const int mi = tkg_lds_fragment_rows(dtype);
+  // K bytes per row of one MFMA k-step: 32 for the 32x32 blocks of bf16
+  // (16 elements) and of the 4-bit path (a 16-byte chunk of packed values
+  // per lane half), 64 for 32x32x64 fp8; the 16x16 blocks take twice that.
+  int kstep_bytes;
+  if (dtype == TKG_DTYPE_FP8) kstep_bytes = 64 * (32 / mi);
+  else kstep_bytes = 32 * (32 / mi);
+  const int steps = rb / kstep_bytes;
+  const int cpk = kstep_bytes / 16;       // 16-byte chunks per k-step
+  const int lanes_per_row = 64 / mi;      // lanes reading one row
+  const int parts = cpk / lanes_per_row;  // 16-byte reads per lane
   if (step < 0 || step >= steps || part < 0 || part >= parts || frag < 0 ||
-      frag >= kBM / 32)
+      frag >= kBM / mi)
     return TKG_ERR_SHAPE;
   for (uint32_t lane = 0; lane < 64; ++lane) {
-    const uint32_t row = (uint32_t)frag * 32u + (lane & 31u);
-    const uint32_t half = lane >> 5;
-    const uint32_t chunk = (uint32_t)(step * 2 * parts) + half * parts + (uint32_t)part;
+    const uint32_t row = (uint32_t)(frag * mi) + lane % (uint32_t)mi;
+    const uint32_t chunk = (uint32_t)(step * cpk) + (lane / (uint32_t)mi) * (uint32_t)parts + (uint32_t)part;
     out64[lane] = tkg::swz_offset((uint32_t)rb, row, chunk);
   }
   return steps;

@@ -37,6 +37,13 @@ __device__ __forceinline__ void dma_b128(__amdgpu_buffer_rsrc_t r,
                                          TKG_LDS void* lds, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, 0, 0, 0);
 }
+// The same with a wave-uniform byte offset `soff` added to every lane's
+// offset (kept in a scalar register instead of per-lane arithmetic).
+__device__ __forceinline__ void dma_b128_soff(__amdgpu_buffer_rsrc_t r,
+                                              TKG_LDS void* lds, uint32_t voff,
+                                              uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, soff, 0, 0);
+}
 // 4 bytes per lane: the wave writes 256 bytes at `lds`, lane l at byte 4*l.
 __device__ __forceinline__ void dma_b32(__amdgpu_buffer_rsrc_t r,
                                         TKG_LDS void* lds, uint32_t voff) {
@@ -80,6 +87,21 @@ __device__ __forceinline__ f32x16_t mfma_fp8(i32x8_t a, i32x8_t b,
   // format 0 = fp8 e4m3 for both operands, no block scaling
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0,
                                                          0, 0);
+}
+
+// D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16). Lane l supplies row
+// l%16 of A and column l%16 of B, 8 consecutive k each (k-quarter l/16); it
+// receives column l%16 of D, rows 4*(l/16) + r in element r.
+__device__ __forceinline__ f32x4_t mfma16_bf16(bf16x8_t a, bf16x8_t b,
+                                               f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// D(16x16, fp32) += A(16x128, OCP e4m3) * B(128x16, OCP e4m3); 32 k per lane.
+__device__ __forceinline__ f32x4_t mfma16_fp8(i32x8_t a, i32x8_t b,
+                                              f32x4_t c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0,
+                                                          0, 0);
 }
 
 // Four fp32 -> four bf16 (round to nearest even), packed in 8 bytes.

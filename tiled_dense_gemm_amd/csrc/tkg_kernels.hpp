@@ -46,6 +46,8 @@ constexpr int kBN = 256;
 hipError_t launch_dense(DenseType dt, const DenseArgs& a, int grid, int variant,
                         hipStream_t stream);
 int dense_num_variants();
+// MFMA block (16 or 32) of the default configuration for dt
+int dense_default_mi(DenseType dt);
 hipError_t launch_fp4(const Fp4Args& a, int grid, int variant,
                       hipStream_t stream);
 int fp4_num_variants();

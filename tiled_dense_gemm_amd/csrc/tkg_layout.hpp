@@ -59,4 +59,35 @@ TKG_HD constexpr uint32_t dma_chunk(uint32_t row_bytes, uint32_t instr,
   return (lane % (row_bytes / 16u)) ^ swz_mask(row_bytes, dma_row(row_bytes, instr, lane));
 }
 
+// Rows of a slab that one staging instruction fills.
+TKG_HD constexpr uint32_t dma_rows_per_instr(uint32_t row_bytes) {
+  return 1024u / row_bytes;
+}
+
+// The per-lane part of a staging offset: instruction q's offset is
+// q * dma_rows_per_instr * row_stride (the same for every lane) plus
+// dma_lane_offset(row_bytes, q & 1, lane, row_stride). The swizzle of a row
+// depends on q only through its parity (rows of one instruction share
+// their upper bits), so two per-lane values cover every instruction.
+TKG_HD constexpr uint32_t dma_lane_offset(uint32_t row_bytes, uint32_t parity,
+                                          uint32_t lane, uint32_t row_stride) {
+  return (dma_row(row_bytes, parity, lane) - parity * dma_rows_per_instr(row_bytes)) * row_stride +
+         dma_chunk(row_bytes, parity, lane) * 16u;
+}
+
+// Checks that split for every instruction of a 256-row slab and every lane.
+TKG_HD constexpr bool dma_offset_split_holds(uint32_t row_bytes) {
+  const uint32_t stride = 1u << 20;  // any row stride larger than a row
+  for (uint32_t q = 0; q < 256u / dma_rows_per_instr(row_bytes); ++q)
+    for (uint32_t lane = 0; lane < 64; ++lane) {
+      const uint32_t full = dma_row(row_bytes, q, lane) * stride + dma_chunk(row_bytes, q, lane) * 16u;
+      const uint32_t split = q * dma_rows_per_instr(row_bytes) * stride +
+                             dma_lane_offset(row_bytes, q & 1u, lane, stride);
+      if (full != split) return false;
+    }
+  return true;
+}
+static_assert(dma_offset_split_holds(128) && dma_offset_split_holds(64),
+              "staging offsets split into a uniform and a two-valued per-lane part");
+
 }  // namespace tkg

@@ -121,10 +121,12 @@ def kernel_fragment_reads(dtype: int) -> List[List[int]]:
         dtype, 0, 0, 0, (tkg.ctypes.c_uint32 * 64)())
     if steps < 0:
         raise tkg.TkgError(steps, "tkg_lds_fragment_offsets")
-    parts = 2 if dtype == tkg.DTYPE_FP8 else 1
+    buf = (tkg.ctypes.c_uint32 * 64)()
+    parts = 2 if tkg.lib.tkg_lds_fragment_offsets(dtype, 0, 1, 0, buf) > 0 else 1
+    frags = 256 // tkg.lds_fragment_rows(dtype)
     return [tkg.lds_fragment_offsets(dtype, step, part, frag)
             for step in range(steps) for part in range(parts)
-            for frag in range(8)]
+            for frag in range(frags)]
 
 
 def scale_read_pattern(row_bytes: int = 8) -> List[int]:
