@@ -121,13 +121,17 @@ const char *tkg_status_string(int status);
  *               round-robin order.
  *   variant  -- bf16/fp8: kernel configuration, as (K bytes per row
  *               of an LDS slab, operand slabs in the LDS ring, waves per
- *               workgroup, waves issuing the global loads, MFMA block):
- *               0 = (128, 4, 8, 4, 16) default, 1 = (128, 5, 8, 4, 16),
- *               2 = (128, 4, 8, 4, 32), 3 = (128, 5, 8, 4, 32),
- *               4 = (128, 4, 8, 8, 32), 5 = (128, 4, 4, 4, 32),
- *               6 = (64, 10, 8, 8, 32); MFMA block 16 = 16x16x32 bf16
- *               MFMAs, 32 = 32x32x16; fp8 always uses 32x32x64.
- *               TKG_ERR_SHAPE outside 0..6.
+ *               workgroup, waves issuing the global loads, MFMA block:
+ *               16 = 16x16x32 bf16 / 16x16x128 fp8, 32 = 32x32x16 /
+ *               32x32x64). bf16: 0 = (128, 4, 8, 4, 16) default,
+ *               1 = (128, 5, 8, 4, 16), 2 = (128, 4, 8, 4, 32),
+ *               3 = (128, 5, 8, 4, 32), 4 = (128, 4, 8, 8, 32),
+ *               5 = (128, 4, 4, 4, 32), 6 = (64, 10, 8, 8, 32),
+ *               7 = (128, 4, 4, 4, 16). fp8: 0 = (128, 4, 4, 4, 32)
+ *               default, 1 = (128, 5, 4, 4, 32), 2 = (128, 4, 8, 4, 32),
+ *               3 = (128, 5, 8, 4, 32), 4 = (128, 4, 8, 8, 32),
+ *               5 = (128, 4, 4, 4, 16), 6 = (64, 10, 8, 8, 32),
+ *               7 = (64, 10, 4, 4, 32). TKG_ERR_SHAPE outside 0..7.
  *               4-bit product: 0 = 4 waves (default), 1 = 8 waves;
  *               TKG_ERR_SHAPE outside 0..1. Every variant of a product
  *               computes the same sums (the tests find them bit-identical).

@@ -30,7 +30,7 @@ pytestmark = pytest.mark.gpu
 BF16_RELFRO = 1e-3
 BF16_ELEM_REL, BF16_ELEM_ABS = 1e-2, 1e-3
 LOWP_RELFRO = 2e-2
-DENSE_VARIANTS = 7   # kernel configurations selectable by tkg_opts.variant
+DENSE_VARIANTS = 8   # kernel configurations selectable by tkg_opts.variant
 
 
 @pytest.fixture(scope="module")

@@ -14,7 +14,7 @@
 // * Load-compute-store-finish (page 2, section 3.4 "The LCSF Template" and
 //   "Multi-Stage Buffer: The Pipeline Depth Parameter", Table 1): every wave
 //   streams its share of a K step straight from global memory into a ring of
-//   LDS slots (one operand slab each, see kRings), several K steps ahead of
+//   LDS slots (one operand slab each, see Ring), several K steps ahead of
 //   the MFMAs; s_waitcnt + s_barrier play the part of arrive/expect. The
 //   loads are issued between the MFMAs of the current K step. The finish step converts the fp32
 //   accumulators (times the fp8 scale) to bf16 and stores them while the
@@ -55,10 +55,22 @@ static_assert(BM == BN, "A and B slabs share offsets");
 struct Ring {
   int bkb, slots, waves_n, loaders, mi;
 };
-constexpr Ring kRings[] = {{128, 4, 4, 1, 16}, {128, 5, 4, 1, 16}, {128, 4, 4, 1, 32},
-                           {128, 5, 4, 1, 32}, {128, 4, 4, 0, 32}, {128, 4, 2, 0, 32},
-                           {64, 10, 4, 0, 32}};
-constexpr int kNumRings = sizeof(kRings) / sizeof(kRings[0]);
+// One table per operand type (variant v selects entry v); entry 0 is the
+// default, the fastest measured at 8192^3 on random operands: for bf16 two
+// waves per SIMD with 16x16x32 MFMAs, for fp8 one wave per SIMD with
+// 32x32x64 MFMAs.
+constexpr Ring kRingsBf16[] = {{128, 4, 4, 1, 16}, {128, 5, 4, 1, 16}, {128, 4, 4, 1, 32},
+                               {128, 5, 4, 1, 32}, {128, 4, 4, 0, 32}, {128, 4, 2, 0, 32},
+                               {64, 10, 4, 0, 32}, {128, 4, 2, 0, 16}};
+constexpr Ring kRingsFp8[] = {{128, 4, 2, 0, 32}, {128, 5, 2, 0, 32}, {128, 4, 4, 1, 32},
+                              {128, 5, 4, 1, 32}, {128, 4, 4, 0, 32}, {128, 4, 2, 0, 16},
+                              {64, 10, 4, 0, 32}, {64, 10, 2, 0, 32}};
+constexpr int kNumRings = sizeof(kRingsBf16) / sizeof(kRingsBf16[0]);
+static_assert(sizeof(kRingsFp8) == sizeof(kRingsBf16), "same variant count");
+template <int DT>
+constexpr Ring ring_of(int v) {
+  return DT == kBf16 ? kRingsBf16[v] : kRingsFp8[v];
+}
 
 struct TileState {
   int m0, n0;
@@ -230,9 +242,10 @@ void gemm_dense_kernel(DenseArgs p) {
   // k-step, so the next k-step's A fragment i is read into the same
   // registers right after it. B fragments are used until the k-step's last
   // row of MFMAs: two sets, the next one read at the k-step's start, unless
-  // registers are short (fp8 16x16: one set, each B fragment re-read right
-  // after its last use, a few MFMAs before its next one).
-  constexpr bool B_SINGLE = (DT == kFp8 && MI == 16);
+  // registers are short (fp8 16x16 at two waves per SIMD: one set, each B
+  // fragment re-read right after its last use, a few MFMAs before its next
+  // one).
+  constexpr bool B_SINGLE = (DT == kFp8 && MI == 16 && WAVES_N == 4);
   constexpr int BSETS = B_SINGLE ? 1 : 2;
   Frag fa[FM], fb[BSETS][FN];
   auto read_one = [&](const TKG_LDS uint8_t* base, uint32_t row0, int s, Frag& v) {
@@ -400,11 +413,8 @@ void gemm_dense_kernel(DenseArgs p) {
 
 template <int DT, int R, bool KTAIL>
 void launch_ring(const DenseArgs& a, int grid, hipStream_t stream) {
-  constexpr Ring r = kRings[R];
-  // fp8 keeps the 32x32 block: the 16x16x128 fragments of a 128x64 wave
-  // tile (96 VGPRs) do not fit beside its accumulators at two waves per SIMD
-  constexpr int MI = (DT == kFp8) ? 32 : r.mi;
-  hipLaunchKernelGGL((gemm_dense_kernel<DT, r.bkb, r.slots, r.waves_n, r.loaders, MI, KTAIL>),
+  constexpr Ring r = ring_of<DT>(R);
+  hipLaunchKernelGGL((gemm_dense_kernel<DT, r.bkb, r.slots, r.waves_n, r.loaders, r.mi, KTAIL>),
                      dim3(grid), dim3(128 * r.waves_n), 0, stream, a);
 }
 
@@ -417,19 +427,22 @@ void launch_variant(int v, const DenseArgs& a, int grid, hipStream_t stream) {
     case 4: launch_ring<DT, 4, KTAIL>(a, grid, stream); break;
     case 5: launch_ring<DT, 5, KTAIL>(a, grid, stream); break;
     case 6: launch_ring<DT, 6, KTAIL>(a, grid, stream); break;
+    case 7: launch_ring<DT, 7, KTAIL>(a, grid, stream); break;
     default: launch_ring<DT, 0, KTAIL>(a, grid, stream); break;
   }
 }
 
-uint32_t dense_stage_kbytes() { return kRings[0].bkb; }
+uint32_t dense_stage_kbytes() { return kRingsBf16[0].bkb; }
+static_assert(kRingsBf16[0].bkb == kRingsFp8[0].bkb, "one default stage width");
 int dense_num_variants() { return kNumRings; }
-int dense_default_mi(DenseType dt) { return dt == kFp8 ? 32 : kRings[0].mi; }
+int dense_default_mi(DenseType dt) { return dt == kFp8 ? kRingsFp8[0].mi : kRingsBf16[0].mi; }
 
 hipError_t launch_dense(DenseType dt, const DenseArgs& a, int grid, int variant,
                         hipStream_t stream) {
   // Whether a stage can reach past K: a ragged last stage, or the zero
   // stage that pads an odd stage count when a loop trip runs two stages.
-  const bool ktail = a.kbytes % (2 * kRings[variant].bkb) != 0;
+  const Ring r = dt == kBf16 ? kRingsBf16[variant] : kRingsFp8[variant];
+  const bool ktail = a.kbytes % (2 * r.bkb) != 0;
   if (dt == kBf16) {
     if (ktail) launch_variant<kBf16, true>(variant, a, grid, stream);
     else launch_variant<kBf16, false>(variant, a, grid, stream);
