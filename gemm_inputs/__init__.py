@@ -28,6 +28,10 @@ import numpy as np
 E4M3_MAX = 448.0
 E2M1_MAX = 6.0
 FP4_BLOCK = 16
+MX_BLOCK = 32
+# largest power of two that the element formats' maxima reach: 6 = 1.5 * 2^2
+# (e2m1), 448 = 1.75 * 2^8 (e4m3)
+MX_EMAX = {"e2m1": 2, "e4m3": 8}
 
 
 def normal(seed: int, rows: int, cols: int, std: float = 1.0) -> np.ndarray:
@@ -145,6 +149,33 @@ def fp4_quantize(x: np.ndarray, block: int = FP4_BLOCK):
 def fp4_operand(seed: int, rows: int, cols: int, std: float = 1.0):
     """Seeded block-scaled 4-bit operand: (packed, scales, tensor scale)."""
     return fp4_quantize(normal(seed, rows, cols, std))
+
+
+def mx_quantize(x: np.ndarray, elem: str):
+    """MX quantization along the last axis (K), in the OCP MX recipe: each
+    block of 32 gets the shared exponent e = floor(log2(amax_block)) -
+    emax(elem), stored as the E8M0 byte e + 127 (clamped to 0..254; a zero
+    block gets 0), and its elements become elem(x / 2^e), rounded to
+    nearest even and saturated.
+    Returns (values: R x K/2 packed e2m1 or R x K e4m3 codes, scales R x K/32)."""
+    R, K = x.shape
+    if K % MX_BLOCK:
+        raise ValueError("K=%d must be a multiple of %d" % (K, MX_BLOCK))
+    xb = x.reshape(R, K // MX_BLOCK, MX_BLOCK)
+    amax = np.max(np.abs(xb), axis=2)
+    with np.errstate(divide="ignore"):
+        e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))), -127.0)
+    e = np.clip(e - MX_EMAX[elem] * (amax > 0), -127, 127).astype(np.int64)
+    scales = (e + 127).astype(np.uint8)
+    y = (xb / np.exp2(e.astype(np.float64))[..., None]).reshape(R, K)
+    if elem == "e2m1":
+        return pack_nibbles(e2m1_codes(y)), scales
+    return e4m3_codes(y), scales
+
+
+def mx_operand(seed: int, rows: int, cols: int, elem: str, std: float = 1.0):
+    """Seeded MX operand: (values, E8M0 scales)."""
+    return mx_quantize(normal(seed, rows, cols, std), elem)
 
 
 # ----------------------------------------------------- structured operands

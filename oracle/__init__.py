@@ -30,6 +30,13 @@ of the bytes the GPU receives, accumulated in IEEE fp64:
   format is e2m1 values in blocks of 16 along K, each block with an e4m3
   scale, plus one fp32 scale per tensor, s = tA * tB.
 
+* MX block-scaled operands (the gfx950-native form of block scaling; OCP
+  Microscaling Formats v1.0, an external specification): elements e2m1
+  ("MXFP4", two per byte, element 2t in the low nibble of byte t) or OCP
+  e4m3 ("MXFP8"), in blocks of 32 along K, each block with one E8M0 scale
+  2^(e-127); value[r, k] = element[r, k] * scale[r, k // 32], no per-tensor
+  scale.
+
 Pins (see tests/test_oracle_pins.py): identity, permutation and rank-1
 closed forms, brute force against exact rational arithmetic on tiny shapes,
 integer-exact products, and code tables of every decoder.
@@ -42,11 +49,13 @@ import os
 import numpy as np
 
 from .formats import (decode_bf16, decode_e2m1_packed, decode_e4m3,
-                      round_to_bf16, E2M1_TABLE, E4M3_TABLE)
+                      decode_e8m0, round_to_bf16, E2M1_TABLE, E4M3_TABLE,
+                      E8M0_TABLE)
 
 __all__ = [
     "gemm_f64", "gemm_bf16", "gemm_fp8", "gemm_fp4_blockscaled",
-    "dequant_fp4_blockscaled", "abs_gemm_f64", "decode_bf16", "decode_e4m3",
+    "dequant_fp4_blockscaled", "dequant_mx", "gemm_mx", "MX_BLOCK",
+    "abs_gemm_f64", "decode_bf16", "decode_e4m3", "decode_e8m0",
     "decode_e2m1_packed", "round_to_bf16", "num_threads",
 ]
 
@@ -138,3 +147,33 @@ def gemm_fp4_blockscaled(A_packed, A_scales, tensor_scale_a, B_packed,
     s = float(np.float32(tensor_scale_a)) * float(np.float32(tensor_scale_b))
     return gemm_f64(dequant_fp4_blockscaled(A_packed, A_scales),
                     dequant_fp4_blockscaled(B_packed, B_scales), s)
+
+
+MX_BLOCK = 32
+
+
+def dequant_mx(values: np.ndarray, scales: np.ndarray, elem: str) -> np.ndarray:
+    """MX operand -> exact fp64 values: element(values)[r, k] *
+    e8m0(scales)[r, k // 32].
+
+    values: R x K/2 uint8 packed e2m1 (elem "e2m1") or R x K uint8 OCP e4m3
+    (elem "e4m3"); scales: R x K/32 uint8 E8M0."""
+    if elem == "e2m1":
+        v = decode_e2m1_packed(values)
+    elif elem == "e4m3":
+        v = decode_e4m3(values)
+    else:
+        raise ValueError("element format %r" % (elem,))
+    s = decode_e8m0(scales)
+    R, K = v.shape
+    if K % MX_BLOCK or s.shape != (R, K // MX_BLOCK):
+        raise ValueError("scale shape %r does not match %d x %d/%d"
+                         % (s.shape, R, K, MX_BLOCK))
+    return v * np.repeat(s, MX_BLOCK, axis=1)
+
+
+def gemm_mx(A_values, A_scales, B_values, B_scales, elem: str) -> np.ndarray:
+    """MX operands (A: M x K, Bt: N x K, see ``dequant_mx``) -> A @ B in
+    fp64."""
+    return gemm_f64(dequant_mx(A_values, A_scales, elem),
+                    dequant_mx(B_values, B_scales, elem))

@@ -22,6 +22,12 @@ fp64). The formats themselves are named, not specified, by the pages:
   1 sign bit (bit 3), 2 exponent bits with bias 1, 1 mantissa bit; no
   infinities or NaN; magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
 
+* E8M0 -- the shared scale of an MX block (OCP Microscaling Formats
+  specification v1.0, an external document; the pages' block-scaled idea,
+  page "ThunderKittens reaches 22.4 PFLOPS on NVIDIA Rubin", "Feeding the
+  faster tensor cores", in the form gfx950's scaled MFMA executes): an
+  unsigned 8-bit exponent, value 2^(e - 127), 0xFF is NaN, no zero.
+
 ``round_to_bf16`` is the oracle's own round-to-nearest-even of an fp64 value
 to bf16, used only to express the bf16 output rounding in comparisons.
 """
@@ -57,13 +63,26 @@ def _e2m1_value(code: int) -> float:
     return s * (1.0 + m / 2.0) * 2.0 ** (e - 1)
 
 
+def _e8m0_value(code: int) -> float:
+    if code == 0xFF:
+        return float("nan")
+    return 2.0 ** (code - 127)
+
+
 E4M3_TABLE = np.array([_e4m3_value(c) for c in range(256)], dtype=np.float64)
+E8M0_TABLE = np.array([_e8m0_value(c) for c in range(256)], dtype=np.float64)
 E2M1_TABLE = np.array([_e2m1_value(c) for c in range(16)], dtype=np.float64)
 
 
 def decode_e4m3(codes: np.ndarray) -> np.ndarray:
     """OCP e4m3 bytes (uint8) -> exact values (float64); 0x7F/0xFF -> NaN."""
     return E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def decode_e8m0(codes: np.ndarray) -> np.ndarray:
+    """E8M0 scale bytes (uint8) -> exact values 2^(e-127) (float64); 0xFF ->
+    NaN."""
+    return E8M0_TABLE[np.asarray(codes, dtype=np.uint8)]
 
 
 def decode_e2m1_packed(packed: np.ndarray) -> np.ndarray:

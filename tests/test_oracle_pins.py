@@ -234,3 +234,97 @@ def test_fp8_scale_is_product_of_fp32_scales():
     C = oracle.gemm_fp8(A, sa, A, sb)
     want = 16 * float(np.float32(sa)) * float(np.float32(sb))
     assert C[0, 0] == want
+
+
+# ------------------------------------------------------------- MX formats
+# OCP Microscaling Formats v1.0 (external specification): E8M0 block
+# scales 2^(e-127), blocks of 32 along K, e2m1 or e4m3 elements.
+
+def test_e8m0_table():
+    from oracle.formats import E8M0_TABLE, decode_e8m0
+    import math
+    for e in range(255):
+        assert E8M0_TABLE[e] == math.ldexp(1.0, e - 127)
+    assert np.isnan(E8M0_TABLE[255])
+    assert decode_e8m0(np.array([127, 0, 254], np.uint8)).tolist() == [1.0, 2.0 ** -127, 2.0 ** 127]
+
+
+def test_e8m0_matches_torch_decode():
+    torch = pytest.importorskip("torch")
+    if not hasattr(torch, "float8_e8m0fnu"):
+        pytest.skip("torch has no float8_e8m0fnu")
+    from oracle.formats import decode_e8m0
+    codes = np.arange(255, dtype=np.uint8)
+    t = torch.from_numpy(codes).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    assert np.array_equal(decode_e8m0(codes), t)
+
+
+@pytest.mark.parametrize("elem", ["e2m1", "e4m3"])
+def test_mx_dequant_uses_its_block_scale(elem):
+    # all elements 1.0, a different scale per block: the result shows each
+    # element took the scale of block k // 32
+    R, K = 3, 128
+    one = 0x2 if elem == "e2m1" else 0x38
+    codes = np.full((R, K), one, np.uint8)
+    vals = gi.pack_nibbles(codes) if elem == "e2m1" else codes
+    scales = (120 + np.arange(R * K // 32).reshape(R, K // 32)).astype(np.uint8)
+    d = oracle.dequant_mx(vals, scales, elem)
+    want = np.repeat(2.0 ** (scales.astype(np.float64) - 127), 32, axis=1)
+    assert np.array_equal(d, want)
+
+
+@pytest.mark.parametrize("elem", ["e2m1", "e4m3"])
+def test_mx_gemm_against_exact_rationals(elem):
+    g = np.random.default_rng(5)
+    M, N, K = 3, 4, 64
+    if elem == "e2m1":
+        Ac, Bc = g.integers(0, 16, (M, K)).astype(np.uint8), g.integers(0, 16, (N, K)).astype(np.uint8)
+        Av, Bv = gi.pack_nibbles(Ac), gi.pack_nibbles(Bc)
+        ev = lambda c: Fraction(E2M1_TABLE[c])
+    else:
+        pool = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+        Ac, Bc = g.choice(pool, (M, K)), g.choice(pool, (N, K))
+        Av, Bv = Ac, Bc
+        ev = lambda c: Fraction(E4M3_TABLE[c])
+    As = g.integers(110, 140, (M, K // 32)).astype(np.uint8)
+    Bs = g.integers(110, 140, (N, K // 32)).astype(np.uint8)
+    C = oracle.gemm_mx(Av, As, Bv, Bs, elem)
+    u = 2.0 ** -53
+    gamma = K * u / (1 - K * u)
+    for i in range(M):
+        for j in range(N):
+            terms = [ev(Ac[i, k]) * Fraction(2) ** (int(As[i, k // 32]) - 127) *
+                     ev(Bc[j, k]) * Fraction(2) ** (int(Bs[j, k // 32]) - 127)
+                     for k in range(K)]
+            exact = sum(terms)
+            # recursive fp64 summation of exact products
+            assert abs(Fraction(C[i, j]) - exact) <= Fraction(gamma) * sum(abs(t) for t in terms)
+
+
+def test_mx_planted_block_size_is_caught():
+    # a dequantizer whose block boundaries sat 16 elements off (the 4-bit
+    # format's block size) disagrees with the definition on a random case
+    g = np.random.default_rng(8)
+    codes = g.integers(0, 16, (2, 64)).astype(np.uint8)
+    scales = g.integers(120, 135, (2, 2)).astype(np.uint8)
+    good = oracle.dequant_mx(gi.pack_nibbles(codes), scales, "e2m1")
+    from oracle.formats import decode_e2m1_packed as dec, decode_e8m0
+    s16 = np.repeat(np.repeat(decode_e8m0(scales), 2, axis=1), 16, axis=1)[:, :64]
+    planted = dec(gi.pack_nibbles(codes)) * np.roll(s16, 16, axis=1)
+    assert not np.array_equal(good, planted)
+    assert np.array_equal(good, dec(gi.pack_nibbles(codes)) * s16)
+
+
+@pytest.mark.parametrize("elem", ["e2m1", "e4m3"])
+def test_mx_quantize_round_trips_representable_values(elem):
+    # values that are an element value times 2^e with one e per block come
+    # back exactly
+    g = np.random.default_rng(11)
+    R, K = 4, 96
+    table = E2M1_TABLE if elem == "e2m1" else E4M3_TABLE[np.isfinite(E4M3_TABLE)]
+    base = g.choice(table, (R, K))
+    base[:, ::32] = table.max()           # each block reaches the format maximum
+    e = g.integers(-6, 7, (R, K // 32)).astype(np.float64)
+    x = base * np.repeat(np.exp2(e), 32, axis=1)
+    vals, scales = gi.mx_quantize(x, elem)
+    assert np.array_equal(oracle.dequant_mx(vals, scales, elem), x)
