@@ -87,3 +87,27 @@ def fp4_operand(seed, rows, cols, std=1.0, device="cuda", block=16):
         packed[r0:r1] = codes[:, 0::2] | (codes[:, 1::2] << 4)
         scales[r0:r1] = sc
     return packed, scales, t
+
+
+def mx_operand(seed, rows, cols, elem, std=1.0, device="cuda"):
+    """(values, E8M0 scales rows x cols/32) in the recipe of
+    gemm_inputs.mx_quantize: values are packed e2m1 (rows x cols/2) or e4m3
+    (rows x cols) codes."""
+    from . import MX_BLOCK, MX_EMAX
+    fp4 = elem == "e2m1"
+    vals = torch.empty((rows, cols // 2 if fp4 else cols), dtype=torch.uint8, device=device)
+    scales = torch.empty((rows, cols // MX_BLOCK), dtype=torch.uint8, device=device)
+    for ci, (r0, r1) in enumerate(_chunks(rows)):
+        x = _normal_chunk(seed, ci, r1 - r0, cols, std, device).to(torch.float64)
+        xb = x.view(r1 - r0, cols // MX_BLOCK, MX_BLOCK)
+        amax = xb.abs().amax(dim=2)
+        e = torch.where(amax > 0, torch.floor(torch.log2(amax.clamp(min=1e-300))) - MX_EMAX[elem],
+                        torch.full_like(amax, -127.0)).clamp(-127, 127)
+        y = (xb / torch.exp2(e)[..., None]).view(r1 - r0, cols)
+        if fp4:
+            codes = _e2m1_codes(y)
+            vals[r0:r1] = codes[:, 0::2] | (codes[:, 1::2] << 4)
+        else:
+            vals[r0:r1] = _e4m3_bytes(y)
+        scales[r0:r1] = (e + 127).to(torch.uint8)
+    return vals, scales

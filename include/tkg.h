@@ -105,6 +105,32 @@ int gemm_fp4_blockscaled(int64_t M, int64_t N, int64_t K, const void *A,
                          const void *B_scales, float b_scale, void *C,
                          void *stream);
 
+/*
+ * MX block-scaled operands -> bf16 (OCP Microscaling formats, the form of
+ * block scaling gfx950's matrix cores execute natively; an external
+ * specification, not the pages').
+ *   gemm_mxfp4: A is M x K/2 bytes of packed e2m1 values (element 2t of a
+ *      row in the LOW nibble of byte t, as gemm_fp4_blockscaled).
+ *   gemm_mxfp8: A is M x K bytes of OCP e4m3 values.
+ *   A_scales: M x K/32 bytes, the E8M0 scale of each block of 32 consecutive
+ *      K-elements of a row: A_real[i][k] = 2^(A_scales[i][k/32] - 127) *
+ *      elem(A[i][k]) (0xFF encodes NaN).
+ *   B, B_scales: the same for B in column-major order (N x K/2 or N x K
+ *      values, N x K/32 scales).
+ *   The matrix cores apply the scales inside the MFMA; fp32 accumulation,
+ *   bf16 result. Requires K % 128 == 0 (K <= 16777088 for MXFP4, 8388480
+ *   for MXFP8). All five pointers 16-byte aligned.
+ * Block scaling factors that travel with low-precision values: page
+ * "ThunderKittens reaches 22.4 PFLOPS on NVIDIA Rubin", section "Feeding
+ * the faster tensor cores".
+ */
+int gemm_mxfp4(int64_t M, int64_t N, int64_t K, const void *A,
+               const void *A_scales, const void *B, const void *B_scales,
+               void *C, void *stream);
+int gemm_mxfp8(int64_t M, int64_t N, int64_t K, const void *A,
+               const void *A_scales, const void *B, const void *B_scales,
+               void *C, void *stream);
+
 /* Static, human-readable name of a tkg_status value (never NULL). */
 const char *tkg_status_string(int status);
 
@@ -146,12 +172,21 @@ typedef struct tkg_opts {
   int32_t variant;
 } tkg_opts;
 
-enum { TKG_DTYPE_BF16 = 0, TKG_DTYPE_FP8 = 1, TKG_DTYPE_FP4_BLOCKSCALED = 2 };
+enum {
+  TKG_DTYPE_BF16 = 0,
+  TKG_DTYPE_FP8 = 1,
+  TKG_DTYPE_FP4_BLOCKSCALED = 2,
+  TKG_DTYPE_MXFP4 = 3,
+  TKG_DTYPE_MXFP8 = 4
+};
 
 /*
  * dtype: TKG_DTYPE_*. Arguments that a dtype does not use (A_scales,
- * B_scales for bf16/fp8; the scales for bf16) are ignored. opts may be NULL
- * (defaults). Same contract and errors as the typed entry points.
+ * B_scales for bf16/fp8; the scales for bf16) are ignored. For the MX
+ * types a_scale * b_scale multiplies the result (the typed entry points
+ * pass 1). opts may be NULL (defaults); the MX types have one kernel
+ * configuration (variant 0). Same contract and errors as the typed entry
+ * points.
  */
 int tkg_gemm_ex(int dtype, int64_t M, int64_t N, int64_t K, const void *A,
                 const void *A_scales, float a_scale, const void *B,

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("gemm_bf16", "gemm_fp8", "gemm_fp4_blockscaled",
+    for n in ("gemm_bf16", "gemm_fp8", "gemm_fp4_blockscaled", "gemm_mxfp4", "gemm_mxfp8",
               "tkg_status_string", "tkg_gemm_ex"):
         assert n in names
 
@@ -54,6 +54,12 @@ L = tkg.lib
     (lambda: L.gemm_fp8(8, 8, 24, A16, 1.0, B16, 1.0, C16, None), S["TKG_ERR_SHAPE"]),
     (lambda: L.gemm_fp4_blockscaled(8, 8, 96, A16, A16, 1.0, B16, B16, 1.0, C16, None), S["TKG_ERR_SHAPE"]),
     (lambda: L.tkg_gemm_ex(7, 8, 8, 8, A16, None, 1.0, B16, None, 1.0, C16, None, None), S["TKG_ERR_SHAPE"]),
+    (lambda: L.gemm_mxfp4(8, 8, 64, A16, A16, B16, B16, C16, None), S["TKG_ERR_SHAPE"]),
+    (lambda: L.gemm_mxfp8(8, 8, 96, A16, A16, B16, B16, C16, None), S["TKG_ERR_SHAPE"]),
+    (lambda: L.gemm_mxfp4(8, 8, 128, A16, None, B16, B16, C16, None), S["TKG_ERR_NULL"]),
+    (lambda: L.gemm_mxfp8(8, 8, 128, A16, A16, B16, None, C16, None), S["TKG_ERR_NULL"]),
+    (lambda: L.gemm_mxfp4(8, 8, 128, A16, A16 + 4, B16, B16, C16, None), S["TKG_ERR_ALIGN"]),
+    (lambda: L.gemm_mxfp8(0, 0, 128, None, None, None, None, None, None), S["TKG_OK"]),
     # null pointers
     (lambda: L.gemm_bf16(8, 8, 8, None, B16, C16, None), S["TKG_ERR_NULL"]),
     (lambda: L.gemm_bf16(8, 8, 8, A16, None, C16, None), S["TKG_ERR_NULL"]),

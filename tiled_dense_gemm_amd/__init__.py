@@ -21,12 +21,14 @@ __all__ = [
     "tkg_status_string", "lds_fragment_offsets", "lds_fragment_rows",
     "lds_row_bytes", "lib",
     "TkgError", "DTYPE_BF16", "DTYPE_FP8", "DTYPE_FP4_BLOCKSCALED",
+    "DTYPE_MXFP4", "DTYPE_MXFP8", "gemm_mxfp4", "gemm_mxfp8",
     "STATUS", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtkg.so")
 
 DTYPE_BF16, DTYPE_FP8, DTYPE_FP4_BLOCKSCALED = 0, 1, 2
+DTYPE_MXFP4, DTYPE_MXFP8 = 3, 4
 STATUS = {"TKG_OK": 0, "TKG_ERR_NULL": -1, "TKG_ERR_SHAPE": -2,
           "TKG_ERR_ALIGN": -3, "TKG_ERR_LAUNCH": -4, "TKG_ERR_DEVICE": -5}
 
@@ -64,6 +66,9 @@ def _load() -> ctypes.CDLL:
     L.gemm_fp4_blockscaled.argtypes = [i64, i64, i64, vp, vp, f32, vp, vp,
                                        f32, vp, vp]
     L.gemm_fp4_blockscaled.restype = i32
+    for name in ("gemm_mxfp4", "gemm_mxfp8"):
+        getattr(L, name).argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp]
+        getattr(L, name).restype = i32
     L.tkg_gemm_ex.argtypes = [i32, i64, i64, i64, vp, vp, f32, vp, vp, f32,
                               vp, vp, ctypes.POINTER(TkgOpts)]
     L.tkg_gemm_ex.restype = i32
@@ -213,6 +218,38 @@ def gemm_fp4_blockscaled(A, A_scales, a_scale, Bt, B_scales, b_scale,
             out.data_ptr(), _stream_ptr(stream))
     _raise(st, "gemm_fp4_blockscaled")
     return out
+
+
+def _gemm_mx(name, elem_per_byte, A, A_scales, Bt, B_scales, out, stream):
+    torch = _torch()
+    M, Kb = A.shape
+    K = Kb * elem_per_byte
+    N = Bt.shape[0]
+    u8 = (torch.uint8,)
+    vt = u8 if elem_per_byte == 2 else _fp8_types()
+    _check_mat(A, "A", M, Kb, vt, None)
+    _check_mat(Bt, "Bt", N, Kb, vt, A.device)
+    _check_mat(A_scales, "A_scales", M, K // 32, u8, A.device)
+    _check_mat(B_scales, "B_scales", N, K // 32, u8, A.device)
+    out = _out(out, M, N, A.device)
+    with torch.cuda.device(A.device):
+        st = getattr(lib, name)(M, N, K, A.data_ptr(), A_scales.data_ptr(),
+                                Bt.data_ptr(), B_scales.data_ptr(),
+                                out.data_ptr(), _stream_ptr(stream))
+    _raise(st, name)
+    return out
+
+
+def gemm_mxfp4(A, A_scales, Bt, B_scales, out=None, stream=None):
+    """MXFP4 product. A: M x K/2 packed e2m1 (uint8), A_scales: M x K/32
+    E8M0 (uint8); Bt, B_scales likewise for B in column-major order."""
+    return _gemm_mx("gemm_mxfp4", 2, A, A_scales, Bt, B_scales, out, stream)
+
+
+def gemm_mxfp8(A, A_scales, Bt, B_scales, out=None, stream=None):
+    """MXFP8 product. A: M x K e4m3 (uint8 or float8_e4m3fn), A_scales:
+    M x K/32 E8M0 (uint8); Bt, B_scales likewise for B (N rows)."""
+    return _gemm_mx("gemm_mxfp8", 1, A, A_scales, Bt, B_scales, out, stream)
 
 
 def tkg_gemm_ex(dtype, M, N, K, A, A_scales, a_scale, Bt, B_scales, b_scale,

@@ -1,0 +1,390 @@
+// MX block-scaled tiled GEMM for gfx950 (MI355X): MXFP4 and MXFP8.
+//
+// The pages' block-scaled low-precision path (page "ThunderKittens reaches
+// 22.4 PFLOPS on NVIDIA Rubin", "Feeding the faster tensor cores": scale
+// factors travel with the 4-bit values) in the form CDNA4's matrix cores
+// execute natively: v_mfma_scale_f32_32x32x64_f8f6f4 multiplies e2m1 (fp4)
+// or e4m3 (fp8) elements and applies one E8M0 scale (2^(e-127)) per 32
+// K-elements of each row and column inside the instruction (OCP Microscaling
+// formats). The product runs at the fp4 / fp8 MFMA rate with no conversion
+// work; C = scale * A * B with fp32 accumulation, bf16 output.
+//
+// Structure as the dense kernels (gemm_dense.hip): 256x256 workgroup tile of
+// 2x2 waves with 128x128 wave tiles (one wave per SIMD, 4x4 accumulators of
+// 32x32 in AGPRs), a 4-slot LDS ring of operand slabs fed straight from
+// global memory, k-steps emitted in program order with the loads and reads
+// placed after the MFMAs, persistent grouped grid with XCD remap. Next to
+// each value slab (256 rows x 128 bytes) the ring holds its scale slab (256
+// rows x the stage's scale bytes).
+//
+// Lane data of one 32x32x64 MFMA (measured on MI355X): lane l supplies row
+// (or column) l % 32. For fp4 its 32 elements are K-elements 32*(l/32) ..
+// +31 of the k-step (16 bytes, two per byte, low nibble first), and its
+// scale is the one of that 32-element block. For fp8 its 32 bytes are
+// K-elements 16*(l/32) .. +15 and 32 + 16*(l/32) .. +15, and its scale is
+// the one of block (l/32) of the k-step, which the two lane halves share.
+#include "tkg_device.hpp"
+#include "tkg_kernels.hpp"
+#include "tkg_layout.hpp"
+
+#include <type_traits>
+
+namespace tkg {
+namespace {
+
+constexpr int BM = kBM, BN = kBN;
+constexpr int BKB = 128;                  // value bytes per row per stage
+constexpr int SLOTS = 4;
+constexpr int SLAB = BM * BKB;            // 32 KiB
+constexpr int WAVES_N = 2, WAVES = 4;
+constexpr int WM = BM / 2, WN = BN / WAVES_N;  // 128 x 128 wave tile
+constexpr int FM = WM / 32, FN = WN / 32;
+constexpr int DMA = SLAB / 1024 / WAVES;  // value loads per wave per slab
+
+template <int FMT>
+struct Mx {
+  static constexpr bool FP4 = FMT == kMxfp4;
+  static constexpr int SB = FP4 ? 8 : 4;          // 32-element blocks per row per stage
+  static constexpr int KSTEPS = FP4 ? 4 : 2;      // 64-element k-steps per stage
+  static constexpr int PARTS = FP4 ? 1 : 2;       // 16-byte reads per lane per fragment
+  static constexpr int SSLAB = BM * SB;           // scale bytes per slab
+  static constexpr int SDMA = SSLAB / 256 / WAVES;  // 4-byte scale loads per wave per slab
+  static constexpr int ROWS_PER_SDMA = 256 / SB;  // rows one scale load covers
+  static constexpr int CB = FP4 ? 4 : 0;          // MFMA operand format: 4 = fp4, 0 = fp8
+  static_assert(SDMA >= 1, "scale slab needs a load per wave");
+};
+
+struct TileState {
+  int m0, n0;
+  __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
+};
+
+__device__ __forceinline__ TileState tile_state(const MxArgs& p, int t) {
+  TileState s;
+  if (t >= p.num_tiles) {  // past the last tile: empty resources read zeros
+    s.m0 = s.n0 = 0;
+    s.ra = make_rsrc(p.A, 0);
+    s.rb = make_rsrc(p.B, 0);
+    s.rsa = make_rsrc(p.As, 0);
+    s.rsb = make_rsrc(p.Bs, 0);
+    return s;
+  }
+  int pm, pn;
+  grouped_tile(t, p.tiles_m, p.tiles_n, p.group_m, pm, pn);
+  s.m0 = pm * BM;
+  s.n0 = pn * BN;
+  const uint32_t rows_a = (uint32_t)min(p.M - s.m0, BM);
+  const uint32_t rows_b = (uint32_t)min(p.N - s.n0, BN);
+  s.ra = make_rsrc(p.A + (size_t)s.m0 * p.vbytes, rows_a * p.vbytes);
+  s.rb = make_rsrc(p.B + (size_t)s.n0 * p.vbytes, rows_b * p.vbytes);
+  s.rsa = make_rsrc(p.As + (size_t)s.m0 * p.sbytes, rows_a * p.sbytes);
+  s.rsb = make_rsrc(p.Bs + (size_t)s.n0 * p.sbytes, rows_b * p.sbytes);
+  return s;
+}
+
+// One scaled MFMA: D += (Bfrag, B scale) x (Afrag, A scale); OPSEL picks the
+// byte of each scale word that holds this k-step's E8M0 scale.
+template <int CB, int OPSEL>
+__device__ __forceinline__ f32x16_t mfma_mx(i32x8_t b, int sb, i32x8_t a, int sa,
+                                            f32x16_t c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, CB, CB, OPSEL, sb,
+                                                         OPSEL, sa);
+}
+
+template <int FMT, bool KTAIL>
+__global__ __launch_bounds__(64 * WAVES)
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_mx_kernel(MxArgs p) {
+  using S = Mx<FMT>;
+  constexpr int KSTEPS = S::KSTEPS, PARTS = S::PARTS, SB = S::SB;
+  constexpr int SSLAB = S::SSLAB, SDMA = S::SDMA;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[SLOTS * (SLAB + SSLAB)];
+  TKG_LDS uint8_t* smem = (TKG_LDS uint8_t*)smem_raw;
+  TKG_LDS uint8_t* ssm = smem + SLOTS * SLAB;   // scale slabs
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int G = gridDim.x;
+  int t = xcd_virtual_id(blockIdx.x, G, p.xcd_remap);
+  if (t >= p.num_tiles) return;
+  const uint32_t nk = (p.vbytes + BKB - 1) / BKB;
+
+  // ---- staging offsets -----------------------------------------------------
+  // values: load q = wave*DMA + i of a slab fills rows dma_row(q); without a
+  // K tail its offset is a scalar part plus one of two per-lane values
+  constexpr int NOFF = KTAIL ? DMA : 2;
+  uint32_t dma_off[NOFF], dma_kb[KTAIL ? DMA : 1];
+  if constexpr (KTAIL) {
+#pragma unroll
+    for (int i = 0; i < DMA; ++i) {
+      const uint32_t q = wave * DMA + i;
+      dma_kb[i] = dma_chunk(BKB, q, lane) * 16u;
+      dma_off[i] = dma_row(BKB, q, lane) * p.vbytes + dma_kb[i];
+    }
+  } else {
+    dma_kb[0] = 0;
+#pragma unroll
+    for (int par = 0; par < 2; ++par) dma_off[par] = dma_lane_offset(BKB, par, lane, p.vbytes);
+  }
+  const uint32_t rows_step = dma_rows_per_instr(BKB) * p.vbytes;
+  // scales: load i of this wave covers rows (wave*SDMA + i) * ROWS_PER_SDMA
+  // onward, lane l row l / (SB/4), bytes 4 * (l % (SB/4)) of the stage
+  constexpr uint32_t LPR = SB / 4;   // lanes per row
+  const uint32_t s_row = lane / LPR, s_part = (lane % LPR) * 4u;
+  const uint32_t s_lane_off = s_row * p.sbytes + s_part;
+  const uint32_t s_rows_step = S::ROWS_PER_SDMA * p.sbytes;
+
+  // ---- fragment reads --------------------------------------------------------
+  // lane l reads row l % 32 of a fragment; k-step s, part q at chunk
+  // fp4: 2s + l/32; fp8: 4s + 2q + l/32 (see the header)
+  const uint32_t frow = lane & 31;
+  const uint32_t khalf = lane >> 5;
+  uint32_t roff[KSTEPS][PARTS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+    for (int q = 0; q < PARTS; ++q)
+      roff[s][q] = swz_offset(BKB, frow, S::FP4 ? 2 * s + khalf : 4 * s + 2 * q + khalf);
+  const uint32_t a_base = wm * WM * BKB, b_base = wn * WN * BKB;
+  const uint32_t as_base = (wm * WM + frow) * SB, bs_base = (wn * WN + frow) * SB;
+
+  // ---- load cursor: slab (tile lt, stage lkt, operand lop) -------------------
+  TileState cur = tile_state(p, t);
+  TileState lts = cur;
+  int lt = t;
+  uint32_t lkt = 0, lop = 0, lslot = 0;
+  auto advance_load = [&]() {
+    lslot = (lslot + 1 == SLOTS) ? 0 : lslot + 1;
+    if (lop == 0) {
+      lop = 1;
+    } else {
+      lop = 0;
+      if (++lkt == nk) {
+        lkt = 0;
+        lt += G;
+        lts = tile_state(p, lt);
+      }
+    }
+  };
+  struct SlabLoad {
+    __amdgpu_buffer_rsrc_t r, rs;
+    uint32_t slot, k0, s0;
+  };
+  auto next_slab = [&]() {
+    SlabLoad s;
+    s.r = lop ? lts.rb : lts.ra;
+    s.rs = lop ? lts.rsb : lts.rsa;
+    s.slot = lslot;
+    s.k0 = lkt * BKB;
+    s.s0 = lkt * SB;
+    advance_load();
+    return s;
+  };
+  // load i of a slab: i < DMA values, then SDMA scale loads
+  constexpr int NLOAD = DMA + SDMA;
+  auto issue_one = [&](const SlabLoad& s, int i) {
+    if (i < DMA) {
+      TKG_LDS uint8_t* dst = smem + s.slot * SLAB + (wave * DMA + i) * 1024;
+      const uint32_t q = wave * DMA + i;
+      if constexpr (KTAIL) {
+        const uint32_t off = (s.k0 + dma_kb[i] < p.vbytes) ? dma_off[i] + s.k0 : kOobOffset;
+        dma_b128(s.r, dst, off);
+      } else {
+        dma_b128_soff(s.r, dst, dma_off[q & 1], s.k0 + q * rows_step);
+      }
+    } else {
+      const int j = i - DMA;
+      TKG_LDS uint8_t* dst = ssm + s.slot * SSLAB + (wave * SDMA + j) * 256;
+      const uint32_t base = (uint32_t)(wave * SDMA + j) * s_rows_step + s.s0;
+      if constexpr (KTAIL) {
+        const uint32_t off = (s.s0 + s_part < p.sbytes) ? s_lane_off + base : kOobOffset;
+        dma_b32(s.rs, dst, off);
+      } else {
+        dma_b32_soff(s.rs, dst, s_lane_off, base);
+      }
+    }
+  };
+  auto issue = [&](const SlabLoad& s) {
+#pragma unroll
+    for (int i = 0; i < NLOAD; ++i) issue_one(s, i);
+  };
+
+  // ---- registers ---------------------------------------------------------------
+  // A fragments single-buffered (re-read after their last MFMA), B double;
+  // scale words of the stage per fragment, read with the stage's first
+  // fragments and shifted so that this lane's block sits in bytes 0 and 2
+  i32x8_t fa[FM], fb[2][FN];
+  using SW = typename std::conditional<S::FP4, u32x2_t, uint32_t>::type;
+  SW sa[FM], sbs[FN];
+  auto read_frag = [&](int slot, uint32_t row0, int s, i32x8_t& v) {
+    const TKG_LDS uint8_t* base = smem + slot * SLAB;
+    const i32x4_t lo = lds_read<i32x4_t>(base, row0 + roff[s][0]);
+    if constexpr (PARTS == 2) {
+      const i32x4_t hi = lds_read<i32x4_t>(base, row0 + roff[s][PARTS - 1]);
+      v = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+      v = i32x8_t{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+    }
+  };
+  auto read_scale = [&](int slot, uint32_t off, SW& w) {
+    const TKG_LDS uint8_t* base = ssm + slot * SSLAB;
+    if constexpr (S::FP4) {
+      const u32x2_t v = lds_read<u32x2_t>(base, off);
+      w = u32x2_t{v[0] >> (8 * khalf), v[1] >> (8 * khalf)};
+    } else {
+      w = lds_read<uint32_t>(base, off) >> (8 * khalf);
+    }
+  };
+  // the word and byte (OPSEL) of k-step s
+  auto sword = [&](const SW& w, int s) -> int {
+    if constexpr (S::FP4) return (int)w[s / 2];
+    else return (int)w;
+  };
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
+
+  // ---- prologue --------------------------------------------------------------
+#pragma unroll
+  for (int b = 0; b < SLOTS; ++b) issue(next_slab());
+  wait_vmcnt<(SLOTS - 2) * NLOAD>();   // slabs 0 and 1 (stage 0) have landed
+  __syncthreads();
+  int aslot = 0, bslot = 1;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    read_frag(aslot, a_base + i * 32 * BKB, 0, fa[i]);
+    read_scale(aslot, as_base + i * 32 * SB, sa[i]);
+  }
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    read_frag(bslot, b_base + j * 32 * BKB, 0, fb[0][j]);
+    read_scale(bslot, bs_base + j * 32 * SB, sbs[j]);
+  }
+
+  // One k-step in program order (see gemm_dense.hip): after MFMA (i, j) the
+  // instructions of its slot. The next k-step's fragments come from slots
+  // (na, nb) at k-step ns; at a stage boundary the next stage's scale words
+  // are read after the k-step's last MFMA that uses the current ones.
+  bool fresh_tile = false;
+  constexpr int NDMA = 2 * NLOAD;
+  SW sa_n[FM], sb_n[FN];
+  auto kstep_body = [&](int c, int s, auto sc, int ns, int na, int nb, bool boundary,
+                        const SlabLoad* l0, const SlabLoad* l1) {
+    constexpr int SC = decltype(sc)::value;   // k-step index inside the stage
+    constexpr int OPSEL = S::FP4 ? 2 * (SC % 2) : 2 * SC;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        acc[i][j] = mfma_mx<S::CB, OPSEL>(fb[c][j], sword(sbs[j], SC), fa[i],
+                                         sword(sa[i], SC), acc[i][j]);
+        const int q = i * FN + j;
+        if (q < FN) read_frag(nb, b_base + q * 32 * BKB, ns, fb[c ^ 1][q]);
+        if (j == FN - 1) read_frag(na, a_base + i * 32 * BKB, ns, fa[i]);
+        if (boundary) {
+          if (q < FM) read_scale(na, as_base + q * 32 * SB, sa_n[q]);
+          else if (q < FM + FN) read_scale(nb, bs_base + (q - FM) * 32 * SB, sb_n[q - FM]);
+#pragma unroll
+          for (int d = q * NDMA / (FM * FN); d < (q + 1) * NDMA / (FM * FN); ++d) {
+            if (d < NLOAD) issue_one(*l0, d);
+            else issue_one(*l1, d - NLOAD);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    (void)s;
+  };
+  auto kstep = [&](int c, auto sc) {
+    constexpr int SC = decltype(sc)::value;
+    if constexpr (SC != KSTEPS - 1) {
+      kstep_body(c, SC, sc, SC + 1, aslot, bslot, false, nullptr, nullptr);
+    } else {
+      const SlabLoad l0 = next_slab();
+      const SlabLoad l1 = next_slab();
+      if (fresh_tile) wait_vmcnt<0>();
+      else wait_vmcnt<(SLOTS - 4) * NLOAD>();
+      fresh_tile = false;
+      lds_barrier();
+      const int na = (aslot + 2) % SLOTS, nb = (bslot + 2) % SLOTS;
+      kstep_body(c, SC, sc, 0, na, nb, true, &l0, &l1);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) sa[i] = sa_n[i];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) sbs[j] = sb_n[j];
+      aslot = na;
+      bslot = nb;
+    }
+  };
+
+  for (;;) {
+    for (uint32_t kt = 0; kt < nk; ++kt) {
+      kstep(0, std::integral_constant<int, 0>{});
+      kstep(1, std::integral_constant<int, 1>{});
+      if constexpr (KSTEPS == 4) {
+        kstep(0, std::integral_constant<int, 2>{});
+        kstep(1, std::integral_constant<int, 3>{});
+      }
+    }
+
+    // ---- finish (as in gemm_dense.hip, 32x32 blocks) ---------------------------
+    const bool vec_ok = (p.N & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int m = cur.m0 + wm * WM + i * 32 + (int)frow;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = cur.n0 + wn * WN + j * 32 + 8 * g + 4 * (int)khalf;
+          const uint2 pk = pack_bf16x4(acc[i][j][4 * g + 0] * p.scale, acc[i][j][4 * g + 1] * p.scale,
+                                       acc[i][j][4 * g + 2] * p.scale, acc[i][j][4 * g + 3] * p.scale);
+          if (m < p.M) {
+            uint16_t* cp = p.C + (size_t)m * (size_t)p.N + n;
+            if (vec_ok && n + 3 < p.N) {
+              *reinterpret_cast<uint2*>(cp) = pk;
+            } else {
+              const uint16_t e[4] = {(uint16_t)(pk.x & 0xFFFF), (uint16_t)(pk.x >> 16),
+                                     (uint16_t)(pk.y & 0xFFFF), (uint16_t)(pk.y >> 16)};
+#pragma unroll
+              for (int u = 0; u < 4; ++u)
+                if (n + u < p.N) cp[u] = e[u];
+            }
+          }
+        }
+        acc[i][j] = f32x16_t{};
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    fresh_tile = true;
+
+    t += G;
+    if (t >= p.num_tiles) break;
+    cur = tile_state(p, t);
+  }
+  // the load cursor ran ahead into empty resources; let those LDS writes land
+  wait_vmcnt<0>();
+}
+
+template <int FMT>
+void launch_fmt(const MxArgs& a, int grid, hipStream_t stream) {
+  // a stage spans BKB bytes of values; a ragged last stage masks its loads
+  if (a.vbytes % BKB != 0)
+    hipLaunchKernelGGL((gemm_mx_kernel<FMT, true>), dim3(grid), dim3(64 * WAVES), 0, stream, a);
+  else
+    hipLaunchKernelGGL((gemm_mx_kernel<FMT, false>), dim3(grid), dim3(64 * WAVES), 0, stream, a);
+}
+
+}  // namespace
+
+hipError_t launch_mx(MxType fmt, const MxArgs& a, int grid, hipStream_t stream) {
+  if (fmt == kMxfp4) launch_fmt<kMxfp4>(a, grid, stream);
+  else launch_fmt<kMxfp8>(a, grid, stream);
+  return hipGetLastError();
+}
+
+}  // namespace tkg

@@ -156,6 +156,49 @@ int run_fp4(int64_t M, int64_t N, int64_t K, const void* A, const void* As,
   return e == hipSuccess ? TKG_OK : TKG_ERR_LAUNCH;
 }
 
+int run_mx(tkg::MxType fmt, int64_t M, int64_t N, int64_t K, const void* A,
+           const void* As, const void* B, const void* Bs, float scale, void* C,
+           void* stream, const tkg_opts* opts) {
+  // K % 128: value rows and scale rows (K/32 bytes) stay 16- and 4-byte
+  // aligned; 256 rows of values below 2^31 bytes (one buffer resource)
+  const int64_t kmax = (fmt == tkg::kMxfp4) ? 16777088 : 8388480;
+  int st = check_common(M, N, K, 128, kmax);
+  if (st != TKG_OK) return st;
+  const int variant = opts ? opts->variant : 0;
+  if (variant != 0) return TKG_ERR_SHAPE;
+  if (M == 0 || N == 0) return TKG_OK;
+  if (C == nullptr ||
+      (K > 0 && (A == nullptr || B == nullptr || As == nullptr || Bs == nullptr)))
+    return TKG_ERR_NULL;
+  if (!aligned16(C) || (K > 0 && (!aligned16(A) || !aligned16(B) ||
+                                  !aligned16(As) || !aligned16(Bs))))
+    return TKG_ERR_ALIGN;
+  Plan pl;
+  st = make_plan(M, N, opts, &pl);
+  if (st != TKG_OK) return st;
+  tkg::MxArgs a;
+  a.A = static_cast<const uint8_t*>(A);
+  a.As = static_cast<const uint8_t*>(As);
+  a.B = static_cast<const uint8_t*>(B);
+  a.Bs = static_cast<const uint8_t*>(Bs);
+  a.C = static_cast<uint16_t*>(C);
+  a.M = (int32_t)M;
+  a.N = (int32_t)N;
+  a.vbytes = (uint32_t)(fmt == tkg::kMxfp4 ? K / 2 : K);
+  a.sbytes = (uint32_t)(K / 32);
+  a.scale = scale;
+  a.tiles_m = pl.tiles_m;
+  a.tiles_n = pl.tiles_n;
+  a.num_tiles = pl.num_tiles;
+  a.group_m = pl.group_m;
+  a.xcd_remap = pl.xcd_remap;
+  if (K == 0) {
+    a.A = a.B = a.As = a.Bs = static_cast<const uint8_t*>(C);
+  }
+  const hipError_t e = tkg::launch_mx(fmt, a, pl.grid, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TKG_OK : TKG_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -179,6 +222,20 @@ int gemm_fp4_blockscaled(int64_t M, int64_t N, int64_t K, const void* A,
                  stream, nullptr);
 }
 
+int gemm_mxfp4(int64_t M, int64_t N, int64_t K, const void* A,
+               const void* A_scales, const void* B, const void* B_scales,
+               void* C, void* stream) {
+  return run_mx(tkg::kMxfp4, M, N, K, A, A_scales, B, B_scales, 1.0f, C, stream,
+                nullptr);
+}
+
+int gemm_mxfp8(int64_t M, int64_t N, int64_t K, const void* A,
+               const void* A_scales, const void* B, const void* B_scales,
+               void* C, void* stream) {
+  return run_mx(tkg::kMxfp8, M, N, K, A, A_scales, B, B_scales, 1.0f, C, stream,
+                nullptr);
+}
+
 int tkg_gemm_ex(int dtype, int64_t M, int64_t N, int64_t K, const void* A,
                 const void* A_scales, float a_scale, const void* B,
                 const void* B_scales, float b_scale, void* C, void* stream,
@@ -192,6 +249,12 @@ int tkg_gemm_ex(int dtype, int64_t M, int64_t N, int64_t K, const void* A,
     case TKG_DTYPE_FP4_BLOCKSCALED:
       return run_fp4(M, N, K, A, A_scales, a_scale, B, B_scales, b_scale, C,
                      stream, opts);
+    case TKG_DTYPE_MXFP4:
+      return run_mx(tkg::kMxfp4, M, N, K, A, A_scales, B, B_scales,
+                    a_scale * b_scale, C, stream, opts);
+    case TKG_DTYPE_MXFP8:
+      return run_mx(tkg::kMxfp8, M, N, K, A, A_scales, B, B_scales,
+                    a_scale * b_scale, C, stream, opts);
     default:
       return TKG_ERR_SHAPE;
   }

@@ -50,6 +50,12 @@ __device__ __forceinline__ void dma_b32(__amdgpu_buffer_rsrc_t r,
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 4, voff, 0, 0, 0);
 }
 
+__device__ __forceinline__ void dma_b32_soff(__amdgpu_buffer_rsrc_t r,
+                                             TKG_LDS void* lds, uint32_t voff,
+                                             uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 4, voff, soff, 0, 0);
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

@@ -38,6 +38,24 @@ struct Fp4Args {
   int32_t xcd_remap;
 };
 
+// MX block-scaled problem: e2m1 values two per byte (K/2 bytes per row) or
+// e4m3 values (K bytes per row), one E8M0 scale per 32 K-elements (K/32
+// bytes per row).
+enum MxType { kMxfp4 = 0, kMxfp8 = 1 };
+struct MxArgs {
+  const uint8_t* A;
+  const uint8_t* As;
+  const uint8_t* B;
+  const uint8_t* Bs;
+  uint16_t* C;
+  int32_t M, N;
+  uint32_t vbytes;  // value bytes per row
+  uint32_t sbytes;  // K/32
+  float scale;
+  int32_t tiles_m, tiles_n, num_tiles, group_m;
+  int32_t xcd_remap;
+};
+
 // Tile shape shared by the kernels and the host-side argument checks.
 constexpr int kBM = 256;
 constexpr int kBN = 256;
@@ -51,6 +69,7 @@ int dense_default_mi(DenseType dt);
 hipError_t launch_fp4(const Fp4Args& a, int grid, int variant,
                       hipStream_t stream);
 int fp4_num_variants();
+hipError_t launch_mx(MxType fmt, const MxArgs& a, int grid, hipStream_t stream);
 
 // K bytes per stage row of each kernel family (for the host).
 uint32_t dense_stage_kbytes();

@@ -30,11 +30,13 @@ __device__ int rf8(unsigned h) {  // four random OCP e4m3 codes, no NaN
   return r;
 }
 
-// KIND: 0 bf16 32x32x16, 1 bf16 16x16x32, 2 fp8 32x32x64, 3 fp8 16x16x128.
+// KIND: 0 bf16 32x32x16, 1 bf16 16x16x32, 2 fp8 32x32x64, 3 fp8 16x16x128,
+// 4 fp8 32x32x64 with E8M0 block scales, 5 fp4 32x32x64 with scales,
+// 6 fp4 16x16x128 with scales.
 // TOGGLE: 1 = two fragment sets alternated; 0 = one set.
 template <int KIND, int WAVES, int TOGGLE>
 __global__ __launch_bounds__(64 * WAVES) void mfma_loop(float* out, long long* clk, int iters) {
-  constexpr bool MI32 = (KIND == 0 || KIND == 2);
+  constexpr bool MI32 = (KIND == 0 || KIND == 2 || KIND == 4 || KIND == 5);
   constexpr bool FP8 = (KIND >= 2);
   constexpr int FM = MI32 ? 4 : 8;
   constexpr int FN = (MI32 ? 2 : 4) * (WAVES == 8 ? 1 : 2);
@@ -55,6 +57,7 @@ __global__ __launch_bounds__(64 * WAVES) void mfma_loop(float* out, long long* c
     }
   Acc acc[FM][FN];
   for (int i = 0; i < FM; ++i) for (int j = 0; j < FN; ++j) acc[i][j] = Acc{};
+  const int scl = 120 + (int)(hsh(seed) % 8);   // E8M0 scale words of the scaled kinds
   const long long t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
   for (int it = 0; it < iters; ++it)
 #pragma unroll
@@ -68,7 +71,10 @@ __global__ __launch_bounds__(64 * WAVES) void mfma_loop(float* out, long long* c
           if constexpr (KIND == 0) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, acc[i][j], 0, 0, 0);
           else if constexpr (KIND == 1) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, acc[i][j], 0, 0, 0);
           else if constexpr (KIND == 2) acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, acc[i][j], 0, 0, 0, 0, 0, 0);
-          else acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, acc[i][j], 0, 0, 0, 0, 0, 0);
+          else if constexpr (KIND == 3) acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, acc[i][j], 0, 0, 0, 0, 0, 0);
+          else if constexpr (KIND == 4) acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, acc[i][j], 0, 0, 0, scl + i, 0, scl + j);
+          else if constexpr (KIND == 5) acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, acc[i][j], 4, 4, 0, scl + i, 0, scl + j);
+          else acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(x, y, acc[i][j], 4, 4, 0, scl + i, 0, scl + j);
         }
   const long long t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
   float s = 0;
@@ -81,8 +87,8 @@ template <int KIND, int WAVES, int TOGGLE>
 void run(const char* name, float* out, long long* clk, bool print) {
   const int iters = 4000, grid = 256;
   const size_t lds = 96 * 1024;  // one workgroup per CU
-  constexpr bool MI32 = (KIND == 0 || KIND == 2);
-  const double kdepth = (KIND == 0) ? 16 : (KIND == 1) ? 32 : (KIND == 2) ? 64 : 128;
+  constexpr bool MI32 = (KIND == 0 || KIND == 2 || KIND == 4 || KIND == 5);
+  const double kdepth = (KIND == 0) ? 16 : (KIND == 1) ? 32 : (KIND == 2 || KIND == 4 || KIND == 5) ? 64 : 128;
   const double fm = MI32 ? 4 : 8, fn = (MI32 ? 2 : 4) * (WAVES == 8 ? 1 : 2), blk = MI32 ? 32 : 16;
   const double flop_per_iter_wave = 2.0 * 2 * fm * fn * blk * blk * kdepth;
   if (hipFuncSetAttribute((const void*)mfma_loop<KIND, WAVES, TOGGLE>,
@@ -118,6 +124,11 @@ int main() {
     run<3, 4, 1>("fp8 16x16x128", out, clk, p);
     run<2, 8, 0>("fp8 32x32x64", out, clk, p);
     run<3, 8, 0>("fp8 16x16x128", out, clk, p);
+    run<4, 4, 1>("fp8 32x32x64, E8M0 scales", out, clk, p);
+    run<5, 4, 1>("fp4 32x32x64, E8M0 scales", out, clk, p);
+    run<6, 4, 1>("fp4 16x16x128, E8M0 scales", out, clk, p);
+    run<5, 8, 1>("fp4 32x32x64, E8M0 scales", out, clk, p);
+    run<6, 8, 1>("fp4 16x16x128, E8M0 scales", out, clk, p);
   }
   if (hipDeviceSynchronize() != hipSuccess) return 2;
   return 0;
