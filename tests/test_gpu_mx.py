@@ -134,6 +134,23 @@ def test_mx_ex_output_scale_and_options(dev, elem):
 
 
 @pytest.mark.parametrize("elem", ELEMS)
+@pytest.mark.parametrize("K", [512, 1536, 2048])
+def test_mx_wide_scale_staging_across_tiles(dev, elem, K):
+    # K % 512 == 0 stages scales 16 bytes per row (several stages at once,
+    # two alternating LDS slots); a small grid makes every workgroup walk
+    # several tiles, with an odd (K = 512, 1536) and an even (2048) number
+    # of such loads per tile, so the slot parity carries across tiles
+    M, N = 700, 1100
+    Av, As = gi.mx_operand(79, M, K, elem)
+    Bv, Bs = gi.mx_operand(80, N, K, elem)
+    args = [_up(Av, dev), _up(As, dev), _up(Bv, dev), _up(Bs, dev)]
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    assert tkg.tkg_gemm_ex(DTYPE[elem], M, N, K, args[0], args[1], 1.0, args[2], args[3],
+                           1.0, C, grid=5) == 0
+    _check(_result(C), Av, As, Bv, Bs, elem, ("wide", K))
+
+
+@pytest.mark.parametrize("elem", ELEMS)
 def test_mx_empty_k_gives_zeros(dev, elem):
     C = torch.full((64, 80), 3.0, dtype=torch.bfloat16, device=dev)
     e = torch.empty((64, 0), dtype=torch.uint8, device=dev)

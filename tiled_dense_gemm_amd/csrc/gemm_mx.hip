@@ -91,14 +91,27 @@ __device__ __forceinline__ f32x16_t mfma_mx(i32x8_t b, int sb, i32x8_t a, int sa
                                                          OPSEL, sa);
 }
 
-template <int FMT, bool KTAIL>
+// Scale staging. Narrow (WIDE = false): every slab load also fetches the
+// stage's SB scale bytes of its 256 rows, 4 bytes per lane. Each lane then
+// touches its own cache line, so these loads cost as many cache lookups as
+// the value loads. Wide (K a multiple of 512, so rows of scales are a whole
+// number of 16-byte pieces): one 16-byte load per row covers U = 16 / SB
+// stages (a superstage); superstages alternate between two LDS slots of
+// 256 rows x 16 bytes per operand, and a stage's scale word sits at byte
+// SB * (stage mod U) of its row.
+template <int FMT, bool KTAIL, bool WIDE>
 __global__ __launch_bounds__(64 * WAVES)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_mx_kernel(MxArgs p) {
   using S = Mx<FMT>;
   constexpr int KSTEPS = S::KSTEPS, PARTS = S::PARTS, SB = S::SB;
   constexpr int SSLAB = S::SSLAB, SDMA = S::SDMA;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[SLOTS * (SLAB + SSLAB)];
+  static_assert(!(WIDE && KTAIL), "wide scale staging needs whole stages");
+  static_assert(SLOTS == 4, "the stage-end wait drains every load, superstages included");
+  constexpr uint32_t U = 16 / SB;                 // stages per superstage
+  constexpr uint32_t WSLOT = 2 * BM * 16;         // one superstage, A then B
+  constexpr int SCALE_LDS = WIDE ? 2 * WSLOT : SLOTS * SSLAB;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[SLOTS * SLAB + SCALE_LDS];
   TKG_LDS uint8_t* smem = (TKG_LDS uint8_t*)smem_raw;
   TKG_LDS uint8_t* ssm = smem + SLOTS * SLAB;   // scale slabs
 
@@ -135,6 +148,9 @@ void gemm_mx_kernel(MxArgs p) {
   const uint32_t s_row = lane / LPR, s_part = (lane % LPR) * 4u;
   const uint32_t s_lane_off = s_row * p.sbytes + s_part;
   const uint32_t s_rows_step = S::ROWS_PER_SDMA * p.sbytes;
+  // wide: wave w fetches rows 64w .. 64w+63 of both operands, lane l row
+  // 64w + l, 16 bytes from the superstage's first scale byte
+  const uint32_t w_lane_off = lane * p.sbytes;
 
   // ---- fragment reads --------------------------------------------------------
   // lane l reads row l % 32 of a fragment; k-step s, part q at chunk
@@ -148,7 +164,12 @@ void gemm_mx_kernel(MxArgs p) {
     for (int q = 0; q < PARTS; ++q)
       roff[s][q] = swz_offset(BKB, frow, S::FP4 ? 2 * s + khalf : 4 * s + 2 * q + khalf);
   const uint32_t a_base = wm * WM * BKB, b_base = wn * WN * BKB;
-  const uint32_t as_base = (wm * WM + frow) * SB, bs_base = (wn * WN + frow) * SB;
+  // scale word of fragment i: narrow at slot * SSLAB + as_base + i * SFRAG,
+  // wide at (superstage slot, stage) + as_base + i * SFRAG
+  constexpr uint32_t SROW = WIDE ? 16 : SB;   // LDS bytes per row of scales
+  constexpr uint32_t SFRAG = 32 * SROW;
+  const uint32_t as_base = (wm * WM + frow) * SROW;
+  const uint32_t bs_base = (WIDE ? BM * 16 : 0) + (wn * WN + frow) * SROW;
 
   // ---- load cursor: slab (tile lt, stage lkt, operand lop) -------------------
   TileState cur = tile_state(p, t);
@@ -182,8 +203,8 @@ void gemm_mx_kernel(MxArgs p) {
     advance_load();
     return s;
   };
-  // load i of a slab: i < DMA values, then SDMA scale loads
-  constexpr int NLOAD = DMA + SDMA;
+  // load i of a slab: i < DMA values, then (narrow) SDMA scale loads
+  constexpr int NLOAD = DMA + (WIDE ? 0 : SDMA);
   auto issue_one = [&](const SlabLoad& s, int i) {
     if (i < DMA) {
       TKG_LDS uint8_t* dst = smem + s.slot * SLAB + (wave * DMA + i) * 1024;
@@ -210,11 +231,18 @@ void gemm_mx_kernel(MxArgs p) {
 #pragma unroll
     for (int i = 0; i < NLOAD; ++i) issue_one(s, i);
   };
+  // wide: the superstage of tile ts that starts at `stage`, into `slot`
+  auto load_superstage = [&](const TileState& ts, uint32_t stage, uint32_t slot) {
+    TKG_LDS uint8_t* dst = ssm + slot * WSLOT + wave * 1024;
+    const uint32_t soff = (uint32_t)wave * 64u * p.sbytes + stage * SB;
+    dma_b128_soff(ts.rsa, dst, w_lane_off, soff);
+    dma_b128_soff(ts.rsb, dst + BM * 16, w_lane_off, soff);
+  };
 
   // ---- registers ---------------------------------------------------------------
   // A fragments single-buffered (re-read after their last MFMA), B double;
-  // scale words of the stage per fragment, read with the stage's first
-  // fragments and shifted so that this lane's block sits in bytes 0 and 2
+  // scale words of the stage per fragment, read during the previous stage's
+  // last k-step and shifted so that this lane's block sits in bytes 0 and 2
   i32x8_t fa[FM], fb[2][FN];
   using SW = typename std::conditional<S::FP4, u32x2_t, uint32_t>::type;
   SW sa[FM], sbs[FN];
@@ -228,14 +256,21 @@ void gemm_mx_kernel(MxArgs p) {
       v = i32x8_t{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
     }
   };
-  auto read_scale = [&](int slot, uint32_t off, SW& w) {
-    const TKG_LDS uint8_t* base = ssm + slot * SSLAB;
-    if constexpr (S::FP4) {
-      const u32x2_t v = lds_read<u32x2_t>(base, off);
-      w = u32x2_t{v[0] >> (8 * khalf), v[1] >> (8 * khalf)};
-    } else {
-      w = lds_read<uint32_t>(base, off) >> (8 * khalf);
-    }
+  // the raw words; lane_block() moves this lane's block into place later, so
+  // that the wait for the read falls after the k-step's MFMAs
+  auto read_scale = [&](uint32_t off, SW& w) {
+    if constexpr (S::FP4) w = lds_read<u32x2_t>(ssm, off);
+    else w = lds_read<uint32_t>(ssm, off);
+  };
+  // where the scale words of the stage after global stage g (this
+  // workgroup's running stage count) begin, given the slot of its values
+  auto scale_base = [&](uint32_t g, int vslot) -> uint32_t {
+    if constexpr (WIDE) return (((g + 1) / U) & 1u) * WSLOT + ((g + 1) % U) * SB;
+    else return (uint32_t)vslot * SSLAB;
+  };
+  auto lane_block = [&](const SW& w) -> SW {
+    if constexpr (S::FP4) return u32x2_t{w[0] >> (8 * khalf), w[1] >> (8 * khalf)};
+    else return w >> (8 * khalf);
   };
   // the word and byte (OPSEL) of k-step s
   auto sword = [&](const SW& w, int s) -> int {
@@ -250,31 +285,43 @@ void gemm_mx_kernel(MxArgs p) {
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
 
   // ---- prologue --------------------------------------------------------------
+  if constexpr (WIDE) load_superstage(cur, 0, 0);
 #pragma unroll
   for (int b = 0; b < SLOTS; ++b) issue(next_slab());
   wait_vmcnt<(SLOTS - 2) * NLOAD>();   // slabs 0 and 1 (stage 0) have landed
   __syncthreads();
   int aslot = 0, bslot = 1;
+  {
+    const uint32_t sa0 = WIDE ? 0u : (uint32_t)aslot * SSLAB;
+    const uint32_t sb0 = WIDE ? 0u : (uint32_t)bslot * SSLAB;
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    read_frag(aslot, a_base + i * 32 * BKB, 0, fa[i]);
-    read_scale(aslot, as_base + i * 32 * SB, sa[i]);
+    for (int i = 0; i < FM; ++i) {
+      read_frag(aslot, a_base + i * 32 * BKB, 0, fa[i]);
+      read_scale(sa0 + as_base + i * SFRAG, sa[i]);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      read_frag(bslot, b_base + j * 32 * BKB, 0, fb[0][j]);
+      read_scale(sb0 + bs_base + j * SFRAG, sbs[j]);
+    }
   }
 #pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    read_frag(bslot, b_base + j * 32 * BKB, 0, fb[0][j]);
-    read_scale(bslot, bs_base + j * 32 * SB, sbs[j]);
-  }
+  for (int i = 0; i < FM; ++i) sa[i] = lane_block(sa[i]);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) sbs[j] = lane_block(sbs[j]);
 
   // One k-step in program order (see gemm_dense.hip): after MFMA (i, j) the
   // instructions of its slot. The next k-step's fragments come from slots
   // (na, nb) at k-step ns; at a stage boundary the next stage's scale words
   // are read after the k-step's last MFMA that uses the current ones.
   bool fresh_tile = false;
+  uint32_t g = 0;   // stages this workgroup has computed (all tiles)
   constexpr int NDMA = 2 * NLOAD;
   SW sa_n[FM], sb_n[FN];
   auto kstep_body = [&](int c, int s, auto sc, int ns, int na, int nb, bool boundary,
                         const SlabLoad* l0, const SlabLoad* l1) {
+    const uint32_t nsa = boundary ? scale_base(g, na) : 0u;
+    const uint32_t nsb = boundary ? scale_base(g, nb) : 0u;
     constexpr int SC = decltype(sc)::value;   // k-step index inside the stage
     constexpr int OPSEL = S::FP4 ? 2 * (SC % 2) : 2 * SC;
 #pragma unroll
@@ -287,8 +334,8 @@ void gemm_mx_kernel(MxArgs p) {
         if (q < FN) read_frag(nb, b_base + q * 32 * BKB, ns, fb[c ^ 1][q]);
         if (j == FN - 1) read_frag(na, a_base + i * 32 * BKB, ns, fa[i]);
         if (boundary) {
-          if (q < FM) read_scale(na, as_base + q * 32 * SB, sa_n[q]);
-          else if (q < FM + FN) read_scale(nb, bs_base + (q - FM) * 32 * SB, sb_n[q - FM]);
+          if (q < FM) read_scale(nsa + as_base + q * SFRAG, sa_n[q]);
+          else if (q < FM + FN) read_scale(nsb + bs_base + (q - FM) * SFRAG, sb_n[q - FM]);
 #pragma unroll
           for (int d = q * NDMA / (FM * FN); d < (q + 1) * NDMA / (FM * FN); ++d) {
             if (d < NLOAD) issue_one(*l0, d);
@@ -299,13 +346,11 @@ void gemm_mx_kernel(MxArgs p) {
       }
     (void)s;
   };
-  auto kstep = [&](int c, auto sc) {
+  auto kstep = [&](int c, auto sc, const SlabLoad& l0, const SlabLoad& l1) {
     constexpr int SC = decltype(sc)::value;
     if constexpr (SC != KSTEPS - 1) {
       kstep_body(c, SC, sc, SC + 1, aslot, bslot, false, nullptr, nullptr);
     } else {
-      const SlabLoad l0 = next_slab();
-      const SlabLoad l1 = next_slab();
       if (fresh_tile) wait_vmcnt<0>();
       else wait_vmcnt<(SLOTS - 4) * NLOAD>();
       fresh_tile = false;
@@ -313,9 +358,9 @@ void gemm_mx_kernel(MxArgs p) {
       const int na = (aslot + 2) % SLOTS, nb = (bslot + 2) % SLOTS;
       kstep_body(c, SC, sc, 0, na, nb, true, &l0, &l1);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) sa[i] = sa_n[i];
+      for (int i = 0; i < FM; ++i) sa[i] = lane_block(sa_n[i]);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) sbs[j] = sb_n[j];
+      for (int j = 0; j < FN; ++j) sbs[j] = lane_block(sb_n[j]);
       aslot = na;
       bslot = nb;
     }
@@ -323,12 +368,27 @@ void gemm_mx_kernel(MxArgs p) {
 
   for (;;) {
     for (uint32_t kt = 0; kt < nk; ++kt) {
-      kstep(0, std::integral_constant<int, 0>{});
-      kstep(1, std::integral_constant<int, 1>{});
-      if constexpr (KSTEPS == 4) {
-        kstep(0, std::integral_constant<int, 2>{});
-        kstep(1, std::integral_constant<int, 3>{});
+      // the cursor moves (and may branch to a new tile) at the top of the
+      // stage, so that no MFMA of the stage is moved past that branch and
+      // behind the stage-end wait
+      const SlabLoad l0 = next_slab();
+      const SlabLoad l1 = next_slab();
+      if constexpr (WIDE) {
+        // the next stage opens a superstage: fetch it now, into the slot no
+        // wave reads any more (the other one holds this stage's scales)
+        if ((g + 1) % U == 0) {
+          const uint32_t slot = ((g + 1) / U) & 1u;
+          if (kt + 1 < nk) load_superstage(cur, kt + 1, slot);
+          else if (t + G < p.num_tiles) load_superstage(tile_state(p, t + G), 0, slot);
+        }
       }
+      kstep(0, std::integral_constant<int, 0>{}, l0, l1);
+      kstep(1, std::integral_constant<int, 1>{}, l0, l1);
+      if constexpr (KSTEPS == 4) {
+        kstep(0, std::integral_constant<int, 2>{}, l0, l1);
+        kstep(1, std::integral_constant<int, 3>{}, l0, l1);
+      }
+      ++g;
     }
 
     // ---- finish (as in gemm_dense.hip, 32x32 blocks) ---------------------------
@@ -372,11 +432,14 @@ void gemm_mx_kernel(MxArgs p) {
 
 template <int FMT>
 void launch_fmt(const MxArgs& a, int grid, hipStream_t stream) {
-  // a stage spans BKB bytes of values; a ragged last stage masks its loads
+  // a stage spans BKB bytes of values; a ragged last stage masks its loads.
+  // Scale rows that are whole 16-byte pieces (K % 512 == 0) are staged wide.
   if (a.vbytes % BKB != 0)
-    hipLaunchKernelGGL((gemm_mx_kernel<FMT, true>), dim3(grid), dim3(64 * WAVES), 0, stream, a);
+    hipLaunchKernelGGL((gemm_mx_kernel<FMT, true, false>), dim3(grid), dim3(64 * WAVES), 0, stream, a);
+  else if (a.sbytes % 16 == 0)
+    hipLaunchKernelGGL((gemm_mx_kernel<FMT, false, true>), dim3(grid), dim3(64 * WAVES), 0, stream, a);
   else
-    hipLaunchKernelGGL((gemm_mx_kernel<FMT, false>), dim3(grid), dim3(64 * WAVES), 0, stream, a);
+    hipLaunchKernelGGL((gemm_mx_kernel<FMT, false, false>), dim3(grid), dim3(64 * WAVES), 0, stream, a);
 }
 
 }  // namespace
