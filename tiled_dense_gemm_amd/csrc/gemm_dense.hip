@@ -325,12 +325,10 @@ void gemm_dense_kernel(DenseArgs p) {
   // loads spread over the MFMAs.
   bool fresh_tile = false;  // finish stores are in flight
   constexpr int NDMA = 2 * DMA;             // slab loads per stage boundary
-  auto kstep = [&](int c, int s, bool last) {
+  auto kstep = [&](int c, int s, bool last, const SlabLoad& l0, const SlabLoad& l1) {
     if (!last) {
       kstep_body(c, s + 1, aslot, bslot, [&](int) {});
     } else {
-      const SlabLoad l0 = next_slab();
-      const SlabLoad l1 = next_slab();
       if (fresh_tile) wait_vmcnt<0>();
       else wait_vmcnt<(SLOTS - 4) * DMA>();
       fresh_tile = false;
@@ -353,8 +351,18 @@ void gemm_dense_kernel(DenseArgs p) {
   for (;;) {
     for (uint32_t kt = 0; kt < nk; kt += TRIP_STAGES) {
 #pragma unroll
-      for (int u = 0; u < TRIP_STAGES * KSTEPS; ++u)
-        kstep(u & 1, u % KSTEPS, u % KSTEPS == KSTEPS - 1);
+      for (int st = 0; st < TRIP_STAGES; ++st) {
+        // the cursor moves (and may branch to a new tile) at the top of the
+        // stage, so that no MFMA of the stage is moved past that branch and
+        // behind the stage-end wait
+        const SlabLoad l0 = next_slab();
+        const SlabLoad l1 = next_slab();
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+          const int u = st * KSTEPS + s;
+          kstep(u & 1, s, s == KSTEPS - 1, l0, l1);
+        }
+      }
     }
 
     // ---- finish: C[m][n .. n+3] from accumulator elements 4g .. 4g+3 -----
