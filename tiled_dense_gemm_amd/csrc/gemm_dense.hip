@@ -29,6 +29,7 @@
 // A K stage holds BKB bytes of K per row: BKB/2 bf16 (BKB/32 MFMA k-steps of
 // 32x32x16) or BKB fp8 (BKB/64 k-steps of 32x32x64).
 #include "tkg_device.hpp"
+#include "tkg_finish.hpp"
 #include "tkg_kernels.hpp"
 #include "tkg_layout.hpp"
 
@@ -112,7 +113,9 @@ void gemm_dense_kernel(DenseArgs p) {
   constexpr int DMA = SLAB / 1024 / LOAD_WAVES;
   static_assert(SLOTS >= 4, "two stages at least");
   static_assert(SLOTS * SLAB <= 160 * 1024, "LDS budget");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[SLOTS * SLAB];
+  // the finish stages through the LDS the ring leaves free (tkg_finish.hpp)
+  using FP = FinishPlan<MI, FM, FN, (160 * 1024 - SLOTS * SLAB) / WAVES>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[SLOTS * SLAB + WAVES * FP::BYTES];
   TKG_LDS uint8_t* smem = (TKG_LDS uint8_t*)smem_raw;
 
   // K bytes per row of one MFMA k-step, 16-byte chunks per k-step (CPK),
@@ -369,6 +372,11 @@ void gemm_dense_kernel(DenseArgs p) {
     // The MFMA ran with B as its first operand, so accumulator (i, j) holds
     // the transposed MIxMI block: lane l owns C row m = l%MI and, in element
     // r, column 4*P*(r/4) + 4*(l/MI) + r%4.
+    if constexpr (FP::USE) {
+      finish_staged<MI, FM, FN, 1, FP::RJ, DT != kBf16>(
+          acc, p.scale, smem + SLOTS * SLAB + wave * FP::BYTES, p.C, p.M, p.N,
+          cur.m0 + wm * WM, cur.n0 + wn * WN, (uint32_t)lane);
+    } else {
     const bool vec_ok = (p.N & 3) == 0;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -400,6 +408,7 @@ void gemm_dense_kernel(DenseArgs p) {
         // keep the scheduler from hoisting every accumulator read at once
         __builtin_amdgcn_sched_barrier(0);
       }
+    }
     }
     fresh_tile = true;
 

@@ -20,6 +20,7 @@
 // one stage holds 128 K-elements per row, i.e. 64 bytes of packed values
 // (swizzled as in tkg_layout.hpp) and 8 bytes of block scales.
 #include "tkg_device.hpp"
+#include "tkg_finish.hpp"
 #include "tkg_kernels.hpp"
 #include "tkg_layout.hpp"
 
@@ -136,7 +137,9 @@ void gemm_fp4_kernel(Fp4Args p) {
   constexpr int DMA_PER_STAGE = 2 * VDMA + 2 * SDMA;  // per lane
   static_assert(SDMA >= 1, "scale staging needs a load per wave");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[STAGES * STAGE_BYTES];
+  // the finish stages through the LDS the ring leaves free (tkg_finish.hpp)
+  using FP = FinishPlan<32, FM, FN, (160 * 1024 - STAGES * STAGE_BYTES) / WAVES>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[STAGES * STAGE_BYTES + WAVES * FP::BYTES];
   TKG_LDS uint8_t* smem = (TKG_LDS uint8_t*)smem_raw;
 
   const int tid = threadIdx.x;
@@ -361,6 +364,11 @@ void gemm_fp4_kernel(Fp4Args p) {
     }
 
     // ---- finish (as in gemm_dense.hip) -----------------------------------
+    if constexpr (FP::USE) {
+      finish_staged<32, FM, FN, 1, FP::RJ, true>(
+          acc, p.scale, smem + STAGES * STAGE_BYTES + wave * FP::BYTES, p.C, p.M, p.N,
+          cur.m0 + wm * WM, cur.n0 + wn * WN, (uint32_t)lane);
+    } else {
     const bool vec_ok = (p.N & 3) == 0;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -390,6 +398,7 @@ void gemm_fp4_kernel(Fp4Args p) {
         acc[i][j] = f32x16_t{};
         __builtin_amdgcn_sched_barrier(0);
       }
+    }
     }
     fresh_tile = true;
 

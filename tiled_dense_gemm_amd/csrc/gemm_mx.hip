@@ -24,6 +24,7 @@
 // K-elements 16*(l/32) .. +15 and 32 + 16*(l/32) .. +15, and its scale is
 // the one of block (l/32) of the k-step, which the two lane halves share.
 #include "tkg_device.hpp"
+#include "tkg_finish.hpp"
 #include "tkg_kernels.hpp"
 #include "tkg_layout.hpp"
 
@@ -111,7 +112,9 @@ void gemm_mx_kernel(MxArgs p) {
   constexpr uint32_t U = 16 / SB;                 // stages per superstage
   constexpr uint32_t WSLOT = 2 * BM * 16;         // one superstage, A then B
   constexpr int SCALE_LDS = WIDE ? 2 * WSLOT : SLOTS * SSLAB;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[SLOTS * SLAB + SCALE_LDS];
+  // the finish stages through the LDS the ring leaves free (tkg_finish.hpp)
+  using FP = FinishPlan<32, FM, FN, (160 * 1024 - SLOTS * SLAB - SCALE_LDS) / WAVES>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[SLOTS * SLAB + SCALE_LDS + WAVES * FP::BYTES];
   TKG_LDS uint8_t* smem = (TKG_LDS uint8_t*)smem_raw;
   TKG_LDS uint8_t* ssm = smem + SLOTS * SLAB;   // scale slabs
 
@@ -392,6 +395,11 @@ void gemm_mx_kernel(MxArgs p) {
     }
 
     // ---- finish (as in gemm_dense.hip, 32x32 blocks) ---------------------------
+    if constexpr (FP::USE) {
+      finish_staged<32, FM, FN, 1, FP::RJ, true>(
+          acc, p.scale, smem + SLOTS * SLAB + SCALE_LDS + wave * FP::BYTES, p.C, p.M, p.N,
+          cur.m0 + wm * WM, cur.n0 + wn * WN, (uint32_t)lane);
+    } else {
     const bool vec_ok = (p.N & 3) == 0;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -419,6 +427,7 @@ void gemm_mx_kernel(MxArgs p) {
         acc[i][j] = f32x16_t{};
         __builtin_amdgcn_sched_barrier(0);
       }
+    }
     }
     fresh_tile = true;
 
