@@ -373,7 +373,7 @@ void gemm_dense_kernel(DenseArgs p) {
     // the transposed MIxMI block: lane l owns C row m = l%MI and, in element
     // r, column 4*P*(r/4) + 4*(l/MI) + r%4.
     if constexpr (FP::USE) {
-      finish_staged<MI, FM, FN, 1, FP::RJ, DT != kBf16>(
+      finish_staged<MI, FM, FN, FP::RJ, DT != kBf16>(
           acc, p.scale, smem + SLOTS * SLAB + wave * FP::BYTES, p.C, p.M, p.N,
           cur.m0 + wm * WM, cur.n0 + wn * WN, (uint32_t)lane);
     } else {

@@ -365,7 +365,7 @@ void gemm_fp4_kernel(Fp4Args p) {
 
     // ---- finish (as in gemm_dense.hip) -----------------------------------
     if constexpr (FP::USE) {
-      finish_staged<32, FM, FN, 1, FP::RJ, true>(
+      finish_staged<32, FM, FN, FP::RJ, true>(
           acc, p.scale, smem + STAGES * STAGE_BYTES + wave * FP::BYTES, p.C, p.M, p.N,
           cur.m0 + wm * WM, cur.n0 + wn * WN, (uint32_t)lane);
     } else {

@@ -259,16 +259,29 @@ void gemm_mx_kernel(MxArgs p) {
       v = i32x8_t{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
     }
   };
-  // the raw words; lane_block() moves this lane's block into place later, so
-  // that the wait for the read falls after the k-step's MFMAs
-  auto read_scale = [&](uint32_t off, SW& w) {
-    if constexpr (S::FP4) w = lds_read<u32x2_t>(ssm, off);
-    else w = lds_read<uint32_t>(ssm, off);
+  // The raw scale bytes a lane reads: narrow, the stage's word(s); wide,
+  // the row's whole 16-byte superstage (reading 32 rows of 16 bytes whole
+  // is conflict-free on the LDS, reading one word of each is not), from
+  // which pick() takes the stage's. lane_block() then moves this lane's
+  // block into place, after the k-step's MFMAs, so that the wait for the
+  // read falls there.
+  using RW = typename std::conditional<WIDE, i32x4_t, SW>::type;
+  auto read_scale = [&](uint32_t off, RW& w) { w = lds_read<RW>(ssm, off); };
+  auto pick = [&](const RW& r, uint32_t j) -> SW {
+    if constexpr (!WIDE) {
+      (void)j;
+      return r;
+    } else if constexpr (S::FP4) {
+      return j ? u32x2_t{(uint32_t)r[2], (uint32_t)r[3]} : u32x2_t{(uint32_t)r[0], (uint32_t)r[1]};
+    } else {
+      return (uint32_t)(j == 0 ? r[0] : j == 1 ? r[1] : j == 2 ? r[2] : r[3]);
+    }
   };
-  // where the scale words of the stage after global stage g (this
-  // workgroup's running stage count) begin, given the slot of its values
+  // where the scale bytes of the stage after global stage g (this
+  // workgroup's running stage count) are read, given the slot of its
+  // values; wide, the stage inside the superstage is (g + 1) mod U
   auto scale_base = [&](uint32_t g, int vslot) -> uint32_t {
-    if constexpr (WIDE) return (((g + 1) / U) & 1u) * WSLOT + ((g + 1) % U) * SB;
+    if constexpr (WIDE) return (((g + 1) / U) & 1u) * WSLOT;
     else return (uint32_t)vslot * SSLAB;
   };
   auto lane_block = [&](const SW& w) -> SW {
@@ -297,21 +310,22 @@ void gemm_mx_kernel(MxArgs p) {
   {
     const uint32_t sa0 = WIDE ? 0u : (uint32_t)aslot * SSLAB;
     const uint32_t sb0 = WIDE ? 0u : (uint32_t)bslot * SSLAB;
+    RW ra[FM], rb[FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       read_frag(aslot, a_base + i * 32 * BKB, 0, fa[i]);
-      read_scale(sa0 + as_base + i * SFRAG, sa[i]);
+      read_scale(sa0 + as_base + i * SFRAG, ra[i]);
     }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       read_frag(bslot, b_base + j * 32 * BKB, 0, fb[0][j]);
-      read_scale(sb0 + bs_base + j * SFRAG, sbs[j]);
+      read_scale(sb0 + bs_base + j * SFRAG, rb[j]);
     }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) sa[i] = lane_block(pick(ra[i], 0));
+#pragma unroll
+    for (int j = 0; j < FN; ++j) sbs[j] = lane_block(pick(rb[j], 0));
   }
-#pragma unroll
-  for (int i = 0; i < FM; ++i) sa[i] = lane_block(sa[i]);
-#pragma unroll
-  for (int j = 0; j < FN; ++j) sbs[j] = lane_block(sbs[j]);
 
   // One k-step in program order (see gemm_dense.hip): after MFMA (i, j) the
   // instructions of its slot. The next k-step's fragments come from slots
@@ -320,7 +334,7 @@ void gemm_mx_kernel(MxArgs p) {
   bool fresh_tile = false;
   uint32_t g = 0;   // stages this workgroup has computed (all tiles)
   constexpr int NDMA = 2 * NLOAD;
-  SW sa_n[FM], sb_n[FN];
+  RW sa_n[FM], sb_n[FN];
   auto kstep_body = [&](int c, int s, auto sc, int ns, int na, int nb, bool boundary,
                         const SlabLoad* l0, const SlabLoad* l1) {
     const uint32_t nsa = boundary ? scale_base(g, na) : 0u;
@@ -360,10 +374,19 @@ void gemm_mx_kernel(MxArgs p) {
       lds_barrier();
       const int na = (aslot + 2) % SLOTS, nb = (bslot + 2) % SLOTS;
       kstep_body(c, SC, sc, 0, na, nb, true, &l0, &l1);
+      const uint32_t jn = (g + 1) % U;
+      if constexpr (WIDE) {
+        // whole rows were read: keep the compiler from narrowing each read
+        // to the one word pick() takes (that single-word form conflicts)
 #pragma unroll
-      for (int i = 0; i < FM; ++i) sa[i] = lane_block(sa_n[i]);
+        for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(sa_n[i]));
 #pragma unroll
-      for (int j = 0; j < FN; ++j) sbs[j] = lane_block(sb_n[j]);
+        for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(sb_n[j]));
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) sa[i] = lane_block(pick(sa_n[i], jn));
+#pragma unroll
+      for (int j = 0; j < FN; ++j) sbs[j] = lane_block(pick(sb_n[j], jn));
       aslot = na;
       bslot = nb;
     }
@@ -396,7 +419,7 @@ void gemm_mx_kernel(MxArgs p) {
 
     // ---- finish (as in gemm_dense.hip, 32x32 blocks) ---------------------------
     if constexpr (FP::USE) {
-      finish_staged<32, FM, FN, 1, FP::RJ, true>(
+      finish_staged<32, FM, FN, FP::RJ, true>(
           acc, p.scale, smem + SLOTS * SLAB + SCALE_LDS + wave * FP::BYTES, p.C, p.M, p.N,
           cur.m0 + wm * WM, cur.n0 + wn * WN, (uint32_t)lane);
     } else {

@@ -12,93 +12,127 @@
 // bounds the finish (measured: the same stores into a 128 KiB region that
 // stays in L2 take as long).
 //
-// Staged form: each wave owns an LDS area of RI*MI rows x RJ*MI columns of
-// bf16. A round writes RI x RJ accumulator blocks there (8 bytes per lane,
-// row-major; rows padded by 16 bytes so that the MI rows one write touches
-// start in different banks, and every address is a per-lane base plus a
-// constant), reads them back 16 bytes per lane in row order and stores them:
-// one store instruction then writes 1 KiB as whole row pieces of RJ*MI*2
-// bytes (64 to 256). A wave's LDS operations execute in order, so the next
-// round may overwrite the area without a wait.
+// Staged form: each wave owns an LDS area of MI rows x RJ*MI columns of bf16
+// (RB = RJ*MI*2 bytes a row, 64 to 256). A round packs RJ accumulator blocks
+// to bf16, pairs them up across lanes with one permlane swap per dword so
+// that every lane holds 8 consecutive columns of its row (16 bytes), writes
+// them, reads the strip back 16 bytes per lane in row order and stores it:
+// one store instruction then writes 1 KiB as whole row pieces of RB bytes.
+// LDS layout, chosen by measurement (SQ_LDS_BANK_CONFLICT on each write
+// and read pattern): the area is NR = MI*RB/256 lines of 256 bytes; row r
+// lives in line R = r mod NR at slot h = r / NR, and its 16-byte chunk c at
+// line chunk (h*RB/16 + c) XOR (R mod 16). The rows one write phase (16
+// lanes) touches then sit in different lines at different chunks, and a
+// read phase covers one whole line; both are served without conflicts
+// (packing 128-byte rows one per line-half instead, with any XOR of row
+// bits, measures 2-way on the writes). A wave's LDS operations execute in
+// order, so the next round may overwrite the area without a wait.
 #pragma once
 #include "tkg_device.hpp"
 
 namespace tkg {
 
-template <int MI, int FM, int FN, int RI, int RJ>
+template <int MI, int RJ>
 struct FinishShape {
   static constexpr int P = 64 / MI;
   static constexpr int NE = MI * MI / 64;      // accumulator elements per lane
-  static constexpr int ROWS = RI * MI;
   static constexpr int RB = RJ * MI * 2;       // staged row bytes
-  static constexpr int RS = RB + 16;           // LDS row stride (padded)
   static constexpr int CPR = RB / 16;          // 16-byte chunks per row
-  static constexpr int RPI = 64 / CPR;         // rows per 1 KiB read
-  static constexpr int BYTES = ROWS * RS;      // LDS bytes per wave
-  static_assert(FM % RI == 0 && FN % RJ == 0, "rounds tile the wave tile");
-  static_assert(CPR >= 4 && CPR <= 64 && (ROWS * RB) % 1024 == 0, "staged strip shape");
+  static constexpr int NR = MI * RB / 256;     // 256-byte LDS lines
+  static constexpr int BYTES = MI * RB;        // LDS bytes per wave
+  static_assert(RB == 64 || RB == 128 || RB == 256, "staged row of 64, 128 or 256 bytes");
+  static_assert(MI == 32 || RJ % 2 == 0, "16x16 blocks pair up across lane groups");
+  static_assert(NR % 4 == 0, "whole 1 KiB reads");
 };
 
-// The widest strip (RI = 1, RJ blocks of the wave tile's FN, at most 256
-// bytes a row) that fits a per-wave LDS budget of BUDGET bytes, with rows of
-// at least 64 bytes; USE is false when none fits (the finish then stores
-// from registers).
+// The widest strip (RJ blocks of the wave tile's FN, rows of 64 to 256
+// bytes) that fits a per-wave LDS budget of BUDGET bytes; USE is false when
+// none fits (the finish then stores from registers).
 template <int MI, int FM, int FN, int BUDGET>
 struct FinishPlan {
   static constexpr bool fits(int rj) {
-    return FN % rj == 0 && rj * MI * 2 >= 64 && rj * MI * 2 <= 256 &&
-           MI * (rj * MI * 2 + 16) <= BUDGET && (MI * rj * MI * 2) % 1024 == 0;
+    return FN % rj == 0 && (MI == 32 || rj % 2 == 0) && rj * MI * 2 >= 64 &&
+           rj * MI * 2 <= 256 && MI * rj * MI * 2 <= BUDGET;
   }
   static constexpr int fit(int rj) { return rj < 1 ? 0 : (fits(rj) ? rj : fit(rj / 2)); }
   static constexpr int RJ = fit(FN);
   static constexpr bool USE = RJ > 0;
-  static constexpr int BYTES = USE ? MI * (RJ * MI * 2 + 16) : 0;
+  static constexpr int BYTES = USE ? MI * RJ * MI * 2 : 0;
 };
 
 // Writes the wave tile whose top-left element is C[m0][n0] (ld = N) and
 // zeroes the accumulators. SCALE multiplies by `scale` before rounding.
-template <int MI, int FM, int FN, int RI, int RJ, bool SCALE, typename Acc>
+template <int MI, int FM, int FN, int RJ, bool SCALE, typename Acc>
 __device__ __forceinline__ void finish_staged(Acc (&acc)[FM][FN], float scale,
                                               TKG_LDS uint8_t* stg, uint16_t* C,
                                               int M, int N, int m0, int n0,
                                               uint32_t lane) {
-  using F = FinishShape<MI, FM, FN, RI, RJ>;
+  using F = FinishShape<MI, RJ>;
   const uint32_t lrow = lane % MI, lgrp = lane / MI;
   const bool vec8 = (N & 7) == 0;
-  // per-lane bases: writes at row lrow, column 4*lgrp; reads at row
-  // lane / CPR, chunk lane % CPR
-  const uint32_t wbase = lrow * F::RS + 8 * lgrp;
-  const uint32_t rrow = lane / F::CPR, rchunk = lane % F::CPR;
-  const uint32_t rbase = rrow * F::RS + 16 * rchunk;
+  // After the swap a lane holds chunk (constant ^ lchunk) of row lrow:
+  // MI = 32: chunk 4*jj + 2*p + lgrp for pair p of element groups;
+  // MI = 16: chunk 2*jj + 2*(lgrp & 1) + (lgrp >> 1) for blocks jj, jj + 1.
+  // The constant has no bits in common with lchunk, nor with the slot
+  // h*CPR, so the write address is wlane ^ (constant << 4).
+  const uint32_t lchunk = MI == 32 ? lgrp : 2 * (lgrp & 1) + (lgrp >> 1);
+  const uint32_t wl = lrow % F::NR, wh = lrow / F::NR;
+  uint32_t wlane = wl * 256 + (((wh * F::CPR) ^ lchunk ^ (wl % 16)) << 4);
+  // Read q covers lines 4q .. 4q+3, lane l line 4q + l/16 at line chunk
+  // l % 16 (row slot (l % 16) / CPR, chunk (l % 16) % CPR); the line's XOR
+  // (4q + l/16) mod 16 = (4q mod 16) ^ (l/16).
+  const uint32_t rline = lane / 16, rpc = lane % 16;
+  uint32_t rlane = rline * 256 + ((rpc ^ rline) << 4);
+  const uint32_t rrow = (rpc / F::CPR) * F::NR + rline;  // + 4q
+  const uint32_t rcol = 8 * (rpc % F::CPR);
+  // opaque per tile: keeps the per-round XORs below from being hoisted
+  // into registers held across the whole kernel
+  asm volatile("" : "+v"(wlane), "+v"(rlane));
+  auto pk = [&](const Acc& a, int g) -> u32x2_t {
+    float v[4];
 #pragma unroll
-  for (int bi = 0; bi < FM; bi += RI) {
+    for (int u = 0; u < 4; ++u) v[u] = SCALE ? a[4 * g + u] * scale : a[4 * g + u];
+    const uint2 r = pack_bf16x4(v[0], v[1], v[2], v[3]);
+    return u32x2_t{r.x, r.y};
+  };
+  auto put = [&](uint32_t cchunk, u32x2_t x, u32x2_t y) {
+    // X in the low lane group of each swap pair, Y in the high one; after
+    // the swap [X, Y] are 8 consecutive columns
+    const auto s0 = MI == 32 ? __builtin_amdgcn_permlane32_swap(x[0], y[0], false, false)
+                             : __builtin_amdgcn_permlane16_swap(x[0], y[0], false, false);
+    const auto s1 = MI == 32 ? __builtin_amdgcn_permlane32_swap(x[1], y[1], false, false)
+                             : __builtin_amdgcn_permlane16_swap(x[1], y[1], false, false);
+    *reinterpret_cast<TKG_LDS i32x4_t*>(stg + (wlane ^ (cchunk << 4))) =
+        i32x4_t{(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+  };
+#pragma unroll
+  for (int bi = 0; bi < FM; ++bi) {
 #pragma unroll
     for (int bj = 0; bj < FN; bj += RJ) {
-#pragma unroll
-      for (int ii = 0; ii < RI; ++ii)
+      if constexpr (MI == 32) {
 #pragma unroll
         for (int jj = 0; jj < RJ; ++jj) {
 #pragma unroll
-          for (int g = 0; g < F::NE / 4; ++g) {
-            float v[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-              v[u] = SCALE ? acc[bi + ii][bj + jj][4 * g + u] * scale
-                           : acc[bi + ii][bj + jj][4 * g + u];
-            // row ii*MI + lrow, column jj*MI + 4*P*g + 4*lgrp
-            const uint2 pk = pack_bf16x4(v[0], v[1], v[2], v[3]);
-            *reinterpret_cast<TKG_LDS u32x2_t*>(
-                stg + wbase + ii * MI * F::RS + (jj * MI + 4 * F::P * g) * 2) = u32x2_t{pk.x, pk.y};
-          }
-          acc[bi + ii][bj + jj] = Acc{};
+          for (int pp = 0; pp < 2; ++pp)
+            put(4 * jj + 2 * pp, pk(acc[bi][bj + jj], 2 * pp), pk(acc[bi][bj + jj], 2 * pp + 1));
+          acc[bi][bj + jj] = Acc{};
           // one block's values in flight at a time (register pressure)
           __builtin_amdgcn_sched_barrier(0);
         }
+      } else {
 #pragma unroll
-      for (int q = 0; q < F::ROWS / F::RPI; ++q) {
-        const i32x4_t v = lds_read<i32x4_t>(stg, rbase + q * F::RPI * F::RS);
-        const int m = m0 + bi * MI + q * F::RPI + (int)rrow;
-        const int n = n0 + bj * MI + 8 * (int)rchunk;
+        for (int jj = 0; jj < RJ; jj += 2) {
+          put(2 * jj, pk(acc[bi][bj + jj], 0), pk(acc[bi][bj + jj + 1], 0));
+          acc[bi][bj + jj] = Acc{};
+          acc[bi][bj + jj + 1] = Acc{};
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < F::NR / 4; ++q) {
+        const i32x4_t v = lds_read<i32x4_t>(stg, q * 1024 + (rlane ^ (((4u * q) % 16) << 4)));
+        const int m = m0 + bi * MI + (int)rrow + 4 * q;
+        const int n = n0 + bj * MI + (int)rcol;
         if (m < M) {
           uint16_t* cp = C + (size_t)m * (size_t)N + n;
           if (vec8 && n + 7 < N) {
