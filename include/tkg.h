@@ -153,10 +153,10 @@ const char *tkg_status_string(int status);
  *               1 = (128, 5, 8, 4, 16), 2 = (128, 4, 8, 4, 32),
  *               3 = (128, 5, 8, 4, 32), 4 = (128, 4, 8, 8, 32),
  *               5 = (128, 4, 4, 4, 32), 6 = (64, 10, 8, 8, 32),
- *               7 = (128, 4, 4, 4, 16). fp8: 0 = (128, 4, 4, 4, 32)
+ *               7 = (128, 4, 4, 4, 16). fp8: 0 = (128, 4, 4, 4, 16)
  *               default, 1 = (128, 5, 4, 4, 32), 2 = (128, 4, 8, 4, 32),
  *               3 = (128, 5, 8, 4, 32), 4 = (128, 4, 8, 8, 32),
- *               5 = (128, 4, 4, 4, 16), 6 = (64, 10, 8, 8, 32),
+ *               5 = (128, 4, 4, 4, 32), 6 = (64, 10, 8, 8, 32),
  *               7 = (64, 10, 4, 4, 32). TKG_ERR_SHAPE outside 0..7.
  *               4-bit product: 0 = 4 waves (default), 1 = 8 waves;
  *               TKG_ERR_SHAPE outside 0..1. Every variant of a product
@@ -215,6 +215,24 @@ int tkg_lds_fragment_offsets(int dtype, int step, int part, int frag,
  * block: 16 for the 16x16 blocks, 32 for 32x32), or a negative tkg_status.
  */
 int tkg_lds_fragment_rows(int dtype);
+
+/*
+ * LDS layout introspection of the finish (C = bf16(scale * acc) through a
+ * per-wave LDS strip; page "ThunderKittens: Simple, Fast, and Adorable AI
+ * Kernels", section 3.4, "The LCSF Template"). Writes the 64 per-lane byte
+ * offsets, relative to the wave's strip, of one 16-byte LDS access:
+ *   mi     -- MFMA block rows, 16 or 32;
+ *   rj     -- accumulator blocks per strip row (strip rows of rj*mi*2 =
+ *             64, 128 or 256 bytes; even for mi = 16);
+ *   kind   -- 0 = the writes of one round (after the lane-pair swap each
+ *             lane writes 8 consecutive columns of its row), 1 = the reads;
+ *   index  -- which write or read of the round.
+ * Returns the number of accesses of that kind per round, or a negative
+ * tkg_status (TKG_ERR_SHAPE for an unsupported shape or index,
+ * TKG_ERR_NULL for a null out64). No GPU work.
+ */
+int tkg_lds_finish_offsets(int mi, int rj, int kind, int index,
+                           uint32_t *out64);
 
 /*
  * Row length in bytes of the staged operand tiles for dtype (the unit the

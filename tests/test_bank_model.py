@@ -17,11 +17,11 @@ from tiled_dense_gemm_amd import lds_bank_model as bm
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 PAGE = json.load(open(os.path.join(GOLD, "bank_model_page1.json")))
 PROBE = json.load(open(os.path.join(GOLD, "lds_probe_gfx950.json")))
-MEASURED = {(p["bytes"], tuple(p["addresses"])): p for p in PROBE["patterns"]}
+MEASURED = {(p["op"], p["bytes"], tuple(p["addresses"])): p for p in PROBE["patterns"]}
 
 
-def measured(addrs, nbytes=16):
-    return MEASURED.get((nbytes, tuple(addrs)))
+def measured(addrs, nbytes=16, op="r"):
+    return MEASURED.get((op, nbytes, tuple(addrs)))
 
 
 def by_name(name):
@@ -66,7 +66,7 @@ def test_kernel_fragment_reads_measured_conflict_free(dtype):
 
 def test_unswizzled_reads_measured_conflicting():
     un = [p for p in PROBE["patterns"] if " unswizzled " in p["name"]]
-    assert len(un) == 80
+    assert len(un) == 112
     assert all(p["degree"] >= 4 for p in un)
 
 
@@ -116,3 +116,85 @@ def test_swizzle_permutes_chunks_of_each_row():
 def test_fp4_scale_reads_measured_conflict_free():
     m = measured(bm.scale_read_pattern(8), 8)
     assert m is not None and m["degree"] == 1
+
+
+def test_mx_superstage_scale_reads_measured_conflict_free():
+    # the MX kernels read each row's whole 16-byte superstage of scales
+    # (rows 16 bytes apart, lane l row l % 32); reading one word or one
+    # 8-byte pair of each row instead measures 4- and 2-way
+    rows = [16 * (l % 32) for l in range(64)]
+    assert measured(rows, 16)["degree"] == 1
+    assert measured(rows, 4)["degree"] >= 4
+    assert measured(rows, 8)["degree"] >= 2
+
+
+FINISH_SHAPES = [(32, 4), (32, 2), (32, 1), (16, 8), (16, 4), (16, 2)]
+
+
+@pytest.mark.parametrize("mi,rj", FINISH_SHAPES)
+def test_finish_strip_measured_conflict_free(mi, rj):
+    # every write and read of the finish's LDS strip, as the library
+    # reports them, appears in the measured table without conflicts
+    for kind, op in ((0, "w"), (1, "r")):
+        n = tkg.lds_finish_count(mi, rj, kind)
+        assert n > 0
+        for i in range(n):
+            m = measured(tkg.lds_finish_offsets(mi, rj, kind, i), 16, op)
+            assert m is not None, (mi, rj, kind, i)
+            assert m["degree"] == 1, m["name"]
+
+
+def test_finish_rejected_layouts_measured_conflicting():
+    for name in ("finish rejected padded rows b64 write", "finish rejected 128-byte rows xor write"):
+        assert by_name(name)["degree"] >= 2
+
+
+def _permlane_swap(x, y, width):
+    # measured on gfx950 (v_permlane32_swap / v_permlane16_swap): the upper
+    # `width` lanes of each 2*width group of x trade places with the lower
+    # `width` lanes of the same group of y
+    nx, ny = list(x), list(y)
+    for g in range(0, 64, 2 * width):
+        for i in range(width):
+            nx[g + width + i], ny[g + i] = y[g + i], x[g + width + i]
+    return nx, ny
+
+
+@pytest.mark.parametrize("mi,rj", FINISH_SHAPES)
+def test_finish_strip_moves_every_element_once(mi, rj):
+    # Host model of the finish: accumulator block jj gives lane l row l % mi
+    # and, in element group g, columns jj*mi + 4*(64/mi)*g + 4*(l // mi) ..
+    # +3; lanes swap (32-wide for mi 32, 16-wide for mi 16) and write 16
+    # bytes at the library's offsets; the reads at the library's offsets
+    # must give lane l of read q the 8 columns rcol .. rcol+7 of row rrow.
+    P, rb = 64 // mi, rj * mi * 2
+    cpr, nr = rb // 16, mi * rb // 256
+    lds = {}
+    cols = lambda jj, g: [[(l % mi, jj * mi + 4 * P * g + 4 * (l // mi) + u) for u in range(4)]
+                          for l in range(64)]
+    if mi == 32:
+        puts = [(cols(jj, 2 * p), cols(jj, 2 * p + 1)) for jj in range(rj) for p in range(2)]
+    else:
+        puts = [(cols(jj, 0), cols(jj + 1, 0)) for jj in range(0, rj, 2)]
+    assert len(puts) == tkg.lds_finish_count(mi, rj, 0)
+    for w, (X, Y) in enumerate(puts):
+        lo = _permlane_swap([v[:2] for v in X], [v[:2] for v in Y], 32 if mi == 32 else 16)
+        hi = _permlane_swap([v[2:] for v in X], [v[2:] for v in Y], 32 if mi == 32 else 16)
+        offs = tkg.lds_finish_offsets(mi, rj, 0, w)
+        for l in range(64):
+            data = lo[0][l] + hi[0][l] + lo[1][l] + hi[1][l]
+            assert 0 <= offs[l] and offs[l] + 16 <= mi * rb
+            for k in range(8):
+                assert offs[l] + 2 * k not in lds
+                lds[offs[l] + 2 * k] = data[k]
+    assert len(lds) == mi * rj * mi
+    got = set()
+    for q in range(tkg.lds_finish_count(mi, rj, 1)):
+        offs = tkg.lds_finish_offsets(mi, rj, 1, q)
+        for l in range(64):
+            row = ((l % 16) // cpr) * nr + l // 16 + 4 * q
+            col = 8 * ((l % 16) % cpr)
+            for k in range(8):
+                assert lds[offs[l] + 2 * k] == (row, col + k)
+                got.add((row, col + k))
+    assert len(got) == mi * rj * mi

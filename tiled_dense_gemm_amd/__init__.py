@@ -81,6 +81,9 @@ def _load() -> ctypes.CDLL:
     L.tkg_lds_row_bytes.restype = i32
     L.tkg_lds_fragment_rows.argtypes = [i32]
     L.tkg_lds_fragment_rows.restype = i32
+    L.tkg_lds_finish_offsets.argtypes = [i32, i32, i32, i32,
+                                         ctypes.POINTER(ctypes.c_uint32)]
+    L.tkg_lds_finish_offsets.restype = i32
     return L
 
 
@@ -113,6 +116,25 @@ def lds_fragment_offsets(dtype: int, step: int, part: int, frag: int):
     if r < 0:
         raise TkgError(r, "tkg_lds_fragment_offsets")
     return list(buf)
+
+
+def lds_finish_offsets(mi: int, rj: int, kind: int, index: int):
+    """The 64 per-lane LDS byte offsets of one access of the finish's
+    staging strip (see tkg.h); kind 0 = write, 1 = read."""
+    buf = (ctypes.c_uint32 * 64)()
+    r = lib.tkg_lds_finish_offsets(int(mi), int(rj), int(kind), int(index), buf)
+    if r < 0:
+        raise TkgError(r, "tkg_lds_finish_offsets")
+    return list(buf)
+
+
+def lds_finish_count(mi: int, rj: int, kind: int) -> int:
+    """Writes (kind 0) or reads (kind 1) per round of the finish strip."""
+    buf = (ctypes.c_uint32 * 64)()
+    r = lib.tkg_lds_finish_offsets(int(mi), int(rj), int(kind), 0, buf)
+    if r < 0:
+        raise TkgError(r, "tkg_lds_finish_offsets")
+    return r
 
 
 # ------------------------------------------------------------ torch layer

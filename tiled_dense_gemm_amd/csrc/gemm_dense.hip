@@ -59,12 +59,13 @@ struct Ring {
 // One table per operand type (variant v selects entry v); entry 0 is the
 // default, the fastest measured at 8192^3 on random operands: for bf16 two
 // waves per SIMD with 16x16x32 MFMAs, for fp8 one wave per SIMD with
-// 32x32x64 MFMAs.
+// 16x16x128 MFMAs (the 16x16 shapes run at a higher clock on the
+// power-limited chip).
 constexpr Ring kRingsBf16[] = {{128, 4, 4, 1, 16}, {128, 5, 4, 1, 16}, {128, 4, 4, 1, 32},
                                {128, 5, 4, 1, 32}, {128, 4, 4, 0, 32}, {128, 4, 2, 0, 32},
                                {64, 10, 4, 0, 32}, {128, 4, 2, 0, 16}};
-constexpr Ring kRingsFp8[] = {{128, 4, 2, 0, 32}, {128, 5, 2, 0, 32}, {128, 4, 4, 1, 32},
-                              {128, 5, 4, 1, 32}, {128, 4, 4, 0, 32}, {128, 4, 2, 0, 16},
+constexpr Ring kRingsFp8[] = {{128, 4, 2, 0, 16}, {128, 5, 2, 0, 32}, {128, 4, 4, 1, 32},
+                              {128, 5, 4, 1, 32}, {128, 4, 4, 0, 32}, {128, 4, 2, 0, 32},
                               {64, 10, 4, 0, 32}, {64, 10, 2, 0, 32}};
 constexpr int kNumRings = sizeof(kRingsBf16) / sizeof(kRingsBf16[0]);
 static_assert(sizeof(kRingsFp8) == sizeof(kRingsBf16), "same variant count");
@@ -328,6 +329,12 @@ void gemm_dense_kernel(DenseArgs p) {
   // loads spread over the MFMAs.
   bool fresh_tile = false;  // finish stores are in flight
   constexpr int NDMA = 2 * DMA;             // slab loads per stage boundary
+  // MFMA slots the loads are spread over: the whole boundary k-step, or its
+  // first three quarters when a stage is a single k-step (the loads are
+  // waited for at the next boundary, one k-step later, and need time to
+  // land; measured: all of it 2640, half 2980, three quarters 3010 TFLOP/s
+  // for fp8 16x16 at 8192^3)
+  constexpr int NSPAN = KSTEPS == 1 ? (3 * NMMA + 3) / 4 : NMMA;
   auto kstep = [&](int c, int s, bool last, const SlabLoad& l0, const SlabLoad& l1) {
     if (!last) {
       kstep_body(c, s + 1, aslot, bslot, [&](int) {});
@@ -340,7 +347,7 @@ void gemm_dense_kernel(DenseArgs p) {
       kstep_body(c, 0, na, nb, [&](int q) {
         if constexpr (IS_LOADER) {
 #pragma unroll
-          for (int d = q * NDMA / NMMA; d < (q + 1) * NDMA / NMMA; ++d) {
+          for (int d = q * NDMA / NSPAN; d < (q + 1) * NDMA / NSPAN && d < NDMA; ++d) {
             if (d < DMA) issue_one(l0, d);
             else issue_one(l1, d - DMA);
           }

@@ -7,6 +7,7 @@
 
 #include "tkg.h"
 #include "tkg_kernels.hpp"
+#include "tkg_finish.hpp"
 #include "tkg_layout.hpp"
 
 namespace {
@@ -315,6 +316,30 @@ int tkg_lds_fragment_offsets(int dtype, int step, int part, int frag,
     out64[lane] = tkg::swz_offset((uint32_t)rb, row, chunk);
   }
   return steps;
+}
+
+int tkg_lds_finish_offsets(int mi, int rj, int kind, int index, uint32_t* out64) {
+  if (out64 == nullptr) return TKG_ERR_NULL;
+  const int rb = rj * mi * 2;
+  if ((mi != 16 && mi != 32) || (rb != 64 && rb != 128 && rb != 256) ||
+      (mi == 16 && rj % 2 != 0))
+    return TKG_ERR_SHAPE;
+  // writes: MI = 32, chunk constant 4*jj + 2*p (2 per block); MI = 16,
+  // 2*jj for each pair of blocks; reads: one per 4 lines of 256 bytes
+  const int writes = mi == 32 ? 2 * rj : rj / 2;
+  const int reads = mi * rb / 1024;
+  const int count = kind == 0 ? writes : reads;
+  if ((kind != 0 && kind != 1) || index < 0 || index >= count) return TKG_ERR_SHAPE;
+  for (uint32_t lane = 0; lane < 64; ++lane) {
+    if (kind == 0) {
+      const uint32_t cc = mi == 32 ? 4u * (uint32_t)(index / 2) + 2u * (uint32_t)(index % 2)
+                                   : 4u * (uint32_t)index;
+      out64[lane] = tkg::finish_write_offset((uint32_t)mi, (uint32_t)rb, lane, cc);
+    } else {
+      out64[lane] = tkg::finish_read_offset(lane, (uint32_t)index);
+    }
+  }
+  return count;
 }
 
 }  // extern "C"

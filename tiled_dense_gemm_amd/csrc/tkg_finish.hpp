@@ -29,8 +29,43 @@
 // order, so the next round may overwrite the area without a wait.
 #pragma once
 #include "tkg_device.hpp"
+#include "tkg_layout.hpp"
 
 namespace tkg {
+
+// ---- staging addresses (host and device: the library reports them) --------
+// Byte offset (in the wave's area) where lane `lane` writes its 16 bytes
+// for the write whose chunk constant is `cchunk` (MI = 32: 4*jj + 2*p for
+// element-group pair p of block jj; MI = 16: 2*jj for blocks jj, jj+1), in
+// a strip of `rb`-byte rows. After the swap the lane holds chunk
+// cchunk ^ lchunk of row lane % MI; lchunk shares no bits with cchunk nor
+// with the slot h * (rb/16), so the whole address is one XOR away from a
+// per-lane base.
+TKG_HD constexpr uint32_t finish_write_base(uint32_t mi, uint32_t rb, uint32_t lane) {
+  const uint32_t lrow = lane % mi, lgrp = lane / mi;
+  const uint32_t lchunk = mi == 32 ? lgrp : 2 * (lgrp & 1) + (lgrp >> 1);
+  const uint32_t nr = mi * rb / 256, line = lrow % nr, slot = lrow / nr;
+  return line * 256 + (((slot * (rb / 16)) ^ lchunk ^ (line % 16)) << 4);
+}
+TKG_HD constexpr uint32_t finish_write_offset(uint32_t mi, uint32_t rb, uint32_t lane,
+                                              uint32_t cchunk) {
+  return finish_write_base(mi, rb, lane) ^ (cchunk << 4);
+}
+// Read q covers lines 4q .. 4q+3: lane l reads line 4q + l/16 at line chunk
+// l % 16, whose XOR (4q + l/16) mod 16 = (4q mod 16) ^ (l/16).
+TKG_HD constexpr uint32_t finish_read_base(uint32_t lane) {
+  return (lane / 16) * 256 + (((lane % 16) ^ (lane / 16)) << 4);
+}
+TKG_HD constexpr uint32_t finish_read_offset(uint32_t lane, uint32_t q) {
+  return q * 1024 + (finish_read_base(lane) ^ (((4 * q) % 16) << 4));
+}
+// Row and first column of the strip that read q gives lane `lane`.
+TKG_HD constexpr uint32_t finish_read_row(uint32_t mi, uint32_t rb, uint32_t lane, uint32_t q) {
+  return ((lane % 16) / (rb / 16)) * (mi * rb / 256) + lane / 16 + 4 * q;
+}
+TKG_HD constexpr uint32_t finish_read_col(uint32_t rb, uint32_t lane) {
+  return 8 * ((lane % 16) % (rb / 16));
+}
 
 template <int MI, int RJ>
 struct FinishShape {
@@ -68,23 +103,11 @@ __device__ __forceinline__ void finish_staged(Acc (&acc)[FM][FN], float scale,
                                               int M, int N, int m0, int n0,
                                               uint32_t lane) {
   using F = FinishShape<MI, RJ>;
-  const uint32_t lrow = lane % MI, lgrp = lane / MI;
   const bool vec8 = (N & 7) == 0;
-  // After the swap a lane holds chunk (constant ^ lchunk) of row lrow:
-  // MI = 32: chunk 4*jj + 2*p + lgrp for pair p of element groups;
-  // MI = 16: chunk 2*jj + 2*(lgrp & 1) + (lgrp >> 1) for blocks jj, jj + 1.
-  // The constant has no bits in common with lchunk, nor with the slot
-  // h*CPR, so the write address is wlane ^ (constant << 4).
-  const uint32_t lchunk = MI == 32 ? lgrp : 2 * (lgrp & 1) + (lgrp >> 1);
-  const uint32_t wl = lrow % F::NR, wh = lrow / F::NR;
-  uint32_t wlane = wl * 256 + (((wh * F::CPR) ^ lchunk ^ (wl % 16)) << 4);
-  // Read q covers lines 4q .. 4q+3, lane l line 4q + l/16 at line chunk
-  // l % 16 (row slot (l % 16) / CPR, chunk (l % 16) % CPR); the line's XOR
-  // (4q + l/16) mod 16 = (4q mod 16) ^ (l/16).
-  const uint32_t rline = lane / 16, rpc = lane % 16;
-  uint32_t rlane = rline * 256 + ((rpc ^ rline) << 4);
-  const uint32_t rrow = (rpc / F::CPR) * F::NR + rline;  // + 4q
-  const uint32_t rcol = 8 * (rpc % F::CPR);
+  uint32_t wlane = finish_write_base(MI, F::RB, lane);
+  uint32_t rlane = finish_read_base(lane);
+  const uint32_t rrow = finish_read_row(MI, F::RB, lane, 0);  // + 4q
+  const uint32_t rcol = finish_read_col(F::RB, lane);
   // opaque per tile: keeps the per-round XORs below from being hoisted
   // into registers held across the whole kernel
   asm volatile("" : "+v"(wlane), "+v"(rlane));

@@ -8,11 +8,18 @@
 //   * every fragment read of the default GEMM kernels (16x16 bf16 blocks,
 //     32x32 fp8 blocks and the 4-bit kernel's 64-byte rows), with the
 //     swizzle of tkg_layout.hpp and without it;
-//   * the 4-bit kernel's 8-byte block-scale reads;
+//   * the 4-bit kernel's 8-byte block-scale reads, and the MX kernels'
+//     16-byte superstage scale rows (whole-row reads, and the single-word
+//     reads they replace);
+//   * the finish's staging strip (tkg_finish.hpp): the writes and reads of
+//     every strip shape, restated here, and two layouts it rejects (rows
+//     padded by 16 bytes with 8-byte writes; 128-byte rows with the chunk
+//     XOR-ed by row bits);
 //   * a search over all 4096 linear row swizzles of 128-byte rows,
 //     chunk ^ A*bits(row mod 16), read with the 16x16 fragment pattern.
-// It prints one line per dispatch, in order: "pattern <id> <bytes> <name>
-// : <64 addresses>", which lds_probe_summary.py joins with the counters.
+// Writes (ds_write) run in a kernel of their own. It prints one line per
+// dispatch, in order: "pattern <id> <bytes> <op> <name> : <64 addresses>"
+// (op r or w), which lds_probe_summary.py joins with the counters.
 //
 // Build: hipcc --offload-arch=gfx950 -O2 -std=c++17 lds_bank_probe.hip -o lds_bank_probe
 #include <hip/hip_runtime.h>
@@ -27,18 +34,22 @@ typedef int i2 __attribute__((ext_vector_type(2)));
 
 constexpr unsigned kSpan = 32768;  // addresses are < kSpan; reads alternate +kSpan
 
-template <int BYTES>
+template <int BYTES, bool WRITE>
 __global__ __launch_bounds__(256) void lds_probe(const unsigned* addrs, int* out, int iters) {
   __shared__ __attribute__((aligned(16))) int smem[2 * kSpan / 4];
   for (unsigned i = threadIdx.x; i < 2 * kSpan / 4; i += 256) smem[i] = (int)(i * 7 + 1);
   __syncthreads();
   const unsigned lane = threadIdx.x & 63;
   const unsigned a = addrs[lane];
-  const LDS_AS char* base = (const LDS_AS char*)smem;
+  LDS_AS char* base = (LDS_AS char*)smem;
   int acc = 0;
   for (int it = 0; it < iters; ++it) {
     const unsigned off = a + ((it & 1) ? kSpan : 0);
-    if constexpr (BYTES == 16) {
+    if constexpr (WRITE && BYTES == 16) {
+      *(LDS_AS i4*)(base + off) = i4{it, (int)lane, acc, 1};
+    } else if constexpr (WRITE) {
+      *(LDS_AS i2*)(base + off) = i2{it, (int)lane};
+    } else if constexpr (BYTES == 16) {
       const i4 v = *(const LDS_AS i4*)(base + off);
       acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
     } else if constexpr (BYTES == 8) {
@@ -49,6 +60,10 @@ __global__ __launch_bounds__(256) void lds_probe(const unsigned* addrs, int* out
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  if constexpr (WRITE) {
+    __syncthreads();
+    acc = smem[threadIdx.x];
+  }
   out[blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
@@ -56,6 +71,7 @@ struct Pattern {
   std::string name;
   unsigned bytes;
   std::vector<unsigned> addr;
+  bool write = false;
 };
 
 // The swizzle of tkg_layout.hpp, restated: XOR mask of the 16-byte chunk
@@ -85,6 +101,21 @@ static Pattern fragment(const char* kind, unsigned row_bytes, unsigned mi, unsig
   return p;
 }
 
+// The finish strip of tkg_finish.hpp, restated: MI-row strip of rb-byte
+// rows kept in 256-byte lines (row r in line r mod NR at slot r / NR, the
+// 16-byte chunk XOR-ed with line mod 16); lane l writes 16 bytes of row
+// l % MI at chunk cchunk ^ lchunk, and read q gives lane l line 4q + l/16
+// at line chunk l % 16.
+static unsigned fin_write(unsigned mi, unsigned rb, unsigned l, unsigned cc) {
+  const unsigned lrow = l % mi, lgrp = l / mi;
+  const unsigned lch = mi == 32 ? lgrp : 2 * (lgrp & 1) + (lgrp >> 1);
+  const unsigned nr = mi * rb / 256, line = lrow % nr, slot = lrow / nr;
+  return line * 256 + ((((slot * (rb / 16)) ^ lch ^ (line % 16)) ^ cc) << 4);
+}
+static unsigned fin_read(unsigned l, unsigned q) {
+  return q * 1024 + ((((l / 16) * 256) + (((l % 16) ^ (l / 16)) << 4)) ^ (((4 * q) % 16) << 4));
+}
+
 int main() {
   std::vector<Pattern> pats;
   auto add = [&](std::string name, unsigned bytes, auto f) {
@@ -101,6 +132,41 @@ int main() {
           [&](unsigned l) { return bytes * (l & ~d) + ((l & d) ? 4096u : 0u); });
   }
   add("b64 4-bit block scales (row l%32, 8-byte rows)", 8, [](unsigned l) { return 8 * (l % 32); });
+  add("b128 MX superstage scale rows (row l%32, 16-byte rows)", 16, [](unsigned l) { return 16 * (l % 32); });
+  add("b32 MX scale word of 16-byte rows (row l%32)", 4, [](unsigned l) { return 16 * (l % 32); });
+  add("b64 MX scale pair of 16-byte rows (row l%32)", 8, [](unsigned l) { return 16 * (l % 32); });
+  // the finish strip: every shape the kernels use (mi, rj)
+  const unsigned fshapes[][2] = {{32, 4}, {32, 2}, {32, 1}, {16, 8}, {16, 4}, {16, 2}};
+  for (const auto& fs : fshapes) {
+    const unsigned mi = fs[0], rj = fs[1], rb = rj * mi * 2;
+    const unsigned nw = mi == 32 ? 2 * rj : rj / 2, nrd = mi * rb / 1024;
+    for (unsigned w = 0; w < nw; ++w) {
+      const unsigned cc = mi == 32 ? 4 * (w / 2) + 2 * (w % 2) : 4 * w;
+      Pattern p{"finish mi" + std::to_string(mi) + " rj" + std::to_string(rj) + " write " +
+                    std::to_string(w),
+                16, std::vector<unsigned>(64), true};
+      for (unsigned l = 0; l < 64; ++l) p.addr[l] = fin_write(mi, rb, l, cc);
+      pats.push_back(p);
+    }
+    for (unsigned q = 0; q < nrd; ++q) {
+      Pattern p{"finish mi" + std::to_string(mi) + " rj" + std::to_string(rj) + " read " +
+                    std::to_string(q),
+                16, std::vector<unsigned>(64)};
+      for (unsigned l = 0; l < 64; ++l) p.addr[l] = fin_read(l, q);
+      pats.push_back(p);
+    }
+  }
+  // rejected finish layouts: 144-byte rows written 8 bytes per lane (the
+  // accumulator layout without the swap), and 128-byte rows whose chunk is
+  // XOR-ed by (row / 2) mod 8, written 16 bytes per lane
+  {
+    Pattern p{"finish rejected padded rows b64 write", 8, std::vector<unsigned>(64), true};
+    for (unsigned l = 0; l < 64; ++l) p.addr[l] = (l % 32) * 144 + 8 * (l / 32);
+    pats.push_back(p);
+    Pattern q{"finish rejected 128-byte rows xor write", 16, std::vector<unsigned>(64), true};
+    for (unsigned l = 0; l < 64; ++l) q.addr[l] = (l % 32) * 128 + (((l / 32) ^ ((l % 32) / 2 % 8)) << 4);
+    pats.push_back(q);
+  }
   // the kernels' fragment reads, swizzled and not
   for (bool on : {true, false}) {
     for (unsigned s = 0; s < 2; ++s)
@@ -108,6 +174,8 @@ int main() {
     for (unsigned s = 0; s < 2; ++s)
       for (unsigned q = 0; q < 2; ++q)
         for (unsigned f = 0; f < 8; ++f) pats.push_back(fragment("fp8 32x32x64", 128, 32, 4, s, q, f, on));
+    for (unsigned q = 0; q < 2; ++q)
+      for (unsigned f = 0; f < 16; ++f) pats.push_back(fragment("fp8 16x16x128", 128, 16, 8, 0, q, f, on));
     for (unsigned s = 0; s < 2; ++s)
       for (unsigned f = 0; f < 8; ++f) pats.push_back(fragment("4-bit values", 64, 32, 2, s, 0, f, on));
   }
@@ -132,11 +200,13 @@ int main() {
   for (size_t i = 0; i < pats.size(); ++i) {
     const Pattern& p = pats[i];
     if (hipMemcpy(d_addr, p.addr.data(), 64 * sizeof(unsigned), hipMemcpyHostToDevice)) return 1;
-    if (p.bytes == 16) hipLaunchKernelGGL(lds_probe<16>, dim3(256), dim3(256), 0, 0, d_addr, out, 2048);
-    else if (p.bytes == 8) hipLaunchKernelGGL(lds_probe<8>, dim3(256), dim3(256), 0, 0, d_addr, out, 2048);
-    else hipLaunchKernelGGL(lds_probe<4>, dim3(256), dim3(256), 0, 0, d_addr, out, 2048);
+    if (p.write && p.bytes == 16) hipLaunchKernelGGL((lds_probe<16, true>), dim3(256), dim3(256), 0, 0, d_addr, out, 2048);
+    else if (p.write) hipLaunchKernelGGL((lds_probe<8, true>), dim3(256), dim3(256), 0, 0, d_addr, out, 2048);
+    else if (p.bytes == 16) hipLaunchKernelGGL((lds_probe<16, false>), dim3(256), dim3(256), 0, 0, d_addr, out, 2048);
+    else if (p.bytes == 8) hipLaunchKernelGGL((lds_probe<8, false>), dim3(256), dim3(256), 0, 0, d_addr, out, 2048);
+    else hipLaunchKernelGGL((lds_probe<4, false>), dim3(256), dim3(256), 0, 0, d_addr, out, 2048);
     if (hipDeviceSynchronize() != hipSuccess) return 2;
-    printf("pattern %zu %u %s :", i, p.bytes, p.name.c_str());
+    printf("pattern %zu %u %c %s :", i, p.bytes, p.write ? 'w' : 'r', p.name.c_str());
     for (unsigned a : p.addr) printf(" %u", a);
     printf("\n");
   }

@@ -3,8 +3,9 @@
 Usage:
     python lds_probe_summary.py PROBE_STDOUT COUNTER_DIR GOLDEN_JSON SUMMARY_MD COMMAND
 
-PROBE_STDOUT: what lds_bank_probe printed ("pattern <id> <bytes> <name> :
-<addresses>", one line per dispatch, in dispatch order); COUNTER_DIR: the
+PROBE_STDOUT: what lds_bank_probe printed ("pattern <id> <bytes> <op>
+<name> : <addresses>", op r = ds_read, w = ds_write, one line per dispatch,
+in dispatch order); COUNTER_DIR: the
 rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE output directory.
 Per dispatch, conflict degree = 1 / (1 - SQ_LDS_BANK_CONFLICT /
 SQ_LDS_IDX_ACTIVE), rounded. Writes the measured table as JSON (read by
@@ -27,8 +28,8 @@ def main(argv) -> int:
         if not line.startswith("pattern "):
             continue
         head, addrs = line.rstrip("\n").split(" : ") if " : " in line else line.rstrip("\n").split(" :")
-        _, pid, nbytes, name = head.split(" ", 3)
-        pats.append({"id": int(pid), "bytes": int(nbytes), "name": name,
+        _, pid, nbytes, op, name = head.split(" ", 4)
+        pats.append({"id": int(pid), "bytes": int(nbytes), "op": op, "name": name,
                      "addresses": [int(a) for a in addrs.split()]})
     per = collections.defaultdict(dict)
     for f in glob.glob(os.path.join(counter_dir, "**", "*counter_collection.csv"), recursive=True):
@@ -56,13 +57,14 @@ def main(argv) -> int:
              "```", command, "```", "",
              "Per dispatch, conflict degree = 1 / (1 - SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE). "
              "Address lists: `tests/golden/lds_probe_gfx950.json`.", "",
-             "| pattern | bytes/lane | conflict / active | degree |", "|---|---|---|---|"]
+             "| pattern | op | bytes/lane | conflict / active | degree |", "|---|---|---|---|---|"]
     for p in rec["patterns"]:
         if " frag " in p["name"] and not p["name"].endswith(" frag 0"):
             continue
-        lines.append("| %s | %d | %.3f | %d |" % (p["name"], p["bytes"], p["conflict_over_active"], p["degree"]))
+        lines.append("| %s | %s | %d | %.3f | %d |" % (p["name"], "write" if p["op"] == "w" else "read",
+                                                      p["bytes"], p["conflict_over_active"], p["degree"]))
     kern = [p for p in rec["patterns"] if " frag " in p["name"]]
-    for kind in ("bf16 16x16x32", "fp8 32x32x64", "4-bit values"):
+    for kind in ("bf16 16x16x32", "fp8 32x32x64", "fp8 16x16x128", "4-bit values"):
         for sw in ("swizzled", "unswizzled"):
             ds = [p["degree"] for p in kern if p["name"].startswith(kind + " " + sw)]
             lines.append("")
