@@ -60,7 +60,11 @@ def measured_traffic(kernel: str):
 
 
 KERNEL_KEYS = {"gemm_dense_kernel<0": "gemm_bf16", "gemm_dense_kernel<1": "gemm_fp8",
-               "gemm_fp4_kernel": "gemm_fp4_blockscaled"}
+               "gemm_fp4_kernel": "gemm_fp4_blockscaled", "gemm_mx_kernel<0": "gemm_mxfp4",
+               "gemm_mx_kernel<1": "gemm_mxfp8"}
+# MX products (e2m1 / e4m3 values with an E8M0 scale per 32) run on the
+# scaled MFMAs at the 4-bit and 8-bit rates
+PEAK_MX_TFLOPS = {"mxfp4": 10100.0, "mxfp8": 5000.0}
 
 
 def _kernel_key(name: str):
@@ -118,7 +122,9 @@ def summarize_profile(trace_dir: str, fetch_dir: str, write_dir: str,
     algo = {"gemm_bf16": (2 * M * K + 2 * N * K + 2 * M * N),
             "gemm_fp8": (M * K + N * K + 2 * M * N),
             "gemm_fp4_blockscaled": (M * K // 2 + N * K // 2 + M * K // 16
-                                     + N * K // 16 + 2 * M * N)}
+                                     + N * K // 16 + 2 * M * N),
+            "gemm_mxfp4": (M * K // 2 + N * K // 2 + M * K // 32 + N * K // 32 + 2 * M * N),
+            "gemm_mxfp8": (M * K + N * K + M * K // 32 + N * K // 32 + 2 * M * N)}
     rec = {"kernel_source_hash": kernel_source_hash(), "size": size,
            "copy_calibration": {"fetch_factor": ff, "write_factor": fw,
                                 "copy_bytes": 1 << 30},
@@ -127,8 +133,10 @@ def summarize_profile(trace_dir: str, fetch_dir: str, write_dir: str,
              "Produced by:", "", "```", command, "```", "",
              "| kernel | launches | mean us | min us | TFLOP/s (mean) | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes/launch (calibrated) | compulsory bytes | ratio |",
              "|---|---|---|---|---|---|---|---|---|---|"]
-    for k in ("gemm_bf16", "gemm_fp8", "gemm_fp4_blockscaled"):
+    for k in ("gemm_bf16", "gemm_fp8", "gemm_fp4_blockscaled", "gemm_mxfp4", "gemm_mxfp8"):
         d = dur.get(k, [])
+        if not d and k.startswith("gemm_mx"):
+            continue
         fk = statistics.mean(fetch[k]) if fetch.get(k) else None
         wk = statistics.mean(write[k]) if write.get(k) else None
         hbm = (fk * 1024 * ff + wk * 1024 * fw) if (fk and wk and ff and fw) else None
@@ -204,6 +212,9 @@ def main() -> int:
     ap.add_argument("--summarize-profile", nargs=3,
                     metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--profile-command", default="")
+    ap.add_argument("--with-mx", action="store_true",
+                    help="also time the MX products (gemm_mxfp4, gemm_mxfp8) on the "
+                         "same shape, reported under next_rows, outside the step")
     args = ap.parse_args()
 
     if args.summarize_profile:
@@ -241,6 +252,12 @@ def main() -> int:
     A4, As4, ta = gdev.fp4_operand(4, M, K, device=dev)
     B4, Bs4, tb = gdev.fp4_operand(5, N, K, device=dev)
     C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    extra = {}
+    if args.with_mx:
+        Am4, Asm4 = gdev.mx_operand(6, M, K, "e2m1", device=dev)
+        Bm4, Bsm4 = gdev.mx_operand(7, N, K, "e2m1", device=dev)
+        Am8, Asm8 = gdev.mx_operand(8, M, K, "e4m3", device=dev)
+        Bm8, Bsm8 = gdev.mx_operand(9, N, K, "e4m3", device=dev)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -251,6 +268,11 @@ def main() -> int:
             A4, As4, ta, B4, Bs4, tb, out=C, stream=stream),
     }
     names = list(calls)
+    if args.with_mx:
+        extra = {
+            "mxfp4": lambda: tkg.gemm_mxfp4(Am4, Asm4, Bm4, Bsm4, out=C, stream=stream),
+            "mxfp8": lambda: tkg.gemm_mxfp8(Am8, Asm8, Bm8, Bsm8, out=C, stream=stream),
+        }
 
     for _ in range(args.warmup):
         for k in names:
@@ -261,6 +283,9 @@ def main() -> int:
         for _ in range(args.steps):
             for k in names:
                 calls[k]()
+        for _ in range(args.steps):
+            for k in extra:
+                extra[k]()
         torch.cuda.synchronize()
         # calibration copy: 1 GiB read + 1 GiB written
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -309,6 +334,29 @@ def main() -> int:
                 "traffic": measured_traffic("gemm_" + dom),
                 "kernel": "gemm_" + dom}
 
+    # the MX products, timed apart from the step (not part of `value`)
+    next_rows = None
+    if extra:
+        next_rows = {}
+        for k, fn in extra.items():
+            for _ in range(args.warmup):
+                fn()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+            torch.cuda.synchronize()
+            for e0, e1 in evs:
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            t = [e0.elapsed_time(e1) for e0, e1 in evs]
+            ms = float(np.mean(t))
+            tf = flops / (ms * 1e-3) / 1e12
+            next_rows["gemm_" + k] = {
+                "ms_mean": round(ms, 4), "ms_min": round(float(np.min(t)), 4),
+                "tflops": round(tf, 1), "peak_tflops": PEAK_MX_TFLOPS[k],
+                "frac_of_peak": round(tf / PEAK_MX_TFLOPS[k], 4)}
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(A16, B16, args.cpu_seconds)
@@ -330,6 +378,8 @@ def main() -> int:
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }
+    if next_rows is not None:
+        out["next_rows"] = next_rows
     print(json.dumps(out), flush=True)
     return 0
 
