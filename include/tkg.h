@@ -149,15 +149,21 @@ const char *tkg_status_string(int status);
  *               of an LDS slab, operand slabs in the LDS ring, waves per
  *               workgroup, waves issuing the global loads, MFMA block:
  *               16 = 16x16x32 bf16 / 16x16x128 fp8, 32 = 32x32x16 /
- *               32x32x64). bf16: 0 = (128, 4, 8, 4, 16) default,
- *               1 = (128, 5, 8, 4, 16), 2 = (128, 4, 8, 4, 32),
- *               3 = (128, 5, 8, 4, 32), 4 = (128, 4, 8, 8, 32),
- *               5 = (128, 4, 4, 4, 32), 6 = (64, 10, 8, 8, 32),
- *               7 = (128, 4, 4, 4, 16). fp8: 0 = (128, 4, 4, 4, 16)
- *               default, 1 = (128, 5, 4, 4, 32), 2 = (128, 4, 8, 4, 32),
- *               3 = (128, 5, 8, 4, 32), 4 = (128, 4, 8, 8, 32),
- *               5 = (128, 4, 4, 4, 32), 6 = (64, 10, 8, 8, 32),
- *               7 = (64, 10, 4, 4, 32). TKG_ERR_SHAPE outside 0..7.
+ *               32x32x64, workgroup tile edge). 0 = automatic (default):
+ *               configuration 8, or configuration 9 when the product has
+ *               fewer 256 x 256 output tiles than the device has compute
+ *               units. bf16: 1 = (128, 5, 8, 4, 16, 256),
+ *               2 = (128, 4, 8, 4, 32, 256), 3 = (128, 5, 8, 4, 32, 256),
+ *               4 = (128, 4, 8, 8, 32, 256), 5 = (128, 4, 4, 4, 32, 256),
+ *               6 = (64, 10, 8, 8, 32, 256), 7 = (128, 4, 4, 4, 16, 256),
+ *               8 = (128, 4, 8, 4, 16, 256), 9 = (128, 4, 4, 4, 16, 128),
+ *               10 = (128, 4, 8, 4, 16, 128). fp8: 1 = (128, 5, 4, 4, 32,
+ *               256), 2 = (128, 4, 8, 4, 32, 256), 3 = (128, 5, 8, 4, 32,
+ *               256), 4 = (128, 4, 8, 8, 32, 256), 5 = (128, 4, 4, 4, 32,
+ *               256), 6 = (64, 10, 8, 8, 32, 256), 7 = (64, 10, 4, 4, 32,
+ *               256), 8 = (128, 4, 4, 4, 16, 256), 9 = (128, 4, 4, 4, 16,
+ *               128), 10 = (128, 4, 8, 4, 16, 128). TKG_ERR_SHAPE outside
+ *               0..10.
  *               4-bit product: 0 = 4 waves (default), 1 = 8 waves;
  *               TKG_ERR_SHAPE outside 0..1. Every variant of a product
  *               computes the same sums (the tests find them bit-identical).

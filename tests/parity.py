@@ -22,10 +22,12 @@ def relfro(G, R):
 
 def sample_tiles(M, N, seed, tile=64, n_random=8):
     """Origins of 64x64 output tiles: the four corners, tiles that straddle
-    the 256-row/column workgroup-tile boundaries, and random ones."""
+    the 128- and 256-row/column workgroup-tile boundaries, and random ones."""
     rng = np.random.default_rng(seed)
     tm, tn = min(tile, M), min(tile, N)
     out = {(0, 0), (M - tm, 0), (0, N - tn), (M - tm, N - tn)}
+    if M > 160 and N > 160:
+        out.add((96, 96))          # straddles the 128-row/column tiles
     if M > 288 and N > 288:
         out.add((224, 224))
         out.add((M // 2 // 256 * 256 - 32, N // 2 // 256 * 256 - 32))

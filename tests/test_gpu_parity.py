@@ -30,7 +30,7 @@ pytestmark = pytest.mark.gpu
 BF16_RELFRO = 1e-3
 BF16_ELEM_REL, BF16_ELEM_ABS = 1e-2, 1e-3
 LOWP_RELFRO = 2e-2
-DENSE_VARIANTS = 8   # kernel configurations selectable by tkg_opts.variant
+DENSE_VARIANTS = 11  # kernel configurations selectable by tkg_opts.variant
 
 
 @pytest.fixture(scope="module")
@@ -151,8 +151,10 @@ def _sampled_bf16(dev, M, N, K, seed):
 @pytest.mark.parametrize("M,N,K", [(1024, 1024, 1024), (2048, 2048, 2048),
                                    (4096, 4096, 4096), (8192, 8192, 8192),
                                    (8192, 14336, 4096), (8192, 4096, 14336),
-                                   (16384, 16384, 16384)])
+                                   (16384, 16384, 16384), (8192, 1024, 8192)])
 def test_bf16_config_shapes_sampled(dev, M, N, K):
+    # (8192, 1024, 8192): one GPU's N/8 share of the 8192^3 product, which
+    # runs on 128 x 128 tiles (fewer 256 x 256 tiles than compute units)
     _sampled_bf16(dev, M, N, K, seed=100 + M % 997 + K % 13)
 
 
@@ -260,17 +262,18 @@ def test_fp8_normal(dev, M, N, K):
     assert relfro(_bf16_result(C), R) <= LOWP_RELFRO
 
 
-@pytest.mark.parametrize("n", [8192, 16384])
-def test_fp8_config_shapes_sampled(dev, n):
-    A, sa = gi.device.fp8_operand(30, n, n, device=dev)
-    Bt, sb = gi.device.fp8_operand(31, n, n, device=dev)
+@pytest.mark.parametrize("M,N,K", [(8192, 8192, 8192), (16384, 16384, 16384),
+                                   (8192, 1024, 8192)])
+def test_fp8_config_shapes_sampled(dev, M, N, K):
+    A, sa = gi.device.fp8_operand(30, M, K, device=dev)
+    Bt, sb = gi.device.fp8_operand(31, N, K, device=dev)
     C = tkg.gemm_fp8(A, sa, Bt, sb)
     torch.cuda.synchronize()
-    for (i0, j0) in sample_tiles(n, n, n):
+    for (i0, j0) in sample_tiles(M, N, K):
         R = oracle.gemm_fp8(to_numpy_u8(A[i0:i0 + 64]), sa,
                             to_numpy_u8(Bt[j0:j0 + 64]), sb)
         G = _bf16_result(C[i0:i0 + 64, j0:j0 + 64])
-        assert relfro(G, R) <= LOWP_RELFRO, (n, i0, j0)
+        assert relfro(G, R) <= LOWP_RELFRO, (M, N, K, i0, j0)
 
 
 # ----------------------------------------------------- block-scaled 4-bit

@@ -38,8 +38,7 @@
 namespace tkg {
 namespace {
 
-constexpr int BM = kBM, BN = kBN;
-static_assert(BM == BN, "A and B slabs share offsets");
+static_assert(kBM == kBN, "A and B slabs share offsets");
 
 // Ring shapes. The LDS ring holds SLOTS operand slabs; a slab is one
 // operand's 256 rows x BKB bytes of K, and a K stage is an A slab and a B
@@ -52,21 +51,32 @@ static_assert(BM == BN, "A and B slabs share offsets");
 // the slab loads, so their partner wave on each SIMD keeps issuing MFMAs
 // while the loaders wait for the memory pipeline to accept loads.
 // MI: the MFMA block, 32 (32x32x16 bf16 / 32x32x64 fp8) or 16 (16x16x32 /
-// 16x16x128).
+// 16x16x128). BT: the workgroup tile, BT x BT (256, or 128 for products
+// with fewer 256 x 256 tiles than compute units). OCC: workgroups per
+// compute unit (2 lets one workgroup's MFMAs cover the other's barriers and
+// loads, for the short stages of 128 x 128 tiles).
 struct Ring {
-  int bkb, slots, waves_n, loaders, mi;
+  int bkb, slots, waves_n, loaders, mi, bt, occ;
 };
 // One table per operand type (variant v selects entry v); entry 0 is the
 // default, the fastest measured at 8192^3 on random operands: for bf16 two
 // waves per SIMD with 16x16x32 MFMAs, for fp8 one wave per SIMD with
 // 16x16x128 MFMAs (the 16x16 shapes run at a higher clock on the
 // power-limited chip).
-constexpr Ring kRingsBf16[] = {{128, 4, 4, 1, 16}, {128, 5, 4, 1, 16}, {128, 4, 4, 1, 32},
-                               {128, 5, 4, 1, 32}, {128, 4, 4, 0, 32}, {128, 4, 2, 0, 32},
-                               {64, 10, 4, 0, 32}, {128, 4, 2, 0, 16}};
-constexpr Ring kRingsFp8[] = {{128, 4, 2, 0, 16}, {128, 5, 2, 0, 32}, {128, 4, 4, 1, 32},
-                              {128, 5, 4, 1, 32}, {128, 4, 4, 0, 32}, {128, 4, 2, 0, 32},
-                              {64, 10, 4, 0, 32}, {64, 10, 2, 0, 32}};
+// Entry 8 repeats entry 0 (variant 0 may resolve to entry 9 instead, see
+// run_dense); entries 9 and 10 are 128 x 128 tiles.
+constexpr Ring kRingsBf16[] = {{128, 4, 4, 1, 16, 256, 1}, {128, 5, 4, 1, 16, 256, 1},
+                               {128, 4, 4, 1, 32, 256, 1}, {128, 5, 4, 1, 32, 256, 1},
+                               {128, 4, 4, 0, 32, 256, 1}, {128, 4, 2, 0, 32, 256, 1},
+                               {64, 10, 4, 0, 32, 256, 1}, {128, 4, 2, 0, 16, 256, 1},
+                               {128, 4, 4, 1, 16, 256, 1}, {128, 4, 2, 0, 16, 128, 2},
+                               {128, 4, 2, 0, 16, 128, 1}};
+constexpr Ring kRingsFp8[] = {{128, 4, 2, 0, 16, 256, 1}, {128, 5, 2, 0, 32, 256, 1},
+                              {128, 4, 4, 1, 32, 256, 1}, {128, 5, 4, 1, 32, 256, 1},
+                              {128, 4, 4, 0, 32, 256, 1}, {128, 4, 2, 0, 32, 256, 1},
+                              {64, 10, 4, 0, 32, 256, 1}, {64, 10, 2, 0, 32, 256, 1},
+                              {128, 4, 2, 0, 16, 256, 1}, {128, 4, 2, 0, 16, 128, 2},
+                              {128, 4, 2, 0, 16, 128, 1}};
 constexpr int kNumRings = sizeof(kRingsBf16) / sizeof(kRingsBf16[0]);
 static_assert(sizeof(kRingsFp8) == sizeof(kRingsBf16), "same variant count");
 template <int DT>
@@ -79,6 +89,7 @@ struct TileState {
   __amdgpu_buffer_rsrc_t ra, rb;
 };
 
+template <int BT>
 __device__ __forceinline__ TileState tile_state(const DenseArgs& p, int t) {
   TileState s;
   if (t >= p.num_tiles) {  // past the last tile: empty resources read zeros
@@ -89,33 +100,36 @@ __device__ __forceinline__ TileState tile_state(const DenseArgs& p, int t) {
   }
   int pm, pn;
   grouped_tile(t, p.tiles_m, p.tiles_n, p.group_m, pm, pn);
-  s.m0 = pm * BM;
-  s.n0 = pn * BN;
+  s.m0 = pm * BT;
+  s.n0 = pn * BT;
   // Resources cover only the rows of this tile that exist, so rows past M
   // (or N) read as zeros. 256 * kbytes < 2^31 is checked on the host.
-  const uint32_t rows_a = (uint32_t)min(p.M - s.m0, BM);
-  const uint32_t rows_b = (uint32_t)min(p.N - s.n0, BN);
+  const uint32_t rows_a = (uint32_t)min(p.M - s.m0, BT);
+  const uint32_t rows_b = (uint32_t)min(p.N - s.n0, BT);
   s.ra = make_rsrc(p.A + (size_t)s.m0 * p.kbytes, rows_a * p.kbytes);
   s.rb = make_rsrc(p.B + (size_t)s.n0 * p.kbytes, rows_b * p.kbytes);
   return s;
 }
 
-template <int DT, int BKB, int SLOTS, int WAVES_N, int LOADERS, int MI, bool KTAIL>
+template <int DT, int BKB, int SLOTS, int WAVES_N, int LOADERS, int MI, int BT, int OCC,
+          bool KTAIL>
 __global__ __launch_bounds__(128 * WAVES_N)
-__attribute__((amdgpu_waves_per_eu(WAVES_N / 2, WAVES_N / 2)))
+__attribute__((amdgpu_waves_per_eu(OCC * WAVES_N / 2, OCC * WAVES_N / 2)))
 void gemm_dense_kernel(DenseArgs p) {
   constexpr int WAVES = 2 * WAVES_N;
-  constexpr int WM = BM / 2, WN = BN / WAVES_N;   // wave tile
+  constexpr int WM = BT / 2, WN = BT / WAVES_N;   // wave tile
   constexpr int FM = WM / MI, FN = WN / MI;       // MIxMI accumulators
   constexpr int NMMA = FM * FN;                   // MFMAs per k-step
-  constexpr int SLAB = BM * BKB;           // bytes of one operand slab
+  constexpr int SLAB = BT * BKB;           // bytes of one operand slab
   // waves that issue slab loads, and b128 loads per such wave per slab
   constexpr int LOAD_WAVES = LOADERS ? WAVES_N : WAVES;
   constexpr int DMA = SLAB / 1024 / LOAD_WAVES;
   static_assert(SLOTS >= 4, "two stages at least");
-  static_assert(SLOTS * SLAB <= 160 * 1024, "LDS budget");
+  static_assert(FM >= 1 && FN >= 1 && DMA >= 1, "wave tile and loads fit the workgroup tile");
+  constexpr int LDS_BUDGET = 160 * 1024 / OCC;   // per workgroup
+  static_assert(SLOTS * SLAB <= LDS_BUDGET, "LDS budget");
   // the finish stages through the LDS the ring leaves free (tkg_finish.hpp)
-  using FP = FinishPlan<MI, FM, FN, (160 * 1024 - SLOTS * SLAB) / WAVES>;
+  using FP = FinishPlan<MI, FM, FN, (LDS_BUDGET - SLOTS * SLAB) / WAVES>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[SLOTS * SLAB + WAVES * FP::BYTES];
   TKG_LDS uint8_t* smem = (TKG_LDS uint8_t*)smem_raw;
 
@@ -189,7 +203,7 @@ void gemm_dense_kernel(DenseArgs p) {
   const uint32_t b_base = wn * WN * BKB;   // within a B slab
 
   // ---- load cursor: slab (tile lt, stage lkt, operand lop) ----------------
-  TileState cur = tile_state(p, t);
+  TileState cur = tile_state<BT>(p, t);
   TileState lts = cur;
   int lt = t;
   uint32_t lkt = 0, lop = 0, lslot = 0;
@@ -202,7 +216,7 @@ void gemm_dense_kernel(DenseArgs p) {
       if (++lkt == nk) {
         lkt = 0;
         lt += G;
-        lts = tile_state(p, lt);
+        lts = tile_state<BT>(p, lt);
       }
     }
   };
@@ -421,7 +435,7 @@ void gemm_dense_kernel(DenseArgs p) {
 
     t += G;
     if (t >= p.num_tiles) break;
-    cur = tile_state(p, t);
+    cur = tile_state<BT>(p, t);
   }
   };
   if (loader)
@@ -438,7 +452,8 @@ void gemm_dense_kernel(DenseArgs p) {
 template <int DT, int R, bool KTAIL>
 void launch_ring(const DenseArgs& a, int grid, hipStream_t stream) {
   constexpr Ring r = ring_of<DT>(R);
-  hipLaunchKernelGGL((gemm_dense_kernel<DT, r.bkb, r.slots, r.waves_n, r.loaders, r.mi, KTAIL>),
+  hipLaunchKernelGGL((gemm_dense_kernel<DT, r.bkb, r.slots, r.waves_n, r.loaders, r.mi, r.bt, r.occ,
+                                        KTAIL>),
                      dim3(grid), dim3(128 * r.waves_n), 0, stream, a);
 }
 
@@ -452,6 +467,9 @@ void launch_variant(int v, const DenseArgs& a, int grid, hipStream_t stream) {
     case 5: launch_ring<DT, 5, KTAIL>(a, grid, stream); break;
     case 6: launch_ring<DT, 6, KTAIL>(a, grid, stream); break;
     case 7: launch_ring<DT, 7, KTAIL>(a, grid, stream); break;
+    case 8: launch_ring<DT, 8, KTAIL>(a, grid, stream); break;
+    case 9: launch_ring<DT, 9, KTAIL>(a, grid, stream); break;
+    case 10: launch_ring<DT, 10, KTAIL>(a, grid, stream); break;
     default: launch_ring<DT, 0, KTAIL>(a, grid, stream); break;
   }
 }
@@ -460,6 +478,12 @@ uint32_t dense_stage_kbytes() { return kRingsBf16[0].bkb; }
 static_assert(kRingsBf16[0].bkb == kRingsFp8[0].bkb, "one default stage width");
 int dense_num_variants() { return kNumRings; }
 int dense_default_mi(DenseType dt) { return dt == kFp8 ? kRingsFp8[0].mi : kRingsBf16[0].mi; }
+int dense_tile(DenseType dt, int variant) {
+  return dt == kFp8 ? kRingsFp8[variant].bt : kRingsBf16[variant].bt;
+}
+int dense_occupancy(DenseType dt, int variant) {
+  return dt == kFp8 ? kRingsFp8[variant].occ : kRingsBf16[variant].occ;
+}
 
 hipError_t launch_dense(DenseType dt, const DenseArgs& a, int grid, int variant,
                         hipStream_t stream) {

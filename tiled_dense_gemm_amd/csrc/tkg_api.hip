@@ -45,16 +45,16 @@ struct Plan {
   int32_t tiles_m, tiles_n, num_tiles, group_m, xcd_remap, grid;
 };
 
-int make_plan(int64_t M, int64_t N, const tkg_opts* o, Plan* pl) {
-  pl->tiles_m = (int32_t)((M + kBM - 1) / kBM);
-  pl->tiles_n = (int32_t)((N + kBN - 1) / kBN);
+int make_plan(int64_t M, int64_t N, int64_t bt, int occ, const tkg_opts* o, Plan* pl) {
+  pl->tiles_m = (int32_t)((M + bt - 1) / bt);
+  pl->tiles_n = (int32_t)((N + bt - 1) / bt);
   const int64_t tiles = (int64_t)pl->tiles_m * pl->tiles_n;
   if (tiles > INT32_MAX / 2) return TKG_ERR_SHAPE;
   pl->num_tiles = (int32_t)tiles;
   int cus = 0;
   const int st = cu_count(&cus);
   if (st != TKG_OK) return st;
-  int grid = (o && o->grid > 0) ? o->grid : cus;
+  int grid = (o && o->grid > 0) ? o->grid : cus * occ;
   if (grid > pl->num_tiles) grid = pl->num_tiles;
   pl->grid = grid;
   int gm = (o && o->group_m > 0) ? o->group_m : 8;
@@ -88,8 +88,21 @@ int run_dense(tkg::DenseType dt, int64_t M, int64_t N, int64_t K,
     return TKG_ERR_NULL;
   if (!aligned16(C) || (K > 0 && (!aligned16(A) || !aligned16(B))))
     return TKG_ERR_ALIGN;
+  // Variant 0 takes 128 x 128 tiles when 256 x 256 ones would leave compute
+  // units idle (fewer tiles than units), e.g. one GPU's N/8 shard of a
+  // product split over 8 GPUs, or K-heavy small products.
+  int variant = opts ? opts->variant : 0;
+  if (variant < 0 || variant >= tkg::dense_num_variants()) return TKG_ERR_SHAPE;
+  if (variant == 0) {
+    int cus = 0;
+    st = cu_count(&cus);
+    if (st != TKG_OK) return st;
+    const int64_t tiles256 = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+    if (tiles256 < cus) variant = tkg::kDenseSmallTileVariant;
+  }
   Plan pl;
-  st = make_plan(M, N, opts, &pl);
+  st = make_plan(M, N, tkg::dense_tile(dt, variant), tkg::dense_occupancy(dt, variant), opts,
+                 &pl);
   if (st != TKG_OK) return st;
   tkg::DenseArgs a;
   a.A = static_cast<const uint8_t*>(A);
@@ -107,8 +120,6 @@ int run_dense(tkg::DenseType dt, int64_t M, int64_t N, int64_t K,
   if (K == 0) {  // empty reduction: the kernel's zero accumulators are C
     a.A = a.B = static_cast<const uint8_t*>(C);
   }
-  const int variant = opts ? opts->variant : 0;
-  if (variant < 0 || variant >= tkg::dense_num_variants()) return TKG_ERR_SHAPE;
   const hipError_t e = tkg::launch_dense(dt, a, pl.grid, variant,
                                          static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TKG_OK : TKG_ERR_LAUNCH;
@@ -129,7 +140,7 @@ int run_fp4(int64_t M, int64_t N, int64_t K, const void* A, const void* As,
                                   !aligned16(As) || !aligned16(Bs))))
     return TKG_ERR_ALIGN;
   Plan pl;
-  st = make_plan(M, N, opts, &pl);
+  st = make_plan(M, N, kBM, 1, opts, &pl);
   if (st != TKG_OK) return st;
   tkg::Fp4Args a;
   a.A = static_cast<const uint8_t*>(A);
@@ -175,7 +186,7 @@ int run_mx(tkg::MxType fmt, int64_t M, int64_t N, int64_t K, const void* A,
                                   !aligned16(As) || !aligned16(Bs))))
     return TKG_ERR_ALIGN;
   Plan pl;
-  st = make_plan(M, N, opts, &pl);
+  st = make_plan(M, N, kBM, 1, opts, &pl);
   if (st != TKG_OK) return st;
   tkg::MxArgs a;
   a.A = static_cast<const uint8_t*>(A);

@@ -66,6 +66,13 @@ hipError_t launch_dense(DenseType dt, const DenseArgs& a, int grid, int variant,
 int dense_num_variants();
 // MFMA block (16 or 32) of the default configuration for dt
 int dense_default_mi(DenseType dt);
+// workgroup tile edge (256 or 128) of variant `variant`
+int dense_tile(DenseType dt, int variant);
+// workgroups per compute unit of variant `variant` (the default grid)
+int dense_occupancy(DenseType dt, int variant);
+// the variant that variant 0 resolves to when the product has fewer
+// 256 x 256 output tiles than compute units
+constexpr int kDenseSmallTileVariant = 9;
 hipError_t launch_fp4(const Fp4Args& a, int grid, int variant,
                       hipStream_t stream);
 int fp4_num_variants();
