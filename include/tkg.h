@@ -39,6 +39,7 @@
 #ifndef TKG_H
 #define TKG_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -51,7 +52,8 @@ typedef enum tkg_status {
   TKG_ERR_SHAPE = -2,  /* negative size, unsupported multiple or too large  */
   TKG_ERR_ALIGN = -3,  /* a matrix pointer is not 16-byte aligned           */
   TKG_ERR_LAUNCH = -4, /* the HIP runtime rejected the launch               */
-  TKG_ERR_DEVICE = -5  /* no usable HIP device / device query failed        */
+  TKG_ERR_DEVICE = -5, /* no usable HIP device / device query failed        */
+  TKG_ERR_WORKSPACE = -6 /* split-K workspace NULL or smaller than required */
 } tkg_status;
 
 /*
@@ -130,6 +132,42 @@ int gemm_mxfp4(int64_t M, int64_t N, int64_t K, const void *A,
 int gemm_mxfp8(int64_t M, int64_t N, int64_t K, const void *A,
                const void *A_scales, const void *B, const void *B_scales,
                void *C, void *stream);
+
+/*
+ * Split-K bf16 / fp8 product for shapes with few output tiles and long K
+ * (small M x N), as C = s * A * B above (dtype TKG_DTYPE_BF16, s = 1, the
+ * scales ignored; or TKG_DTYPE_FP8, s = a_scale * b_scale; same operand
+ * layouts, alignment and K rules as gemm_bf16 / gemm_fp8). K is cut into
+ * `splits` ranges of whole stages (0 = automatic: enough (tile, range)
+ * work units for every workgroup slot of the device, each range at least
+ * 32 stages long; at most 64); each
+ * work unit computes its tile's partial sum over its range in fp32 into
+ * `workspace`, and a second kernel adds the partials of each output
+ * element in range order, multiplies by s and rounds to bf16. The result
+ * equals the plain product up to fp32 summation order. When the plan has
+ * one range the plain product runs and the workspace is not used.
+ *   workspace -- device memory owned by the caller, 16-byte aligned, at
+ *               least tkg_gemm_splitk_workspace_size(...) bytes, not
+ *               shared with a concurrent call; its contents are scratch.
+ * Returns TKG_ERR_WORKSPACE if the workspace is NULL or too small (when
+ * one is needed), else the errors of gemm_bf16 / gemm_fp8. Splitting the
+ * reduction over K is the stream-K / split-K reading of page
+ * "ThunderKittens: Simple, Fast, and Adorable AI Kernels", section 3.4,
+ * "Persistent Grid Launch" (Table 2: setup-bound products with short work
+ * per tile).
+ */
+int tkg_gemm_splitk(int dtype, int64_t M, int64_t N, int64_t K, const void *A,
+                    float a_scale, const void *B, float b_scale, void *C,
+                    void *workspace, size_t workspace_bytes, int splits,
+                    void *stream);
+/* Bytes of workspace tkg_gemm_splitk needs for these arguments (0 when it
+ * runs the plain product), or a negative tkg_status. */
+int64_t tkg_gemm_splitk_workspace_size(int dtype, int64_t M, int64_t N,
+                                       int64_t K, int splits);
+/* The number of K ranges tkg_gemm_splitk uses for these arguments, or a
+ * negative tkg_status. */
+int tkg_gemm_splitk_count(int dtype, int64_t M, int64_t N, int64_t K,
+                          int splits);
 
 /* Static, human-readable name of a tkg_status value (never NULL). */
 const char *tkg_status_string(int status);

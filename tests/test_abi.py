@@ -82,6 +82,37 @@ def test_argument_errors(call, want):
     assert call() == want
 
 
+def test_splitk_plan_and_errors():
+    # explicit range counts need no device: the plan is host arithmetic
+    # (stages of 128 K-bytes, ranges of whole two-stage chunks, at most 64)
+    bf, f8 = tkg.DTYPE_BF16, tkg.DTYPE_FP8
+    assert tkg.splitk_count(bf, 1024, 1024, 16384, 8) == 8
+    assert tkg.splitk_count(bf, 1024, 1024, 1024, 64) == 8      # 8 two-stage chunks of K
+    assert tkg.splitk_count(f8, 512, 512, 1040, 3) == 3         # chunks 5 -> ranges of 2, 2, 1
+    assert tkg.splitk_count(bf, 100, 100, 0, 4) == 1            # empty K: the plain product
+    assert tkg.splitk_workspace_size(bf, 1024, 1024, 16384, 8) == 64 * 8 * 128 * 128 * 4
+    assert tkg.splitk_workspace_size(bf, 1000, 130, 4096, 2) == 8 * 2 * 2 * 128 * 128 * 4
+    assert tkg.splitk_workspace_size(bf, 512, 512, 4096, 1) == 0
+    assert tkg.splitk_workspace_size(bf, 0, 512, 4096, 4) == 0
+    assert L.tkg_gemm_splitk_workspace_size(2, 8, 8, 64, 2) == S["TKG_ERR_SHAPE"]
+    assert L.tkg_gemm_splitk_workspace_size(bf, 8, 8, 12, 2) == S["TKG_ERR_SHAPE"]
+    assert L.tkg_gemm_splitk_count(bf, 8, 8, 64, -1) == S["TKG_ERR_SHAPE"]
+    # a needed workspace that is missing or short is refused before any launch
+    assert L.tkg_gemm_splitk(bf, 256, 256, 8192, A16, 1.0, B16, 1.0, C16, None, 0, 4,
+                             None) == S["TKG_ERR_WORKSPACE"]
+    need = tkg.splitk_workspace_size(bf, 256, 256, 8192, 4)
+    assert L.tkg_gemm_splitk(bf, 256, 256, 8192, A16, 1.0, B16, 1.0, C16, A16, need - 1, 4,
+                             None) == S["TKG_ERR_WORKSPACE"]
+    assert L.tkg_gemm_splitk(bf, 256, 256, 8192, A16, 1.0, B16, 1.0, C16, A16 + 8, need, 4,
+                             None) == S["TKG_ERR_ALIGN"]
+    assert L.tkg_gemm_splitk(bf, 256, 256, 8192, None, 1.0, B16, 1.0, C16, A16, need, 4,
+                             None) == S["TKG_ERR_NULL"]
+    assert L.tkg_gemm_splitk(2, 256, 256, 8192, A16, 1.0, B16, 1.0, C16, A16, need, 4,
+                             None) == S["TKG_ERR_SHAPE"]
+    assert L.tkg_gemm_splitk(bf, 0, 256, 8192, None, 1.0, None, 1.0, None, None, 0, 4,
+                             None) == S["TKG_OK"]
+
+
 def test_lds_introspection_errors():
     buf = (ctypes.c_uint32 * 64)()
     assert L.tkg_lds_fragment_offsets(0, 99, 0, 0, buf) == S["TKG_ERR_SHAPE"]

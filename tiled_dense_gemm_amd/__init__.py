@@ -30,7 +30,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtkg.so")
 DTYPE_BF16, DTYPE_FP8, DTYPE_FP4_BLOCKSCALED = 0, 1, 2
 DTYPE_MXFP4, DTYPE_MXFP8 = 3, 4
 STATUS = {"TKG_OK": 0, "TKG_ERR_NULL": -1, "TKG_ERR_SHAPE": -2,
-          "TKG_ERR_ALIGN": -3, "TKG_ERR_LAUNCH": -4, "TKG_ERR_DEVICE": -5}
+          "TKG_ERR_ALIGN": -3, "TKG_ERR_LAUNCH": -4, "TKG_ERR_DEVICE": -5,
+          "TKG_ERR_WORKSPACE": -6}
 
 
 class TkgError(RuntimeError):
@@ -84,6 +85,13 @@ def _load() -> ctypes.CDLL:
     L.tkg_lds_finish_offsets.argtypes = [i32, i32, i32, i32,
                                          ctypes.POINTER(ctypes.c_uint32)]
     L.tkg_lds_finish_offsets.restype = i32
+    L.tkg_gemm_splitk.argtypes = [i32, i64, i64, i64, vp, f32, vp, f32, vp, vp,
+                                  ctypes.c_size_t, i32, vp]
+    L.tkg_gemm_splitk.restype = i32
+    L.tkg_gemm_splitk_workspace_size.argtypes = [i32, i64, i64, i64, i32]
+    L.tkg_gemm_splitk_workspace_size.restype = i64
+    L.tkg_gemm_splitk_count.argtypes = [i32, i64, i64, i64, i32]
+    L.tkg_gemm_splitk_count.restype = i32
     return L
 
 
@@ -216,6 +224,51 @@ def gemm_fp8(A, scale_a, Bt, scale_b, out=None, stream=None):
                           _stream_ptr(stream))
     _raise(st, "gemm_fp8")
     return out
+
+
+def gemm_splitk(A, Bt, scale_a=1.0, scale_b=1.0, splits=0, workspace=None,
+                out=None, stream=None):
+    """Split-K product (see tkg.h tkg_gemm_splitk): bf16 A, Bt (scales
+    ignored) or e4m3 A, Bt with fp32 scales. `workspace` (a device tensor of
+    at least splitk_workspace_size(...) bytes) is allocated here through
+    torch when not given."""
+    torch = _torch()
+    M, K = A.shape
+    N = Bt.shape[0]
+    if A.dtype == torch.bfloat16:
+        dtype = DTYPE_BF16
+        _check_mat(A, "A", M, K, (torch.bfloat16,), None)
+        _check_mat(Bt, "Bt", N, K, (torch.bfloat16,), A.device)
+    else:
+        dtype = DTYPE_FP8
+        _check_mat(A, "A", M, K, _fp8_types(), None)
+        _check_mat(Bt, "Bt", N, K, _fp8_types(), A.device)
+    out = _out(out, M, N, A.device)
+    need = splitk_workspace_size(dtype, M, N, K, splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
+    ws_ptr = None if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(A.device):
+        st = lib.tkg_gemm_splitk(dtype, M, N, K, A.data_ptr(), float(scale_a),
+                                 Bt.data_ptr(), float(scale_b), out.data_ptr(),
+                                 ws_ptr, ws_bytes, int(splits), _stream_ptr(stream))
+    _raise(st, "tkg_gemm_splitk")
+    return out
+
+
+def splitk_workspace_size(dtype, M, N, K, splits=0) -> int:
+    r = lib.tkg_gemm_splitk_workspace_size(int(dtype), int(M), int(N), int(K), int(splits))
+    if r < 0:
+        raise TkgError(r, "tkg_gemm_splitk_workspace_size")
+    return r
+
+
+def splitk_count(dtype, M, N, K, splits=0) -> int:
+    r = lib.tkg_gemm_splitk_count(int(dtype), int(M), int(N), int(K), int(splits))
+    if r < 0:
+        raise TkgError(r, "tkg_gemm_splitk_count")
+    return r
 
 
 def gemm_fp4_blockscaled(A, A_scales, a_scale, Bt, B_scales, b_scale,

@@ -87,17 +87,28 @@ constexpr Ring ring_of(int v) {
 struct TileState {
   int m0, n0;
   __amdgpu_buffer_rsrc_t ra, rb;
+  uint32_t k0, nk;   // the unit's first K byte and its stage count
 };
 
-template <int BT>
-__device__ __forceinline__ TileState tile_state(const DenseArgs& p, int t) {
+// Work unit u: split u % splits of tile u / splits (one split: the tile).
+// The unit's stage count is rounded up to whole loop trips (TRIP stages);
+// the extra stage reads zeros.
+template <int BT, int BKB, int TRIP>
+__device__ __forceinline__ TileState tile_state(const DenseArgs& p, int u) {
   TileState s;
-  if (t >= p.num_tiles) {  // past the last tile: empty resources read zeros
+  if (u >= p.num_units) {  // past the last unit: empty resources read zeros
     s.m0 = s.n0 = 0;
     s.ra = make_rsrc(p.A, 0);
     s.rb = make_rsrc(p.B, 0);
+    s.k0 = 0;
+    s.nk = TRIP;
     return s;
   }
+  const int t = p.splits == 1 ? u : u / p.splits;
+  s.k0 = (uint32_t)(u - t * p.splits) * p.ksplit;
+  const uint32_t klen = min(p.ksplit, p.kbytes - s.k0);
+  const uint32_t nk_raw = (klen + BKB - 1) / BKB;
+  s.nk = (TRIP == 2) ? (nk_raw + (nk_raw & 1)) : nk_raw;
   int pm, pn;
   grouped_tile(t, p.tiles_m, p.tiles_n, p.group_m, pm, pn);
   s.m0 = pm * BT;
@@ -154,13 +165,8 @@ void gemm_dense_kernel(DenseArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int G = gridDim.x;
-  int t = xcd_virtual_id(blockIdx.x, G, p.xcd_remap);
-  if (t >= p.num_tiles) return;
-
-  // Number of K stages per tile, rounded up to whole loop trips; the extra
-  // stage reads zeros.
-  const uint32_t nk_raw = (p.kbytes + BKB - 1) / BKB;
-  const uint32_t nk = (TRIP_STAGES == 2) ? (nk_raw + (nk_raw & 1)) : nk_raw;
+  int t = xcd_virtual_id(blockIdx.x, G, p.xcd_remap);   // work unit
+  if (t >= p.num_units) return;
 
   // ---- per-lane staging offsets (tile independent) -----------------------
   // DMA instruction i of this wave fills rows dma_row(q), q = lw*DMA + i.
@@ -203,7 +209,7 @@ void gemm_dense_kernel(DenseArgs p) {
   const uint32_t b_base = wn * WN * BKB;   // within a B slab
 
   // ---- load cursor: slab (tile lt, stage lkt, operand lop) ----------------
-  TileState cur = tile_state<BT>(p, t);
+  TileState cur = tile_state<BT, BKB, TRIP_STAGES>(p, t);
   TileState lts = cur;
   int lt = t;
   uint32_t lkt = 0, lop = 0, lslot = 0;
@@ -213,10 +219,10 @@ void gemm_dense_kernel(DenseArgs p) {
       lop = 1;
     } else {
       lop = 0;
-      if (++lkt == nk) {
+      if (++lkt == lts.nk) {
         lkt = 0;
         lt += G;
-        lts = tile_state<BT>(p, lt);
+        lts = tile_state<BT, BKB, TRIP_STAGES>(p, lt);
       }
     }
   };
@@ -229,7 +235,7 @@ void gemm_dense_kernel(DenseArgs p) {
     SlabLoad s;
     s.r = lop ? lts.rb : lts.ra;
     s.slot = lslot;
-    s.k0 = lkt * BKB;
+    s.k0 = lts.k0 + lkt * BKB;
     advance_load();
     return s;
   };
@@ -373,7 +379,7 @@ void gemm_dense_kernel(DenseArgs p) {
   };
 
   for (;;) {
-    for (uint32_t kt = 0; kt < nk; kt += TRIP_STAGES) {
+    for (uint32_t kt = 0; kt < cur.nk; kt += TRIP_STAGES) {
 #pragma unroll
       for (int st = 0; st < TRIP_STAGES; ++st) {
         // the cursor moves (and may branch to a new tile) at the top of the
@@ -393,7 +399,23 @@ void gemm_dense_kernel(DenseArgs p) {
     // The MFMA ran with B as its first operand, so accumulator (i, j) holds
     // the transposed MIxMI block: lane l owns C row m = l%MI and, in element
     // r, column 4*P*(r/4) + 4*(l/MI) + r%4.
-    if constexpr (FP::USE) {
+    if (p.splits > 1) {
+      // split-K: this unit's fp32 partial sums, in accumulator order
+      // (wave, block, element group, lane), 16 bytes per lane per store
+      float* w = p.ws + ((size_t)t * WAVES + wave) * (FM * FN * NE * 64);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+          for (int g = 0; g < NE / 4; ++g)
+            *reinterpret_cast<f32x4_t*>(w + (((i * FN + j) * (NE / 4) + g) * 64 + lane) * 4) =
+                f32x4_t{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                        acc[i][j][4 * g + 3]};
+          acc[i][j] = Acc{};
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    } else if constexpr (FP::USE) {
       finish_staged<MI, FM, FN, FP::RJ, DT != kBf16>(
           acc, p.scale, smem + SLOTS * SLAB + wave * FP::BYTES, p.C, p.M, p.N,
           cur.m0 + wm * WM, cur.n0 + wn * WN, (uint32_t)lane);
@@ -434,8 +456,8 @@ void gemm_dense_kernel(DenseArgs p) {
     fresh_tile = true;
 
     t += G;
-    if (t >= p.num_tiles) break;
-    cur = tile_state<BT>(p, t);
+    if (t >= p.num_units) break;
+    cur = tile_state<BT, BKB, TRIP_STAGES>(p, t);
   }
   };
   if (loader)
@@ -445,6 +467,53 @@ void gemm_dense_kernel(DenseArgs p) {
   // The load cursor ran ahead into empty resources; let those LDS writes
   // land before the workgroup's LDS is released.
   wait_vmcnt<0>();
+}
+
+// Split-K reduction: one workgroup per output tile; thread q of the tile's
+// BT*BT/4 element groups adds the splits' partials in order, scales, rounds
+// to bf16 and stores the four columns it covers (the layout of the main
+// kernel's accumulators: wave, block (i, j), element group g, lane).
+template <int DT, int WAVES_N, int MI, int BT>
+__global__ __launch_bounds__(256) void gemm_dense_reduce(DenseArgs p) {
+  constexpr int WAVES = 2 * WAVES_N;
+  constexpr int WM = BT / 2, WN = BT / WAVES_N;
+  constexpr int FM = WM / MI, FN = WN / MI;
+  constexpr int NE = MI * MI / 64, P = 64 / MI;
+  constexpr int UNIT = FM * FN * NE * 64 * WAVES;   // floats per unit
+  const int tile = blockIdx.x;
+  int pm, pn;
+  grouped_tile(tile, p.tiles_m, p.tiles_n, p.group_m, pm, pn);
+  const float* base = p.ws + (size_t)tile * p.splits * UNIT;
+  for (int q = threadIdx.x; q < UNIT / 4; q += 256) {
+    const int lane = q % 64;
+    const int g = (q / 64) % (NE / 4);
+    const int blk = (q / 64 / (NE / 4)) % (FM * FN);
+    const int wave = q / 64 / (NE / 4) / (FM * FN);
+    const int i = blk / FN, j = blk % FN;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    f32x4_t sum = *reinterpret_cast<const f32x4_t*>(base + (size_t)q * 4);
+    for (int sp = 1; sp < p.splits; ++sp) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(base + (size_t)sp * UNIT + (size_t)q * 4);
+      sum[0] += v[0];
+      sum[1] += v[1];
+      sum[2] += v[2];
+      sum[3] += v[3];
+    }
+    const int m = pm * BT + wm * WM + i * MI + lane % MI;
+    const int n = pn * BT + wn * WN + j * MI + 4 * P * g + 4 * (lane / MI);
+    if (m >= p.M) continue;
+    const float sc = DT == kBf16 ? 1.0f : p.scale;
+    const uint2 pk = pack_bf16x4(sum[0] * sc, sum[1] * sc, sum[2] * sc, sum[3] * sc);
+    uint16_t* cp = p.C + (size_t)m * (size_t)p.N + n;
+    if ((p.N & 3) == 0 && n + 3 < p.N) {
+      *reinterpret_cast<uint2*>(cp) = pk;
+    } else {
+      const uint16_t e[4] = {(uint16_t)(pk.x & 0xFFFF), (uint16_t)(pk.x >> 16),
+                             (uint16_t)(pk.y & 0xFFFF), (uint16_t)(pk.y >> 16)};
+      for (int u = 0; u < 4; ++u)
+        if (n + u < p.N) cp[u] = e[u];
+    }
+  }
 }
 
 }  // namespace
@@ -483,6 +552,28 @@ int dense_tile(DenseType dt, int variant) {
 }
 int dense_occupancy(DenseType dt, int variant) {
   return dt == kFp8 ? kRingsFp8[variant].occ : kRingsBf16[variant].occ;
+}
+uint32_t dense_unit_ws_bytes(DenseType dt, int variant) {
+  const int bt = dense_tile(dt, variant);
+  return (uint32_t)(bt * bt * 4);
+}
+uint32_t dense_variant_stage_kbytes(DenseType dt, int variant) {
+  return dt == kFp8 ? kRingsFp8[variant].bkb : kRingsBf16[variant].bkb;
+}
+
+template <int DT, int R>
+void launch_reduce_ring(const DenseArgs& a, hipStream_t stream) {
+  constexpr Ring r = ring_of<DT>(R);
+  hipLaunchKernelGGL((gemm_dense_reduce<DT, r.waves_n, r.mi, r.bt>), dim3(a.num_tiles), dim3(256), 0,
+                     stream, a);
+}
+
+hipError_t launch_dense_reduce(DenseType dt, const DenseArgs& a, int variant, hipStream_t stream) {
+  // split-K runs on the small-tile configuration only
+  if (variant != kDenseSmallTileVariant) return hipErrorInvalidValue;
+  if (dt == kBf16) launch_reduce_ring<kBf16, kDenseSmallTileVariant>(a, stream);
+  else launch_reduce_ring<kFp8, kDenseSmallTileVariant>(a, stream);
+  return hipGetLastError();
 }
 
 hipError_t launch_dense(DenseType dt, const DenseArgs& a, int grid, int variant,

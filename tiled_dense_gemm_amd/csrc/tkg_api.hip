@@ -117,11 +117,121 @@ int run_dense(tkg::DenseType dt, int64_t M, int64_t N, int64_t K,
   a.num_tiles = pl.num_tiles;
   a.group_m = pl.group_m;
   a.xcd_remap = pl.xcd_remap;
+  a.splits = 1;
+  a.num_units = pl.num_tiles;
+  a.ksplit = a.kbytes;
+  a.ws = nullptr;
   if (K == 0) {  // empty reduction: the kernel's zero accumulators are C
     a.A = a.B = static_cast<const uint8_t*>(C);
   }
   const hipError_t e = tkg::launch_dense(dt, a, pl.grid, variant,
                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TKG_OK : TKG_ERR_LAUNCH;
+}
+
+// Split-K plan on the small-tile configuration: `req` splits (0 = enough
+// work units for every workgroup slot of the device), each a multiple of
+// two stages of K, at most 64; splits = 1 means the plain product.
+struct SplitPlan {
+  int splits;
+  uint32_t ksplit;
+  size_t ws_bytes;
+  int tiles;
+};
+
+int splitk_plan(tkg::DenseType dt, int64_t M, int64_t N, int64_t K, int req, SplitPlan* sp) {
+  if (req < 0) return TKG_ERR_SHAPE;
+  const int v = tkg::kDenseSmallTileVariant;
+  const int64_t bt = tkg::dense_tile(dt, v);
+  const int64_t tiles = ((M + bt - 1) / bt) * ((N + bt - 1) / bt);
+  const int64_t kbytes = K * (1 + (dt == tkg::kBf16));
+  const int64_t unit = 2 * (int64_t)tkg::dense_variant_stage_kbytes(dt, v);  // K bytes
+  const int64_t chunks = (kbytes + unit - 1) / unit;
+  int64_t s = req;
+  if (s == 0) {
+    int cus = 0;
+    const int st = cu_count(&cus);
+    if (st != TKG_OK) return st;
+    const int64_t slots = (int64_t)cus * tkg::dense_occupancy(dt, v);
+    s = tiles > 0 ? (slots + tiles - 1) / tiles : 1;
+    // at least 16 two-stage chunks per range: shorter ranges lose more to
+    // the partial-sum traffic and the second kernel than the idle units
+    // cost (measured: 1024 x 1024 x 4096 bf16, 8 ranges of 4 chunks, 216 ->
+    // 165 TFLOP/s; 1024 x 1024 x 16384, 8 ranges of 16, 232 -> 414)
+    const int64_t cap = chunks / 16;
+    if (s > cap) s = cap;
+  }
+  sp->tiles = (int)tiles;
+  if (chunks == 0) {   // empty reduction: the plain product writes zeros
+    sp->splits = 1;
+    sp->ksplit = 0;
+    sp->ws_bytes = 0;
+    return TKG_OK;
+  }
+  if (s > 64) s = 64;
+  if (s > chunks) s = chunks;
+  if (s < 1) s = 1;
+  const int64_t per = (chunks + s - 1) / s;        // two-stage chunks per split
+  sp->ksplit = (uint32_t)(per * unit);
+  sp->splits = (int)((kbytes + sp->ksplit - 1) / sp->ksplit);
+  if (sp->splits < 1) sp->splits = 1;
+  sp->tiles = (int)tiles;
+  sp->ws_bytes = sp->splits > 1 ? (size_t)tiles * sp->splits * tkg::dense_unit_ws_bytes(dt, v) : 0;
+  return TKG_OK;
+}
+
+int run_dense_splitk(tkg::DenseType dt, int64_t M, int64_t N, int64_t K, const void* A,
+                     const void* B, void* C, float scale, void* ws, size_t ws_bytes,
+                     int req, void* stream) {
+  const int64_t eb = 1 + (dt == tkg::kBf16);
+  const int64_t kmult = (dt == tkg::kBf16) ? 8 : 16;
+  const int64_t kmax = (dt == tkg::kBf16) ? 4194303 : 8388607;
+  int st = check_common(M, N, K, kmult, kmax);
+  if (st != TKG_OK) return st;
+  if (req < 0) return TKG_ERR_SHAPE;
+  if (M == 0 || N == 0) return TKG_OK;
+  SplitPlan sp;
+  st = splitk_plan(dt, M, N, K, req, &sp);
+  if (st != TKG_OK) return st;
+  if (sp.splits == 1) {
+    tkg_opts o{0, 0, 1, tkg::kDenseSmallTileVariant};
+    return run_dense(dt, M, N, K, A, B, C, scale, stream, &o);
+  }
+  if (C == nullptr || A == nullptr || B == nullptr) return TKG_ERR_NULL;
+  if (!aligned16(C) || !aligned16(A) || !aligned16(B)) return TKG_ERR_ALIGN;
+  if (ws == nullptr || ws_bytes < sp.ws_bytes) return TKG_ERR_WORKSPACE;
+  if (!aligned16(ws)) return TKG_ERR_ALIGN;
+  const int v = tkg::kDenseSmallTileVariant;
+  Plan pl;
+  st = make_plan(M, N, tkg::dense_tile(dt, v), tkg::dense_occupancy(dt, v), nullptr, &pl);
+  if (st != TKG_OK) return st;
+  int cus = 0;
+  st = cu_count(&cus);
+  if (st != TKG_OK) return st;
+  const int64_t units = (int64_t)pl.num_tiles * sp.splits;
+  if (units > INT32_MAX / 2) return TKG_ERR_SHAPE;
+  int grid = cus * tkg::dense_occupancy(dt, v);
+  if (grid > units) grid = (int)units;
+  tkg::DenseArgs a;
+  a.A = static_cast<const uint8_t*>(A);
+  a.B = static_cast<const uint8_t*>(B);
+  a.C = static_cast<uint16_t*>(C);
+  a.M = (int32_t)M;
+  a.N = (int32_t)N;
+  a.kbytes = (uint32_t)(K * eb);
+  a.scale = scale;
+  a.tiles_m = pl.tiles_m;
+  a.tiles_n = pl.tiles_n;
+  a.num_tiles = pl.num_tiles;
+  a.group_m = pl.group_m;
+  a.xcd_remap = pl.xcd_remap;
+  a.splits = sp.splits;
+  a.num_units = (int32_t)units;
+  a.ksplit = sp.ksplit;
+  a.ws = static_cast<float*>(ws);
+  hipError_t e = tkg::launch_dense(dt, a, grid, v, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return TKG_ERR_LAUNCH;
+  e = tkg::launch_dense_reduce(dt, a, v, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TKG_OK : TKG_ERR_LAUNCH;
 }
 
@@ -280,6 +390,7 @@ const char* tkg_status_string(int status) {
     case TKG_ERR_ALIGN: return "TKG_ERR_ALIGN: pointer not 16-byte aligned";
     case TKG_ERR_LAUNCH: return "TKG_ERR_LAUNCH: kernel launch failed";
     case TKG_ERR_DEVICE: return "TKG_ERR_DEVICE: no usable HIP device";
+    case TKG_ERR_WORKSPACE: return "TKG_ERR_WORKSPACE: split-K workspace missing or too small";
     default: return "unknown tkg status";
   }
 }
@@ -351,6 +462,42 @@ int tkg_lds_finish_offsets(int mi, int rj, int kind, int index, uint32_t* out64)
     }
   }
   return count;
+}
+
+int tkg_gemm_splitk(int dtype, int64_t M, int64_t N, int64_t K, const void* A,
+                    float a_scale, const void* B, float b_scale, void* C, void* workspace,
+                    size_t workspace_bytes, int splits, void* stream) {
+  if (dtype == TKG_DTYPE_BF16)
+    return run_dense_splitk(tkg::kBf16, M, N, K, A, B, C, 1.0f, workspace, workspace_bytes,
+                            splits, stream);
+  if (dtype == TKG_DTYPE_FP8)
+    return run_dense_splitk(tkg::kFp8, M, N, K, A, B, C, a_scale * b_scale, workspace,
+                            workspace_bytes, splits, stream);
+  return TKG_ERR_SHAPE;
+}
+
+int64_t tkg_gemm_splitk_workspace_size(int dtype, int64_t M, int64_t N, int64_t K,
+                                       int splits) {
+  if (dtype != TKG_DTYPE_BF16 && dtype != TKG_DTYPE_FP8) return TKG_ERR_SHAPE;
+  const tkg::DenseType dt = dtype == TKG_DTYPE_BF16 ? tkg::kBf16 : tkg::kFp8;
+  const int64_t kmult = (dt == tkg::kBf16) ? 8 : 16;
+  const int64_t kmax = (dt == tkg::kBf16) ? 4194303 : 8388607;
+  int st = check_common(M, N, K, kmult, kmax);
+  if (st != TKG_OK) return st;
+  if (M == 0 || N == 0) return 0;
+  SplitPlan sp;
+  st = splitk_plan(dt, M, N, K, splits, &sp);
+  if (st != TKG_OK) return st;
+  return (int64_t)sp.ws_bytes;
+}
+
+int tkg_gemm_splitk_count(int dtype, int64_t M, int64_t N, int64_t K, int splits) {
+  if (dtype != TKG_DTYPE_BF16 && dtype != TKG_DTYPE_FP8) return TKG_ERR_SHAPE;
+  const tkg::DenseType dt = dtype == TKG_DTYPE_BF16 ? tkg::kBf16 : tkg::kFp8;
+  if (M < 0 || N < 0 || K < 0) return TKG_ERR_SHAPE;
+  SplitPlan sp;
+  const int st = splitk_plan(dt, M, N, K, splits, &sp);
+  return st != TKG_OK ? st : sp.splits;
 }
 
 }  // extern "C"

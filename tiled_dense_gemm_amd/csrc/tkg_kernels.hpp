@@ -19,6 +19,13 @@ struct DenseArgs {
   float scale;
   int32_t tiles_m, tiles_n, num_tiles, group_m;
   int32_t xcd_remap;  // 1: give each XCD a contiguous range of tiles
+  // split-K: work unit u is split u % splits of tile u / splits and covers
+  // K bytes [split * ksplit, min((split + 1) * ksplit, kbytes)); with
+  // splits > 1 the units write fp32 partial sums to ws (see
+  // launch_dense_reduce) instead of C. splits = 1: ksplit >= kbytes.
+  int32_t splits, num_units;
+  uint32_t ksplit;
+  float* ws;
 };
 
 // Block-scaled 4-bit problem: values packed two per byte (K/2 bytes per row)
@@ -70,6 +77,14 @@ int dense_default_mi(DenseType dt);
 int dense_tile(DenseType dt, int variant);
 // workgroups per compute unit of variant `variant` (the default grid)
 int dense_occupancy(DenseType dt, int variant);
+// bytes of fp32 partial sums one split-K work unit of `variant` writes
+uint32_t dense_unit_ws_bytes(DenseType dt, int variant);
+// K bytes of one stage of `variant` (split boundaries are multiples of two)
+uint32_t dense_variant_stage_kbytes(DenseType dt, int variant);
+// C = scale * (sum over splits of the partial sums in a.ws), one workgroup
+// per output tile, splits added in order 0, 1, ...
+hipError_t launch_dense_reduce(DenseType dt, const DenseArgs& a, int variant,
+                               hipStream_t stream);
 // the variant that variant 0 resolves to when the product has fewer
 // 256 x 256 output tiles than compute units
 constexpr int kDenseSmallTileVariant = 9;
