@@ -93,7 +93,7 @@ struct TileState {
 // Work unit u: split u % splits of tile u / splits (one split: the tile).
 // The unit's stage count is rounded up to whole loop trips (TRIP stages);
 // the extra stage reads zeros.
-template <int BT, int BKB, int TRIP>
+template <int BT, int BKB, int TRIP, bool SPLITK>
 __device__ __forceinline__ TileState tile_state(const DenseArgs& p, int u) {
   TileState s;
   if (u >= p.num_units) {  // past the last unit: empty resources read zeros
@@ -104,9 +104,14 @@ __device__ __forceinline__ TileState tile_state(const DenseArgs& p, int u) {
     s.nk = TRIP;
     return s;
   }
-  const int t = p.splits == 1 ? u : u / p.splits;
-  s.k0 = (uint32_t)(u - t * p.splits) * p.ksplit;
-  const uint32_t klen = min(p.ksplit, p.kbytes - s.k0);
+  int t = u;
+  uint32_t klen = p.kbytes;
+  s.k0 = 0;
+  if constexpr (SPLITK) {
+    t = u / p.splits;
+    s.k0 = (uint32_t)(u - t * p.splits) * p.ksplit;
+    klen = min(p.ksplit, p.kbytes - s.k0);
+  }
   const uint32_t nk_raw = (klen + BKB - 1) / BKB;
   s.nk = (TRIP == 2) ? (nk_raw + (nk_raw & 1)) : nk_raw;
   int pm, pn;
@@ -123,7 +128,7 @@ __device__ __forceinline__ TileState tile_state(const DenseArgs& p, int u) {
 }
 
 template <int DT, int BKB, int SLOTS, int WAVES_N, int LOADERS, int MI, int BT, int OCC,
-          bool KTAIL>
+          bool SPLITK, bool KTAIL>
 __global__ __launch_bounds__(128 * WAVES_N)
 __attribute__((amdgpu_waves_per_eu(OCC * WAVES_N / 2, OCC * WAVES_N / 2)))
 void gemm_dense_kernel(DenseArgs p) {
@@ -209,7 +214,7 @@ void gemm_dense_kernel(DenseArgs p) {
   const uint32_t b_base = wn * WN * BKB;   // within a B slab
 
   // ---- load cursor: slab (tile lt, stage lkt, operand lop) ----------------
-  TileState cur = tile_state<BT, BKB, TRIP_STAGES>(p, t);
+  TileState cur = tile_state<BT, BKB, TRIP_STAGES, SPLITK>(p, t);
   TileState lts = cur;
   int lt = t;
   uint32_t lkt = 0, lop = 0, lslot = 0;
@@ -222,7 +227,7 @@ void gemm_dense_kernel(DenseArgs p) {
       if (++lkt == lts.nk) {
         lkt = 0;
         lt += G;
-        lts = tile_state<BT, BKB, TRIP_STAGES>(p, lt);
+        lts = tile_state<BT, BKB, TRIP_STAGES, SPLITK>(p, lt);
       }
     }
   };
@@ -399,7 +404,7 @@ void gemm_dense_kernel(DenseArgs p) {
     // The MFMA ran with B as its first operand, so accumulator (i, j) holds
     // the transposed MIxMI block: lane l owns C row m = l%MI and, in element
     // r, column 4*P*(r/4) + 4*(l/MI) + r%4.
-    if (p.splits > 1) {
+    if constexpr (SPLITK) {
       // split-K: this unit's fp32 partial sums, in accumulator order
       // (wave, block, element group, lane), 16 bytes per lane per store
       float* w = p.ws + ((size_t)t * WAVES + wave) * (FM * FN * NE * 64);
@@ -457,7 +462,7 @@ void gemm_dense_kernel(DenseArgs p) {
 
     t += G;
     if (t >= p.num_units) break;
-    cur = tile_state<BT, BKB, TRIP_STAGES>(p, t);
+    cur = tile_state<BT, BKB, TRIP_STAGES, SPLITK>(p, t);
   }
   };
   if (loader)
@@ -518,11 +523,11 @@ __global__ __launch_bounds__(256) void gemm_dense_reduce(DenseArgs p) {
 
 }  // namespace
 
-template <int DT, int R, bool KTAIL>
+template <int DT, int R, bool KTAIL, bool SPLITK = false>
 void launch_ring(const DenseArgs& a, int grid, hipStream_t stream) {
   constexpr Ring r = ring_of<DT>(R);
   hipLaunchKernelGGL((gemm_dense_kernel<DT, r.bkb, r.slots, r.waves_n, r.loaders, r.mi, r.bt, r.occ,
-                                        KTAIL>),
+                                        SPLITK, KTAIL>),
                      dim3(grid), dim3(128 * r.waves_n), 0, stream, a);
 }
 
@@ -582,6 +587,21 @@ hipError_t launch_dense(DenseType dt, const DenseArgs& a, int grid, int variant,
   // stage that pads an odd stage count when a loop trip runs two stages.
   const Ring r = dt == kBf16 ? kRingsBf16[variant] : kRingsFp8[variant];
   const bool ktail = a.kbytes % (2 * r.bkb) != 0;
+  if (a.splits > 1) {
+    // split-K work units: a separate instance of the small-tile kernel
+    // (the per-unit K range and the partial-sum store stay out of the
+    // plain kernels' registers)
+    if (variant != kDenseSmallTileVariant) return hipErrorInvalidValue;
+    constexpr int V = kDenseSmallTileVariant;
+    if (dt == kBf16) {
+      if (ktail) launch_ring<kBf16, V, true, true>(a, grid, stream);
+      else launch_ring<kBf16, V, false, true>(a, grid, stream);
+    } else {
+      if (ktail) launch_ring<kFp8, V, true, true>(a, grid, stream);
+      else launch_ring<kFp8, V, false, true>(a, grid, stream);
+    }
+    return hipGetLastError();
+  }
   if (dt == kBf16) {
     if (ktail) launch_variant<kBf16, true>(variant, a, grid, stream);
     else launch_variant<kBf16, false>(variant, a, grid, stream);
