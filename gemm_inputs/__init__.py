@@ -1,4 +1,4 @@
-"""Seeded synthetic operands for the tiled dense GEMM.
+"""Seeded synthetic operands for the tiled dense GEMM and attention forward.
 
 This module is shared by the GPU path's tests and benchmark and by the
 oracle's tests. It holds none of the product's arithmetic: it only draws
@@ -11,6 +11,10 @@ entries i.i.d. N(0, 1) (optionally divided by sqrt(K)); fp8 operands are
 quantized with one fp32 scale per tensor, s = amax/448; the block-scaled
 4-bit operands follow ``fp4_operand``'s recipe. A uses ``seed`` and B uses
 ``seed + 1`` by convention of the callers.
+
+Attention operands (``attention_operands``): Q [B, Hq, Nq, D] and K, V
+[B, Hkv, Nk, D] with i.i.d. N(0, std^2) entries rounded to bf16, Q from
+``seed``, K from ``seed + 1``, V from ``seed + 2``.
 
 Layouts: A is M x K row-major; B is handed over column-major, i.e. as an
 N x K row-major array ("Bt"). Both are K-contiguous.
@@ -176,6 +180,16 @@ def mx_quantize(x: np.ndarray, elem: str):
 def mx_operand(seed: int, rows: int, cols: int, elem: str, std: float = 1.0):
     """Seeded MX operand: (values, E8M0 scales)."""
     return mx_quantize(normal(seed, rows, cols, std), elem)
+
+
+def attention_operands(seed: int, B: int, Hq: int, Hkv: int, Nq: int, Nk: int,
+                       D: int, std_q: float = 1.0, std_kv: float = 1.0):
+    """Seeded bf16 attention inputs (uint16 bits): Q [B, Hq, Nq, D],
+    K and V [B, Hkv, Nk, D]."""
+    q = bf16_operand(seed, B * Hq * Nq, D, std_q).reshape(B, Hq, Nq, D)
+    k = bf16_operand(seed + 1, B * Hkv * Nk, D, std_kv).reshape(B, Hkv, Nk, D)
+    v = bf16_operand(seed + 2, B * Hkv * Nk, D, std_kv).reshape(B, Hkv, Nk, D)
+    return q, k, v
 
 
 # ----------------------------------------------------- structured operands
