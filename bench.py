@@ -212,6 +212,9 @@ def main() -> int:
     ap.add_argument("--summarize-profile", nargs=3,
                     metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--profile-command", default="")
+    ap.add_argument("--with-attn", action="store_true",
+                    help="also time attention forward (tkg_attention_fwd) on its "
+                         "workloads, reported under next_rows, outside the step")
     ap.add_argument("--with-mx", action="store_true",
                     help="also time the MX products (gemm_mxfp4, gemm_mxfp8) on the "
                          "same shape, reported under next_rows, outside the step")
@@ -357,6 +360,10 @@ def main() -> int:
                 "tflops": round(tf, 1), "peak_tflops": PEAK_MX_TFLOPS[k],
                 "frac_of_peak": round(tf / PEAK_MX_TFLOPS[k], 4)}
 
+    if args.with_attn:
+        next_rows = next_rows or {}
+        next_rows.update(time_attention(args, dev, stream))
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(A16, B16, args.cpu_seconds)
@@ -382,6 +389,61 @@ def main() -> int:
         out["next_rows"] = next_rows
     print(json.dumps(out), flush=True)
     return 0
+
+
+# attention forward workloads: (name, B, Hq, Hkv, N, D, causal). The pages
+# fix head dimension 64 / 128, sequence lengths 1024..16384, causal,
+# non-causal and grouped-query; batch and heads are this benchmark's choice
+# (model width 2048 = Hq * D).
+ATTN_WORKLOADS = [
+    ("attn_fwd_d128", 16, 16, 16, 4096, 128, False),
+    ("attn_fwd_d128_causal", 16, 16, 16, 4096, 128, True),
+    ("attn_fwd_d64", 16, 32, 32, 4096, 64, False),
+    ("attn_fwd_d128_gqa8_causal_n16k", 1, 16, 2, 16384, 128, True),
+]
+
+
+def attention_flops(B, Hq, N, D, causal):
+    pairs = N * (N + 1) // 2 if causal else N * N
+    return 4.0 * D * B * Hq * pairs
+
+
+def time_attention(args, dev, stream):
+    import numpy as np
+    import torch
+
+    import gemm_inputs.device as gdev
+    import tiled_dense_gemm_amd as tkg
+
+    rows = {}
+    for name, B, Hq, Hkv, N, D, causal in ATTN_WORKLOADS:
+        Q = gdev.bf16_operand(20, B * Hq * N, D, device=dev).view(B, Hq, N, D)
+        K = gdev.bf16_operand(21, B * Hkv * N, D, device=dev).view(B, Hkv, N, D)
+        V = gdev.bf16_operand(22, B * Hkv * N, D, device=dev).view(B, Hkv, N, D)
+        O = torch.empty_like(Q)
+        fn = lambda: tkg.tkg_attention_fwd(Q, K, V, causal=causal, out=O, stream=stream)
+        for _ in range(args.warmup):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        t = [e0.elapsed_time(e1) for e0, e1 in evs]
+        ms = float(np.mean(t))
+        tf = attention_flops(B, Hq, N, D, causal) / (ms * 1e-3) / 1e12
+        rows[name] = {
+            "workload": "B=%d Hq=%d Hkv=%d N=%d D=%d %s, bf16 N(0,1) inputs"
+                        % (B, Hq, Hkv, N, D, "causal" if causal else "non-causal"),
+            "ms_mean": round(ms, 4), "ms_min": round(float(np.min(t)), 4),
+            "tflops": round(tf, 1), "peak_tflops": PEAK_TFLOPS["bf16"],
+            "frac_of_peak": round(tf / PEAK_TFLOPS["bf16"], 4)}
+        del Q, K, V, O
+        torch.cuda.empty_cache()
+    return rows
 
 
 def cpu_baseline(A16, B16, seconds):

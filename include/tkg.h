@@ -53,7 +53,8 @@ typedef enum tkg_status {
   TKG_ERR_ALIGN = -3,  /* a matrix pointer is not 16-byte aligned           */
   TKG_ERR_LAUNCH = -4, /* the HIP runtime rejected the launch               */
   TKG_ERR_DEVICE = -5, /* no usable HIP device / device query failed        */
-  TKG_ERR_WORKSPACE = -6 /* split-K workspace NULL or smaller than required */
+  TKG_ERR_WORKSPACE = -6, /* split-K workspace NULL or smaller than required */
+  TKG_ERR_VALUE = -7   /* a scalar argument is out of range                 */
 } tkg_status;
 
 /*
@@ -168,6 +169,55 @@ int64_t tkg_gemm_splitk_workspace_size(int dtype, int64_t M, int64_t N,
  * negative tkg_status. */
 int tkg_gemm_splitk_count(int dtype, int64_t M, int64_t N, int64_t K,
                           int splits);
+
+/*
+ * Softmax attention forward, bf16 in and out, fp32 accumulation:
+ *   O[b, h, i, :] = sum_j softmax_j(scale * Q[b, h, i, :] . K[b, g, j, :]) V[b, g, j, :]
+ *   lse[b, h, i]  = log sum_j exp(scale * Q[b, h, i, :] . K[b, g, j, :])
+ * with g = h / (Hq / Hkv) (grouped-query attention; Hkv = Hq is plain
+ * multi-head attention) and, if `causal`, j <= i only. The operation and
+ * its steps are those of page "ThunderKittens: Simple, Fast, and Adorable
+ * AI Kernels", section 3, "PyTorch-Like Operations on Tiles" (Q K^T, row
+ * max, exp, row sum, P V, online rescaling) and "The LCSF Template" (the
+ * finish divides by the normalisation constant); its variants (causal,
+ * non-causal, grouped-query, head dimension 64 or 128) are those of the
+ * same page's section 5, "Attention: Matching FA3 on Forward,
+ * Outperforming on Backward".
+ *   Q:   [B, Hq, Nq, D] bf16, row-major (D contiguous), device memory.
+ *   K,V: [B, Hkv, Nk, D] bf16, row-major, device memory.
+ *   O:   [B, Hq, Nq, D] bf16, written; must not overlap the inputs.
+ *   lse: [B, Hq, Nq] fp32 (natural log), written; may be NULL (not stored).
+ *   D is 64 or 128; Hq % Hkv == 0; causal requires Nq == Nk; Nq * 2D and
+ *   Nk * 2D below 2^31 bytes (one head's rows); scale finite and > 0
+ *   (1/sqrt(D) is the usual choice). The caller owns every buffer; the
+ *   call allocates nothing and is asynchronous on `stream` (a hipStream_t,
+ *   NULL = default stream).
+ * Returns TKG_OK (nothing launched when B, Hq or Nq is 0), TKG_ERR_SHAPE
+ * (unsupported D, negative or inconsistent sizes, Nk = 0 with queries, or
+ * too large), TKG_ERR_VALUE (scale), TKG_ERR_NULL (Q, K, V or O NULL),
+ * TKG_ERR_ALIGN (Q, K, V, O not 16-byte aligned or lse not 4-byte aligned),
+ * TKG_ERR_LAUNCH.
+ */
+int tkg_attention_fwd(const void *Q, const void *K, const void *V, void *O,
+                      float *lse, int64_t B, int64_t Hq, int64_t Hkv,
+                      int64_t Nq, int64_t Nk, int64_t D, float scale,
+                      int causal, void *stream);
+
+/*
+ * LDS addresses of the attention kernel's key/value ring, for host-side
+ * checks of its bank-conflict freedom (no GPU work). Writes 64 values to
+ * out64, one per lane of a wave, for head dimension d (64 or 128):
+ *   kind 0: byte offset in the K tile of K fragment read (kb = i0 < 2,
+ *           ks = i1 < d/16), 16 bytes per lane;
+ *   kind 1: byte offset in the V tile of transposing read (kb = i0 < 2,
+ *           s = i1 < 2, t = i2 < 2, db = i3 < d/32), 8 bytes per lane;
+ *   kind 2, 3: for ring copy piece i0 < d/8 of the K (2) or V (3) tile,
+ *           the byte offset, within the key block, of the global 16 bytes
+ *           each lane copies (lane l lands at LDS byte 1024 i0 + 16 l).
+ * Returns TKG_OK, TKG_ERR_SHAPE or TKG_ERR_NULL.
+ */
+int tkg_attn_lds_offsets(int d, int kind, int i0, int i1, int i2, int i3,
+                         uint32_t *out64);
 
 /* Static, human-readable name of a tkg_status value (never NULL). */
 const char *tkg_status_string(int status);

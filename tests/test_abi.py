@@ -23,7 +23,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("gemm_bf16", "gemm_fp8", "gemm_fp4_blockscaled", "gemm_mxfp4", "gemm_mxfp8",
-              "tkg_status_string", "tkg_gemm_ex"):
+              "tkg_status_string", "tkg_gemm_ex", "tkg_attention_fwd", "tkg_attn_lds_offsets"):
         assert n in names
 
 
@@ -77,6 +77,25 @@ L = tkg.lib
     (lambda: L.gemm_bf16(0, 8, 8, None, None, None, None), S["TKG_OK"]),
     (lambda: L.gemm_fp8(8, 0, 16, None, 1.0, None, 1.0, None, None), S["TKG_OK"]),
     (lambda: L.gemm_fp4_blockscaled(0, 0, 64, None, None, 1.0, None, None, 1.0, None, None), S["TKG_OK"]),
+    # attention forward: (Q, K, V, O, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, stream)
+    (lambda: L.tkg_attention_fwd(A16, B16, C16, A16, None, 1, 2, 2, 8, 8, 96, 0.1, 0, None), S["TKG_ERR_SHAPE"]),
+    (lambda: L.tkg_attention_fwd(A16, B16, C16, A16, None, 1, 3, 2, 8, 8, 64, 0.1, 0, None), S["TKG_ERR_SHAPE"]),
+    (lambda: L.tkg_attention_fwd(A16, B16, C16, A16, None, 1, 2, 0, 8, 8, 64, 0.1, 0, None), S["TKG_ERR_SHAPE"]),
+    (lambda: L.tkg_attention_fwd(A16, B16, C16, A16, None, 1, 2, 2, 8, 9, 64, 0.1, 1, None), S["TKG_ERR_SHAPE"]),
+    (lambda: L.tkg_attention_fwd(A16, B16, C16, A16, None, -1, 2, 2, 8, 8, 64, 0.1, 0, None), S["TKG_ERR_SHAPE"]),
+    (lambda: L.tkg_attention_fwd(A16, B16, C16, A16, None, 1, 2, 2, 8, 0, 64, 0.1, 0, None), S["TKG_ERR_SHAPE"]),
+    (lambda: L.tkg_attention_fwd(A16, B16, C16, A16, None, 1, 2, 2, 1 << 24, 8, 64, 0.1, 0, None), S["TKG_ERR_SHAPE"]),
+    (lambda: L.tkg_attention_fwd(A16, B16, C16, A16, None, 1, 2, 2, 8, 8, 64, 0.0, 0, None), S["TKG_ERR_VALUE"]),
+    (lambda: L.tkg_attention_fwd(A16, B16, C16, A16, None, 1, 2, 2, 8, 8, 64, -1.0, 0, None), S["TKG_ERR_VALUE"]),
+    (lambda: L.tkg_attention_fwd(A16, B16, C16, A16, None, 1, 2, 2, 8, 8, 64, float("inf"), 0, None), S["TKG_ERR_VALUE"]),
+    (lambda: L.tkg_attention_fwd(A16, B16, C16, A16, None, 1, 2, 2, 8, 8, 64, float("nan"), 0, None), S["TKG_ERR_VALUE"]),
+    (lambda: L.tkg_attention_fwd(A16, None, C16, A16, None, 1, 2, 2, 8, 8, 64, 0.1, 0, None), S["TKG_ERR_NULL"]),
+    (lambda: L.tkg_attention_fwd(A16, B16, C16, None, None, 1, 2, 2, 8, 8, 64, 0.1, 0, None), S["TKG_ERR_NULL"]),
+    (lambda: L.tkg_attention_fwd(A16 + 8, B16, C16, A16, None, 1, 2, 2, 8, 8, 64, 0.1, 0, None), S["TKG_ERR_ALIGN"]),
+    (lambda: L.tkg_attention_fwd(A16, B16, C16, A16, C16 + 2, 1, 2, 2, 8, 8, 64, 0.1, 0, None), S["TKG_ERR_ALIGN"]),
+    (lambda: L.tkg_attention_fwd(None, None, None, None, None, 0, 2, 2, 8, 8, 64, 0.1, 0, None), S["TKG_OK"]),
+    (lambda: L.tkg_attention_fwd(None, None, None, None, None, 1, 2, 2, 0, 8, 128, 0.1, 0, None), S["TKG_OK"]),
+    (lambda: L.tkg_attention_fwd(None, None, None, None, None, 1, 0, 0, 8, 8, 64, 0.1, 0, None), S["TKG_OK"]),
 ])
 def test_argument_errors(call, want):
     assert call() == want

@@ -22,7 +22,7 @@ __all__ = [
     "lds_row_bytes", "lib",
     "TkgError", "DTYPE_BF16", "DTYPE_FP8", "DTYPE_FP4_BLOCKSCALED",
     "DTYPE_MXFP4", "DTYPE_MXFP8", "gemm_mxfp4", "gemm_mxfp8",
-    "STATUS", "LIB_PATH",
+    "STATUS", "LIB_PATH", "tkg_attention_fwd", "attn_lds_offsets",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtkg.so")
@@ -31,7 +31,7 @@ DTYPE_BF16, DTYPE_FP8, DTYPE_FP4_BLOCKSCALED = 0, 1, 2
 DTYPE_MXFP4, DTYPE_MXFP8 = 3, 4
 STATUS = {"TKG_OK": 0, "TKG_ERR_NULL": -1, "TKG_ERR_SHAPE": -2,
           "TKG_ERR_ALIGN": -3, "TKG_ERR_LAUNCH": -4, "TKG_ERR_DEVICE": -5,
-          "TKG_ERR_WORKSPACE": -6}
+          "TKG_ERR_WORKSPACE": -6, "TKG_ERR_VALUE": -7}
 
 
 class TkgError(RuntimeError):
@@ -92,10 +92,26 @@ def _load() -> ctypes.CDLL:
     L.tkg_gemm_splitk_workspace_size.restype = i64
     L.tkg_gemm_splitk_count.argtypes = [i32, i64, i64, i64, i32]
     L.tkg_gemm_splitk_count.restype = i32
+    L.tkg_attention_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                    i64, i64, f32, i32, vp]
+    L.tkg_attention_fwd.restype = i32
+    L.tkg_attn_lds_offsets.argtypes = [i32, i32, i32, i32, i32, i32,
+                                       ctypes.POINTER(ctypes.c_uint32)]
+    L.tkg_attn_lds_offsets.restype = i32
     return L
 
 
 lib = _load()
+
+
+def attn_lds_offsets(d: int, kind: int, i0=0, i1=0, i2=0, i3=0):
+    """The 64 per-lane LDS (or copy source) offsets of the attention
+    kernel's ring (``tkg_attn_lds_offsets``); no GPU work."""
+    out = (ctypes.c_uint32 * 64)()
+    st = lib.tkg_attn_lds_offsets(d, kind, i0, i1, i2, i3, out)
+    if st != 0:
+        raise TkgError(st, "tkg_attn_lds_offsets")
+    return list(out)
 
 
 def tkg_status_string(status: int) -> str:
@@ -339,3 +355,55 @@ def tkg_gemm_ex(dtype, M, N, K, A, A_scales, a_scale, Bt, B_scales, b_scale,
                                ptr(A_scales), float(a_scale), ptr(Bt),
                                ptr(B_scales), float(b_scale), ptr(out),
                                _stream_ptr(stream), ctypes.byref(o))
+
+
+def _check_4d(x, name, shape, device):
+    torch = _torch()
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError("%s has dtype %s, expected bfloat16" % (name, x.dtype))
+    if tuple(x.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(x.shape), tuple(shape)))
+    if not x.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if x.device.type != "cuda" or (device is not None and x.device != device):
+        raise ValueError("%s must be on the GPU (%s)" % (name, device))
+
+
+def tkg_attention_fwd(Q, K, V, causal=False, scale=None, out=None, lse=None,
+                      stream=None):
+    """Softmax attention forward (``tkg_attention_fwd``): Q [B, Hq, Nq, D],
+    K and V [B, Hkv, Nk, D] bf16 on the GPU; returns O [B, Hq, Nq, D] bf16.
+    ``lse``: None (not stored), True (allocate and return (O, lse)) or an
+    fp32 [B, Hq, Nq] tensor to fill (then (O, lse) is returned).
+    ``scale`` defaults to 1/sqrt(D)."""
+    import math
+    torch = _torch()
+    if Q.dim() != 4 or K.dim() != 4:
+        raise ValueError("Q, K, V must be [B, H, N, D]")
+    B, Hq, Nq, D = Q.shape
+    Hkv, Nk = K.shape[1], K.shape[2]
+    _check_4d(Q, "Q", (B, Hq, Nq, D), None)
+    _check_4d(K, "K", (B, Hkv, Nk, D), Q.device)
+    _check_4d(V, "V", (B, Hkv, Nk, D), Q.device)
+    if out is None:
+        out = torch.empty((B, Hq, Nq, D), dtype=torch.bfloat16, device=Q.device)
+    else:
+        _check_4d(out, "out", (B, Hq, Nq, D), Q.device)
+    want_lse = lse is not None and lse is not False
+    if lse is True:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=Q.device)
+    if want_lse:
+        if (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Nq)
+                or not lse.is_contiguous() or lse.device != Q.device):
+            raise ValueError("lse must be a contiguous fp32 [B, Hq, Nq] GPU tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D) if D > 0 else 1.0
+    with torch.cuda.device(Q.device):
+        st = lib.tkg_attention_fwd(Q.data_ptr(), K.data_ptr(), V.data_ptr(),
+                                   out.data_ptr(), lse.data_ptr() if want_lse else None,
+                                   B, Hq, Hkv, Nq, Nk, D, float(scale),
+                                   1 if causal else 0, _stream_ptr(stream))
+    _raise(st, "tkg_attention_fwd")
+    return (out, lse) if want_lse else out

@@ -9,6 +9,7 @@
 #include "tkg_kernels.hpp"
 #include "tkg_finish.hpp"
 #include "tkg_layout.hpp"
+#include "tkg_attn_layout.hpp"
 
 namespace {
 
@@ -321,9 +322,89 @@ int run_mx(tkg::MxType fmt, int64_t M, int64_t N, int64_t K, const void* A,
   return e == hipSuccess ? TKG_OK : TKG_ERR_LAUNCH;
 }
 
+int run_attention(const void* Q, const void* K, const void* V, void* O, float* lse,
+                  int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+                  float scale, int causal, void* stream) {
+  if (D != 64 && D != 128) return TKG_ERR_SHAPE;
+  if (B < 0 || Hq < 0 || Hkv < 0 || Nq < 0 || Nk < 0) return TKG_ERR_SHAPE;
+  if (Hq > 0 && (Hkv <= 0 || Hq % Hkv != 0)) return TKG_ERR_SHAPE;
+  if (causal && Nq != Nk) return TKG_ERR_SHAPE;
+  // one buffer resource per head's Q (and K, V) rows: below 2^31 bytes
+  if (Nq * 2 * D > INT32_MAX || Nk * 2 * D > INT32_MAX) return TKG_ERR_SHAPE;
+  const int64_t qblocks = (Nq + tkg::kAttnBlockQ - 1) / tkg::kAttnBlockQ;
+  if (B > INT32_MAX || Hq > INT32_MAX || (B > 0 && Hq * qblocks > INT32_MAX / B))
+    return TKG_ERR_SHAPE;
+  if (B == 0 || Hq == 0 || Nq == 0) return TKG_OK;
+  if (Nk == 0) return TKG_ERR_SHAPE;  // a softmax over no keys
+  if (!(scale > 0.0f) || !(scale <= 3.402823466e38f)) return TKG_ERR_VALUE;
+  if (Q == nullptr || K == nullptr || V == nullptr || O == nullptr) return TKG_ERR_NULL;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+    return TKG_ERR_ALIGN;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return TKG_ERR_DEVICE;
+  tkg::AttnArgs a;
+  a.Q = static_cast<const uint16_t*>(Q);
+  a.K = static_cast<const uint16_t*>(K);
+  a.V = static_cast<const uint16_t*>(V);
+  a.O = static_cast<uint16_t*>(O);
+  a.lse = lse;
+  a.Hq = (int32_t)Hq;
+  a.Hkv = (int32_t)Hkv;
+  a.Nq = (int32_t)Nq;
+  a.Nk = (int32_t)Nk;
+  a.group = (int32_t)(Hq / Hkv);
+  a.qblocks = (int32_t)qblocks;
+  a.num_wg = (int32_t)(B * Hq * qblocks);
+  a.c = (float)((double)scale * 1.4426950408889634);  // scale * log2(e)
+  a.xcd_remap = 1;
+  const hipError_t e = tkg::launch_attn(a, (int)D, causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? TKG_OK : TKG_ERR_LAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
+
+int tkg_attention_fwd(const void* Q, const void* K, const void* V, void* O, float* lse,
+                      int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk, int64_t D,
+                      float scale, int causal, void* stream) {
+  return run_attention(Q, K, V, O, lse, B, Hq, Hkv, Nq, Nk, D, scale, causal, stream);
+}
+
+int tkg_attn_lds_offsets(int d, int kind, int i0, int i1, int i2, int i3, uint32_t* out64) {
+  if (out64 == nullptr) return TKG_ERR_NULL;
+  if ((d != 64 && d != 128) || i0 < 0 || i1 < 0 || i2 < 0 || i3 < 0) return TKG_ERR_SHAPE;
+  const uint32_t D = (uint32_t)d;
+  for (uint32_t lane = 0; lane < 64; ++lane) {
+    switch (kind) {
+      case 0:  // K fragment read (kb = i0 < 2, ks = i1 < D/16)
+        if (i0 >= 2 || i1 >= d / 16) return TKG_ERR_SHAPE;
+        out64[lane] = tkg::attn_k_read(D, lane, (uint32_t)i0, (uint32_t)i1);
+        break;
+      case 1:  // V transposing read (kb < 2, s < 2, t < 2, db < D/32)
+        if (i0 >= 2 || i1 >= 2 || i2 >= 2 || i3 >= d / 32) return TKG_ERR_SHAPE;
+        out64[lane] = tkg::attn_v_read(D, lane, (uint32_t)i0, (uint32_t)i1, (uint32_t)i2,
+                                       (uint32_t)i3);
+        break;
+      case 2:  // ring copy into the K tile: piece i0 < D/8 (1 KiB), LDS byte of lane's chunk
+      case 3: {  // ... into the V tile
+        if (i0 >= d / 8) return TKG_ERR_SHAPE;
+        const uint32_t chunk = (uint32_t)i0 * 64 + lane;
+        const uint32_t row = chunk / (D / 8), cs = chunk % (D / 8);
+        // the global chunk this lane fetches, and where the layout puts it
+        const uint32_t c = cs ^ (kind == 2 ? tkg::attn_k_swz(D, row) : tkg::attn_v_swz(D, row));
+        const uint32_t at = kind == 2 ? tkg::attn_k_offset(D, row, c) : tkg::attn_v_offset(D, row, c);
+        if (at != chunk * 16) return TKG_ERR_SHAPE;  // layout and copy disagree
+        out64[lane] = row * 2 * D + 16 * c;         // global byte offset in the block
+        break;
+      }
+      default:
+        return TKG_ERR_SHAPE;
+    }
+  }
+  return TKG_OK;
+}
 
 int gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
               void* C, void* stream) {
@@ -391,6 +472,7 @@ const char* tkg_status_string(int status) {
     case TKG_ERR_LAUNCH: return "TKG_ERR_LAUNCH: kernel launch failed";
     case TKG_ERR_DEVICE: return "TKG_ERR_DEVICE: no usable HIP device";
     case TKG_ERR_WORKSPACE: return "TKG_ERR_WORKSPACE: split-K workspace missing or too small";
+    case TKG_ERR_VALUE: return "TKG_ERR_VALUE: a scalar argument is out of range";
     default: return "unknown tkg status";
   }
 }

@@ -63,6 +63,26 @@ struct MxArgs {
   int32_t xcd_remap;
 };
 
+// Softmax attention forward: O = softmax(scale * Q K^T) V per (batch, query
+// head), bf16 [B, H, N, D] tensors, D contiguous. Query head h reads
+// key/value head h / group. lse (fp32 [B, Hq, Nq], natural log) may be null.
+struct AttnArgs {
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* V;
+  uint16_t* O;
+  float* lse;
+  int32_t Hq, Hkv, Nq, Nk;
+  int32_t group;       // Hq / Hkv
+  int32_t qblocks;     // query blocks per head
+  int32_t num_wg;      // B * Hq * qblocks
+  float c;             // scale * log2(e)
+  int32_t xcd_remap;
+};
+// query rows per workgroup
+constexpr int kAttnBlockQ = 256;
+hipError_t launch_attn(const AttnArgs& a, int D, bool causal, hipStream_t stream);
+
 // Tile shape shared by the kernels and the host-side argument checks.
 constexpr int kBM = 256;
 constexpr int kBN = 256;
