@@ -290,6 +290,8 @@ def main() -> int:
             for k in extra:
                 extra[k]()
         torch.cuda.synchronize()
+        if args.with_attn:
+            profile_attention(args, dev, stream)
         # calibration copy: 1 GiB read + 1 GiB written
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -408,19 +410,39 @@ def attention_flops(B, Hq, N, D, causal):
     return 4.0 * D * B * Hq * pairs
 
 
+def _attention_inputs(dev, B, Hq, Hkv, N, D):
+    import torch
+
+    import gemm_inputs.device as gdev
+    Q = gdev.bf16_operand(20, B * Hq * N, D, device=dev).view(B, Hq, N, D)
+    K = gdev.bf16_operand(21, B * Hkv * N, D, device=dev).view(B, Hkv, N, D)
+    V = gdev.bf16_operand(22, B * Hkv * N, D, device=dev).view(B, Hkv, N, D)
+    return Q, K, V, torch.empty_like(Q)
+
+
+def profile_attention(args, dev, stream):
+    """`steps` untimed launches of each attention workload (profiler runs)."""
+    import torch
+
+    import tiled_dense_gemm_amd as tkg
+    for name, B, Hq, Hkv, N, D, causal in ATTN_WORKLOADS:
+        Q, K, V, O = _attention_inputs(dev, B, Hq, Hkv, N, D)
+        for _ in range(args.steps):
+            tkg.tkg_attention_fwd(Q, K, V, causal=causal, out=O, stream=stream)
+        torch.cuda.synchronize()
+        del Q, K, V, O
+        torch.cuda.empty_cache()
+
+
 def time_attention(args, dev, stream):
     import numpy as np
     import torch
 
-    import gemm_inputs.device as gdev
     import tiled_dense_gemm_amd as tkg
 
     rows = {}
     for name, B, Hq, Hkv, N, D, causal in ATTN_WORKLOADS:
-        Q = gdev.bf16_operand(20, B * Hq * N, D, device=dev).view(B, Hq, N, D)
-        K = gdev.bf16_operand(21, B * Hkv * N, D, device=dev).view(B, Hkv, N, D)
-        V = gdev.bf16_operand(22, B * Hkv * N, D, device=dev).view(B, Hkv, N, D)
-        O = torch.empty_like(Q)
+        Q, K, V, O = _attention_inputs(dev, B, Hq, Hkv, N, D)
         fn = lambda: tkg.tkg_attention_fwd(Q, K, V, causal=causal, out=O, stream=stream)
         for _ in range(args.warmup):
             fn()

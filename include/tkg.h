@@ -207,11 +207,11 @@ int tkg_attention_fwd(const void *Q, const void *K, const void *V, void *O,
  * LDS addresses of the attention kernel's key/value ring, for host-side
  * checks of its bank-conflict freedom (no GPU work). Writes 64 values to
  * out64, one per lane of a wave, for head dimension d (64 or 128):
- *   kind 0: byte offset in the K tile of K fragment read (kb = i0 < 2,
- *           ks = i1 < d/16), 16 bytes per lane;
- *   kind 1: byte offset in the V tile of transposing read (kb = i0 < 2,
+ *   kind 0: byte offset in the K tile (32 keys) of K fragment read
+ *           (kb = i0 = 0, ks = i1 < d/16), 16 bytes per lane;
+ *   kind 1: byte offset in the V tile of transposing read (kb = i0 = 0,
  *           s = i1 < 2, t = i2 < 2, db = i3 < d/32), 8 bytes per lane;
- *   kind 2, 3: for ring copy piece i0 < d/8 of the K (2) or V (3) tile,
+ *   kind 2, 3: for ring copy piece i0 < d/16 of the K (2) or V (3) tile,
  *           the byte offset, within the key block, of the global 16 bytes
  *           each lane copies (lane l lands at LDS byte 1024 i0 + 16 l).
  * Returns TKG_OK, TKG_ERR_SHAPE or TKG_ERR_NULL.

@@ -12,7 +12,7 @@ import pytest
 
 import tiled_dense_gemm_amd as tkg
 
-BK = 64
+BK = 32  # keys per ring slot
 
 
 def tr_read(image_u16, addrs):
@@ -32,7 +32,7 @@ def tile_image(d, kind):
     """LDS image (uint16 element ids key * d + dim) of one K (kind 2) or V
     (kind 3) tile as the ring copies fill it."""
     img = np.full(BK * d, -1, dtype=np.int64)
-    for piece in range(d // 8):
+    for piece in range(BK * 2 * d // 1024):
         src = tkg.attn_lds_offsets(d, kind, piece)
         for lane in range(64):
             key, byte = divmod(src[lane], 2 * d)
@@ -51,10 +51,10 @@ def test_ring_copies_place_every_element_once(d, kind):
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_k_fragment_reads(d):
-    # MFMA A operand of k-step ks for 32-key block kb: lane l holds key
-    # 32 kb + l % 32, dims 16 ks + 8 (l / 32) .. +7
+    # MFMA A operand of k-step ks: lane l holds key l % 32, dims
+    # 16 ks + 8 (l / 32) .. +7
     img = tile_image(d, 2)
-    for kb in range(2):
+    for kb in range(BK // 32):
         for ks in range(d // 16):
             offs = tkg.attn_lds_offsets(d, 0, kb, ks)
             for lane in range(64):
@@ -72,7 +72,7 @@ def test_v_transposing_reads(d):
     # the score accumulator's elements 8 s .. 8 s + 7 (rows 8 (e / 4) +
     # 4 (l / 32) + e % 4 of the 32x32 block)
     img = tile_image(d, 3)
-    for kb in range(2):
+    for kb in range(BK // 32):
         for s in range(2):
             for db in range(d // 32):
                 for t in range(2):
@@ -94,11 +94,11 @@ def test_argument_errors():
     with pytest.raises(tkg.TkgError):
         tkg.attn_lds_offsets(96, 0, 0, 0)
     with pytest.raises(tkg.TkgError):
-        tkg.attn_lds_offsets(64, 0, 2, 0)
+        tkg.attn_lds_offsets(64, 0, 1, 0)
     with pytest.raises(tkg.TkgError):
         tkg.attn_lds_offsets(128, 1, 0, 0, 0, 4)
     with pytest.raises(tkg.TkgError):
-        tkg.attn_lds_offsets(64, 2, 8)
+        tkg.attn_lds_offsets(64, 2, 4)
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -106,12 +106,12 @@ def test_kernel_address_decomposition(d):
     # the kernel forms every read address from one per-lane base with a
     # compile-time XOR and a compile-time add
     k0 = tkg.attn_lds_offsets(d, 0, 0, 0)
-    for kb in range(2):
+    for kb in range(BK // 32):
         for ks in range(d // 16):
             want = [(k0[l] ^ (32 * ks)) + 32 * kb * 2 * d for l in range(64)]
             assert tkg.attn_lds_offsets(d, 0, kb, ks) == want
     v0 = tkg.attn_lds_offsets(d, 1, 0, 0, 0, 0)
-    for kb in range(2):
+    for kb in range(BK // 32):
         for s in range(2):
             for t in range(2):
                 for db in range(d // 32):

@@ -6,9 +6,13 @@
 // through a multi-stage shared-memory buffer while the queries stay put, the
 // finish step divides by the normalisation constant).
 //
-// Workgroup: 8 waves, 256 query rows of one (batch, head), 32 rows per wave
-// held in registers for the whole kernel. Keys and values stream through a
-// 4-slot LDS ring, 64 keys per slot, loaded by direct global->LDS copies.
+// Workgroup: W waves (4 by default), 32 query rows of one (batch, head) per
+// wave, held in registers for the whole kernel. Keys and values stream
+// through an LDS ring of 32-key slots, loaded by direct global->LDS copies.
+// Two loop forms: one block per iteration (the resident waves hide each
+// other's waits), or a software pipeline that computes the next block's
+// scores on the MFMAs while the VALUs turn the current block's scores into
+// probabilities (launch configurations at the end of the file).
 //
 // Per wave and key block the MFMAs run with the keys as the A operand, so
 // the score accumulator holds S^T: lane l owns query l % 32 and 16 of the
@@ -86,10 +90,13 @@ __device__ __forceinline__ float sum_with_partner(float x) {
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// OCC: waves per SIMD, i.e. OCC * 4 / W workgroups per compute unit.
+template <int D, bool CAUSAL, int W, int SL, int OCC, bool PIPE>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void attn_fwd_kernel(AttnArgs p) {
-  using S = AttnShape<D>;
+  using S = AttnShape<D, W, SL>;
+  static_assert(W % 4 == 0 && (OCC * 4) % W == 0, "whole workgroups per compute unit");
+  static_assert(S::SLOTS * S::STAGE * (OCC * 4 / W) <= 160 * 1024, "LDS of the resident workgroups");
   __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[S::SLOTS * S::STAGE];
   TKG_LDS uint8_t* smem = (TKG_LDS uint8_t*)smem_raw;
   const uint32_t lane = threadIdx.x % 64;
@@ -112,7 +119,8 @@ void attn_fwd_kernel(AttnArgs p) {
   const int wblk = q0w < p.Nq ? (wend + S::BK - 1) / S::BK : 0;  // of this wave
 
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.Q + qoff, (uint32_t)p.Nq * S::ROWB);
-  const bool loads_v = (int)wave * S::NPW >= S::NI / 2;  // waves 0..3 load K, 4..7 V
+  // the first half of the waves copies K tiles, the second half V tiles
+  const bool loads_v = (int)wave * S::NPW >= S::NI / 2;
   const i32x4_t rkv = rsrc_words((loads_v ? p.V : p.K) + kvoff, (uint32_t)p.Nk * S::ROWB);
 
   // ---- ring loads: piece i (1 KiB) of a slot is K (i < NI/2) or V. Lane
@@ -133,9 +141,9 @@ void attn_fwd_kernel(AttnArgs p) {
     for (int j = 0; j < S::NPW; ++j) dma_b128_ring(rkv, dst + j * 1024, dma_off[j] + k0b);
   };
 
-  // ---- LDS read addresses: K fragment (kb, ks) at 32 kb ROWB + (lane_k ^
-  // 32 ks); V read (kb, s, t, db) at TILE + (32 kb + 16 s + 8 t) ROWB +
-  // (lane_v ^ 64 db) (attn_k_read / attn_v_read)
+  // ---- LDS read addresses: K fragment ks at (lane_k ^ 32 ks); V read (s, t,
+  // db) at TILE + (16 s + 8 t) ROWB + (lane_v ^ 64 db) (attn_k_read and
+  // attn_v_read with kb = 0)
   const uint32_t lane_k = attn_k_read(D, lane, 0, 0);
   const uint32_t lane_v = attn_v_read(D, lane, 0, 0, 0, 0);
 
@@ -146,37 +154,40 @@ void attn_fwd_kernel(AttnArgs p) {
   float m = -INFINITY;  // reference max, log2 units (same in lanes l, l ^ 32)
   float l = 0.0f;       // this lane's part of the row sum
   const float c = p.c;
+  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
 
-  auto compute = [&](int blk, uint32_t sbase) {
-    // S^T = K Q^T for two 32-key blocks
-    f32x16_t sacc[2] = {f32x16_t{}, f32x16_t{}};
+  // ---- the steps of one 32-key block. A slot's K tile is at its base, its
+  // V tile TILE bytes after.
+  // S^T = K Q^T
+  auto s_mma = [&](uint32_t sbase, f32x16_t& sa) {
+    sa = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < S::KS; ++ks) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8_t kf =
-            lds_read<bf16x8_t>(smem, sbase + 32 * kb * S::ROWB + (lane_k ^ (32u * ks)));
-        sacc[kb] = mfma_bf16(kf, qf[ks], sacc[kb]);
-      }
+      const bf16x8_t kf = lds_read<bf16x8_t>(smem, sbase + (lane_k ^ (32u * ks)));
+      sa = mfma_bf16(kf, qf[ks], sa);
     }
-    // keys past Nk, and (causal) keys after the query, get -inf
+  };
+  // keys past Nk, and (causal) keys after the query, get -inf; only the
+  // wave's last block can hold such keys
+  auto needs_mask = [&](int blk) {
     const int key0 = blk * S::BK;
-    if (key0 + S::BK > p.Nk || (CAUSAL && key0 + S::BK - 1 > q0w)) {
-      const int q = q0w + (int)lr;
+    return key0 + S::BK > p.Nk || (CAUSAL && key0 + S::BK - 1 > q0w);
+  };
+  auto mask = [&](f32x16_t& sa, int blk) {
+    const int key0 = blk * S::BK, q = q0w + (int)lr;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = key0 + 32 * kb + 8 * (e / 4) + 4 * (int)hh + e % 4;
-          if (key >= p.Nk || (CAUSAL && key > q)) sacc[kb][e] = -INFINITY;
-        }
+    for (int e = 0; e < 16; ++e) {
+      const int key = key0 + 8 * (e / 4) + 4 * (int)hh + e % 4;
+      if (key >= p.Nk || (CAUSAL && key > q)) sa[e] = -INFINITY;
     }
-    // row max of the block (scores are scaled after: c > 0)
-    float mx = sacc[0][0];
+  };
+  // the block's row max in log2 units (scores scale after: c > 0), both
+  // halves of the row (lanes l, l ^ 32); raises the reference max m when
+  // it grows by more than the slack, rescaling O and the row sum
+  auto update_max = [&](const f32x16_t& sa) {
+    float mx = sa[0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sa[e]);
     const float mloc = max_with_partner(mx) * c;
     if (__builtin_amdgcn_ballot_w64(mloc > m + kRescaleSlack)) {
       const float mn = fmaxf(m, mloc);
@@ -188,44 +199,75 @@ void attn_fwd_kernel(AttnArgs p) {
         for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
       m = mn;
     }
-    // probabilities in bf16; P^T operand of k-step s = elements 8s .. 8s+7
-    bf16x8_t pf[2][2];
+  };
+  // probability pair t (scores 2t, 2t+1) in bf16, into the P^T operand of
+  // k-step t / 4 (accumulator elements 8s .. 8s+7), added to the row sum
+  auto prob_pair = [&](const f32x16_t& sa, int t, bf16x8_t (&pk)[2]) {
+    const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[2 * t], c, -m));
+    const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[2 * t + 1], c, -m));
+    const bf16x2_t pr = {(__bf16)e0, (__bf16)e1};
+    pk[t / 4][2 * (t % 4)] = pr[0];
+    pk[t / 4][2 * (t % 4) + 1] = pr[1];
+    l = __builtin_amdgcn_fdot2_f32_bf16(pr, one, l, false);
+    return pr;
+  };
+  // V^T fragments of the block (A operands of its P V MFMAs)
+  auto v_frags = [&](uint32_t sbase, bf16x8_t (&vf)[2][S::DB]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        bf16x8_t x;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          x[j] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][8 * s + j], c, -m));
-        pf[kb][s] = x;
-#pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          const bf16x2_t pair = {x[j], x[j + 1]};
-          const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
-          l = __builtin_amdgcn_fdot2_f32_bf16(pair, one, l, false);
-        }
+      for (int db = 0; db < S::DB; ++db) {
+        const uint32_t a = sbase + S::TILE + 16 * s * S::ROWB + (lane_v ^ (64u * db));
+        const s16x4_t v0 = lds_read_tr16(smem, a);
+        const s16x4_t v1 = lds_read_tr16(smem, a + 8 * S::ROWB);
+        vf[s][db] = __builtin_bit_cast(bf16x8_t,
+                                       __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
       }
-    // O^T += V^T P^T
+  };
+  // O^T += V^T P^T
+  auto pv_mma = [&](const bf16x8_t (&pk)[2], const bf16x8_t (&vf)[2][S::DB]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
+      for (int db = 0; db < S::DB; ++db) o[db] = mfma_bf16(vf[s][db], pk[s], o[db]);
+  };
+  // Pipelined phase 1, in issue order: the K fragment reads of the next
+  // block (four in flight) and the V^T fragment reads of the current one,
+  // then per MFMA of the next block's S^T one or two pairs of the current
+  // block's probabilities ahead of it; the fences keep this order.
+  auto phase1 = [&](uint32_t cur, uint32_t nxt, f32x16_t& sn, const f32x16_t& sc,
+                    bf16x8_t (&pk)[2], bf16x8_t (&vf)[2][S::DB]) {
+    constexpr int PPM = 8 / S::KS;              // probability pairs per MFMA
+    constexpr int KA = S::KS < 4 ? S::KS : 4;   // K reads in flight
+    bf16x8_t kf[S::KS];
 #pragma unroll
-        for (int db = 0; db < S::DB; ++db) {
-          const uint32_t a = sbase + S::TILE + (32 * kb + 16 * s) * S::ROWB + (lane_v ^ (64u * db));
-          const s16x4_t v0 = lds_read_tr16(smem, a);
-          const s16x4_t v1 = lds_read_tr16(smem, a + 8 * S::ROWB);
-          const s16x8_t vv = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[db] = mfma_bf16(__builtin_bit_cast(bf16x8_t, vv), pf[kb][s], o[db]);
-        }
+    for (int i = 0; i < KA; ++i) kf[i] = lds_read<bf16x8_t>(smem, nxt + (lane_k ^ (32u * i)));
+    v_frags(cur, vf);
+    __builtin_amdgcn_sched_barrier(0);
+    sn = f32x16_t{};
+#pragma unroll
+    for (int i = 0; i < S::KS; ++i) {
+#pragma unroll
+      for (int t = PPM * i; t < PPM * (i + 1); ++t) {
+        const bf16x2_t pr = prob_pair(sc, t, pk);
+        // (anchors the pair here: it is only read after the mask branch,
+        // and the compiler would otherwise sink it there)
+        asm volatile("" : "+v"(l) : "v"(pr));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + KA < S::KS)
+        kf[i + KA] = lds_read<bf16x8_t>(smem, nxt + (lane_k ^ (32u * (i + KA))));
+      sn = mfma_bf16(kf[i], qf[i], sn);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
-  // ---- the ring: wait for this wave's copies of block blk, barrier (all
-  // copies landed, everyone done with the slot about to be refilled), issue
-  // block blk + SLOTS - 1, compute blk. Blocks past the last one read
-  // zeros, or keys the workgroup does not use, into slots that are never
-  // read: the prologue issues them unconditionally so the counts are exact.
+  // ---- the ring. At the top of an iteration: wait for this wave's copies
+  // of the blocks the iteration reads, barrier (every copy landed; every
+  // wave is done with the slot about to be refilled, block blk - 1's),
+  // issue block blk + SLOTS - 1. Blocks past the last one read zeros, or
+  // keys the workgroup does not use, into slots that are never read: the
+  // prologue issues them unconditionally so the counts are exact.
   issue(0, 0);
   // Q^T fragments (B operand): lane l holds query q0w + l % 32, d =
   // 16 ks + 8 (l / 32) .. +7; rows past Nq read zeros. They arrive with
@@ -243,15 +285,68 @@ void attn_fwd_kernel(AttnArgs p) {
   for (int ks = 0; ks < S::KS; ++ks) asm volatile("" : "+v"(qf[ks]));
 #pragma unroll
   for (int st = 1; st < S::SLOTS - 1; ++st) issue(st, st);
-  for (int blk = 0; blk < nblk; ++blk) {
+  // blocks blk + AHEAD + 1 .. blk + SLOTS - 2 may still be in flight when
+  // iteration blk starts (the pipelined loop also reads block blk + 1)
+  constexpr int AHEAD = PIPE ? 1 : 0;
+  auto top = [&](int blk) {
     if (blk + S::SLOTS - 2 < nblk)
-      wait_vmcnt<(S::SLOTS - 2) * S::NPW>();
+      wait_vmcnt<(S::SLOTS - 2 - AHEAD) * S::NPW>();
     else
       wait_vmcnt<0>();
     lds_barrier();
     const int nx = blk + S::SLOTS - 1;
     if (nx < nblk) issue(nx, nx % S::SLOTS);
-    if (blk < wblk) compute(blk, (uint32_t)(blk % S::SLOTS) * S::STAGE);
+  };
+
+  if constexpr (!PIPE) {
+    // one block per iteration: scores, max, probabilities, P V; the other
+    // waves on the SIMD fill each wave's dependency waits
+    for (int blk = 0; blk < nblk; ++blk) {
+      top(blk);
+      if (blk < wblk) {
+        const uint32_t cur = (uint32_t)(blk % S::SLOTS) * S::STAGE;
+        f32x16_t sc;
+        bf16x8_t pk[2], vf[2][S::DB];
+        s_mma(cur, sc);
+        if (needs_mask(blk)) mask(sc, blk);
+        update_max(sc);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) prob_pair(sc, t, pk);
+        v_frags(cur, vf);
+        pv_mma(pk, vf);
+      }
+    }
+  } else {
+    // Software pipeline: iteration blk computes block blk + 1's scores on
+    // the MFMAs while the VALUs turn block blk's scores into
+    // probabilities (phase1), then accumulates block blk's P V while the
+    // VALUs take block blk + 1's max. On a wave's last block, block
+    // blk + 1 lies wholly past its keys (past Nk, or after every query of
+    // the wave): its scores are masked to -inf, which leaves the max alone,
+    // so the last iteration needs no other path.
+    auto step = [&](int blk, f32x16_t& sc, f32x16_t& sn) {
+      top(blk);
+      if (blk < wblk) {
+        const uint32_t cur = (uint32_t)(blk % S::SLOTS) * S::STAGE;
+        const uint32_t nxt = (uint32_t)((blk + 1) % S::SLOTS) * S::STAGE;
+        bf16x8_t pk[2], vf[2][S::DB];
+        phase1(cur, nxt, sn, sc, pk, vf);
+        if (needs_mask(blk + 1)) mask(sn, blk + 1);
+        pv_mma(pk, vf);
+        update_max(sn);
+      }
+    };
+    lds_barrier();  // block 0 landed in every wave
+    f32x16_t sa, sb;  // scores of even / odd blocks
+    if (wblk > 0) {
+      s_mma(0, sa);
+      if (needs_mask(0)) mask(sa, 0);
+      update_max(sa);
+    }
+    for (int blk = 0; blk < nblk; blk += 2) {
+      step(blk, sa, sb);
+      if (blk + 1 < nblk) step(blk + 1, sb, sa);
+    }
   }
 
   // ---- finish: divide by the row sum, store bf16 rows and the log-sum-exp
@@ -273,18 +368,39 @@ void attn_fwd_kernel(AttnArgs p) {
   }
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch_one(const AttnArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL>), dim3(a.num_wg), dim3(64 * AttnShape<D>::WAVES),
-                     0, stream, a);
-  return hipGetLastError();
-}
+// Launch configurations: (waves, ring slots, waves per SIMD, pipelined).
+// Measured on the B=16 N=4096 workloads (TFLOP/s, non-causal / causal):
+// D = 128: (4, 4, 2, pipelined) 1080 / 933, (4, 3, 3, plain) 1020 / 930,
+// (8, 8, 2, pipelined) 993 / 853; D = 64: (4, 4, 4, plain) 950,
+// (8, 8, 2, pipelined) 810, (4, 4, 2, pipelined) 839. Four waves per
+// workgroup (128 query rows) balance causal work better than eight; at
+// D = 64 the softmax outweighs the MFMAs and more resident waves win.
+#ifndef TKG_ATTN_CFG128
+#define TKG_ATTN_CFG128 4, 4, 2, true
+#endif
+#ifndef TKG_ATTN_CFG64
+#define TKG_ATTN_CFG64 4, 4, 4, false
+#endif
+template <int D, int W, int SL, int OCC, bool PIPE>
+struct AttnCfg {
+  static constexpr int BQ = AttnShape<D, W, SL>::BQ;
+  template <bool CAUSAL>
+  static hipError_t launch(const AttnArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, W, SL, OCC, PIPE>), dim3(a.num_wg),
+                       dim3(64 * W), 0, stream, a);
+    return hipGetLastError();
+  }
+};
+using Cfg128 = AttnCfg<128, TKG_ATTN_CFG128>;
+using Cfg64 = AttnCfg<64, TKG_ATTN_CFG64>;
 
 }  // namespace
 
+int attn_block_q(int D) { return D == 64 ? Cfg64::BQ : D == 128 ? Cfg128::BQ : 0; }
+
 hipError_t launch_attn(const AttnArgs& a, int D, bool causal, hipStream_t stream) {
-  if (D == 64) return causal ? launch_one<64, true>(a, stream) : launch_one<64, false>(a, stream);
-  if (D == 128) return causal ? launch_one<128, true>(a, stream) : launch_one<128, false>(a, stream);
+  if (D == 64) return causal ? Cfg64::launch<true>(a, stream) : Cfg64::launch<false>(a, stream);
+  if (D == 128) return causal ? Cfg128::launch<true>(a, stream) : Cfg128::launch<false>(a, stream);
   return hipErrorInvalidValue;
 }
 

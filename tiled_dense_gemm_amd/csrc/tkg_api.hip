@@ -331,7 +331,8 @@ int run_attention(const void* Q, const void* K, const void* V, void* O, float* l
   if (causal && Nq != Nk) return TKG_ERR_SHAPE;
   // one buffer resource per head's Q (and K, V) rows: below 2^31 bytes
   if (Nq * 2 * D > INT32_MAX || Nk * 2 * D > INT32_MAX) return TKG_ERR_SHAPE;
-  const int64_t qblocks = (Nq + tkg::kAttnBlockQ - 1) / tkg::kAttnBlockQ;
+  const int64_t bq = tkg::attn_block_q((int)D);
+  const int64_t qblocks = (Nq + bq - 1) / bq;
   if (B > INT32_MAX || Hq > INT32_MAX || (B > 0 && Hq * qblocks > INT32_MAX / B))
     return TKG_ERR_SHAPE;
   if (B == 0 || Hq == 0 || Nq == 0) return TKG_OK;
@@ -378,18 +379,18 @@ int tkg_attn_lds_offsets(int d, int kind, int i0, int i1, int i2, int i3, uint32
   const uint32_t D = (uint32_t)d;
   for (uint32_t lane = 0; lane < 64; ++lane) {
     switch (kind) {
-      case 0:  // K fragment read (kb = i0 < 2, ks = i1 < D/16)
-        if (i0 >= 2 || i1 >= d / 16) return TKG_ERR_SHAPE;
+      case 0:  // K fragment read (kb = i0 = 0: a slot holds 32 keys, ks = i1 < D/16)
+        if (i0 >= 1 || i1 >= d / 16) return TKG_ERR_SHAPE;
         out64[lane] = tkg::attn_k_read(D, lane, (uint32_t)i0, (uint32_t)i1);
         break;
-      case 1:  // V transposing read (kb < 2, s < 2, t < 2, db < D/32)
-        if (i0 >= 2 || i1 >= 2 || i2 >= 2 || i3 >= d / 32) return TKG_ERR_SHAPE;
+      case 1:  // V transposing read (kb = 0, s < 2, t < 2, db < D/32)
+        if (i0 >= 1 || i1 >= 2 || i2 >= 2 || i3 >= d / 32) return TKG_ERR_SHAPE;
         out64[lane] = tkg::attn_v_read(D, lane, (uint32_t)i0, (uint32_t)i1, (uint32_t)i2,
                                        (uint32_t)i3);
         break;
-      case 2:  // ring copy into the K tile: piece i0 < D/8 (1 KiB), LDS byte of lane's chunk
+      case 2:  // ring copy into the K tile: piece i0 < D/16 (1 KiB of 32 rows)
       case 3: {  // ... into the V tile
-        if (i0 >= d / 8) return TKG_ERR_SHAPE;
+        if (i0 >= d / 16) return TKG_ERR_SHAPE;
         const uint32_t chunk = (uint32_t)i0 * 64 + lane;
         const uint32_t row = chunk / (D / 8), cs = chunk % (D / 8);
         // the global chunk this lane fetches, and where the layout puts it

@@ -2,7 +2,7 @@
 // device: the library reports the addresses so the bank model can check
 // them without a GPU).
 //
-// A ring slot holds one block of BK = 64 keys: the K tile, then the V tile,
+// A ring slot holds one block of BK = 32 keys: the K tile, then the V tile,
 // each BK rows of D bf16 (ROWB = 2D bytes), a row's 16-byte chunk c stored
 // at chunk c XOR f(row):
 // * K is read 16 bytes per lane (one MFMA A fragment: 8 consecutive d of
@@ -20,24 +20,27 @@
 
 namespace tkg {
 
-template <int D>
+// Kernel shape: W waves of 32 query rows each (BQ = 32 W rows per
+// workgroup), SLOTS ring slots of BK = 32 keys.
+template <int D, int W, int SL>
 struct AttnShape {
   static_assert(D == 64 || D == 128, "head dimension 64 or 128");
-  static constexpr int WAVES = 8;        // waves per workgroup
+  static constexpr int WAVES = W;        // waves per workgroup
   static constexpr int QW = 32;          // query rows per wave
   static constexpr int BQ = WAVES * QW;  // query rows per workgroup
-  static constexpr int BK = 64;          // keys per ring slot
+  static constexpr int BK = 32;          // keys per ring slot
   static constexpr int ROWB = 2 * D;     // bytes per K/V row
   static constexpr int CPR = D / 8;      // 16-byte chunks per row
   static constexpr int RPL = 256 / ROWB; // rows per 256-byte line
   static constexpr int TILE = BK * ROWB; // bytes of K (or V) per slot
   static constexpr int STAGE = 2 * TILE; // bytes per slot
-  static constexpr int SLOTS = 4;
+  static constexpr int SLOTS = SL;
   static constexpr int NI = STAGE / 1024;  // 1 KiB DMA pieces per slot
   static constexpr int NPW = NI / WAVES;   // pieces per wave
-  static constexpr int KS = D / 16;        // k-steps of Q K^T
-  static constexpr int DB = D / 32;        // 32-row blocks of O^T
+  static constexpr int KS = D / 16;        // k-steps of Q K^T (its MFMAs per block)
+  static constexpr int DB = D / 32;        // 32-row blocks of O^T (2 DB MFMAs per block)
   static_assert(NPW * WAVES == NI && (NI / 2) % NPW == 0, "a wave loads K or V, not both");
+  static_assert(SLOTS >= 3, "ring of three slots at least");
 };
 
 TKG_HD constexpr uint32_t attn_rpl(uint32_t d) { return 256 / (2 * d); }
@@ -56,7 +59,7 @@ TKG_HD constexpr uint32_t attn_v_offset(uint32_t d, uint32_t row, uint32_t c) {
 }
 
 // Lane `lane`'s read of K fragment (kb, ks): key row 32 kb + lane % 32,
-// chunk 2 ks + lane / 32.
+// chunk 2 ks + lane / 32 (a 32-key slot uses kb = 0).
 TKG_HD constexpr uint32_t attn_k_read(uint32_t d, uint32_t lane, uint32_t kb, uint32_t ks) {
   return attn_k_offset(d, 32 * kb + lane % 32, 2 * ks + lane / 32);
 }

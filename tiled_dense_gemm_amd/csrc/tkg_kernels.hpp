@@ -79,8 +79,8 @@ struct AttnArgs {
   float c;             // scale * log2(e)
   int32_t xcd_remap;
 };
-// query rows per workgroup
-constexpr int kAttnBlockQ = 256;
+// query rows per workgroup for head dimension D (0: unsupported D)
+int attn_block_q(int D);
 hipError_t launch_attn(const AttnArgs& a, int D, bool causal, hipStream_t stream);
 
 // Tile shape shared by the kernels and the host-side argument checks.
