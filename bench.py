@@ -36,13 +36,25 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4_blockscaled": 2500.0}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_8192.json")
 
 
-def kernel_source_hash() -> str:
+# sources only the attention kernel is built from
+ATTN_SOURCES = ("attn_fwd.hip", "tkg_attn_layout.hpp")
+
+
+def kernel_source_hash(family: str = "gemm") -> str:
+    """Hash of the kernel sources a family is built from (the GEMM family:
+    every source but the attention-only files; attention: every source but
+    the GEMM kernels)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tiled_dense_gemm_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp")):
-            h.update(name.encode())
-            h.update(open(os.path.join(csrc, name), "rb").read())
+        if not name.endswith((".hip", ".hpp")):
+            continue
+        if family == "gemm" and name in ATTN_SOURCES:
+            continue
+        if family == "attention" and name.startswith("gemm_"):
+            continue
+        h.update(name.encode())
+        h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -56,6 +68,22 @@ def measured_traffic(kernel: str):
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
     k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+ATTN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
+
+
+def measured_attention_traffic(name: str):
+    """HBM bytes per launch of an attention workload from the committed
+    counter runs, or None when they were taken on other kernel sources."""
+    try:
+        rec = json.load(open(ATTN_TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash("attention"):
+        return None
+    k = rec.get("workloads", {}).get(name)
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
@@ -200,6 +228,133 @@ def summarize_profile(trace_dir: str, fetch_dir: str, write_dir: str,
     return 0
 
 
+def _attention_workload(kname: str, grid_x: int, wg_x: int):
+    """The ATTN_WORKLOADS entry a traced attention dispatch ran, from its
+    kernel instance (head dimension, causal) and grid size."""
+    import re
+    m = re.search(r"attn_fwd_kernel<(\d+), (true|false)", kname)
+    if not m or wg_x <= 0:
+        return None
+    D, causal = int(m.group(1)), m.group(2) == "true"
+    bq = 32 * (wg_x // 64)
+    for name, B, Hq, Hkv, N, d, c in ATTN_WORKLOADS:
+        if d == D and c == causal and B * Hq * ((N + bq - 1) // bq) * wg_x == grid_x:
+            return name
+    return None
+
+
+def summarize_attention_profile(trace_dir, fetch_dir, write_dir, out_md, out_json, command):
+    """Committed summary of the attention kernels: durations from the
+    --kernel-trace run of `bench.py --with-attn`, HBM bytes from the
+    FETCH_SIZE / WRITE_SIZE runs of `bench.py --profile --with-attn`
+    (calibrated by the 1 GiB copies at its end), other counter passes from
+    sibling directories."""
+    import csv
+    import glob
+    import statistics
+
+    def rows(d, pattern):
+        out = []
+        for f in glob.glob(os.path.join(d, "**", pattern), recursive=True):
+            out += list(csv.DictReader(open(f)))
+        return out
+
+    def key(r):
+        gx = int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0)
+        wx = int(r.get("Workgroup_Size_X") or r.get("Workgroup_Size") or 0)
+        return _attention_workload(r["Kernel_Name"], gx, wx)
+
+    dur = {}
+    for r in rows(trace_dir, "*kernel_trace.csv"):
+        k = key(r)
+        if k:
+            dur.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+
+    def counter(d, cname):
+        per, cal = {}, []
+        for r in rows(d, "*counter_collection.csv"):
+            if r["Counter_Name"] != cname:
+                continue
+            v = float(r["Counter_Value"])
+            k = key(r) if "attn_fwd" in r["Kernel_Name"] else None
+            if k:
+                per.setdefault(k, []).append(v)
+            elif "copy" in r["Kernel_Name"] and v > 512 * 1024:
+                cal.append(v)
+        return per, cal
+
+    fetch, fcal = counter(fetch_dir, "FETCH_SIZE")
+    write, wcal = counter(write_dir, "WRITE_SIZE")
+    gib_kib = 1024.0 * 1024.0
+    ff = gib_kib / statistics.mean(fcal) if fcal else None
+    fw = gib_kib / statistics.mean(wcal) if wcal else None
+    rec = {"kernel_source_hash": kernel_source_hash("attention"),
+           "copy_calibration": {"fetch_factor": ff, "write_factor": fw, "copy_bytes": 1 << 30},
+           "command": command, "workloads": {}}
+    lines = ["# Attention forward kernels on one MI355X (rocprofv3)", "",
+             "Produced by:", "", "```", command, "```", "",
+             "Algorithmic flops: 4 D per visible (query, key) pair (Q K^T and P V); "
+             "compulsory bytes: Q, K, V read once and O written once (bf16).", "",
+             "| workload | launches | mean us | min us | TFLOP/s (mean) | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes/launch (calibrated) | compulsory bytes | ratio |",
+             "|---|---|---|---|---|---|---|---|---|---|"]
+    for name, B, Hq, Hkv, N, D, causal in ATTN_WORKLOADS:
+        d = dur.get(name, [])
+        fk = statistics.mean(fetch[name]) if fetch.get(name) else None
+        wk = statistics.mean(write[name]) if write.get(name) else None
+        hbm = (fk * 1024 * ff + wk * 1024 * fw) if (fk and wk and ff and fw) else None
+        algo = 2 * D * (2 * B * Hq * N + 2 * B * Hkv * N)
+        flops = attention_flops(B, Hq, N, D, causal)
+        mean_us = statistics.mean(d) if d else None
+        rec["workloads"][name] = {"launches": len(d), "mean_us": mean_us,
+                                  "min_us": min(d) if d else None,
+                                  "tflops": flops / (mean_us * 1e-6) / 1e12 if d else None,
+                                  "fetch_kib": fk, "write_kib": wk,
+                                  "hbm_bytes_per_launch": hbm, "compulsory_bytes": algo}
+        lines.append("| %s | %d | %s | %s | %s | %s | %s | %s | %d | %s |" % (
+            name, len(d), "%.1f" % mean_us if d else "-", "%.1f" % min(d) if d else "-",
+            "%.1f" % (flops / (mean_us * 1e-6) / 1e12) if d else "-",
+            "%.0f" % fk if fk else "-", "%.0f" % wk if wk else "-",
+            "%.3g" % hbm if hbm else "-", algo, "%.2f" % (hbm / algo) if hbm else "-"))
+    lines += ["", "Copy calibration: FETCH_SIZE factor %s, WRITE_SIZE factor %s." % (
+        "%.4f" % ff if ff else "-", "%.4f" % fw if fw else "-"), ""]
+    extra = {}
+    parent = os.path.dirname(os.path.abspath(trace_dir))
+    for dd in sorted(glob.glob(os.path.join(parent, "*"))):
+        if os.path.abspath(dd) in (os.path.abspath(fetch_dir), os.path.abspath(write_dir)):
+            continue
+        for r in rows(dd, "*counter_collection.csv"):
+            k = key(r) if "attn_fwd" in r["Kernel_Name"] else None
+            if k:
+                extra.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(
+                    float(r["Counter_Value"]))
+    if extra:
+        names = sorted({c for k in extra for c in extra[k]})
+        ks = [w[0] for w in ATTN_WORKLOADS if w[0] in extra]
+        lines += ["Other counters (mean per launch, summed over the device):", "",
+                  "| counter | " + " | ".join(ks) + " |", "|---" * (len(ks) + 1) + "|"]
+        for c in names:
+            lines.append("| %s | " % c + " | ".join(
+                "%.4g" % statistics.mean(extra[k][c]) if c in extra[k] else "-" for k in ks) + " |")
+        lines.append("")
+        for k in ks:
+            e = extra[k]
+            if "SQ_LDS_BANK_CONFLICT" in e and "SQ_LDS_IDX_ACTIVE" in e:
+                rec["workloads"][k]["lds_bank_conflict_over_active"] = (
+                    statistics.mean(e["SQ_LDS_BANK_CONFLICT"]) /
+                    max(1.0, statistics.mean(e["SQ_LDS_IDX_ACTIVE"])))
+            if "GRBM_GUI_ACTIVE" in e and rec["workloads"][k]["mean_us"]:
+                # GPU-active cycles per XCD over the launch: the average clock
+                ghz = statistics.mean(e["GRBM_GUI_ACTIVE"]) / 8.0 / (rec["workloads"][k]["mean_us"] * 1e3)
+                rec["workloads"][k]["clock_ghz_estimate"] = ghz
+                lines.append("%s: about %.2f GHz over the launch (GRBM_GUI_ACTIVE per XCD / "
+                             "traced duration)" % (k, ghz))
+        lines.append("")
+    open(out_md, "w").write("\n".join(lines))
+    json.dump(rec, open(out_json, "w"), indent=1)
+    print("\n".join(lines))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,6 +367,8 @@ def main() -> int:
     ap.add_argument("--summarize-profile", nargs=3,
                     metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--profile-command", default="")
+    ap.add_argument("--summarize-attn-profile", nargs=3,
+                    metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--with-attn", action="store_true",
                     help="also time attention forward (tkg_attention_fwd) on its "
                          "workloads, reported under next_rows, outside the step")
@@ -226,6 +383,12 @@ def main() -> int:
             os.path.join(ROOT, "profiles", "gemm_kernels_%d.md" % args.size),
             TRAFFIC_FILE if args.size == 8192 else
             os.path.join(ROOT, "profiles", "traffic_%d.json" % args.size),
+            args.profile_command)
+
+    if args.summarize_attn_profile:
+        return summarize_attention_profile(
+            *args.summarize_attn_profile,
+            os.path.join(ROOT, "profiles", "attention_fwd.md"), ATTN_TRAFFIC_FILE,
             args.profile_command)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -462,7 +625,8 @@ def time_attention(args, dev, stream):
                         % (B, Hq, Hkv, N, D, "causal" if causal else "non-causal"),
             "ms_mean": round(ms, 4), "ms_min": round(float(np.min(t)), 4),
             "tflops": round(tf, 1), "peak_tflops": PEAK_TFLOPS["bf16"],
-            "frac_of_peak": round(tf / PEAK_TFLOPS["bf16"], 4)}
+            "frac_of_peak": round(tf / PEAK_TFLOPS["bf16"], 4),
+            "hbm_bytes_per_launch": measured_attention_traffic(name)}
         del Q, K, V, O
         torch.cuda.empty_cache()
     return rows
