@@ -65,7 +65,8 @@ def test_kernel_fragment_reads_measured_conflict_free(dtype):
 
 
 def test_unswizzled_reads_measured_conflicting():
-    un = [p for p in PROBE["patterns"] if " unswizzled " in p["name"]]
+    un = [p for p in PROBE["patterns"] if " unswizzled " in p["name"]
+          and not p["name"].startswith("4-bit values 16x16x32")]
     assert len(un) == 112
     assert all(p["degree"] >= 4 for p in un)
 
@@ -116,6 +117,15 @@ def test_swizzle_permutes_chunks_of_each_row():
 def test_fp4_scale_reads_measured_conflict_free():
     m = measured(bm.scale_read_pattern(8), 8)
     assert m is not None and m["degree"] == 1
+
+
+def test_fp4_16x16_reads_measured_conflicting():
+    # the 16x16 fragment reads (row l % 16, chunk l / 16) measure 2-way on
+    # the 64-byte-row swizzle; the 4-bit kernel keeps 32x32 blocks
+    for kind in ("swizzled", "unswizzled"):
+        pats = [p for p in PROBE["patterns"]
+                if p["name"].startswith("4-bit values 16x16x32 %s " % kind)]
+        assert len(pats) == 16 and all(p["degree"] == 2 for p in pats)
 
 
 def test_mx_superstage_scale_reads_measured_conflict_free():

@@ -86,3 +86,4 @@ def scale_read_pattern(row_bytes: int = 8) -> List[int]:
     """LDS addresses of the 4-bit kernel's block-scale reads: lane l reads
     the 8 bytes of row l % 32 (rows `row_bytes` apart)."""
     return [(l % 32) * row_bytes for l in range(64)]
+

@@ -132,6 +132,8 @@ int main() {
           [&](unsigned l) { return bytes * (l & ~d) + ((l & d) ? 4096u : 0u); });
   }
   add("b64 4-bit block scales (row l%32, 8-byte rows)", 8, [](unsigned l) { return 8 * (l % 32); });
+  add("b32 4-bit block scale word (row l%16, word l/32 of 8-byte rows)", 4,
+      [](unsigned l) { return 8 * (l % 16) + 4 * (l / 32); });
   add("b128 MX superstage scale rows (row l%32, 16-byte rows)", 16, [](unsigned l) { return 16 * (l % 32); });
   add("b32 MX scale word of 16-byte rows (row l%32)", 4, [](unsigned l) { return 16 * (l % 32); });
   add("b64 MX scale pair of 16-byte rows (row l%32)", 8, [](unsigned l) { return 16 * (l % 32); });
@@ -178,6 +180,7 @@ int main() {
       for (unsigned f = 0; f < 16; ++f) pats.push_back(fragment("fp8 16x16x128", 128, 16, 8, 0, q, f, on));
     for (unsigned s = 0; s < 2; ++s)
       for (unsigned f = 0; f < 8; ++f) pats.push_back(fragment("4-bit values", 64, 32, 2, s, 0, f, on));
+    for (unsigned f = 0; f < 16; ++f) pats.push_back(fragment("4-bit values 16x16x32", 64, 16, 4, 0, 0, f, on));
   }
   // linear swizzle search on the 16x16 pattern (rows 0..15, chunks 0..3)
   for (unsigned A = 0; A < 4096; ++A)
