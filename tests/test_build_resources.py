@@ -23,6 +23,7 @@ DEFAULT_PATHS = [
     "gemm_dense_kernelILi1ELi128ELi4ELi2ELi0ELi16ELi128ELi2ELb",     # fp8 128x128 (+split-K)
     "gemm_fp4_kernelILi2E",
     "gemm_mx_kernel",
+    "attn_fwd_kernel",
 ]
 
 
@@ -44,7 +45,22 @@ def test_default_kernels_barely_spill(report):
 
 def test_every_kernel_fits_the_lds(report):
     for k, v in report.items():
-        if "gemm" in k:
+        if "gemm" in k or "attn" in k:
             assert v["LDS Size"] <= 160 * 1024, (k, v)
         if "ELi128ELi2ELb" in k:   # two workgroups per CU share its LDS
             assert v["LDS Size"] <= 80 * 1024, (k, v)
+
+
+def test_attention_occupancy(report):
+    # (D, waves per workgroup, slots, waves per SIMD): the registers allow
+    # the waves per SIMD the configuration asks for, and the LDS of the
+    # workgroups resident on a CU fits
+    import re
+    hits = {k: v for k, v in report.items() if "attn_fwd_kernel" in k}
+    assert len(hits) == 4
+    for k, v in hits.items():
+        m = re.search(r"attn_fwd_kernelILi(\d+)ELb(\d)ELi(\d+)ELi(\d+)ELi(\d+)ELb(\d)E", k)
+        assert m, k
+        waves, occ = int(m.group(3)), int(m.group(5))
+        assert v["Occupancy"] >= occ, (k, v)
+        assert v["LDS Size"] * (occ * 4 // waves) <= 160 * 1024, (k, v)
