@@ -371,11 +371,17 @@ def main() -> int:
                     metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--with-attn", action="store_true",
                     help="also time attention forward (tkg_attention_fwd) on its "
-                         "workloads, reported under next_rows, outside the step")
+                         "workloads, reported under next_rows, outside the step "
+                         "(the default; kept for older command lines)")
     ap.add_argument("--with-mx", action="store_true",
                     help="also time the MX products (gemm_mxfp4, gemm_mxfp8) on the "
-                         "same shape, reported under next_rows, outside the step")
+                         "same shape, reported under next_rows, outside the step "
+                         "(the default; kept for older command lines)")
+    ap.add_argument("--no-attn", action="store_true", help="skip the attention rows")
+    ap.add_argument("--no-mx", action="store_true", help="skip the MX rows")
     args = ap.parse_args()
+    args.with_attn = not args.no_attn
+    args.with_mx = not args.no_mx
 
     if args.summarize_profile:
         return summarize_profile(
