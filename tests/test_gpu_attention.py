@@ -96,8 +96,9 @@ def test_peaked_scores(dev, D, causal):
 @pytest.mark.parametrize("rising", [True, False])
 def test_row_max_moving_every_block(dev, rising):
     # scores rising (falling) by 0.25 per key with scale 1: the row max
-    # jumps by 16 every 64-key block, past the kernel's rescale slack (or
-    # never moves after the first block)
+    # jumps by 0.25 * 32 * log2(e) = 11.5 (log2 units) every 32-key block,
+    # past the kernel's rescale slack of 8 (or never moves after the first
+    # block)
     D, N = 64, 512
     q = np.zeros((1, 1, 32, D))
     q[..., 0] = 1.0
@@ -156,11 +157,13 @@ def test_empty_and_rejected(dev):
 # ------------------------------------------------ full-size, sampled rows
 
 FULL = [
-    # the measured workloads: B, Hq, Hkv, N, D, causal
+    # the measured workloads (B, Hq, Hkv, N, D, causal) and the long end of
+    # the pages' sequence range at D = 64
     (16, 16, 16, 4096, 128, False),
     (16, 16, 16, 4096, 128, True),
     (4, 32, 32, 4096, 64, False),
     (1, 16, 2, 16384, 128, True),
+    (1, 32, 4, 16384, 64, True),
 ]
 
 
@@ -188,3 +191,22 @@ def test_full_size_sampled_rows(dev, B, Hq, Hkv, N, D, causal):
             _check(Gf[i][None, None, None], Gl[i][None, None, None],
                    Qf[i][None, None, None], Kf[:, :, :n], Vf[:, :, :n], False,
                    what=(b, h, int(i)))
+
+
+def test_full_size_more_keys_than_queries(dev):
+    # 512 queries against 16384 keys (a prefill chunk against its context)
+    B, Hq, Hkv, Nq, Nk, D = 2, 8, 2, 512, 16384, 128
+    Q = gi.device.bf16_operand(211, B * Hq * Nq, D, device=dev).view(B, Hq, Nq, D)
+    K = gi.device.bf16_operand(212, B * Hkv * Nk, D, device=dev).view(B, Hkv, Nk, D)
+    V = gi.device.bf16_operand(213, B * Hkv * Nk, D, device=dev).view(B, Hkv, Nk, D)
+    O, lse = tkg.tkg_attention_fwd(Q, K, V, lse=True)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (1, 7)):
+        kv = h // (Hq // Hkv)
+        Kf = decode_bf16(to_numpy_u16(K[b, kv]))[None, None]
+        Vf = decode_bf16(to_numpy_u16(V[b, kv]))[None, None]
+        rows = [0, 1, 127, 128, 511]
+        Qf = decode_bf16(to_numpy_u16(Q[b, h, rows]))[None, None]
+        _check(decode_bf16(to_numpy_u16(O[b, h, rows]))[None, None],
+               lse[b, h, rows].cpu().numpy().astype(np.float64)[None, None],
+               Qf, Kf, Vf, False, what=(b, h))
