@@ -103,11 +103,32 @@ void attn_fwd_kernel(AttnArgs p) {
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);  // uniform
   const uint32_t lr = lane % 32, hh = lane / 32;
 
-  // ---- work item: query block qb of head (b, h); causal blocks heaviest first
-  const int v = xcd_virtual_id(blockIdx.x, p.num_wg, p.xcd_remap);
-  const int bh = v / p.qblocks;
-  int qb = v - bh * p.qblocks;
-  if (CAUSAL) qb = p.qblocks - 1 - qb;
+  // ---- work item: query block qb of head bh = (b, h). Non-causal: the
+  // query blocks of a head are consecutive, and the XCD remap gives every
+  // XCD whole heads (their K and V stay in its L2). Causal (work grows with
+  // qb): every XCD still owns whole heads, but runs its items heaviest
+  // first across all of them (longest-processing-time order, so the tail of
+  // the grid holds the light blocks); without whole heads per XCD, the
+  // order is heaviest first over the grid.
+  int bh, qb;
+  {
+    const int nbh = p.num_wg / p.qblocks;
+    if (!CAUSAL) {
+      const int v = xcd_virtual_id(blockIdx.x, p.num_wg, p.xcd_remap);
+      bh = v / p.qblocks;
+      qb = v - bh * p.qblocks;
+    } else if (p.xcd_remap && nbh % 8 == 0) {
+      const int v = xcd_virtual_id(blockIdx.x, p.num_wg, 1);
+      const int per = p.num_wg / 8, hpx = nbh / 8;  // items and heads per XCD
+      const int x = v / per, r = v - x * per;
+      qb = p.qblocks - 1 - r / hpx;
+      bh = x * hpx + r % hpx;
+    } else {
+      const int v = blockIdx.x;
+      qb = p.qblocks - 1 - v / nbh;
+      bh = v % nbh;
+    }
+  }
   const int b = bh / p.Hq, h = bh - b * p.Hq;
   const size_t qoff = (size_t)bh * (size_t)p.Nq * D;
   const size_t kvoff = ((size_t)b * p.Hkv + h / p.group) * (size_t)p.Nk * D;
