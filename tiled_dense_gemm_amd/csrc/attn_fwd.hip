@@ -34,6 +34,8 @@
 // product, so numerator and denominator use the same weights.
 #include <math.h>
 
+#include <algorithm>
+
 #include "tkg_attn_layout.hpp"
 #include "tkg_device.hpp"
 #include "tkg_kernels.hpp"
@@ -106,10 +108,11 @@ void attn_fwd_kernel(AttnArgs p) {
   // ---- work item: query block qb of head bh = (b, h). Non-causal: the
   // query blocks of a head are consecutive, and the XCD remap gives every
   // XCD whole heads (their K and V stay in its L2). Causal (work grows with
-  // qb): every XCD still owns whole heads, but runs its items heaviest
-  // first across all of them (longest-processing-time order, so the tail of
-  // the grid holds the light blocks); without whole heads per XCD, the
-  // order is heaviest first over the grid.
+  // qb): every XCD still owns whole heads and walks them in windows of
+  // lpt_heads heads, whose K and V stay cached; inside a window it runs the
+  // items heaviest first across the window's heads (longest-processing-
+  // time order, so light blocks fill the gaps at the end). Without whole
+  // heads per XCD, the order is heaviest first over the grid.
   int bh, qb;
   {
     const int nbh = p.num_wg / p.qblocks;
@@ -121,8 +124,10 @@ void attn_fwd_kernel(AttnArgs p) {
       const int v = xcd_virtual_id(blockIdx.x, p.num_wg, 1);
       const int per = p.num_wg / 8, hpx = nbh / 8;  // items and heads per XCD
       const int x = v / per, r = v - x * per;
-      qb = p.qblocks - 1 - r / hpx;
-      bh = x * hpx + r % hpx;
+      const int wi = p.lpt_heads * p.qblocks;       // items per window
+      const int w = r / wi, rr = r - w * wi;
+      qb = p.qblocks - 1 - rr / p.lpt_heads;
+      bh = x * hpx + w * p.lpt_heads + rr % p.lpt_heads;
     } else {
       const int v = blockIdx.x;
       qb = p.qblocks - 1 - v / nbh;
@@ -419,7 +424,30 @@ using Cfg64 = AttnCfg<64, TKG_ATTN_CFG64>;
 
 int attn_block_q(int D) { return D == 64 ? Cfg64::BQ : D == 128 ? Cfg128::BQ : 0; }
 
-hipError_t launch_attn(const AttnArgs& a, int D, bool causal, hipStream_t stream) {
+// Causal longest-first windows: as many of an XCD's heads as keep their
+// keys and values within this many bytes. Measured (causal, TFLOP/s):
+// ordering across all of an XCD's heads pushed the working set out to HBM
+// at B=16 Hq=16 N=4096 D=128 (6.8x the compulsory bytes, 808); windows of
+// 1, 2, 4, 8 and 16 MiB gave 933, 937, 961, 968 and 948 there, and over
+// ten causal workloads (N 1024-16384, D 64 and 128) 8 MiB was best or
+// within 2% except D=128 N=1024 (4 MiB 750, 8 MiB 709).
+#ifndef TKG_ATTN_LPT_BYTES
+#define TKG_ATTN_LPT_BYTES (8 << 20)
+#endif
+static int lpt_window(const AttnArgs& a, int D) {
+  const int nbh = a.num_wg / a.qblocks;
+  if (nbh % 8 != 0) return 1;
+  const int hpx = nbh / 8;
+  // K and V bytes per query head (a key/value head serves `group` of them)
+  const int64_t share = std::max<int64_t>(1, (int64_t)a.Nk * D * 4 / a.group);
+  int w = (int)std::min<int64_t>(hpx, std::max<int64_t>(1, TKG_ATTN_LPT_BYTES / share));
+  while (hpx % w != 0) --w;
+  return w;
+}
+
+hipError_t launch_attn(const AttnArgs& args, int D, bool causal, hipStream_t stream) {
+  AttnArgs a = args;
+  a.lpt_heads = causal ? lpt_window(a, D) : 1;
   if (D == 64) return causal ? Cfg64::launch<true>(a, stream) : Cfg64::launch<false>(a, stream);
   if (D == 128) return causal ? Cfg128::launch<true>(a, stream) : Cfg128::launch<false>(a, stream);
   return hipErrorInvalidValue;

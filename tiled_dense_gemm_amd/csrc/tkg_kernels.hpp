@@ -78,6 +78,7 @@ struct AttnArgs {
   int32_t num_wg;      // B * Hq * qblocks
   float c;             // scale * log2(e)
   int32_t xcd_remap;
+  int32_t lpt_heads;   // causal order: heads per longest-first window (set by launch_attn)
 };
 // query rows per workgroup for head dimension D (0: unsupported D)
 int attn_block_q(int D);
