@@ -210,3 +210,26 @@ def test_full_size_more_keys_than_queries(dev):
         _check(decode_bf16(to_numpy_u16(O[b, h, rows]))[None, None],
                lse[b, h, rows].cpu().numpy().astype(np.float64)[None, None],
                Qf, Kf, Vf, False, what=(b, h))
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,D", [
+    (16, 16, 16, 4096, 128),   # 256 heads: longest-first windows of 4 heads per XCD
+    (16, 32, 32, 1024, 64),    # 512 heads, 8 query blocks each: windows of 32
+    (1, 16, 2, 16384, 128),    # grouped-query, 16 heads
+    (3, 5, 5, 1000, 64),       # head count not a multiple of the 8 XCDs
+])
+def test_causal_grid_writes_every_row(dev, B, Hq, Hkv, N, D):
+    # the causal work-item order is a permutation of (head, query block):
+    # with O and lse pre-filled with NaN, every element must be written
+    print("attention every row", B, Hq, Hkv, N, D, flush=True)
+    Q = gi.device.bf16_operand(221, B * Hq * N, D, device=dev).view(B, Hq, N, D)
+    K = gi.device.bf16_operand(222, B * Hkv * N, D, device=dev).view(B, Hkv, N, D)
+    V = gi.device.bf16_operand(223, B * Hkv * N, D, device=dev).view(B, Hkv, N, D)
+    O = torch.full((B, Hq, N, D), float("nan"), dtype=torch.bfloat16, device=dev)
+    lse = torch.full((B, Hq, N), float("nan"), dtype=torch.float32, device=dev)
+    tkg.tkg_attention_fwd(Q, K, V, causal=True, out=O, lse=lse)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(O).all()) and bool(torch.isfinite(lse).all())
+    # row 0 of every head attends to key 0 alone: O = V[0], lse = score
+    kv = torch.arange(Hq, device=dev) // (Hq // Hkv)
+    assert torch.equal(O[:, :, 0].view(torch.int16), V[:, kv, 0].view(torch.int16))
