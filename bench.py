@@ -12,9 +12,10 @@ launch on the stream the kernels run on (the pages time 10 warmup + 10
 timed iterations, page "ThunderKittens: Simple, Fast, and Adorable AI
 Kernels", section 5 "Evaluation Methodology").
 
-``cpu_baseline``: the CPU oracle (plain fp64 C, OpenMP) timed on a bounded
-sample of the same bf16 product, 64 x 64 output tiles, for a context
-number; it is test infrastructure and takes no part in the GPU path.
+``cpu_baseline``: the CPU oracle (its decode of each format and its plain
+fp64 C product, OpenMP) timed on a bounded sample of the same three
+products, 64 x 64 output tiles of each in turn, for a context number; it is
+test infrastructure and takes no part in the GPU path.
 
 ``--profile`` runs only the GPU part (for rocprofv3) plus a 1 GiB device
 copy that calibrates the HBM byte counters.
@@ -537,7 +538,8 @@ def main() -> int:
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(A16, B16, args.cpu_seconds)
+        cpu = cpu_baseline(((A16, B16), (A8, sa, B8, sb), (A4, As4, ta, B4, Bs4, tb)),
+                           args.cpu_seconds)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "TFLOP/s",
@@ -638,33 +640,51 @@ def time_attention(args, dev, stream):
     return rows
 
 
-def cpu_baseline(A16, B16, seconds):
-    """The oracle on 64x64 output tiles of the bf16 product until `seconds`
-    of CPU time are spent; the rate is scaled to TFLOP/s."""
+def cpu_baseline(ops, seconds):
+    """The oracle on 64x64 output tiles of the step's three products (bf16,
+    fp8, block-scaled 4-bit, in turn: the oracle's own decode and fp64
+    product for each format) until `seconds` of CPU time are spent; the
+    rate is the tiles' FLOP over that time, in TFLOP/s."""
     import numpy as np
     import torch
 
     import oracle
-    from oracle.formats import decode_bf16
 
+    def rows(x, r0):
+        t = x[r0:r0 + 64]
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.cpu().numpy()
+
+    (A16, B16), (A8, sa, B8, sb), (A4, As4, ta, B4, Bs4, tb) = ops
     K = A16.shape[1]
+    M, N = A16.shape[0], B16.shape[0]
     rng = np.random.default_rng(0)
-    done = 0
+    done = [0, 0, 0]
     t_used = 0.0
-    while t_used < seconds or done < 2:
-        i0 = int(rng.integers(0, A16.shape[0] - 64 + 1))
-        j0 = int(rng.integers(0, B16.shape[0] - 64 + 1))
-        a = decode_bf16(A16[i0:i0 + 64].view(torch.int16).cpu().numpy().view(np.uint16))
-        b = decode_bf16(B16[j0:j0 + 64].view(torch.int16).cpu().numpy().view(np.uint16))
+    while t_used < seconds or min(done) < 2:
+        f = (done[0] + done[1] + done[2]) % 3
+        i0 = int(rng.integers(0, M - 64 + 1))
+        j0 = int(rng.integers(0, N - 64 + 1))
+        if f == 0:
+            args = (rows(A16, i0), rows(B16, j0))
+            fn = oracle.gemm_bf16
+        elif f == 1:
+            args = (rows(A8, i0), sa, rows(B8, j0), sb)
+            fn = oracle.gemm_fp8
+        else:
+            args = (rows(A4, i0), rows(As4, i0), ta, rows(B4, j0), rows(Bs4, j0), tb)
+            fn = oracle.gemm_fp4_blockscaled
         t = time.perf_counter()
-        oracle.gemm_f64(a, b)
+        fn(*args)
         t_used += time.perf_counter() - t
-        done += 1
-    rate = done * 2.0 * 64 * 64 * K / t_used / 1e12
+        done[f] += 1
+    rate = sum(done) * 2.0 * 64 * 64 * K / t_used / 1e12
     return {"value": round(rate, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": "%d random 64x64 output tiles of the %d^3 bf16 product "
-                      "(fp64 plain C oracle, %.1f s)" % (done, K, t_used)}
+            "sample": "%d random 64x64 output tiles each of the %d^3 bf16, fp8 and "
+                      "block-scaled 4-bit products, in turn (the oracle's decode and "
+                      "fp64 plain C product, %.1f s)" % (min(done), K, t_used)}
 
 
 if __name__ == "__main__":
