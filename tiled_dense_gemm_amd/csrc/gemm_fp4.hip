@@ -73,21 +73,6 @@ __device__ __forceinline__ TileState tile_state(const Fp4Args& p, int t) {
   return s;
 }
 
-// Eight e2m1 values (one dword, element 2t in the low nibble of byte t)
-// times a block scale -> eight exact fp16 values.
-__device__ __forceinline__ f16x8_t dequant8(uint32_t packed, float scale,
-                                            f16x2_t mant) {
-  f16x2_t h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, scale, 0);
-  f16x2_t h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, scale, 1);
-  f16x2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, scale, 2);
-  f16x2_t h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, scale, 3);
-  h0 = h0 * mant;
-  h1 = h1 * mant;
-  h2 = h2 * mant;
-  h3 = h3 * mant;
-  return f16x8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
-}
-
 // Block scale (byte BYTE of `word`, OCP e4m3) -> the scale operand of the
 // convert and the fp16 factor still to apply. The convert uses only the
 // magnitude of its scale's power of two (measured on gfx950: mantissa and
@@ -105,23 +90,12 @@ __device__ __forceinline__ void split_scale(uint32_t word, float& s,
   mant = f16x2_t{m, m};
 }
 
-// VALU instructions placed after each MFMA (6 measured fastest among
-// 3, 4, 6, 8 and 12 at 8192^3).
-constexpr int kValuPerMfma = 6;
-
-// Scheduling recipe for one k-step of NMMA MFMAs: the LDS reads (NREAD,
-// three after each of the first MFMAs) and slab loads (NDMA, one after each
-// MFMA) are front-loaded; the dequantization VALU work of the next k-step is
-// spread over all MFMAs, so the matrix core is fed while the VALU converts.
-template <int NMMA, int NREAD, int NDMA, int Q = 0>
-__device__ __forceinline__ void interleave_fp4() {
-  if constexpr (Q < NMMA) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    constexpr int r = NREAD - 3 * Q >= 3 ? 3 : (NREAD - 3 * Q > 0 ? NREAD - 3 * Q : 0);
-    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
-    if constexpr (Q < NDMA) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);  // VALU
-    interleave_fp4<NMMA, NREAD, NDMA, Q + 1>();
+// Compile-time loop: f(integral_constant<int, I>) for I = B .. E-1.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
   }
 }
 
@@ -224,21 +198,6 @@ void gemm_fp4_kernel(Fp4Args p) {
     i32x4_t a[FM], b[FN];     // packed values of one chunk
     u32x2_t sa[FM], sb[FN];   // the row's 8 block scales of the stage
   };
-  // chunk s of buffer `buf`; the scales are read with chunk 0 and carried
-  auto read_raw = [&](int buf, int s, Raw& r, const Raw& prev) {
-    const TKG_LDS uint8_t* st = smem + buf * STAGE_BYTES;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      r.a[i] = lds_read<i32x4_t>(st, av_base + i * 32 * VB + roff[s]);
-      r.sa[i] = (s == 0) ? lds_read<u32x2_t>(st, as_base + i * 32 * SB) : prev.sa[i];
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      r.b[j] = lds_read<i32x4_t>(st, bv_base + j * 32 * VB + roff[s]);
-      r.sb[j] = (s == 0) ? lds_read<u32x2_t>(st, bs_base + j * 32 * SB) : prev.sb[j];
-    }
-  };
-
   f32x16_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -251,23 +210,82 @@ void gemm_fp4_kernel(Fp4Args p) {
   struct Deq {
     f16x8_t a[FM], b[FN];
   };
-  // k-step q (0..3) of chunk s: dword q of the chunk, whose block (16
-  // elements) is 2*(2s + khalf) + q/2 of the stage, i.e. byte
-  // 2*khalf + q/2 of scale word s.
-  auto dequant = [&](const Raw& r, int s, auto qc, Deq& d) {
-    constexpr int q = decltype(qc)::value;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      float sc; f16x2_t m;
-      split_scale<q / 2>(r.sa[i][s] >> (16 * khalf), sc, m);
-      d.a[i] = dequant8((uint32_t)r.a[i][q], sc, m);
+  constexpr int NMMA = FM * FN;
+  constexpr int NF = FM + FN;               // fragments converted per k-step
+  constexpr int NDMA = 2 * VDMA + 2 * SDMA;
+  static_assert(NDMA <= NMMA && NF <= NMMA, "one load and two reads per MFMA at most");
+  // LDS reads of one fragment: its 16 bytes of packed values of chunk s,
+  // and (with chunk 0) the row's 8 scale bytes of the stage
+  auto read_val = [&](int b, int s, int f, Raw& r) {
+    const TKG_LDS uint8_t* st = smem + b * STAGE_BYTES;
+    if (f < FM) r.a[f] = lds_read<i32x4_t>(st, av_base + f * 32 * VB + roff[s]);
+    else r.b[f - FM] = lds_read<i32x4_t>(st, bv_base + (f - FM) * 32 * VB + roff[s]);
+  };
+  auto read_scale = [&](int b, int f, Raw& r) {
+    const TKG_LDS uint8_t* st = smem + b * STAGE_BYTES;
+    if (f < FM) r.sa[f] = lds_read<u32x2_t>(st, as_base + f * 32 * SB);
+    else r.sb[f - FM] = lds_read<u32x2_t>(st, bs_base + (f - FM) * 32 * SB);
+  };
+  auto issue_one = [&](const StageLoad& s, int buf_, int d) {
+    TKG_LDS uint8_t* st = smem + buf_ * STAGE_BYTES;
+    if (d < 2 * VDMA) {
+      const int i = d / 2;
+      const uint32_t off = (s.k0 + vkb[i] < p.vbytes) ? voff[i] + s.k0 : kOobOffset;
+      const uint32_t q = wave * VDMA + i;
+      if (d % 2 == 0) dma_b128(s.rav, st + q * 1024, off);
+      else dma_b128(s.rbv, st + OFF_BV + q * 1024, off);
+    } else {
+      const int i = (d - 2 * VDMA) / 2;
+      const uint32_t off = (s.s0 + skb < p.sbytes) ? soff[i] + s.s0 : kOobOffset;
+      const uint32_t q = wave * SDMA + i;
+      if (d % 2 == 0) dma_b32(s.ras, st + OFF_AS + q * 256, off);
+      else dma_b32(s.rbs, st + OFF_BS + q * 256, off);
     }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      float sc; f16x2_t m;
-      split_scale<q / 2>(r.sb[j][s] >> (16 * khalf), sc, m);
-      d.b[j] = dequant8((uint32_t)r.b[j][q], sc, m);
+  };
+  // Half h of fragment f's conversion for k-step q of chunk s (f < FM: A
+  // fragment f, else B fragment f - FM): half 0 splits the block scale and
+  // converts values 0-3, half 1 values 4-7. Dword q of the chunk lies in
+  // block 2 (2s + khalf) + q/2 of the stage, i.e. byte 2 khalf + q/2 of
+  // scale word s.
+  struct Split {
+    float sc;
+    f16x2_t m;
+  };
+  auto conv_half = [&](const Raw& r, int s, auto qc, auto fc, auto hc, Split& sp, Deq& d) {
+    constexpr int q = decltype(qc)::value, f = decltype(fc)::value, h = decltype(hc)::value;
+    constexpr bool IS_A = f < FM;
+    constexpr int fi = IS_A ? f : f - FM;
+    const uint32_t packed = (uint32_t)(IS_A ? r.a[fi][q] : r.b[fi][q]);
+    if constexpr (h == 0) {
+      const uint32_t w = (IS_A ? r.sa[fi][s] : r.sb[fi][s]) >> (16 * khalf);
+      split_scale<q / 2>(w, sp.sc, sp.m);
     }
+    const f16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, sp.sc, 2 * h) * sp.m;
+    const f16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, sp.sc, 2 * h + 1) * sp.m;
+    f16x8_t& v = IS_A ? d.a[fi] : d.b[fi];
+    v[4 * h + 0] = lo[0];
+    v[4 * h + 1] = lo[1];
+    v[4 * h + 2] = hi[0];
+    v[4 * h + 3] = hi[1];
+  };
+  // One k-step in program order: MFMA (i, j), then the conversion halves
+  // and the loads or reads of its slot, then a scheduling fence, so the
+  // conversion of the next k-step (from raw r, chunk s, dword q) is spread
+  // evenly over this k-step's MFMAs.
+  auto kstep = [&](const Deq& cur, Deq& nxt, const Raw& r, int s, auto qc, auto&& extra) {
+    Split sp[NF];
+    static_for<0, NMMA>([&](auto slot_c) {
+      constexpr int slot = decltype(slot_c)::value;
+      constexpr int i = slot / FN, j = slot % FN;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur.b[j], cur.a[i], acc[i][j], 0, 0, 0);
+      static_for<slot * 2 * NF / NMMA, (slot + 1) * 2 * NF / NMMA>([&](auto hx_c) {
+        constexpr int hx = decltype(hx_c)::value;
+        conv_half(r, s, qc, std::integral_constant<int, hx / 2>{},
+                  std::integral_constant<int, hx % 2>{}, sp[hx / 2], nxt);
+      });
+      extra(slot);
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
   // Keeps the conversion of a k-step ahead of a block boundary: without it
   // the compiler sinks the VALU work past the loop's branch, where it can no
@@ -278,21 +296,11 @@ void gemm_fp4_kernel(Fp4Args p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(d.b[j]));
   };
-  auto mma = [&](const Deq& d) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(d.b[j], d.a[i], acc[i][j], 0, 0, 0);
-  };
+  auto none = [&](int) {};
   using Q0 = std::integral_constant<int, 0>;
   using Q1 = std::integral_constant<int, 1>;
   using Q2 = std::integral_constant<int, 2>;
   using Q3 = std::integral_constant<int, 3>;
-  constexpr int NMMA = FM * FN;
-  constexpr int NREAD0 = 2 * (FM + FN);   // chunk 0: values + scales
-  constexpr int NREAD1 = FM + FN;         // chunk 1: values
-  constexpr int NDMA = 2 * VDMA + 2 * SDMA;
 
   // ---- prologue ------------------------------------------------------------
 #pragma unroll
@@ -302,64 +310,60 @@ void gemm_fp4_kernel(Fp4Args p) {
 
   Raw raw[2];
   Deq deq[2];
-  read_raw(0, 0, raw[0], raw[0]);
-  dequant(raw[0], 0, Q0{}, deq[0]);
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    read_val(0, 0, f, raw[0]);
+    read_scale(0, f, raw[0]);
+  }
+  {
+    Split sp[NF];
+    static_for<0, NF>([&](auto fc) {
+      conv_half(raw[0], 0, Q0{}, fc, std::integral_constant<int, 0>{}, sp[decltype(fc)::value], deq[0]);
+      conv_half(raw[0], 0, Q0{}, fc, std::integral_constant<int, 1>{}, sp[decltype(fc)::value], deq[0]);
+    });
+  }
 
   // Eight k-steps per stage (chunk s = u/4, k-step q = u%4). k-step u
   // multiplies deq[u&1] while deq[(u+1)&1] is filled with k-step u+1; the
   // last k-step converts chunk 0 of the next stage. Chunk 1 is read from LDS
-  // at u = 0; at u = 4 (all waves have read the stage) the next stage must
-  // have landed, the barrier frees this buffer for the cursor's next stage,
-  // and chunk 0 of the next stage is read.
+  // during k-step 0; before k-step 4 (all waves have read the stage) the
+  // next stage must have landed, the barrier frees this buffer for the
+  // cursor's next stage, whose loads go out during k-step 4 together with
+  // the reads of the next stage's chunk 0.
   int buf = 0;
   bool fresh_tile = false;  // finish stores are in flight
   for (;;) {
     for (uint32_t kt = 0; kt < p.nk; ++kt) {
       // the cursor moves here so that no branch splits the stage's k-steps
       const StageLoad nl = next_stage();
-      read_raw(buf, 1, raw[1], raw[0]);
-      dequant(raw[0], 0, Q1{}, deq[1]);
-      mma(deq[0]);
-      interleave_fp4<NMMA, NREAD1, 0>();
-      __builtin_amdgcn_sched_barrier(0);
-      dequant(raw[0], 0, Q2{}, deq[0]);
-      mma(deq[1]);
-      interleave_fp4<NMMA, 0, 0>();
-      __builtin_amdgcn_sched_barrier(0);
-      dequant(raw[0], 0, Q3{}, deq[1]);
-      mma(deq[0]);
-      interleave_fp4<NMMA, 0, 0>();
-      __builtin_amdgcn_sched_barrier(0);
-      dequant(raw[1], 1, Q0{}, deq[0]);
-      mma(deq[1]);
-      interleave_fp4<NMMA, 0, 0>();
+#pragma unroll
+      for (int f = 0; f < FM; ++f) raw[1].sa[f] = raw[0].sa[f];
+#pragma unroll
+      for (int f = 0; f < FN; ++f) raw[1].sb[f] = raw[0].sb[f];
+      kstep(deq[0], deq[1], raw[0], 0, Q1{}, [&](int slot) {
+        if (slot < NF) read_val(buf, 1, slot, raw[1]);
+      });
+      kstep(deq[1], deq[0], raw[0], 0, Q2{}, none);
+      kstep(deq[0], deq[1], raw[0], 0, Q3{}, none);
+      kstep(deq[1], deq[0], raw[1], 1, Q0{}, none);
       pin(deq[0]);
-      __builtin_amdgcn_sched_barrier(0);
 
       if (fresh_tile) wait_vmcnt<0>();
       else wait_vmcnt<(STAGES - 2) * DMA_PER_STAGE>();
       fresh_tile = false;
       lds_barrier();
-      issue(nl, buf);
       const int nbuf = (buf + 1 == STAGES) ? 0 : buf + 1;
-      read_raw(nbuf, 0, raw[0], raw[0]);
-      dequant(raw[1], 1, Q1{}, deq[1]);
-      mma(deq[0]);
-      interleave_fp4<NMMA, NREAD0, NDMA>();
-      __builtin_amdgcn_sched_barrier(0);
-      dequant(raw[1], 1, Q2{}, deq[0]);
-      mma(deq[1]);
-      interleave_fp4<NMMA, 0, 0>();
-      __builtin_amdgcn_sched_barrier(0);
-      dequant(raw[1], 1, Q3{}, deq[1]);
-      mma(deq[0]);
-      interleave_fp4<NMMA, 0, 0>();
-      __builtin_amdgcn_sched_barrier(0);
-      dequant(raw[0], 0, Q0{}, deq[0]);
-      mma(deq[1]);
-      interleave_fp4<NMMA, 0, 0>();
+      kstep(deq[0], deq[1], raw[1], 1, Q1{}, [&](int slot) {
+        if (slot < NDMA) issue_one(nl, buf, slot);
+        if (slot < NF) {
+          read_val(nbuf, 0, slot, raw[0]);
+          read_scale(nbuf, slot, raw[0]);
+        }
+      });
+      kstep(deq[1], deq[0], raw[1], 1, Q2{}, none);
+      kstep(deq[0], deq[1], raw[1], 1, Q3{}, none);
+      kstep(deq[1], deq[0], raw[0], 0, Q0{}, none);
       pin(deq[0]);
-      __builtin_amdgcn_sched_barrier(0);
       buf = nbuf;
     }
 
