@@ -255,14 +255,22 @@ void gemm_fp4_kernel(Fp4Args p) {
     constexpr int q = decltype(qc)::value, f = decltype(fc)::value, h = decltype(hc)::value;
     constexpr bool IS_A = f < FM;
     constexpr int fi = IS_A ? f : f - FM;
-    const uint32_t packed = (uint32_t)(IS_A ? r.a[fi][q] : r.b[fi][q]);
-    if constexpr (h == 0) {
-      const uint32_t w = (IS_A ? r.sa[fi][s] : r.sb[fi][s]) >> (16 * khalf);
-      split_scale<q / 2>(w, sp.sc, sp.m);
-    }
+    const i32x4_t& rv = [&]() -> const i32x4_t& {
+      if constexpr (IS_A) return r.a[fi];
+      else return r.b[fi];
+    }();
+    const u32x2_t& rs = [&]() -> const u32x2_t& {
+      if constexpr (IS_A) return r.sa[fi];
+      else return r.sb[fi];
+    }();
+    f16x8_t& v = [&]() -> f16x8_t& {
+      if constexpr (IS_A) return d.a[fi];
+      else return d.b[fi];
+    }();
+    const uint32_t packed = (uint32_t)rv[q];
+    if constexpr (h == 0) split_scale<q / 2>(rs[s] >> (16 * khalf), sp.sc, sp.m);
     const f16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, sp.sc, 2 * h) * sp.m;
     const f16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, sp.sc, 2 * h + 1) * sp.m;
-    f16x8_t& v = IS_A ? d.a[fi] : d.b[fi];
     v[4 * h + 0] = lo[0];
     v[4 * h + 1] = lo[1];
     v[4 * h + 2] = hi[0];
