@@ -103,8 +103,20 @@ def _kernel_key(name: str):
     return None
 
 
+def _bench_line(path):
+    """The JSON line a bench run printed (None without a log)."""
+    if not path or not os.path.exists(path):
+        return None
+    line = None
+    for l in open(path):
+        if l.startswith("{") and '"metric"' in l:
+            line = l
+    return json.loads(line) if line else None
+
+
 def summarize_profile(trace_dir: str, fetch_dir: str, write_dir: str,
-                      size: int, out_md: str, out_json: str, command: str) -> int:
+                      size: int, out_md: str, out_json: str, command: str,
+                      bench_log: str = None) -> int:
     """Turn rocprofv3 CSV output into the committed summaries.
 
     trace_dir: --kernel-trace --stats run of the timed bench;
@@ -121,12 +133,26 @@ def summarize_profile(trace_dir: str, fetch_dir: str, write_dir: str,
             out += list(csv.DictReader(open(f)))
         return out
 
-    dur = {}
+    # launches in start order; the summary keeps the last `steps` of each
+    # kernel, the launches the bench run timed with HIP events (the others
+    # are its warmup)
+    bench = _bench_line(bench_log)
+    steps = bench["steps"] if bench else None
+    launches = {}
     for r in rows(trace_dir, "*kernel_trace.csv"):
         k = _kernel_key(r["Kernel_Name"])
         if k:
-            dur.setdefault(k, []).append(
-                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+            launches.setdefault(k, []).append(
+                (int(r["Start_Timestamp"]),
+                 (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3))
+    dur = {k: [d for _, d in sorted(v)][-steps:] if steps else [d for _, d in sorted(v)]
+           for k, v in launches.items()}
+    event_us = {}
+    if bench:
+        for k, v in list(bench.get("kernels", {}).items()) + list(
+                (bench.get("next_rows") or {}).items()):
+            if "ms_mean" in v:
+                event_us[k] = v["ms_mean"] * 1e3
 
     def counter(d, cname):
         per, cal = {}, []
@@ -160,8 +186,12 @@ def summarize_profile(trace_dir: str, fetch_dir: str, write_dir: str,
            "command": command, "kernels": {}}
     lines = ["# GEMM kernels at M=N=K=%d on one MI355X (rocprofv3)" % size, "",
              "Produced by:", "", "```", command, "```", "",
-             "| kernel | launches | mean us | min us | TFLOP/s (mean) | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes/launch (calibrated) | compulsory bytes | ratio |",
-             "|---|---|---|---|---|---|---|---|---|---|"]
+             ("Durations: the kernel trace's last %d launches of each kernel, the "
+              "ones the traced bench run timed; beside them the mean that run's "
+              "HIP events measured around the same launches." % steps) if steps else
+             "Durations: every traced launch.", "",
+             "| kernel | launches | mean us | min us | HIP-event mean us (same run) | TFLOP/s (mean) | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes/launch (calibrated) | compulsory bytes | ratio |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
     for k in ("gemm_bf16", "gemm_fp8", "gemm_fp4_blockscaled", "gemm_mxfp4", "gemm_mxfp8"):
         d = dur.get(k, [])
         if not d and k.startswith("gemm_mx"):
@@ -172,12 +202,14 @@ def summarize_profile(trace_dir: str, fetch_dir: str, write_dir: str,
         mean_us = statistics.mean(d) if d else None
         rec["kernels"][k] = {"launches": len(d), "mean_us": mean_us,
                              "min_us": min(d) if d else None,
+                             "event_mean_us": event_us.get(k),
                              "fetch_kib": fk, "write_kib": wk,
                              "hbm_bytes_per_launch": hbm,
                              "compulsory_bytes": algo[k]}
-        lines.append("| %s | %d | %s | %s | %s | %s | %s | %s | %d | %s |" % (
+        lines.append("| %s | %d | %s | %s | %s | %s | %s | %s | %s | %d | %s |" % (
             k, len(d), "%.1f" % mean_us if d else "-",
             "%.1f" % min(d) if d else "-",
+            "%.1f" % event_us[k] if k in event_us else "-",
             "%.1f" % (flops / (mean_us * 1e-6) / 1e12) if d else "-",
             "%.0f" % fk if fk else "-", "%.0f" % wk if wk else "-",
             "%.3g" % hbm if hbm else "-", algo[k],
@@ -244,7 +276,8 @@ def _attention_workload(kname: str, grid_x: int, wg_x: int):
     return None
 
 
-def summarize_attention_profile(trace_dir, fetch_dir, write_dir, out_md, out_json, command):
+def summarize_attention_profile(trace_dir, fetch_dir, write_dir, out_md, out_json, command,
+                                bench_log=None):
     """Committed summary of the attention kernels: durations from the
     --kernel-trace run of `bench.py --with-attn`, HBM bytes from the
     FETCH_SIZE / WRITE_SIZE runs of `bench.py --profile --with-attn`
@@ -265,11 +298,21 @@ def summarize_attention_profile(trace_dir, fetch_dir, write_dir, out_md, out_jso
         wx = int(r.get("Workgroup_Size_X") or r.get("Workgroup_Size") or 0)
         return _attention_workload(r["Kernel_Name"], gx, wx)
 
-    dur = {}
+    # as for the GEMMs: the last `steps` launches of each workload are the
+    # ones the traced bench run timed with HIP events
+    bench = _bench_line(bench_log)
+    steps = bench["steps"] if bench else None
+    launches = {}
     for r in rows(trace_dir, "*kernel_trace.csv"):
         k = key(r)
         if k:
-            dur.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+            launches.setdefault(k, []).append(
+                (int(r["Start_Timestamp"]),
+                 (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3))
+    dur = {k: [d for _, d in sorted(v)][-steps:] if steps else [d for _, d in sorted(v)]
+           for k, v in launches.items()}
+    event_us = {k: v["ms_mean"] * 1e3 for k, v in ((bench or {}).get("next_rows") or {}).items()
+                if "ms_mean" in v}
 
     def counter(d, cname):
         per, cal = {}, []
@@ -296,8 +339,12 @@ def summarize_attention_profile(trace_dir, fetch_dir, write_dir, out_md, out_jso
              "Produced by:", "", "```", command, "```", "",
              "Algorithmic flops: 4 D per visible (query, key) pair (Q K^T and P V); "
              "compulsory bytes: Q, K, V read once and O written once (bf16).", "",
-             "| workload | launches | mean us | min us | TFLOP/s (mean) | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes/launch (calibrated) | compulsory bytes | ratio |",
-             "|---|---|---|---|---|---|---|---|---|---|"]
+             ("Durations: the kernel trace's last %d launches of each workload, the "
+              "ones the traced bench run timed; beside them the mean that run's "
+              "HIP events measured." % steps) if steps else "Durations: every traced launch.",
+             "",
+             "| workload | launches | mean us | min us | HIP-event mean us (same run) | TFLOP/s (mean) | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes/launch (calibrated) | compulsory bytes | ratio |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
     for name, B, Hq, Hkv, N, D, causal in ATTN_WORKLOADS:
         d = dur.get(name, [])
         fk = statistics.mean(fetch[name]) if fetch.get(name) else None
@@ -308,11 +355,13 @@ def summarize_attention_profile(trace_dir, fetch_dir, write_dir, out_md, out_jso
         mean_us = statistics.mean(d) if d else None
         rec["workloads"][name] = {"launches": len(d), "mean_us": mean_us,
                                   "min_us": min(d) if d else None,
+                                  "event_mean_us": event_us.get(name),
                                   "tflops": flops / (mean_us * 1e-6) / 1e12 if d else None,
                                   "fetch_kib": fk, "write_kib": wk,
                                   "hbm_bytes_per_launch": hbm, "compulsory_bytes": algo}
-        lines.append("| %s | %d | %s | %s | %s | %s | %s | %s | %d | %s |" % (
+        lines.append("| %s | %d | %s | %s | %s | %s | %s | %s | %s | %d | %s |" % (
             name, len(d), "%.1f" % mean_us if d else "-", "%.1f" % min(d) if d else "-",
+            "%.1f" % event_us[name] if name in event_us else "-",
             "%.1f" % (flops / (mean_us * 1e-6) / 1e12) if d else "-",
             "%.0f" % fk if fk else "-", "%.0f" % wk if wk else "-",
             "%.3g" % hbm if hbm else "-", algo, "%.2f" % (hbm / algo) if hbm else "-"))
@@ -368,6 +417,9 @@ def main() -> int:
     ap.add_argument("--summarize-profile", nargs=3,
                     metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--profile-command", default="")
+    ap.add_argument("--bench-log", default=None,
+                    help="log of the traced bench run (its JSON line gives the timed "
+                         "launch count and the HIP-event means)")
     ap.add_argument("--summarize-attn-profile", nargs=3,
                     metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--with-attn", action="store_true",
@@ -390,13 +442,13 @@ def main() -> int:
             os.path.join(ROOT, "profiles", "gemm_kernels_%d.md" % args.size),
             TRAFFIC_FILE if args.size == 8192 else
             os.path.join(ROOT, "profiles", "traffic_%d.json" % args.size),
-            args.profile_command)
+            args.profile_command, args.bench_log)
 
     if args.summarize_attn_profile:
         return summarize_attention_profile(
             *args.summarize_attn_profile,
             os.path.join(ROOT, "profiles", "attention_fwd.md"), ATTN_TRAFFIC_FILE,
-            args.profile_command)
+            args.profile_command, args.bench_log)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU "
