@@ -41,13 +41,46 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_8192.json")
 ATTN_SOURCES = ("attn_fwd.hip", "tkg_attn_layout.hpp")
 
 
-def kernel_source_hash(family: str = "gemm") -> str:
-    """Hash of the kernel sources a family is built from (the GEMM family:
-    every source but the attention-only files; attention: every source but
-    the GEMM kernels)."""
+def _code_only(text: str) -> str:
+    """C++ source without its comments and whitespace (string and character
+    literals kept), so that a comment edit leaves the hash of the code that
+    was measured unchanged."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            i = text.find("\n", i)
+            i = n if i < 0 else i
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            if not c.isspace():
+                out.append(c)
+            i += 1
+    return "".join(out)
+
+
+def kernel_source_hash(family: str = "gemm", read=None) -> str:
+    """Hash of the code (comments and whitespace removed) of the kernel
+    sources a family is built from (the GEMM family: every source but the
+    attention-only files; attention: every source but the GEMM kernels).
+    `read(name)` returns a source's text (default: the file in csrc/)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tiled_dense_gemm_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    if read is None:
+        def read(name):
+            return open(os.path.join(csrc, name), encoding="utf-8").read()
+        names = os.listdir(csrc)
+    else:
+        names = read(None)
+    for name in sorted(names):
         if not name.endswith((".hip", ".hpp")):
             continue
         if family == "gemm" and name in ATTN_SOURCES:
@@ -55,7 +88,7 @@ def kernel_source_hash(family: str = "gemm") -> str:
         if family == "attention" and name.startswith("gemm_"):
             continue
         h.update(name.encode())
-        h.update(open(os.path.join(csrc, name), "rb").read())
+        h.update(_code_only(read(name)).encode())
     return h.hexdigest()[:16]
 
 

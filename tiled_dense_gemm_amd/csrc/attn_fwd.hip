@@ -398,7 +398,9 @@ void attn_fwd_kernel(AttnArgs p) {
 // Measured on the B=16 N=4096 workloads (TFLOP/s, non-causal / causal):
 // D = 128: (4, 4, 2, pipelined) 1080 / 933, (4, 3, 3, plain) 1020 / 930,
 // (8, 8, 2, pipelined) 993 / 853; D = 64: (4, 4, 4, plain) 950,
-// (8, 8, 2, pipelined) 810, (4, 4, 2, pipelined) 839. Four waves per
+// (8, 8, 2, pipelined) 810, (4, 4, 2, pipelined) 839; against (4, 4, 4,
+// plain) at 905-918 in another run, (4, 4, 5, plain) 910-916 and (4, 5, 4,
+// plain) 860. Four waves per
 // workgroup (128 query rows) balance causal work better than eight; at
 // D = 64 the softmax outweighs the MFMAs and more resident waves win.
 #ifndef TKG_ATTN_CFG128
