@@ -60,9 +60,11 @@ struct Ring {
 };
 // One table per operand type (variant v selects entry v); entry 0 is the
 // default, the fastest measured at 8192^3 on random operands: for bf16 two
-// waves per SIMD with 16x16x32 MFMAs, for fp8 one wave per SIMD with
-// 16x16x128 MFMAs (the 16x16 shapes run at a higher clock on the
-// power-limited chip).
+// waves per SIMD with 16x16x32 MFMAs (the 16x16 shape runs at a higher
+// clock on the power-limited chip); for fp8 two waves per SIMD with
+// 32x32x64 MFMAs and loader waves (in the bench step, after the bf16
+// product: 2795-2802 against 2652-2656 TFLOP/s for one wave per SIMD with
+// 16x16x128, now entry 2; 16x16x128 at two waves per SIMD spills).
 // Entry 8 repeats entry 0 (variant 0 may resolve to entry 9 instead, see
 // run_dense); entries 9 and 10 are 128 x 128 tiles.
 constexpr Ring kRingsBf16[] = {{128, 4, 4, 1, 16, 256, 1}, {128, 5, 4, 1, 16, 256, 1},
@@ -71,11 +73,11 @@ constexpr Ring kRingsBf16[] = {{128, 4, 4, 1, 16, 256, 1}, {128, 5, 4, 1, 16, 25
                                {64, 10, 4, 0, 32, 256, 1}, {128, 4, 2, 0, 16, 256, 1},
                                {128, 4, 4, 1, 16, 256, 1}, {128, 4, 2, 0, 16, 128, 2},
                                {128, 4, 2, 0, 16, 128, 1}};
-constexpr Ring kRingsFp8[] = {{128, 4, 2, 0, 16, 256, 1}, {128, 5, 2, 0, 32, 256, 1},
-                              {128, 4, 4, 1, 32, 256, 1}, {128, 5, 4, 1, 32, 256, 1},
+constexpr Ring kRingsFp8[] = {{128, 4, 4, 1, 32, 256, 1}, {128, 5, 2, 0, 32, 256, 1},
+                              {128, 4, 2, 0, 16, 256, 1}, {128, 5, 4, 1, 32, 256, 1},
                               {128, 4, 4, 0, 32, 256, 1}, {128, 4, 2, 0, 32, 256, 1},
                               {64, 10, 4, 0, 32, 256, 1}, {64, 10, 2, 0, 32, 256, 1},
-                              {128, 4, 2, 0, 16, 256, 1}, {128, 4, 2, 0, 16, 128, 2},
+                              {128, 4, 4, 1, 32, 256, 1}, {128, 4, 2, 0, 16, 128, 2},
                               {128, 4, 2, 0, 16, 128, 1}};
 constexpr int kNumRings = sizeof(kRingsBf16) / sizeof(kRingsBf16[0]);
 static_assert(sizeof(kRingsFp8) == sizeof(kRingsBf16), "same variant count");
