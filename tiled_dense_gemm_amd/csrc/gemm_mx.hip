@@ -10,10 +10,12 @@
 // work; C = scale * A * B with fp32 accumulation, bf16 output.
 //
 // Structure as the dense kernels (gemm_dense.hip): 256x256 workgroup tile of
-// 2x2 waves with 128x128 wave tiles (one wave per SIMD, 4x4 accumulators of
-// 32x32 in AGPRs), a 4-slot LDS ring of operand slabs fed straight from
-// global memory, k-steps emitted in program order with the loads and reads
-// placed after the MFMAs, persistent grouped grid with XCD remap. Next to
+// 2x4 waves with 128x64 wave tiles (two waves per SIMD, 4x2 accumulators of
+// 32x32) when the scales are staged wide, else 2x2 waves with 128x128 wave
+// tiles (one wave per SIMD, 4x4 accumulators in AGPRs); a 4-slot LDS ring
+// of operand slabs fed straight from global memory, k-steps emitted in
+// program order with the loads and reads placed after the MFMAs,
+// persistent grouped grid with XCD remap. Next to
 // each value slab (256 rows x 128 bytes) the ring holds its scale slab (256
 // rows x the stage's scale bytes).
 //
@@ -37,12 +39,16 @@ constexpr int BM = kBM, BN = kBN;
 constexpr int BKB = 128;                  // value bytes per row per stage
 constexpr int SLOTS = 4;
 constexpr int SLAB = BM * BKB;            // 32 KiB
-constexpr int WAVES_N = 2, WAVES = 4;
-constexpr int WM = BM / 2, WN = BN / WAVES_N;  // 128 x 128 wave tile
-constexpr int FM = WM / 32, FN = WN / 32;
-constexpr int DMA = SLAB / 1024 / WAVES;  // value loads per wave per slab
+constexpr int WM = BM / 2;               // wave tile rows (2 x WAVES_N waves)
+// Waves per workgroup row of the wide-scale kernel: 2 (4 waves, 128 x 128
+// wave tiles, one per SIMD) or 4 (8 waves, 128 x 64, two per SIMD; at
+// 8192^3, same process, bit-identical: MXFP4 4364 against 4029 TFLOP/s,
+// MXFP8 2622 against 2564). The other kernels run 2.
+#ifndef TKG_MX_WIDE_WAVES_N
+#define TKG_MX_WIDE_WAVES_N 4
+#endif
 
-template <int FMT>
+template <int FMT, int WAVES>
 struct Mx {
   static constexpr bool FP4 = FMT == kMxfp4;
   static constexpr int SB = FP4 ? 8 : 4;          // 32-element blocks per row per stage
@@ -52,7 +58,7 @@ struct Mx {
   static constexpr int SDMA = SSLAB / 256 / WAVES;  // 4-byte scale loads per wave per slab
   static constexpr int ROWS_PER_SDMA = 256 / SB;  // rows one scale load covers
   static constexpr int CB = FP4 ? 4 : 0;          // MFMA operand format: 4 = fp4, 0 = fp8
-  static_assert(SDMA >= 1, "scale slab needs a load per wave");
+  static_assert(SDMA >= 1 || WAVES != 4, "scale slab needs a load per wave");
 };
 
 struct TileState {
@@ -100,11 +106,16 @@ __device__ __forceinline__ f32x16_t mfma_mx(i32x8_t b, int sb, i32x8_t a, int sa
 // stages (a superstage); superstages alternate between two LDS slots of
 // 256 rows x 16 bytes per operand, and a stage's scale word sits at byte
 // SB * (stage mod U) of its row.
-template <int FMT, bool KTAIL, bool WIDE>
-__global__ __launch_bounds__(64 * WAVES)
-__attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int FMT, bool KTAIL, bool WIDE, int WAVES_N>
+__global__ __launch_bounds__(128 * WAVES_N)
+__attribute__((amdgpu_waves_per_eu(WAVES_N / 2, WAVES_N / 2)))
 void gemm_mx_kernel(MxArgs p) {
-  using S = Mx<FMT>;
+  constexpr int WAVES = 2 * WAVES_N;
+  constexpr int WN = BN / WAVES_N;                // wave tile columns
+  constexpr int FM = WM / 32, FN = WN / 32;       // 32x32 accumulators
+  constexpr int DMA = SLAB / 1024 / WAVES;        // value loads per wave per slab
+  static_assert(WIDE || WAVES == 4, "eight waves stage their scales wide");
+  using S = Mx<FMT, WAVES>;
   constexpr int KSTEPS = S::KSTEPS, PARTS = S::PARTS, SB = S::SB;
   constexpr int SSLAB = S::SSLAB, SDMA = S::SDMA;
   static_assert(!(WIDE && KTAIL), "wide scale staging needs whole stages");
@@ -151,8 +162,9 @@ void gemm_mx_kernel(MxArgs p) {
   const uint32_t s_row = lane / LPR, s_part = (lane % LPR) * 4u;
   const uint32_t s_lane_off = s_row * p.sbytes + s_part;
   const uint32_t s_rows_step = S::ROWS_PER_SDMA * p.sbytes;
-  // wide: wave w fetches rows 64w .. 64w+63 of both operands, lane l row
-  // 64w + l, 16 bytes from the superstage's first scale byte
+  // wide: with 4 waves, wave w fetches rows 64w .. 64w+63 of both
+  // operands; with 8, rows 64 (w % 4) .. +63 of A (w < 4) or B; lane l
+  // the row's 16 bytes from the superstage's first scale byte
   const uint32_t w_lane_off = lane * p.sbytes;
 
   // ---- fragment reads --------------------------------------------------------
@@ -236,10 +248,17 @@ void gemm_mx_kernel(MxArgs p) {
   };
   // wide: the superstage of tile ts that starts at `stage`, into `slot`
   auto load_superstage = [&](const TileState& ts, uint32_t stage, uint32_t slot) {
-    TKG_LDS uint8_t* dst = ssm + slot * WSLOT + wave * 1024;
-    const uint32_t soff = (uint32_t)wave * 64u * p.sbytes + stage * SB;
-    dma_b128_soff(ts.rsa, dst, w_lane_off, soff);
-    dma_b128_soff(ts.rsb, dst + BM * 16, w_lane_off, soff);
+    if constexpr (WAVES == 4) {
+      TKG_LDS uint8_t* dst = ssm + slot * WSLOT + wave * 1024;
+      const uint32_t soff = (uint32_t)wave * 64u * p.sbytes + stage * SB;
+      dma_b128_soff(ts.rsa, dst, w_lane_off, soff);
+      dma_b128_soff(ts.rsb, dst + BM * 16, w_lane_off, soff);
+    } else {
+      const int w4 = wave % 4;
+      TKG_LDS uint8_t* dst = ssm + slot * WSLOT + (wave / 4) * (BM * 16) + w4 * 1024;
+      const uint32_t soff = (uint32_t)w4 * 64u * p.sbytes + stage * SB;
+      dma_b128_soff(wave < 4 ? ts.rsa : ts.rsb, dst, w_lane_off, soff);
+    }
   };
 
   // ---- registers ---------------------------------------------------------------
@@ -466,12 +485,14 @@ template <int FMT>
 void launch_fmt(const MxArgs& a, int grid, hipStream_t stream) {
   // a stage spans BKB bytes of values; a ragged last stage masks its loads.
   // Scale rows that are whole 16-byte pieces (K % 512 == 0) are staged wide.
+  constexpr int WW = TKG_MX_WIDE_WAVES_N;
   if (a.vbytes % BKB != 0)
-    hipLaunchKernelGGL((gemm_mx_kernel<FMT, true, false>), dim3(grid), dim3(64 * WAVES), 0, stream, a);
+    hipLaunchKernelGGL((gemm_mx_kernel<FMT, true, false, 2>), dim3(grid), dim3(256), 0, stream, a);
   else if (a.sbytes % 16 == 0)
-    hipLaunchKernelGGL((gemm_mx_kernel<FMT, false, true>), dim3(grid), dim3(64 * WAVES), 0, stream, a);
+    hipLaunchKernelGGL((gemm_mx_kernel<FMT, false, true, WW>), dim3(grid), dim3(128 * WW), 0,
+                       stream, a);
   else
-    hipLaunchKernelGGL((gemm_mx_kernel<FMT, false, false>), dim3(grid), dim3(64 * WAVES), 0, stream, a);
+    hipLaunchKernelGGL((gemm_mx_kernel<FMT, false, false, 2>), dim3(grid), dim3(256), 0, stream, a);
 }
 
 }  // namespace
