@@ -47,6 +47,14 @@ constexpr int WM = BM / 2;               // wave tile rows (2 x WAVES_N waves)
 #ifndef TKG_MX_WIDE_WAVES_N
 #define TKG_MX_WIDE_WAVES_N 4
 #endif
+// With 8 waves: 1 = only the first wave row (one wave per SIMD) issues the
+// global->LDS loads, as in the dense kernels; 0 = every wave loads. Same
+// process, bit-identical: MXFP4 4415 against 4319 TFLOP/s, MXFP8 2665
+// against 2630 (its loader copy keeps 60 bytes per lane in scratch, and is
+// still faster).
+#ifndef TKG_MX_LOADERS
+#define TKG_MX_LOADERS 1
+#endif
 
 template <int FMT, int WAVES>
 struct Mx {
@@ -113,9 +121,11 @@ void gemm_mx_kernel(MxArgs p) {
   constexpr int WAVES = 2 * WAVES_N;
   constexpr int WN = BN / WAVES_N;                // wave tile columns
   constexpr int FM = WM / 32, FN = WN / 32;       // 32x32 accumulators
-  constexpr int DMA = SLAB / 1024 / WAVES;        // value loads per wave per slab
+  constexpr bool LOADERS = WAVES == 8 && TKG_MX_LOADERS;
+  constexpr int LOAD_WAVES = LOADERS ? 4 : WAVES;   // waves that issue loads
+  constexpr int DMA = SLAB / 1024 / LOAD_WAVES;   // value loads per loading wave per slab
   static_assert(WIDE || WAVES == 4, "eight waves stage their scales wide");
-  using S = Mx<FMT, WAVES>;
+  using S = Mx<FMT, LOAD_WAVES>;
   constexpr int KSTEPS = S::KSTEPS, PARTS = S::PARTS, SB = S::SB;
   constexpr int SSLAB = S::SSLAB, SDMA = S::SDMA;
   static_assert(!(WIDE && KTAIL), "wide scale staging needs whole stages");
@@ -133,6 +143,8 @@ void gemm_mx_kernel(MxArgs p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int lw = LOADERS ? wn : wave;             // index among the loading waves
+  const bool loader = !LOADERS || wm == 0;
   const int G = gridDim.x;
   int t = xcd_virtual_id(blockIdx.x, G, p.xcd_remap);
   if (t >= p.num_tiles) return;
@@ -146,7 +158,7 @@ void gemm_mx_kernel(MxArgs p) {
   if constexpr (KTAIL) {
 #pragma unroll
     for (int i = 0; i < DMA; ++i) {
-      const uint32_t q = wave * DMA + i;
+      const uint32_t q = lw * DMA + i;
       dma_kb[i] = dma_chunk(BKB, q, lane) * 16u;
       dma_off[i] = dma_row(BKB, q, lane) * p.vbytes + dma_kb[i];
     }
@@ -222,8 +234,8 @@ void gemm_mx_kernel(MxArgs p) {
   constexpr int NLOAD = DMA + (WIDE ? 0 : SDMA);
   auto issue_one = [&](const SlabLoad& s, int i) {
     if (i < DMA) {
-      TKG_LDS uint8_t* dst = smem + s.slot * SLAB + (wave * DMA + i) * 1024;
-      const uint32_t q = wave * DMA + i;
+      TKG_LDS uint8_t* dst = smem + s.slot * SLAB + (lw * DMA + i) * 1024;
+      const uint32_t q = lw * DMA + i;
       if constexpr (KTAIL) {
         const uint32_t off = (s.k0 + dma_kb[i] < p.vbytes) ? dma_off[i] + s.k0 : kOobOffset;
         dma_b128(s.r, dst, off);
@@ -232,8 +244,8 @@ void gemm_mx_kernel(MxArgs p) {
       }
     } else {
       const int j = i - DMA;
-      TKG_LDS uint8_t* dst = ssm + s.slot * SSLAB + (wave * SDMA + j) * 256;
-      const uint32_t base = (uint32_t)(wave * SDMA + j) * s_rows_step + s.s0;
+      TKG_LDS uint8_t* dst = ssm + s.slot * SSLAB + (lw * SDMA + j) * 256;
+      const uint32_t base = (uint32_t)(lw * SDMA + j) * s_rows_step + s.s0;
       if constexpr (KTAIL) {
         const uint32_t off = (s.s0 + s_part < p.sbytes) ? s_lane_off + base : kOobOffset;
         dma_b32(s.rs, dst, off);
@@ -248,9 +260,9 @@ void gemm_mx_kernel(MxArgs p) {
   };
   // wide: the superstage of tile ts that starts at `stage`, into `slot`
   auto load_superstage = [&](const TileState& ts, uint32_t stage, uint32_t slot) {
-    if constexpr (WAVES == 4) {
-      TKG_LDS uint8_t* dst = ssm + slot * WSLOT + wave * 1024;
-      const uint32_t soff = (uint32_t)wave * 64u * p.sbytes + stage * SB;
+    if constexpr (LOAD_WAVES == 4) {
+      TKG_LDS uint8_t* dst = ssm + slot * WSLOT + lw * 1024;
+      const uint32_t soff = (uint32_t)lw * 64u * p.sbytes + stage * SB;
       dma_b128_soff(ts.rsa, dst, w_lane_off, soff);
       dma_b128_soff(ts.rsb, dst + BM * 16, w_lane_off, soff);
     } else {
@@ -261,6 +273,10 @@ void gemm_mx_kernel(MxArgs p) {
     }
   };
 
+  // The rest in two copies: waves that issue loads and (with LOADERS) waves
+  // that only compute. Both run the same barriers.
+  auto main_loop = [&](auto loader_tag) {
+  constexpr bool IS_LOADER = decltype(loader_tag)::value;
   // ---- registers ---------------------------------------------------------------
   // A fragments single-buffered (re-read after their last MFMA), B double;
   // scale words of the stage per fragment, read during the previous stage's
@@ -320,9 +336,12 @@ void gemm_mx_kernel(MxArgs p) {
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
 
   // ---- prologue --------------------------------------------------------------
-  if constexpr (WIDE) load_superstage(cur, 0, 0);
+  if constexpr (WIDE && IS_LOADER) load_superstage(cur, 0, 0);
 #pragma unroll
-  for (int b = 0; b < SLOTS; ++b) issue(next_slab());
+  for (int b = 0; b < SLOTS; ++b) {
+    const SlabLoad l = next_slab();
+    if constexpr (IS_LOADER) issue(l);
+  }
   wait_vmcnt<(SLOTS - 2) * NLOAD>();   // slabs 0 and 1 (stage 0) have landed
   __syncthreads();
   int aslot = 0, bslot = 1;
@@ -372,10 +391,12 @@ void gemm_mx_kernel(MxArgs p) {
         if (boundary) {
           if (q < FM) read_scale(nsa + as_base + q * SFRAG, sa_n[q]);
           else if (q < FM + FN) read_scale(nsb + bs_base + (q - FM) * SFRAG, sb_n[q - FM]);
+          if constexpr (IS_LOADER) {
 #pragma unroll
-          for (int d = q * NDMA / (FM * FN); d < (q + 1) * NDMA / (FM * FN); ++d) {
-            if (d < NLOAD) issue_one(*l0, d);
-            else issue_one(*l1, d - NLOAD);
+            for (int d = q * NDMA / (FM * FN); d < (q + 1) * NDMA / (FM * FN); ++d) {
+              if (d < NLOAD) issue_one(*l0, d);
+              else issue_one(*l1, d - NLOAD);
+            }
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -418,7 +439,7 @@ void gemm_mx_kernel(MxArgs p) {
       // behind the stage-end wait
       const SlabLoad l0 = next_slab();
       const SlabLoad l1 = next_slab();
-      if constexpr (WIDE) {
+      if constexpr (WIDE && IS_LOADER) {
         // the next stage opens a superstage: fetch it now, into the slot no
         // wave reads any more (the other one holds this stage's scales)
         if ((g + 1) % U == 0) {
@@ -477,6 +498,11 @@ void gemm_mx_kernel(MxArgs p) {
     if (t >= p.num_tiles) break;
     cur = tile_state(p, t);
   }
+  };
+  if (loader)
+    main_loop(std::true_type{});
+  else
+    main_loop(std::false_type{});
   // the load cursor ran ahead into empty resources; let those LDS writes land
   wait_vmcnt<0>();
 }
