@@ -18,7 +18,7 @@ REPORT = os.path.join(os.path.dirname(os.path.dirname(__file__)), "tiled_dense_g
 # workgroups per CU, split-K)
 DEFAULT_PATHS = [
     "gemm_dense_kernelILi0ELi128ELi4ELi4ELi1ELi16ELi256ELi1ELb0E",   # bf16
-    "gemm_dense_kernelILi1ELi128ELi4ELi2ELi0ELi16ELi256ELi1ELb0E",   # fp8
+    "gemm_dense_kernelILi1ELi128ELi4ELi4ELi1ELi32ELi256ELi1ELb0E",   # fp8
     "gemm_dense_kernelILi0ELi128ELi4ELi2ELi0ELi16ELi128ELi2ELb",     # bf16 128x128 (+split-K)
     "gemm_dense_kernelILi1ELi128ELi4ELi2ELi0ELi16ELi128ELi2ELb",     # fp8 128x128 (+split-K)
     "gemm_fp4_kernelILi2E",
