@@ -233,25 +233,24 @@ const char *tkg_status_string(int status);
  *   xcd_remap -- 1 (default when grid is a multiple of 8) gives each XCD a
  *               contiguous range of tiles; 0 leaves the hardware's
  *               round-robin order.
- *   variant  -- bf16/fp8: kernel configuration, as (K bytes per row
- *               of an LDS slab, operand slabs in the LDS ring, waves per
- *               workgroup, waves issuing the global loads, MFMA block:
- *               16 = 16x16x32 bf16 / 16x16x128 fp8, 32 = 32x32x16 /
- *               32x32x64, workgroup tile edge). 0 = automatic (default):
- *               configuration 8, or configuration 9 when the product has
- *               fewer 256 x 256 output tiles than the device has compute
- *               units. bf16: 1 = (128, 5, 8, 4, 16, 256),
- *               2 = (128, 4, 8, 4, 32, 256), 3 = (128, 5, 8, 4, 32, 256),
- *               4 = (128, 4, 8, 8, 32, 256), 5 = (128, 4, 4, 4, 32, 256),
- *               6 = (64, 10, 8, 8, 32, 256), 7 = (128, 4, 4, 4, 16, 256),
- *               8 = (128, 4, 8, 4, 16, 256), 9 = (128, 4, 4, 4, 16, 128),
- *               10 = (128, 4, 8, 4, 16, 128). fp8: 1 = (128, 5, 4, 4, 32,
- *               256), 2 = (128, 4, 8, 4, 32, 256), 3 = (128, 5, 8, 4, 32,
- *               256), 4 = (128, 4, 8, 8, 32, 256), 5 = (128, 4, 4, 4, 32,
- *               256), 6 = (64, 10, 8, 8, 32, 256), 7 = (64, 10, 4, 4, 32,
- *               256), 8 = (128, 4, 4, 4, 16, 256), 9 = (128, 4, 4, 4, 16,
- *               128), 10 = (128, 4, 8, 4, 16, 128). TKG_ERR_SHAPE outside
- *               0..10.
+ *   variant  -- bf16/fp8: index of a kernel configuration, 0 .. n-1
+ *               with n = tkg_variant_info(dtype, 0, NULL);
+ *               tkg_variant_info() describes each (LDS ring shape, waves,
+ *               MFMA block, tile, swizzle, schedule). 0 = automatic: the
+ *               default configuration, or the 128 x 128 tile
+ *               configuration 4 when the product has fewer 256 x 256
+ *               output tiles than the device has compute units. The others
+ *               are the measured alternatives: bf16 1 = 5-slot ring,
+ *               2 = 32x32x16 blocks, 3 = one wave per SIMD, 4 / 5 = 128 x
+ *               128 tiles at two / one workgroups per compute unit, 6 =
+ *               swizzle off (plain LDS rows), 7 = early release of the B
+ *               slab, 8 = ping-pong, 9 = one-stage ring, 10 .. 14 = 64-byte
+ *               stages (32x32x16 blocks) in a ring of 1 .. 5 stages,
+ *               15 = ping-pong on four 64-byte stages; fp8 1 = 5-slot
+ *               ring, 2 = one wave per SIMD
+ *               on 16x16x128 blocks, 3 = one wave per SIMD on 32x32x64,
+ *               4 / 5 as bf16, 6 = swizzle off, 7 = early B release,
+ *               8 = ping-pong. TKG_ERR_SHAPE outside 0 .. n-1.
  *               4-bit product: 0 = 4 waves (default), 1 = 8 waves;
  *               TKG_ERR_SHAPE outside 0..1. Every variant of a product
  *               computes the same sums (the tests find them bit-identical).
@@ -286,6 +285,39 @@ int tkg_gemm_ex(int dtype, int64_t M, int64_t N, int64_t K, const void *A,
                 const void *A_scales, float a_scale, const void *B,
                 const void *B_scales, float b_scale, void *C, void *stream,
                 const tkg_opts *opts);
+
+/*
+ * Description of kernel configuration `variant` of dtype (TKG_DTYPE_BF16,
+ * _FP8 or _FP4_BLOCKSCALED; the MX types have the one configuration 0),
+ * written to *out when out is not NULL. Returns the number of
+ * configurations of the dtype, or a negative tkg_status (TKG_ERR_SHAPE for
+ * an unknown dtype or variant). No GPU work.
+ */
+typedef struct tkg_variant_desc {
+  int32_t stage_kbytes; /* K bytes per row of one LDS operand slab            */
+  int32_t slots;        /* operand slabs in the LDS ring (2 = one stage)      */
+  int32_t waves;        /* waves per workgroup                                */
+  int32_t load_waves;   /* waves that issue the global->LDS loads             */
+  int32_t mfma_block;   /* 16 (16x16 MFMA blocks) or 32 (32x32)               */
+  int32_t tile;         /* workgroup tile edge (tile x tile outputs)          */
+  int32_t per_cu;       /* workgroups per compute unit of the default grid    */
+  int32_t swizzle;      /* 1 = swizzled LDS rows, 0 = plain rows              */
+  int32_t schedule;     /* 0 interleaved, 1 early B release, 2 ping-pong      */
+} tkg_variant_desc;
+int tkg_variant_info(int dtype, int variant, tkg_variant_desc *out);
+
+/*
+ * Whether tkg_gemm_ex(dtype, M, N, K, ..., variant) runs the masked kernel
+ * instance, whose every global->LDS load carries its whole offset per lane
+ * so that the buffer bounds check turns rows past M or N and chunks past K
+ * into zeros (1), or the unmasked one, which passes part of each offset as
+ * the scalar offset that the bounds check does not cover (0). The unmasked
+ * instance runs only when every tile is whole (M and N multiples of the
+ * tile edge) and every stage lies inside K. `variant` is the configuration
+ * itself (0 = the default one, not resolved by tile count). Returns 1, 0 or
+ * a negative tkg_status. No GPU work.
+ */
+int tkg_launch_masked(int dtype, int64_t M, int64_t N, int64_t K, int variant);
 
 /*
  * LDS layout introspection for the CPU bank-conflict model (no GPU work).

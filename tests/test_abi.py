@@ -156,3 +156,68 @@ def test_build_script_loads_without_its_package():
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
     assert callable(mod.build) and mod.LIB.endswith("libtkg.so")
+
+
+def test_splitk_count_rejects_oversized_k():
+    # K beyond the product's limit is a shape error in the count query too
+    # (it used to divide by a split length that overflowed to zero)
+    for k in (1 << 31, 1 << 23, 4194312):
+        assert L.tkg_gemm_splitk_count(0, 256, 256, k, 1) == S["TKG_ERR_SHAPE"]
+    assert L.tkg_gemm_splitk_count(1, 256, 256, 1 << 24, 0) == S["TKG_ERR_SHAPE"]
+    assert L.tkg_gemm_splitk_count(0, 256, 256, 12, 1) == S["TKG_ERR_SHAPE"]   # K % 8
+    assert L.tkg_gemm_splitk_count(0, -1, 256, 1024, 1) == S["TKG_ERR_SHAPE"]
+    assert L.tkg_gemm_splitk_count(0, 256, 256, 4194296, 1) == 1
+
+
+def test_variant_table():
+    # every dtype reports its configurations; the defaults are the measured
+    # ones, and the ablation entries differ from the default in one field
+    assert tkg.num_variants(tkg.DTYPE_BF16) == 16
+    assert tkg.num_variants(tkg.DTYPE_FP8) == 9
+    assert tkg.num_variants(tkg.DTYPE_FP4_BLOCKSCALED) == 2
+    assert tkg.num_variants(tkg.DTYPE_MXFP4) == tkg.num_variants(tkg.DTYPE_MXFP8) == 1
+    for d in (tkg.DTYPE_BF16, tkg.DTYPE_FP8):
+        v0 = tkg.variant_info(d, 0)
+        assert (v0["stage_kbytes"], v0["slots"], v0["waves"], v0["load_waves"], v0["tile"],
+                v0["swizzle"], v0["schedule"]) == (128, 4, 8, 4, 256, 1, 0)
+        small = tkg.variant_info(d, 4)
+        assert small["tile"] == 128 and small["per_cu"] == 2
+        swz = tkg.variant_info(d, 6)
+        assert swz["swizzle"] == 0 and {k: v for k, v in swz.items() if k != "swizzle"} == \
+            {k: v for k, v in v0.items() if k != "swizzle"}
+        assert tkg.variant_info(d, 7)["schedule_name"] == "early B release"
+        assert tkg.variant_info(d, 8)["schedule_name"] == "ping-pong"
+        n = tkg.num_variants(d)
+        assert L.tkg_variant_info(d, n, None) == S["TKG_ERR_SHAPE"]
+        assert L.tkg_variant_info(d, -1, None) == S["TKG_ERR_SHAPE"]
+    # the ring-depth sweep: 64-byte stages in rings of 1 .. 5 stages
+    depth = [tkg.variant_info(tkg.DTYPE_BF16, v) for v in range(10, 15)]
+    assert [d["slots"] // 2 for d in depth] == [1, 2, 3, 4, 5]
+    assert {d["stage_kbytes"] for d in depth} == {64}
+    assert L.tkg_variant_info(9, 0, None) == S["TKG_ERR_SHAPE"]
+
+
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_masked_instance_choice(dtype):
+    # the unmasked instance (part of each load's offset in the scalar offset,
+    # which the buffer bounds check does not cover) runs only on whole tiles
+    # with every stage inside K
+    eb = 2 if dtype == 0 else 1
+    for v in range(tkg.num_variants(dtype)):
+        info = tkg.variant_info(dtype, v)
+        bt, trip = info["tile"], 2 * info["stage_kbytes"] // eb   # K elements
+        assert not tkg.launch_masked(dtype, 8 * bt, 4 * bt, 4 * trip, v), v
+        assert tkg.launch_masked(dtype, 8 * bt - 1, 4 * bt, 4 * trip, v), v
+        assert tkg.launch_masked(dtype, 8 * bt, 4 * bt + 16, 4 * trip, v), v
+        assert tkg.launch_masked(dtype, 300, 260, 8192, v), v
+        assert tkg.launch_masked(dtype, 8 * bt, 4 * bt, 4 * trip + 16, v), v
+    assert tkg.launch_masked(tkg.DTYPE_FP4_BLOCKSCALED, 8192, 8192, 8192)
+    assert not tkg.launch_masked(tkg.DTYPE_MXFP4, 8192, 8192, 8192)
+    assert tkg.launch_masked(tkg.DTYPE_MXFP4, 300, 8192, 8192)
+    assert tkg.launch_masked(tkg.DTYPE_MXFP8, 8192, 8200, 8192)
+    # a stage is 128 bytes of values: an MXFP4 row of 8320 elements ends
+    # mid-stage, an MXFP8 one does not
+    assert tkg.launch_masked(tkg.DTYPE_MXFP4, 8192, 8192, 8320)
+    assert not tkg.launch_masked(tkg.DTYPE_MXFP8, 8192, 8192, 8320)
+    assert L.tkg_launch_masked(0, -1, 8, 8, 0) == S["TKG_ERR_SHAPE"]
+    assert L.tkg_launch_masked(0, 8, 8, 8, 99) == S["TKG_ERR_SHAPE"]

@@ -172,3 +172,17 @@ def test_mx_config_shapes_sampled(dev, elem, n):
         R = oracle.gemm_mx(a, sa, b, sb, elem)
         assert relfro(_result(C[i0:i0 + 64, j0:j0 + 64]), R) <= MX_RELFRO, (n, i0, j0)
     del C
+
+
+@pytest.mark.parametrize("elem", ELEMS)
+def test_mx_ragged_tiles_long_k(dev, elem):
+    # Regression: ragged M and N with K a multiple of 512 (the wide scale
+    # staging shape) must take the masked instance: rows past M / N lie
+    # beyond the operands and only per-lane offsets are bounds-checked.
+    M, N, K = 300, 260, 4096
+    assert tkg.launch_masked(DTYPE[elem], M, N, K)
+    assert not tkg.launch_masked(DTYPE[elem], 512, 256, K)
+    Av, As = gi.mx_operand(90, M, K, elem)
+    Bv, Bs = gi.mx_operand(91, N, K, elem)
+    C = GEMM[elem](_up(Av, dev), _up(As, dev), _up(Bv, dev), _up(Bs, dev))
+    _check(_result(C), Av, As, Bv, Bs, elem, ("ragged long K", M, N, K))

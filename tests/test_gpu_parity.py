@@ -30,7 +30,6 @@ pytestmark = pytest.mark.gpu
 BF16_RELFRO = 1e-3
 BF16_ELEM_REL, BF16_ELEM_ABS = 1e-2, 1e-3
 LOWP_RELFRO = 2e-2
-DENSE_VARIANTS = 11  # kernel configurations selectable by tkg_opts.variant
 
 
 @pytest.fixture(scope="module")
@@ -53,6 +52,30 @@ def check_bf16(G, A64, Bt64, what=""):
     err = relfro(G, round_to_bf16(R))
     assert err <= BF16_RELFRO, (what, err)
     bound = BF16_ELEM_REL * oracle.abs_gemm_f64(A64, Bt64) + BF16_ELEM_ABS
+    assert np.all(np.abs(G - R) <= bound), (what, float(np.max(np.abs(G - R) - bound)))
+    return err
+
+
+def lowp_elem_bound(absprod, K):
+    """Per-element bound for products of exactly representable operands
+    (fp8 and 4-bit): each product is exact in fp32, the fp32 sum of K terms
+    is off by at most K 2^-24 (|A||B|)_ij, the fp32 scale multiply by 2^-24
+    relative, and the bf16 rounding by 2^-9 relative:
+    |G - C| <= (2^-9 + (K + 2) 2^-24) (|A||B|)_ij (x 1.001 for the bound's
+    own rounding)."""
+    return (2.0 ** -9 + (K + 2) * 2.0 ** -24) * 1.001 * absprod + 1e-30
+
+
+def check_fp8_elementwise(G, a, sa, b, sb, what=""):
+    """fp8: relative Frobenius <= 2e-2 against the oracle on the same
+    dequantized inputs (the stated tolerance) and the per-element bound of
+    lowp_elem_bound."""
+    R = oracle.gemm_fp8(a, sa, b, sb)
+    err = relfro(G, R)
+    assert err <= LOWP_RELFRO, (what, err)
+    Ad = decode_e4m3(a) * float(sa)
+    Bd = decode_e4m3(b) * float(sb)
+    bound = lowp_elem_bound(oracle.abs_gemm_f64(Ad, Bd), a.shape[1])
     assert np.all(np.abs(G - R) <= bound), (what, float(np.max(np.abs(G - R) - bound)))
     return err
 
@@ -174,35 +197,80 @@ def test_bf16_launch_options_agree(dev):
         assert torch.equal(C.view(torch.int16), ref.view(torch.int16)), (grid, gm, xr)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-def test_kernel_variants_agree(dev, dtype):
-    # every compiled kernel configuration (LDS ring shape, waves per
-    # workgroup) computes the same bits, including ragged edges
-    M, N, K = 1300, 700, 1088
+def _dense_operands(dev, dtype, M, N, K, seed):
     if dtype == "bf16":
-        A = gi.device.bf16_operand(3, M, K, std=K ** -0.5, device=dev)
-        Bt = gi.device.bf16_operand(4, N, K, std=K ** -0.5, device=dev)
-        d, sa, sb = tkg.DTYPE_BF16, 1.0, 1.0
+        A = gi.device.bf16_operand(seed, M, K, std=K ** -0.5, device=dev)
+        Bt = gi.device.bf16_operand(seed + 1, N, K, std=K ** -0.5, device=dev)
+        return A, Bt, tkg.DTYPE_BF16, 1.0, 1.0
+    A, sa = gi.device.fp8_operand(seed, M, K, device=dev)
+    Bt, sb = gi.device.fp8_operand(seed + 1, N, K, device=dev)
+    return A, Bt, tkg.DTYPE_FP8, sa, sb
+
+
+def _check_dense(dtype, A, Bt, sa, sb, C, what):
+    a = to_numpy_u16(A) if dtype == "bf16" else to_numpy_u8(A)
+    b = to_numpy_u16(Bt) if dtype == "bf16" else to_numpy_u8(Bt)
+    G = _bf16_result(C)
+    if dtype == "bf16":
+        check_bf16(G, decode_bf16(a), decode_bf16(b), what)
     else:
-        A, sa = gi.device.fp8_operand(3, M, K, device=dev)
-        Bt, sb = gi.device.fp8_operand(4, N, K, device=dev)
-        d = tkg.DTYPE_FP8
+        check_fp8_elementwise(G, a, sa, b, sb, what)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("M,N,K,grid", [(1300, 700, 1088, 0), (1024, 768, 2048, 0),
+                                        (1024, 768, 2048, 5), (520, 1280, 1664, 3)])
+def test_kernel_variants_agree(dev, dtype, M, N, K, grid):
+    # every compiled kernel configuration (LDS ring shape and depth, waves
+    # per workgroup, MFMA block, swizzle on or off, interleaved, early-B or
+    # ping-pong schedule) computes the same bits: on ragged edges (masked
+    # instances), on whole tiles (unmasked instances) and with fewer
+    # workgroups than tiles (the persistent loop crosses tiles and finishes)
+    A, Bt, d, sa, sb = _dense_operands(dev, dtype, M, N, K, 3)
+    nv = tkg.num_variants(d)
+    assert nv >= 9
     outs = []
-    for v in range(DENSE_VARIANTS):
+    for v in range(nv):
+        C = torch.full((M, N), 3.0, dtype=torch.bfloat16, device=dev)
+        assert tkg.tkg_gemm_ex(d, M, N, K, A, None, sa, Bt, None, sb, C, variant=v,
+                               grid=grid) == 0, v
+        outs.append(C)
+    for v in range(1, nv):
+        assert torch.equal(outs[v].view(torch.int16), outs[0].view(torch.int16)), (
+            v, tkg.variant_info(d, v))
+    _check_dense(dtype, A, Bt, sa, sb, outs[0], ("variants", M, N, K, grid))
+    assert tkg.tkg_gemm_ex(d, M, N, K, A, None, sa, Bt, None, sb, outs[0], variant=nv) == -2
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_kernel_variants_k_zero(dev, dtype):
+    # K = 0 writes zeros in every configuration (the ping-pong loop has no
+    # k-step to hang the finish on)
+    d = tkg.DTYPE_BF16 if dtype == "bf16" else tkg.DTYPE_FP8
+    A = torch.empty((300, 0), dtype=torch.uint8, device=dev)
+    for v in range(tkg.num_variants(d)):
+        C = torch.full((300, 520), 5.0, dtype=torch.bfloat16, device=dev)
+        assert tkg.tkg_gemm_ex(d, 300, 520, 0, A, None, 1.0, A, None, 1.0, C, variant=v) == 0
+        assert torch.count_nonzero(C).item() == 0, v
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("M,N,K", [(300, 260, 8192), (2048 + 40, 1024 + 8, 4096)])
+def test_ragged_tiles_long_k(dev, dtype, M, N, K):
+    # Regression: ragged M / N tiles with K a whole number of stages. The
+    # rows past M (N) lie beyond the operands, so these launches must take
+    # the masked instance, whose loads are bounds-checked per lane (the
+    # scalar offset of the unmasked one is outside the bounds check). The
+    # instance choice is checked here through tkg_launch_masked, the
+    # results on every configuration.
+    d = tkg.DTYPE_BF16 if dtype == "bf16" else tkg.DTYPE_FP8
+    for v in (0, tkg.num_variants(d) - 1):
+        assert tkg.launch_masked(d, M, N, K, v)
+    A, Bt, d, sa, sb = _dense_operands(dev, dtype, M, N, K, 11)
+    for v in range(tkg.num_variants(d)):
         C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         assert tkg.tkg_gemm_ex(d, M, N, K, A, None, sa, Bt, None, sb, C, variant=v) == 0
-        outs.append(C)
-    for v in range(1, DENSE_VARIANTS):
-        assert torch.equal(outs[v].view(torch.int16), outs[0].view(torch.int16)), v
-    a = A.view(torch.int16).cpu().numpy().view(np.uint16) if dtype == "bf16" else to_numpy_u8(A)
-    b = Bt.view(torch.int16).cpu().numpy().view(np.uint16) if dtype == "bf16" else to_numpy_u8(Bt)
-    G = _bf16_result(outs[0])
-    if dtype == "bf16":
-        check_bf16(G, decode_bf16(a), decode_bf16(b), "variants")
-    else:
-        assert relfro(G, oracle.gemm_fp8(a, sa, b, sb)) <= LOWP_RELFRO
-    assert tkg.tkg_gemm_ex(d, M, N, K, A, None, sa, Bt, None, sb, outs[0],
-                           variant=DENSE_VARIANTS) == -2
+        _check_dense(dtype, A, Bt, sa, sb, C, ("ragged long K", v))
 
 
 def test_bf16_side_stream(dev):
@@ -270,10 +338,9 @@ def test_fp8_config_shapes_sampled(dev, M, N, K):
     C = tkg.gemm_fp8(A, sa, Bt, sb)
     torch.cuda.synchronize()
     for (i0, j0) in sample_tiles(M, N, K):
-        R = oracle.gemm_fp8(to_numpy_u8(A[i0:i0 + 64]), sa,
-                            to_numpy_u8(Bt[j0:j0 + 64]), sb)
         G = _bf16_result(C[i0:i0 + 64, j0:j0 + 64])
-        assert relfro(G, R) <= LOWP_RELFRO, (M, N, K, i0, j0)
+        check_fp8_elementwise(G, to_numpy_u8(A[i0:i0 + 64]), sa,
+                              to_numpy_u8(Bt[j0:j0 + 64]), sb, (M, N, K, i0, j0))
 
 
 # ----------------------------------------------------- block-scaled 4-bit
@@ -372,9 +439,14 @@ def test_fp4_config_shapes_sampled(dev, n):
     torch.cuda.synchronize()
     tiles = sample_tiles(n, n, n, n_random=4 if n > 20000 else 8)
     for (i0, j0) in tiles:
-        R = oracle.gemm_fp4_blockscaled(
-            to_numpy_u8(Ap[i0:i0 + 64]), to_numpy_u8(As[i0:i0 + 64]), ta,
-            to_numpy_u8(Bp[j0:j0 + 64]), to_numpy_u8(Bs[j0:j0 + 64]), tb)
+        a, asc = to_numpy_u8(Ap[i0:i0 + 64]), to_numpy_u8(As[i0:i0 + 64])
+        b, bsc = to_numpy_u8(Bp[j0:j0 + 64]), to_numpy_u8(Bs[j0:j0 + 64])
+        R = oracle.gemm_fp4_blockscaled(a, asc, ta, b, bsc, tb)
         G = _bf16_result(C[i0:i0 + 64, j0:j0 + 64])
         assert relfro(G, R) <= LOWP_RELFRO, (n, i0, j0)
+        # per element (the MX tests' form): fp32 sums of exact products
+        absprod = float(ta) * float(tb) * oracle.abs_gemm_f64(
+            oracle.dequant_fp4_blockscaled(a, asc), oracle.dequant_fp4_blockscaled(b, bsc))
+        bound = lowp_elem_bound(absprod, n)
+        assert np.all(np.abs(G - R) <= bound), (n, i0, j0, float(np.max(np.abs(G - R) - bound)))
     del C

@@ -105,3 +105,27 @@ def test_splitk_repeated_calls_reuse_workspace(dev):
     a = to_numpy_u16(A).view(np.uint16); b = to_numpy_u16(Bt).view(np.uint16)
     check_bf16(_res(C), decode_bf16(a), decode_bf16(b), "first")
     check_bf16(_res(C2), decode_bf16(a[:100, :4096]), decode_bf16(b[:300, :4096]), "second")
+
+
+def test_splitk_side_stream_owned_workspace(dev):
+    # the binding allocates the workspace itself and runs on a side stream:
+    # the block must stay reserved for that stream (record_stream) while an
+    # allocation on the current stream follows at once
+    M, N, K = 512, 512, 16384
+    a = gi.bf16_operand(50, M, K, std=K ** -0.5)
+    b = gi.bf16_operand(51, N, K, std=K ** -0.5)
+    A = torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    Bt = torch.from_numpy(b.view(np.int16)).to(dev).view(torch.bfloat16)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    C.record_stream(s)
+    need = tkg.splitk_workspace_size(tkg.DTYPE_BF16, M, N, K, 8)
+    for _ in range(3):
+        tkg.gemm_splitk(A, Bt, splits=8, out=C, stream=s)
+        # same-size block on the current stream, written right away
+        junk = torch.empty(need, dtype=torch.uint8, device=dev)
+        junk.fill_(0x7F)
+    s.synchronize()
+    torch.cuda.synchronize()
+    check_bf16(_res(C), decode_bf16(a), decode_bf16(b), "side stream")

@@ -23,6 +23,8 @@ __all__ = [
     "TkgError", "DTYPE_BF16", "DTYPE_FP8", "DTYPE_FP4_BLOCKSCALED",
     "DTYPE_MXFP4", "DTYPE_MXFP8", "gemm_mxfp4", "gemm_mxfp8",
     "STATUS", "LIB_PATH", "tkg_attention_fwd", "attn_lds_offsets",
+    "num_variants", "variant_info", "launch_masked", "gemm_splitk",
+    "splitk_workspace_size", "splitk_count",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtkg.so")
@@ -44,6 +46,12 @@ class TkgError(RuntimeError):
 class TkgOpts(ctypes.Structure):
     _fields_ = [("grid", ctypes.c_int32), ("group_m", ctypes.c_int32),
                 ("xcd_remap", ctypes.c_int32), ("variant", ctypes.c_int32)]
+
+
+class VariantDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "stage_kbytes", "slots", "waves", "load_waves", "mfma_block", "tile",
+        "per_cu", "swizzle", "schedule")]
 
 
 def _load() -> ctypes.CDLL:
@@ -98,6 +106,10 @@ def _load() -> ctypes.CDLL:
     L.tkg_attn_lds_offsets.argtypes = [i32, i32, i32, i32, i32, i32,
                                        ctypes.POINTER(ctypes.c_uint32)]
     L.tkg_attn_lds_offsets.restype = i32
+    L.tkg_variant_info.argtypes = [i32, i32, ctypes.POINTER(VariantDesc)]
+    L.tkg_variant_info.restype = i32
+    L.tkg_launch_masked.argtypes = [i32, i64, i64, i64, i32]
+    L.tkg_launch_masked.restype = i32
     return L
 
 
@@ -116,6 +128,37 @@ def attn_lds_offsets(d: int, kind: int, i0=0, i1=0, i2=0, i3=0):
 
 def tkg_status_string(status: int) -> str:
     return lib.tkg_status_string(int(status)).decode()
+
+
+SCHEDULES = {0: "interleaved", 1: "early B release", 2: "ping-pong"}
+
+
+def num_variants(dtype: int) -> int:
+    """Kernel configurations of a dtype (``tkg_variant_info``)."""
+    r = lib.tkg_variant_info(int(dtype), 0, None)
+    if r < 0:
+        raise TkgError(r, "tkg_variant_info")
+    return r
+
+
+def variant_info(dtype: int, variant: int) -> dict:
+    """The configuration behind ``variant`` of a dtype (see tkg.h)."""
+    d = VariantDesc()
+    r = lib.tkg_variant_info(int(dtype), int(variant), ctypes.byref(d))
+    if r < 0:
+        raise TkgError(r, "tkg_variant_info")
+    out = {n: getattr(d, n) for n, _ in VariantDesc._fields_}
+    out["schedule_name"] = SCHEDULES.get(d.schedule, "?")
+    return out
+
+
+def launch_masked(dtype: int, M: int, N: int, K: int, variant: int = 0) -> bool:
+    """Whether the launch runs the masked kernel instance (every load
+    bounds-checked per lane; ``tkg_launch_masked``). No GPU work."""
+    r = lib.tkg_launch_masked(int(dtype), int(M), int(N), int(K), int(variant))
+    if r < 0:
+        raise TkgError(r, "tkg_launch_masked")
+    return bool(r)
 
 
 def lds_row_bytes(dtype: int) -> int:
@@ -261,7 +304,8 @@ def gemm_splitk(A, Bt, scale_a=1.0, scale_b=1.0, splits=0, workspace=None,
         _check_mat(Bt, "Bt", N, K, _fp8_types(), A.device)
     out = _out(out, M, N, A.device)
     need = splitk_workspace_size(dtype, M, N, K, splits)
-    if workspace is None and need > 0:
+    own = workspace is None and need > 0
+    if own:
         workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
     ws_ptr = None if workspace is None else workspace.data_ptr()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -269,6 +313,10 @@ def gemm_splitk(A, Bt, scale_a=1.0, scale_b=1.0, splits=0, workspace=None,
         st = lib.tkg_gemm_splitk(dtype, M, N, K, A.data_ptr(), float(scale_a),
                                  Bt.data_ptr(), float(scale_b), out.data_ptr(),
                                  ws_ptr, ws_bytes, int(splits), _stream_ptr(stream))
+    if own and stream is not None:
+        # the kernels use the block on `stream`: keep the caching allocator
+        # from handing it out again before that stream is past them
+        workspace.record_stream(stream)
     _raise(st, "tkg_gemm_splitk")
     return out
 

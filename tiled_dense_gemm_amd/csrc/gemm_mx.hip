@@ -509,10 +509,12 @@ void gemm_mx_kernel(MxArgs p) {
 
 template <int FMT>
 void launch_fmt(const MxArgs& a, int grid, hipStream_t stream) {
-  // a stage spans BKB bytes of values; a ragged last stage masks its loads.
-  // Scale rows that are whole 16-byte pieces (K % 512 == 0) are staged wide.
+  // A ragged last stage, or a ragged M or N tile (rows past the operand,
+  // which the scalar part of an unmasked load's offset would reach outside
+  // the bounds check), runs the masked instance. Scale rows that are whole
+  // 16-byte pieces (K % 512 == 0) are staged wide.
   constexpr int WW = TKG_MX_WIDE_WAVES_N;
-  if (a.vbytes % BKB != 0)
+  if (mx_masked((MxType)FMT, a.M, a.N, a.vbytes, a.sbytes))
     hipLaunchKernelGGL((gemm_mx_kernel<FMT, true, false, 2>), dim3(grid), dim3(256), 0, stream, a);
   else if (a.sbytes % 16 == 0)
     hipLaunchKernelGGL((gemm_mx_kernel<FMT, false, true, WW>), dim3(grid), dim3(128 * WW), 0,
@@ -522,6 +524,12 @@ void launch_fmt(const MxArgs& a, int grid, hipStream_t stream) {
 }
 
 }  // namespace
+
+bool mx_masked(MxType fmt, int64_t M, int64_t N, uint32_t vbytes, uint32_t sbytes) {
+  (void)fmt;
+  (void)sbytes;
+  return vbytes % BKB != 0 || M % BM != 0 || N % BN != 0;
+}
 
 hipError_t launch_mx(MxType fmt, const MxArgs& a, int grid, hipStream_t stream) {
   if (fmt == kMxfp4) launch_fmt<kMxfp4>(a, grid, stream);

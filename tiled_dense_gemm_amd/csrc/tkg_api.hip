@@ -93,7 +93,7 @@ int run_dense(tkg::DenseType dt, int64_t M, int64_t N, int64_t K,
   // units idle (fewer tiles than units), e.g. one GPU's N/8 shard of a
   // product split over 8 GPUs, or K-heavy small products.
   int variant = opts ? opts->variant : 0;
-  if (variant < 0 || variant >= tkg::dense_num_variants()) return TKG_ERR_SHAPE;
+  if (variant < 0 || variant >= tkg::dense_num_variants(dt)) return TKG_ERR_SHAPE;
   if (variant == 0) {
     int cus = 0;
     st = cu_count(&cus);
@@ -173,6 +173,7 @@ int splitk_plan(tkg::DenseType dt, int64_t M, int64_t N, int64_t K, int req, Spl
   if (s > chunks) s = chunks;
   if (s < 1) s = 1;
   const int64_t per = (chunks + s - 1) / s;        // two-stage chunks per split
+  if (per * unit > (int64_t)UINT32_MAX) return TKG_ERR_SHAPE;
   sp->ksplit = (uint32_t)(per * unit);
   sp->splits = (int)((kbytes + sp->ksplit - 1) / sp->ksplit);
   if (sp->splits < 1) sp->splits = 1;
@@ -577,10 +578,58 @@ int64_t tkg_gemm_splitk_workspace_size(int dtype, int64_t M, int64_t N, int64_t 
 int tkg_gemm_splitk_count(int dtype, int64_t M, int64_t N, int64_t K, int splits) {
   if (dtype != TKG_DTYPE_BF16 && dtype != TKG_DTYPE_FP8) return TKG_ERR_SHAPE;
   const tkg::DenseType dt = dtype == TKG_DTYPE_BF16 ? tkg::kBf16 : tkg::kFp8;
-  if (M < 0 || N < 0 || K < 0) return TKG_ERR_SHAPE;
+  const int64_t kmult = (dt == tkg::kBf16) ? 8 : 16;
+  const int64_t kmax = (dt == tkg::kBf16) ? 4194303 : 8388607;
+  int st = check_common(M, N, K, kmult, kmax);
+  if (st != TKG_OK) return st;
   SplitPlan sp;
-  const int st = splitk_plan(dt, M, N, K, splits, &sp);
+  st = splitk_plan(dt, M, N, K, splits, &sp);
   return st != TKG_OK ? st : sp.splits;
+}
+
+int tkg_variant_info(int dtype, int variant, tkg_variant_desc* out) {
+  tkg_variant_desc d{};
+  int n = 0;
+  if (dtype == TKG_DTYPE_BF16 || dtype == TKG_DTYPE_FP8) {
+    const tkg::DenseType dt = dtype == TKG_DTYPE_BF16 ? tkg::kBf16 : tkg::kFp8;
+    n = tkg::dense_num_variants(dt);
+    if (variant < 0 || variant >= n) return TKG_ERR_SHAPE;
+    tkg::dense_variant_desc(dt, variant, &d.stage_kbytes, &d.slots, &d.waves, &d.load_waves,
+                            &d.mfma_block, &d.tile, &d.per_cu, &d.swizzle, &d.schedule);
+  } else if (dtype == TKG_DTYPE_FP4_BLOCKSCALED) {
+    n = tkg::fp4_num_variants();
+    if (variant < 0 || variant >= n) return TKG_ERR_SHAPE;
+    // a stage of 64 bytes of packed values per row (and 8 of scales); a
+    // ring of 4 stages, i.e. 8 operand slabs
+    d = tkg_variant_desc{(int32_t)tkg::fp4_stage_vbytes(), 8, variant == 1 ? 8 : 4,
+                         variant == 1 ? 8 : 4, 32, kBM, 1, 1, 0};
+  } else if (dtype == TKG_DTYPE_MXFP4 || dtype == TKG_DTYPE_MXFP8) {
+    n = 1;
+    if (variant != 0) return TKG_ERR_SHAPE;
+    d = tkg_variant_desc{128, 4, 8, 4, 32, kBM, 1, 1, 0};
+  } else {
+    return TKG_ERR_SHAPE;
+  }
+  if (out != nullptr) *out = d;
+  return n;
+}
+
+int tkg_launch_masked(int dtype, int64_t M, int64_t N, int64_t K, int variant) {
+  if (M < 0 || N < 0 || K < 0) return TKG_ERR_SHAPE;
+  const int n = tkg_variant_info(dtype, variant, nullptr);
+  if (n < 0) return n;
+  switch (dtype) {
+    case TKG_DTYPE_BF16:
+      return tkg::dense_masked(tkg::kBf16, variant, M, N, (uint32_t)(K * 2)) ? 1 : 0;
+    case TKG_DTYPE_FP8:
+      return tkg::dense_masked(tkg::kFp8, variant, M, N, (uint32_t)K) ? 1 : 0;
+    case TKG_DTYPE_FP4_BLOCKSCALED:
+      return 1;   // every load of the 4-bit kernel carries its whole offset per lane
+    case TKG_DTYPE_MXFP4:
+      return tkg::mx_masked(tkg::kMxfp4, M, N, (uint32_t)(K / 2), (uint32_t)(K / 32)) ? 1 : 0;
+    default:
+      return tkg::mx_masked(tkg::kMxfp8, M, N, (uint32_t)K, (uint32_t)(K / 32)) ? 1 : 0;
+  }
 }
 
 }  // extern "C"

@@ -88,10 +88,18 @@ hipError_t launch_attn(const AttnArgs& a, int D, bool causal, hipStream_t stream
 constexpr int kBM = 256;
 constexpr int kBN = 256;
 
-// variant: index of a compiled ring shape (0 = default; out of range = 0).
+// variant: index of a compiled ring shape (0 = default), below
+// dense_num_variants(dt); hipErrorInvalidValue otherwise.
 hipError_t launch_dense(DenseType dt, const DenseArgs& a, int grid, int variant,
                         hipStream_t stream);
-int dense_num_variants();
+int dense_num_variants(DenseType dt);
+// the configuration of `variant` (see tkg_variant_desc in tkg.h)
+void dense_variant_desc(DenseType dt, int variant, int32_t* stage_kbytes, int32_t* slots,
+                        int32_t* waves, int32_t* load_waves, int32_t* mfma_block,
+                        int32_t* tile, int32_t* per_cu, int32_t* swizzle, int32_t* schedule);
+// whether the launch runs the masked instance (every load's whole offset
+// per-lane and bounds-checked): ragged M or N tiles, or a K tail
+bool dense_masked(DenseType dt, int variant, int64_t M, int64_t N, uint32_t kbytes);
 // MFMA block (16 or 32) of the default configuration for dt
 int dense_default_mi(DenseType dt);
 // workgroup tile edge (256 or 128) of variant `variant`
@@ -108,11 +116,14 @@ hipError_t launch_dense_reduce(DenseType dt, const DenseArgs& a, int variant,
                                hipStream_t stream);
 // the variant that variant 0 resolves to when the product has fewer
 // 256 x 256 output tiles than compute units
-constexpr int kDenseSmallTileVariant = 9;
+constexpr int kDenseSmallTileVariant = 4;
 hipError_t launch_fp4(const Fp4Args& a, int grid, int variant,
                       hipStream_t stream);
 int fp4_num_variants();
 hipError_t launch_mx(MxType fmt, const MxArgs& a, int grid, hipStream_t stream);
+// whether the MX launch runs the masked instance (ragged M or N tiles, or a
+// ragged last stage): every load's whole offset per lane, bounds-checked
+bool mx_masked(MxType fmt, int64_t M, int64_t N, uint32_t vbytes, uint32_t sbytes);
 
 // K bytes per stage row of each kernel family (for the host).
 uint32_t dense_stage_kbytes();

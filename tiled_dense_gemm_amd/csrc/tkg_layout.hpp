@@ -41,16 +41,18 @@
 namespace tkg {
 
 // XOR mask applied to the chunk index of row `r` in a tile whose rows are
-// `row_bytes` long (64 or 128).
-TKG_HD constexpr uint32_t swz_mask(uint32_t row_bytes, uint32_t r) {
-  return row_bytes == 128 ? ((r & 7u) ^ (((r >> 3) & 1u) * 7u)) : ((r >> 2) & 3u);
+// `row_bytes` long (64 or 128). `on` = false gives the plain row-major
+// layout (no swizzle), kept for the swizzle ablation.
+TKG_HD constexpr uint32_t swz_mask(uint32_t row_bytes, uint32_t r, bool on = true) {
+  return !on ? 0u
+             : row_bytes == 128 ? ((r & 7u) ^ (((r >> 3) & 1u) * 7u)) : ((r >> 2) & 3u);
 }
 
 // Byte offset, inside a tile of `row_bytes`-long rows, of logical chunk
 // `chunk` (16 bytes) of row `r`.
 TKG_HD constexpr uint32_t swz_offset(uint32_t row_bytes, uint32_t r,
-                                     uint32_t chunk) {
-  return r * row_bytes + ((chunk ^ swz_mask(row_bytes, r)) << 4);
+                                     uint32_t chunk, bool on = true) {
+  return r * row_bytes + ((chunk ^ swz_mask(row_bytes, r, on)) << 4);
 }
 
 // Direct global->LDS staging: one wave instruction writes 1 KiB of LDS, lane
@@ -62,8 +64,8 @@ TKG_HD constexpr uint32_t dma_row(uint32_t row_bytes, uint32_t instr,
   return instr * (1024u / row_bytes) + lane / (row_bytes / 16u);
 }
 TKG_HD constexpr uint32_t dma_chunk(uint32_t row_bytes, uint32_t instr,
-                                    uint32_t lane) {
-  return (lane % (row_bytes / 16u)) ^ swz_mask(row_bytes, dma_row(row_bytes, instr, lane));
+                                    uint32_t lane, bool on = true) {
+  return (lane % (row_bytes / 16u)) ^ swz_mask(row_bytes, dma_row(row_bytes, instr, lane), on);
 }
 
 // Rows of a slab that one staging instruction fills.
@@ -77,24 +79,27 @@ TKG_HD constexpr uint32_t dma_rows_per_instr(uint32_t row_bytes) {
 // depends on q only through its parity (rows of one instruction share
 // their upper bits), so two per-lane values cover every instruction.
 TKG_HD constexpr uint32_t dma_lane_offset(uint32_t row_bytes, uint32_t parity,
-                                          uint32_t lane, uint32_t row_stride) {
+                                          uint32_t lane, uint32_t row_stride,
+                                          bool on = true) {
   return (dma_row(row_bytes, parity, lane) - parity * dma_rows_per_instr(row_bytes)) * row_stride +
-         dma_chunk(row_bytes, parity, lane) * 16u;
+         dma_chunk(row_bytes, parity, lane, on) * 16u;
 }
 
 // Checks that split for every instruction of a 256-row slab and every lane.
-TKG_HD constexpr bool dma_offset_split_holds(uint32_t row_bytes) {
+TKG_HD constexpr bool dma_offset_split_holds(uint32_t row_bytes, bool on) {
   const uint32_t stride = 1u << 20;  // any row stride larger than a row
   for (uint32_t q = 0; q < 256u / dma_rows_per_instr(row_bytes); ++q)
     for (uint32_t lane = 0; lane < 64; ++lane) {
-      const uint32_t full = dma_row(row_bytes, q, lane) * stride + dma_chunk(row_bytes, q, lane) * 16u;
+      const uint32_t full =
+          dma_row(row_bytes, q, lane) * stride + dma_chunk(row_bytes, q, lane, on) * 16u;
       const uint32_t split = q * dma_rows_per_instr(row_bytes) * stride +
-                             dma_lane_offset(row_bytes, q & 1u, lane, stride);
+                             dma_lane_offset(row_bytes, q & 1u, lane, stride, on);
       if (full != split) return false;
     }
   return true;
 }
-static_assert(dma_offset_split_holds(128) && dma_offset_split_holds(64),
+static_assert(dma_offset_split_holds(128, true) && dma_offset_split_holds(64, true) &&
+                  dma_offset_split_holds(128, false) && dma_offset_split_holds(64, false),
               "staging offsets split into a uniform and a two-valued per-lane part");
 
 }  // namespace tkg
