@@ -161,6 +161,27 @@ int tkg_gemm_splitk(int dtype, int64_t M, int64_t N, int64_t K, const void *A,
                     float a_scale, const void *B, float b_scale, void *C,
                     void *workspace, size_t workspace_bytes, int splits,
                     void *stream);
+/*
+ * The split-K product of tkg_gemm_splitk without a caller workspace and
+ * without any allocation: for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). The fp32 partial sums go to a scratch array of
+ * TKG_NOALLOC_SCRATCH_BYTES (32 MiB) that the library holds in device
+ * memory on each device it runs on, for the life of the process; the call
+ * itself allocates and frees nothing. Same arguments, results and errors
+ * as tkg_gemm_splitk, except: TKG_ERR_WORKSPACE when the plan needs more
+ * than TKG_NOALLOC_SCRATCH_BYTES (tkg_gemm_splitk_workspace_size() gives
+ * the need; fewer splits need less), nothing launched; TKG_ERR_DEVICE if
+ * the scratch address cannot be resolved. Calls on one device share the
+ * scratch: calls that overlap in time on one device (different streams
+ * without ordering between them) race and give wrong results; calls on one
+ * stream are ordered and safe. The caller passes A, B and C.
+ */
+#define TKG_NOALLOC_SCRATCH_BYTES (32u << 20)
+int tkg_gemm_splitk_noalloc(int dtype, int64_t M, int64_t N, int64_t K,
+                            const void *A, float a_scale, const void *B,
+                            float b_scale, void *C, int splits, void *stream);
+
 /* Bytes of workspace tkg_gemm_splitk needs for these arguments (0 when it
  * runs the plain product), or a negative tkg_status. */
 int64_t tkg_gemm_splitk_workspace_size(int dtype, int64_t M, int64_t N,

@@ -24,7 +24,8 @@ __all__ = [
     "DTYPE_MXFP4", "DTYPE_MXFP8", "gemm_mxfp4", "gemm_mxfp8",
     "STATUS", "LIB_PATH", "tkg_attention_fwd", "attn_lds_offsets",
     "num_variants", "variant_info", "launch_masked", "gemm_splitk",
-    "splitk_workspace_size", "splitk_count",
+    "splitk_workspace_size", "splitk_count", "gemm_splitk_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtkg.so")
@@ -96,6 +97,8 @@ def _load() -> ctypes.CDLL:
     L.tkg_gemm_splitk.argtypes = [i32, i64, i64, i64, vp, f32, vp, f32, vp, vp,
                                   ctypes.c_size_t, i32, vp]
     L.tkg_gemm_splitk.restype = i32
+    L.tkg_gemm_splitk_noalloc.argtypes = [i32, i64, i64, i64, vp, f32, vp, f32, vp, i32, vp]
+    L.tkg_gemm_splitk_noalloc.restype = i32
     L.tkg_gemm_splitk_workspace_size.argtypes = [i32, i64, i64, i64, i32]
     L.tkg_gemm_splitk_workspace_size.restype = i64
     L.tkg_gemm_splitk_count.argtypes = [i32, i64, i64, i64, i32]
@@ -318,6 +321,33 @@ def gemm_splitk(A, Bt, scale_a=1.0, scale_b=1.0, splits=0, workspace=None,
         # from handing it out again before that stream is past them
         workspace.record_stream(stream)
     _raise(st, "tkg_gemm_splitk")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # TKG_NOALLOC_SCRATCH_BYTES in tkg.h
+
+
+def gemm_splitk_noalloc(A, Bt, out, scale_a=1.0, scale_b=1.0, splits=0, stream=None):
+    """Split-K product without allocation (tkg_gemm_splitk_noalloc): the
+    partial sums use the library's device scratch, and the caller passes
+    the result tensor `out` (M x N bf16)."""
+    torch = _torch()
+    M, K = A.shape
+    N = Bt.shape[0]
+    if A.dtype == torch.bfloat16:
+        dtype = DTYPE_BF16
+        _check_mat(A, "A", M, K, (torch.bfloat16,), None)
+        _check_mat(Bt, "Bt", N, K, (torch.bfloat16,), A.device)
+    else:
+        dtype = DTYPE_FP8
+        _check_mat(A, "A", M, K, _fp8_types(), None)
+        _check_mat(Bt, "Bt", N, K, _fp8_types(), A.device)
+    _check_mat(out, "out", M, N, (torch.bfloat16,), A.device)
+    with torch.cuda.device(A.device):
+        st = lib.tkg_gemm_splitk_noalloc(dtype, M, N, K, A.data_ptr(), float(scale_a),
+                                         Bt.data_ptr(), float(scale_b), out.data_ptr(),
+                                         int(splits), _stream_ptr(stream))
+    _raise(st, "tkg_gemm_splitk_noalloc")
     return out
 
 

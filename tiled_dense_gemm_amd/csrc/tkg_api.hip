@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 #include <stdint.h>
 
 #include "tkg.h"
@@ -41,6 +42,37 @@ int cu_count(int* out) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Scratch of the allocation-free split-K entry point: the fp32 partial sums
+// live in this file-scope device array, which each device that loads the
+// library holds until the process ends. In host code `scratch` names a
+// host-side stand-in, never the device memory: kernels and copies take the
+// address hipGetSymbolAddress gives for the current device, resolved once
+// per device and kept in g_scratch. Calls that overlap on one device share
+// the array and race; nothing in it needs clearing (every work unit writes
+// its whole slot before the reduction reads it).
+__device__ __attribute__((aligned(256))) uint8_t scratch[TKG_NOALLOC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_ptr(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TKG_ERR_DEVICE;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      void* q = nullptr;
+      if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr)
+        return TKG_ERR_DEVICE;
+      g_scratch[dev].store(q, std::memory_order_release);
+      p = q;
+    }
+  }
+  *out = p;
+  return TKG_OK;
+}
 
 struct Plan {
   int32_t tiles_m, tiles_n, num_tiles, group_m, xcd_remap, grid;
@@ -473,7 +505,9 @@ const char* tkg_status_string(int status) {
     case TKG_ERR_ALIGN: return "TKG_ERR_ALIGN: pointer not 16-byte aligned";
     case TKG_ERR_LAUNCH: return "TKG_ERR_LAUNCH: kernel launch failed";
     case TKG_ERR_DEVICE: return "TKG_ERR_DEVICE: no usable HIP device";
-    case TKG_ERR_WORKSPACE: return "TKG_ERR_WORKSPACE: split-K workspace missing or too small";
+    case TKG_ERR_WORKSPACE:
+      return "TKG_ERR_WORKSPACE: split-K workspace missing or too small (or, without "
+             "allocation, more than TKG_NOALLOC_SCRATCH_BYTES)";
     case TKG_ERR_VALUE: return "TKG_ERR_VALUE: a scalar argument is out of range";
     default: return "unknown tkg status";
   }
@@ -558,6 +592,18 @@ int tkg_gemm_splitk(int dtype, int64_t M, int64_t N, int64_t K, const void* A,
     return run_dense_splitk(tkg::kFp8, M, N, K, A, B, C, a_scale * b_scale, workspace,
                             workspace_bytes, splits, stream);
   return TKG_ERR_SHAPE;
+}
+
+int tkg_gemm_splitk_noalloc(int dtype, int64_t M, int64_t N, int64_t K, const void* A,
+                            float a_scale, const void* B, float b_scale, void* C, int splits,
+                            void* stream) {
+  if (dtype != TKG_DTYPE_BF16 && dtype != TKG_DTYPE_FP8) return TKG_ERR_SHAPE;
+  const tkg::DenseType dt = dtype == TKG_DTYPE_BF16 ? tkg::kBf16 : tkg::kFp8;
+  void* ws = nullptr;
+  const int st = scratch_ptr(&ws);
+  if (st != TKG_OK) return st;
+  return run_dense_splitk(dt, M, N, K, A, B, C, dt == tkg::kBf16 ? 1.0f : a_scale * b_scale,
+                          ws, (size_t)TKG_NOALLOC_SCRATCH_BYTES, splits, stream);
 }
 
 int64_t tkg_gemm_splitk_workspace_size(int dtype, int64_t M, int64_t N, int64_t K,
