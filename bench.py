@@ -3,22 +3,35 @@
 One step is one pass of the whole hot path over synthetic operands already
 resident in HBM: gemm_bf16, gemm_fp8 (per-tensor scales) and
 gemm_fp4_blockscaled (e2m1 values, e4m3 block scales per 16, fp32 tensor
-scales), each 8192 x 8192 x 8192 with bf16 output. ``value`` is the step's
-counted flops (3 x 2 M N K) over its time; the per-kernel rates and their
-fractions of the MI355X dense MFMA peak are in ``kernels``; ``roofline``
-covers the kernel that takes the longest. Timing: W untimed warmup steps,
-then K timed steps between synchronizations, with HIP events around every
-launch on the stream the kernels run on (the pages time 10 warmup + 10
-timed iterations, page "ThunderKittens: Simple, Fast, and Adorable AI
-Kernels", section 5 "Evaluation Methodology").
+scales), each 8192 x 8192 x 8192 with bf16 output. ``headline`` gives the
+metric itself: bf16 and fp8 TFLOP/s and their fractions of the MI355X dense
+MFMA peak. ``value`` is the step's counted flops (3 x 2 M N K) over its
+time; ``kernels`` the per-product rates; ``rooflines`` one entry per
+product (the 4-bit one against the fp16 rate it issues and against the fp4
+dense peak), with HBM traffic, MFMA busy fraction and clock from the
+committed counter runs of the same kernel code; ``roofline`` repeats the
+entry of the step's longest kernel. Timing: W untimed warmup steps, then K
+timed steps between synchronizations, with HIP events around every launch
+on the stream the kernels run on (the pages time 10 warmup + 10 timed
+iterations, page "ThunderKittens: Simple, Fast, and Adorable AI Kernels",
+section 5 "Evaluation Methodology").
+
+``configs``: every other configuration of the workload list (256^3 to
+16384^3 and the FFN shapes in bf16, fp8 16384^3, the 4-bit product at
+16384^3 and 65536^3, and one GPU's N/8 shard of 8192^3), each timed on its
+own operands after the step. ``next_rows``: the MX products and attention
+forward. ``launch_log``: every GEMM launch of the run in dispatch order, so
+a kernel trace of the same run can be attributed launch by launch.
 
 ``cpu_baseline``: the CPU oracle (its decode of each format and its plain
 fp64 C product, OpenMP) timed on a bounded sample of the same three
-products, 64 x 64 output tiles of each in turn, for a context number; it is
-test infrastructure and takes no part in the GPU path.
+products -- full-width row panels -- for a context number, with the host's
+CPU model and thread count; it is test infrastructure and takes no part in
+the GPU path.
 
-``--profile`` runs only the GPU part (for rocprofv3) plus a 1 GiB device
-copy that calibrates the HBM byte counters.
+``--profile`` runs only the step's products (and the MX and attention
+rows) for rocprofv3 counter passes, plus 1 GiB device copies that
+calibrate the HBM byte counters.
 """
 from __future__ import annotations
 
@@ -33,7 +46,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "GEMM TFLOP/s at 8192^3 bf16 and fp8 on 1 MI355X; % of dense MFMA peak"
+# MI355X published dense MFMA peaks (TFLOP/s). The block-scaled 4-bit
+# product (e4m3 scale per 16) runs exact fp16 MFMAs, so its row carries the
+# fp16 rate it issues and, beside it, the fp4 dense peak.
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4_blockscaled": 2500.0}
+PEAK_FP4_DENSE = 10100.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_8192.json")
 
 
@@ -92,9 +109,9 @@ def kernel_source_hash(family: str = "gemm", read=None) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch from the committed counter runs, or None when
-    they were taken on other kernel sources."""
+def measured(kernel: str, field: str):
+    """A per-kernel figure of the committed counter runs (traffic_8192.json),
+    or None when they were taken on other kernel sources."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
@@ -102,7 +119,13 @@ def measured_traffic(kernel: str):
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
     k = rec.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("hbm_bytes_per_launch")
+    return None if k is None else k.get(field)
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed counter runs, or None when
+    they were taken on other kernel sources."""
+    return measured(kernel, "hbm_bytes_per_launch")
 
 
 ATTN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
@@ -147,12 +170,30 @@ def _bench_line(path):
     return json.loads(line) if line else None
 
 
+def _attribute(launches, blocks):
+    """Split each kernel family's launches (in start order) over the bench
+    run's launch log: {workload name: [durations of its timed launches]}.
+    Families absent from the log are returned whole under their key."""
+    out, pos = {}, {}
+    for b in blocks:
+        k = b["key"]
+        seq = launches.get(k, [])
+        i = pos.get(k, 0)
+        out[b["name"]] = [d for _, d in seq[i + b["warmup"]:i + b["warmup"] + b["timed"]]]
+        pos[k] = i + b["warmup"] + b["timed"]
+    for k, seq in launches.items():
+        if k not in pos:
+            out[k] = [d for _, d in seq]
+    return out
+
+
 def summarize_profile(trace_dir: str, fetch_dir: str, write_dir: str,
                       size: int, out_md: str, out_json: str, command: str,
                       bench_log: str = None) -> int:
     """Turn rocprofv3 CSV output into the committed summaries.
 
-    trace_dir: --kernel-trace --stats run of the timed bench;
+    trace_dir: --kernel-trace --stats run of the timed bench, whose launch
+    log (bench_log) attributes every traced launch to its workload;
     fetch_dir / write_dir: --pmc FETCH_SIZE / WRITE_SIZE runs of
     `bench.py --profile` (which ends with three 1 GiB device copies that
     calibrate the counters: bytes = counter * (1 GiB / counter_of_copy))."""
@@ -166,11 +207,7 @@ def summarize_profile(trace_dir: str, fetch_dir: str, write_dir: str,
             out += list(csv.DictReader(open(f)))
         return out
 
-    # launches in start order; the summary keeps the last `steps` of each
-    # kernel, the launches the bench run timed with HIP events (the others
-    # are its warmup)
     bench = _bench_line(bench_log)
-    steps = bench["steps"] if bench else None
     launches = {}
     for r in rows(trace_dir, "*kernel_trace.csv"):
         k = _kernel_key(r["Kernel_Name"])
@@ -178,8 +215,13 @@ def summarize_profile(trace_dir: str, fetch_dir: str, write_dir: str,
             launches.setdefault(k, []).append(
                 (int(r["Start_Timestamp"]),
                  (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3))
-    dur = {k: [d for _, d in sorted(v)][-steps:] if steps else [d for _, d in sorted(v)]
-           for k, v in launches.items()}
+    for k in launches:
+        launches[k].sort()
+    blocks = (bench or {}).get("launch_log") or []
+    by_name = _attribute(launches, blocks)
+    step_of = {"gemm_" + k: "step_" + k for k in ("bf16", "fp8", "fp4_blockscaled")}
+    step_of.update({"gemm_mxfp4": "next_mxfp4", "gemm_mxfp8": "next_mxfp8"})
+    dur = {k: by_name.get(step_of[k], by_name.get(k, [])) for k in step_of}
     event_us = {}
     if bench:
         for k, v in list(bench.get("kernels", {}).items()) + list(
@@ -216,13 +258,12 @@ def summarize_profile(trace_dir: str, fetch_dir: str, write_dir: str,
     rec = {"kernel_source_hash": kernel_source_hash(), "size": size,
            "copy_calibration": {"fetch_factor": ff, "write_factor": fw,
                                 "copy_bytes": 1 << 30},
-           "command": command, "kernels": {}}
+           "command": command, "kernels": {}, "configs": {}}
     lines = ["# GEMM kernels at M=N=K=%d on one MI355X (rocprofv3)" % size, "",
              "Produced by:", "", "```", command, "```", "",
-             ("Durations: the kernel trace's last %d launches of each kernel, the "
-              "ones the traced bench run timed; beside them the mean that run's "
-              "HIP events measured around the same launches." % steps) if steps else
-             "Durations: every traced launch.", "",
+             "Durations: the kernel trace's launches that the traced bench run timed "
+             "with HIP events (its launch log names every launch's workload and "
+             "warmup/timed role); beside them that run's HIP-event means.", "",
              "| kernel | launches | mean us | min us | HIP-event mean us (same run) | TFLOP/s (mean) | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes/launch (calibrated) | compulsory bytes | ratio |",
              "|---|---|---|---|---|---|---|---|---|---|---|"]
     for k in ("gemm_bf16", "gemm_fp8", "gemm_fp4_blockscaled", "gemm_mxfp4", "gemm_mxfp8"):
@@ -250,6 +291,31 @@ def summarize_profile(trace_dir: str, fetch_dir: str, write_dir: str,
     lines += ["", "Copy calibration: FETCH_SIZE factor %s, WRITE_SIZE factor %s "
               "(1 GiB copy / counter reading)." % (
                   "%.4f" % ff if ff else "-", "%.4f" % fw if fw else "-"), ""]
+    cfg = (bench or {}).get("configs") or {}
+    if cfg:
+        lines += ["The other configurations, timed after the step in the same traced run:",
+                  "", "| workload | dtype | M x N x K | launches | trace mean us | "
+                  "HIP-event mean us | TFLOP/s (trace) | fraction of peak |",
+                  "|---|---|---|---|---|---|---|---|"]
+        for name, c in cfg.items():
+            d = by_name.get(name, [])
+            if not d:
+                continue
+            mean_us = statistics.mean(d)
+            cf = 2.0 * c["M"] * c["N"] * c["K"]
+            tf = cf / (mean_us * 1e-6) / 1e12
+            frac = tf / c["peak_tflops"]
+            rec["configs"][name] = {"launches": len(d), "mean_us": mean_us,
+                                    "event_mean_us": c["ms_mean"] * 1e3, "tflops": tf,
+                                    "frac_of_peak": frac}
+            extra_frac = ""
+            if c["dtype"] == "fp4_blockscaled":
+                extra_frac = " (%.3f of the fp4 dense peak)" % (tf / PEAK_FP4_DENSE)
+                rec["configs"][name]["frac_of_fp4_dense_peak"] = tf / PEAK_FP4_DENSE
+            lines.append("| %s | %s | %dx%dx%d | %d | %.1f | %.1f | %.1f | %.3f%s |" % (
+                name, c["dtype"], c["M"], c["N"], c["K"], len(d), mean_us,
+                c["ms_mean"] * 1e3, tf, frac, extra_frac))
+        lines.append("")
     # optional SQ/TCC counter passes: every other counter_collection.csv
     # under the trace dir's parent that is not the FETCH/WRITE pass
     extra = {}
@@ -273,6 +339,8 @@ def summarize_profile(trace_dir: str, fetch_dir: str, write_dir: str,
                 for k in sorted(extra)) + " |")
         for k in sorted(extra):
             e = extra[k]
+            if k not in rec["kernels"]:
+                continue
             if "SQ_VALU_MFMA_BUSY_CYCLES" in e and "GRBM_GUI_ACTIVE" in e:
                 # MFMA busy cycles per SIMD over GPU-active cycles per XCD
                 util = (statistics.mean(e["SQ_VALU_MFMA_BUSY_CYCLES"]) / 1024.0) / (
@@ -280,6 +348,14 @@ def summarize_profile(trace_dir: str, fetch_dir: str, write_dir: str,
                 rec["kernels"][k]["mfma_busy_fraction"] = util
                 lines.append("")
                 lines.append("%s: MFMA busy %.1f%% of active cycles (1024 SIMDs, 8 XCDs)" % (k, 100 * util))
+            if "GRBM_GUI_ACTIVE" in e and rec["kernels"][k].get("mean_us"):
+                # GPU-active cycles per XCD over the traced launch duration: the
+                # average shader clock of the launch
+                ghz = statistics.mean(e["GRBM_GUI_ACTIVE"]) / 8.0 / (
+                    rec["kernels"][k]["mean_us"] * 1e3)
+                rec["kernels"][k]["clock_ghz_estimate"] = ghz
+                lines.append("%s: about %.2f GHz over the launch (GRBM_GUI_ACTIVE per XCD / "
+                             "traced duration)" % (k, ghz))
             if "SQ_LDS_BANK_CONFLICT" in e and "SQ_LDS_IDX_ACTIVE" in e:
                 rec["kernels"][k]["lds_bank_conflict_over_active"] = (
                     statistics.mean(e["SQ_LDS_BANK_CONFLICT"]) /
@@ -438,31 +514,118 @@ def summarize_attention_profile(trace_dir, fetch_dir, write_dir, out_md, out_jso
     return 0
 
 
+# Every BASELINE configuration beyond the step, timed after it: (name, dtype,
+# M, N, K, operand std (None = 1/sqrt(K)), warmup, timed launches). The
+# N/8 shard is one GPU's share of the 8192^3 product split over 8 GPUs.
+CONFIGS = [
+    ("bf16_256", "bf16", 256, 256, 256, 1.0, 10, 20),
+    ("bf16_1024", "bf16", 1024, 1024, 1024, None, 10, 20),
+    ("bf16_2048", "bf16", 2048, 2048, 2048, None, 10, 20),
+    ("bf16_4096", "bf16", 4096, 4096, 4096, None, 10, 10),
+    ("bf16_16384", "bf16", 16384, 16384, 16384, None, 3, 10),
+    ("bf16_ffn_up_8192x14336x4096", "bf16", 8192, 14336, 4096, None, 5, 10),
+    ("bf16_ffn_down_8192x4096x14336", "bf16", 8192, 4096, 14336, None, 5, 10),
+    ("bf16_shard_8192x1024x8192", "bf16", 8192, 1024, 8192, None, 5, 10),
+    ("fp8_16384", "fp8", 16384, 16384, 16384, 1.0, 3, 10),
+    ("fp8_shard_8192x1024x8192", "fp8", 8192, 1024, 8192, 1.0, 5, 10),
+    ("fp4_16384", "fp4_blockscaled", 16384, 16384, 16384, 1.0, 3, 10),
+    ("fp4_65536", "fp4_blockscaled", 65536, 65536, 65536, 1.0, 1, 3),
+]
+
+
+class LaunchLog:
+    """Times blocks of launches with HIP events on the launching stream and
+    records, in dispatch order, which kernel family ran how many warmup and
+    timed launches for which workload, so a kernel trace of the same run
+    can be attributed launch by launch."""
+
+    def __init__(self, stream):
+        self.stream = stream
+        self.blocks = []
+
+    def time(self, name, key, fn, warmup, steps):
+        import numpy as np
+        import torch
+        for _ in range(warmup):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(self.stream)
+        for i in range(steps):
+            fn()
+            ev[i + 1].record(self.stream)
+        torch.cuda.synchronize()
+        t = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+        self.blocks.append({"name": name, "key": key, "warmup": warmup, "timed": steps})
+        return {"ms_mean": round(float(np.mean(t)), 4), "ms_min": round(float(np.min(t)), 4),
+                "ms_median": round(float(np.median(t)), 4)}
+
+
+def _rate(flops, ms, peak):
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"tflops": round(tf, 1), "peak_tflops": peak, "frac_of_peak": round(tf / peak, 4)}
+
+
+def _operands(gdev, dtype, M, N, K, std, dev, seed):
+    if dtype == "bf16":
+        sd = K ** -0.5 if std is None else std
+        return (gdev.bf16_operand(seed, M, K, std=sd, device=dev),
+                gdev.bf16_operand(seed + 1, N, K, std=sd, device=dev))
+    if dtype == "fp8":
+        A, sa = gdev.fp8_operand(seed, M, K, device=dev)
+        B, sb = gdev.fp8_operand(seed + 1, N, K, device=dev)
+        return A, sa, B, sb
+    A, As, ta = gdev.fp4_operand(seed, M, K, device=dev)
+    B, Bs, tb = gdev.fp4_operand(seed + 1, N, K, device=dev)
+    return A, As, ta, B, Bs, tb
+
+
+def _call(tkg, dtype, ops, C, stream):
+    if dtype == "bf16":
+        return lambda: tkg.gemm_bf16(ops[0], ops[1], out=C, stream=stream)
+    if dtype == "fp8":
+        return lambda: tkg.gemm_fp8(ops[0], ops[1], ops[2], ops[3], out=C, stream=stream)
+    return lambda: tkg.gemm_fp4_blockscaled(*ops, out=C, stream=stream)
+
+
+def _roofline(kernel, tflops, peak, basis):
+    """One roofline entry: achieved = algorithmic flops / event-timed launch
+    duration; traffic and MFMA busy from the committed counter runs of the
+    same kernel code (None once the kernels have changed since)."""
+    return {"kernel": kernel, "bound": "mfma", "achieved": tflops, "peak": peak,
+            "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "peak_basis": basis,
+            "traffic": measured_traffic(kernel),
+            "mfma_busy": measured(kernel, "mfma_busy_fraction"),
+            "clock_ghz": measured(kernel, "clock_ghz_estimate")}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--size", type=int, default=8192)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="CPU budget of the oracle baseline when the whole bf16 "
+                         "product would take longer than 45 s")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the timed sweep over the other configurations")
     ap.add_argument("--profile", action="store_true")
     ap.add_argument("--summarize-profile", nargs=3,
                     metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--profile-command", default="")
     ap.add_argument("--bench-log", default=None,
-                    help="log of the traced bench run (its JSON line gives the timed "
-                         "launch count and the HIP-event means)")
+                    help="log of the traced bench run (its JSON line gives the launch "
+                         "log and the HIP-event means)")
     ap.add_argument("--summarize-attn-profile", nargs=3,
                     metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--with-attn", action="store_true",
-                    help="also time attention forward (tkg_attention_fwd) on its "
-                         "workloads, reported under next_rows, outside the step "
+                    help="time attention forward on its workloads under next_rows "
                          "(the default; kept for older command lines)")
     ap.add_argument("--with-mx", action="store_true",
-                    help="also time the MX products (gemm_mxfp4, gemm_mxfp8) on the "
-                         "same shape, reported under next_rows, outside the step "
-                         "(the default; kept for older command lines)")
+                    help="time the MX products under next_rows (the default; kept "
+                         "for older command lines)")
     ap.add_argument("--no-attn", action="store_true", help="skip the attention rows")
     ap.add_argument("--no-mx", action="store_true", help="skip the MX rows")
     args = ap.parse_args()
@@ -490,7 +653,6 @@ def main() -> int:
               file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     import gemm_inputs.device as gdev
@@ -531,6 +693,7 @@ def main() -> int:
             "mxfp4": lambda: tkg.gemm_mxfp4(Am4, Asm4, Bm4, Bsm4, out=C, stream=stream),
             "mxfp8": lambda: tkg.gemm_mxfp8(Am8, Asm8, Bm8, Bsm8, out=C, stream=stream),
         }
+    log = LaunchLog(stream)
 
     for _ in range(args.warmup):
         for k in names:
@@ -557,6 +720,7 @@ def main() -> int:
               % (args.steps, "+".join(names), n), flush=True)
         return 0
 
+    # ---- the step: the three products back to back, K times -------------
     # events on the stream the kernels are launched on
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
           for _ in range(args.steps)]
@@ -569,7 +733,11 @@ def main() -> int:
             ev[s][i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    for k in names:
+        log.blocks.append({"name": "step_" + k, "key": "gemm_" + k,
+                           "warmup": args.warmup, "timed": args.steps})
 
+    import numpy as np
     per = {k: [] for k in names}
     for s in range(args.steps):
         for i, k in enumerate(names):
@@ -578,45 +746,65 @@ def main() -> int:
     kernels = {}
     for k in names:
         ms = float(np.mean(per[k]))
-        tf = flops / (ms * 1e-3) / 1e12
-        kernels["gemm_" + k] = {
-            "ms_mean": round(ms, 4), "ms_min": round(float(np.min(per[k])), 4),
-            "ms_median": round(float(np.median(per[k])), 4),
-            "tflops": round(tf, 1), "peak_tflops": PEAK_TFLOPS[k],
-            "frac_of_peak": round(tf / PEAK_TFLOPS[k], 4)}
+        peak = PEAK_TFLOPS[k]
+        kernels["gemm_" + k] = dict(
+            {"ms_mean": round(ms, 4), "ms_min": round(float(np.min(per[k])), 4),
+             "ms_median": round(float(np.median(per[k])), 4)},
+            **_rate(flops, ms, peak))
+    k4 = kernels["gemm_fp4_blockscaled"]
+    k4["peak_basis"] = "fp16 MFMA rate, the instruction the exact dequantized path issues"
+    k4["frac_of_fp4_dense_peak"] = round(k4["tflops"] / PEAK_FP4_DENSE, 4)
     value = len(names) * flops / (step_ms * 1e-3) / 1e12
 
-    dom = max(names, key=lambda k: kernels["gemm_" + k]["ms_mean"])
-    dk = kernels["gemm_" + dom]
-    roofline = {"bound": "mfma", "achieved": dk["tflops"],
-                "peak": PEAK_TFLOPS[dom], "unit": "TFLOP/s",
-                "frac": round(dk["tflops"] / PEAK_TFLOPS[dom], 4),
-                "traffic": measured_traffic("gemm_" + dom),
-                "kernel": "gemm_" + dom}
+    headline = {
+        "bf16": {"tflops": kernels["gemm_bf16"]["tflops"],
+                 "frac_of_dense_peak": kernels["gemm_bf16"]["frac_of_peak"],
+                 "dense_peak_tflops": PEAK_TFLOPS["bf16"]},
+        "fp8": {"tflops": kernels["gemm_fp8"]["tflops"],
+                "frac_of_dense_peak": kernels["gemm_fp8"]["frac_of_peak"],
+                "dense_peak_tflops": PEAK_TFLOPS["fp8"]},
+        "workload": "M=N=K=%d, ms mean over %d timed launches after %d warmup steps"
+                    % (n, args.steps, args.warmup)}
 
-    # the MX products, timed apart from the step (not part of `value`)
+    rooflines = [
+        _roofline("gemm_bf16", kernels["gemm_bf16"]["tflops"], PEAK_TFLOPS["bf16"],
+                  "bf16 dense MFMA"),
+        _roofline("gemm_fp8", kernels["gemm_fp8"]["tflops"], PEAK_TFLOPS["fp8"],
+                  "fp8 dense MFMA"),
+        _roofline("gemm_fp4_blockscaled", k4["tflops"], PEAK_TFLOPS["fp4_blockscaled"],
+                  "fp16 dense MFMA (the instruction the exact path issues)"),
+        _roofline("gemm_fp4_blockscaled", k4["tflops"], PEAK_FP4_DENSE, "fp4 dense MFMA"),
+    ]
+    # the contract's roofline: the step's dominant (longest) kernel
+    dom = max(names, key=lambda k: kernels["gemm_" + k]["ms_mean"])
+    roofline = dict(rooflines[names.index(dom)])
+
+    # ---- the other configurations, each on its own operands -------------
+    configs = None
+    if not args.no_configs:
+        configs = {}
+        for cname, dtype, cm, cn, ck, std, cw, cs in CONFIGS:
+            ops = _operands(gdev, dtype, cm, cn, ck, std, dev, 30)
+            Cc = torch.empty((cm, cn), dtype=torch.bfloat16, device=dev)
+            torch.cuda.synchronize()
+            r = log.time(cname, "gemm_" + dtype, _call(tkg, dtype, ops, Cc, stream), cw, cs)
+            cf = 2.0 * cm * cn * ck
+            row = {"dtype": dtype, "M": cm, "N": cn, "K": ck}
+            row.update(r)
+            row.update(_rate(cf, r["ms_mean"], PEAK_TFLOPS[dtype]))
+            if dtype == "fp4_blockscaled":
+                row["frac_of_fp4_dense_peak"] = round(row["tflops"] / PEAK_FP4_DENSE, 4)
+            configs[cname] = row
+            del ops, Cc
+            torch.cuda.empty_cache()
+
+    # ---- next rows: the MX products and attention, outside the step -----
     next_rows = None
     if extra:
         next_rows = {}
         for k, fn in extra.items():
-            for _ in range(args.warmup):
-                fn()
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(args.steps)]
-            torch.cuda.synchronize()
-            for e0, e1 in evs:
-                e0.record(stream)
-                fn()
-                e1.record(stream)
-            torch.cuda.synchronize()
-            t = [e0.elapsed_time(e1) for e0, e1 in evs]
-            ms = float(np.mean(t))
-            tf = flops / (ms * 1e-3) / 1e12
-            next_rows["gemm_" + k] = {
-                "ms_mean": round(ms, 4), "ms_min": round(float(np.min(t)), 4),
-                "tflops": round(tf, 1), "peak_tflops": PEAK_MX_TFLOPS[k],
-                "frac_of_peak": round(tf / PEAK_MX_TFLOPS[k], 4)}
-
+            r = log.time("next_" + k, "gemm_" + k, fn, args.warmup, args.steps)
+            next_rows["gemm_" + k] = dict(r, **_rate(flops, r["ms_mean"], PEAK_MX_TFLOPS[k]))
     if args.with_attn:
         next_rows = next_rows or {}
         next_rows.update(time_attention(args, dev, stream))
@@ -628,20 +816,25 @@ def main() -> int:
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "TFLOP/s",
+        "headline": headline,
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(step_ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16+fp8+fp4",
         "data": "synthetic",
-        "config": {"workload": "C = A*B at M=N=K=%d: bf16 (A, B ~ N(0,1)/sqrt(K)), "
-                               "fp8 e4m3 with per-tensor amax/448 scales, and "
-                               "block-scaled e2m1 (e4m3 scale per 16, fp32 tensor "
-                               "scale); A row-major, B column-major, bf16 C" % n,
+        "config": {"workload": "one step = C = A*B at M=N=K=%d in bf16 (A, B ~ N(0,1)/sqrt(K)), "
+                               "fp8 e4m3 with per-tensor amax/448 scales, and block-scaled "
+                               "e2m1 (e4m3 scale per 16, fp32 tensor scale), back to back; "
+                               "value = the step's 3 x 2MNK flops over its time; "
+                               "A row-major, B column-major, bf16 C" % n,
                    "M": M, "N": N, "K": K, "global_batch": 1, "seq_len": None,
                    "parallelism": "single GPU"},
         "kernels": kernels,
         "roofline": roofline,
+        "rooflines": rooflines,
         "cpu_baseline": cpu,
+        "configs": configs,
         "wall_s_timed": round(wall, 3),
+        "launch_log": log.blocks,
     }
     if next_rows is not None:
         out["next_rows"] = next_rows
@@ -725,51 +918,95 @@ def time_attention(args, dev, stream):
     return rows
 
 
-def cpu_baseline(ops, seconds):
-    """The oracle on 64x64 output tiles of the step's three products (bf16,
-    fp8, block-scaled 4-bit, in turn: the oracle's own decode and fp64
-    product for each format) until `seconds` of CPU time are spent; the
-    rate is the tiles' FLOP over that time, in TFLOP/s."""
+def _host_description():
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": affinity,
+            "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS")}
+
+
+def cpu_baseline(ops, seconds, full_limit_s=45.0):
+    """The oracle (its decode of each format and its plain fp64 C product,
+    OpenMP over rows) on the step's products. bf16: the whole 8192^3
+    product, in row panels (R rows of A against all columns of B, full K:
+    the loop the full product runs), when a first panel predicts it within
+    `full_limit_s`; otherwise panels until `seconds` and the full time
+    extrapolated (the loop is latency-bound on the in-order fp64 sum, so the
+    rate does not depend on R). fp8 and 4-bit: row panels for about a tenth
+    of `seconds` each, the full time extrapolated. value: the bf16 rate."""
     import numpy as np
     import torch
 
     import oracle
 
-    def rows(x, r0):
-        t = x[r0:r0 + 64]
+    def rows(x, r0, r1):
+        t = x[r0:r1]
         if t.dtype == torch.bfloat16:
             return t.view(torch.int16).cpu().numpy().view(np.uint16)
         return t.cpu().numpy()
 
     (A16, B16), (A8, sa, B8, sb), (A4, As4, ta, B4, Bs4, tb) = ops
-    K = A16.shape[1]
-    M, N = A16.shape[0], B16.shape[0]
-    rng = np.random.default_rng(0)
-    done = [0, 0, 0]
-    t_used = 0.0
-    while t_used < seconds or min(done) < 2:
-        f = (done[0] + done[1] + done[2]) % 3
-        i0 = int(rng.integers(0, M - 64 + 1))
-        j0 = int(rng.integers(0, N - 64 + 1))
-        if f == 0:
-            args = (rows(A16, i0), rows(B16, j0))
-            fn = oracle.gemm_bf16
-        elif f == 1:
-            args = (rows(A8, i0), sa, rows(B8, j0), sb)
-            fn = oracle.gemm_fp8
+    M, K = A16.shape
+    N = B16.shape[0]
+    full = {"bf16": (rows(B16, 0, N),), "fp8": (rows(B8, 0, N),),
+            "fp4_blockscaled": (rows(B4, 0, N), rows(Bs4, 0, N))}
+
+    def panel(name, r0, r1):
+        if name == "bf16":
+            args, fn = (rows(A16, r0, r1), full[name][0]), oracle.gemm_bf16
+        elif name == "fp8":
+            args, fn = (rows(A8, r0, r1), sa, full[name][0], sb), oracle.gemm_fp8
         else:
-            args = (rows(A4, i0), rows(As4, i0), ta, rows(B4, j0), rows(Bs4, j0), tb)
+            args = (rows(A4, r0, r1), rows(As4, r0, r1), ta, full[name][0], full[name][1], tb)
             fn = oracle.gemm_fp4_blockscaled
         t = time.perf_counter()
         fn(*args)
-        t_used += time.perf_counter() - t
-        done[f] += 1
-    rate = sum(done) * 2.0 * 64 * 64 * K / t_used / 1e12
-    return {"value": round(rate, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+        return time.perf_counter() - t
+
+    per = {}
+    for name in ("bf16", "fp8", "fp4_blockscaled"):
+        budget = seconds if name == "bf16" else seconds / 10.0
+        done_rows, used, r = 0, 0.0, 64
+        whole = False
+        while done_rows < M:
+            r = min(r, M - done_rows)
+            used += panel(name, done_rows, done_rows + r)
+            done_rows += r
+            predicted = used / done_rows * M
+            if name == "bf16" and predicted <= full_limit_s:
+                whole = True
+                r = 1024
+                continue
+            if used >= budget:
+                break
+            r *= 2
+        rate = 2.0 * done_rows * N * K / used / 1e12
+        per[name] = {"tflops": round(rate, 5), "rows": done_rows, "seconds": round(used, 2),
+                     "whole_product": whole and done_rows == M,
+                     "full_product_s": round(used if done_rows == M else
+                                             2.0 * M * N * K / (rate * 1e12), 1)}
+    b = per["bf16"]
+    return {"value": b["tflops"], "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": "%d random 64x64 output tiles each of the %d^3 bf16, fp8 and "
-                      "block-scaled 4-bit products, in turn (the oracle's decode and "
-                      "fp64 plain C product, %.1f s)" % (min(done), K, t_used)}
+            "sample": ("the whole %dx%dx%d bf16 product (%.1f s)" % (M, N, K, b["seconds"])
+                       if b["whole_product"] else
+                       "%d of %d rows of the %dx%dx%d bf16 product, full width and K "
+                       "(%.1f s; full time extrapolated)" % (b["rows"], M, M, N, K, b["seconds"]))
+                      + "; fp8 and block-scaled 4-bit: full-width row panels (%d and %d rows), "
+                        "full time extrapolated; the oracle's decode and plain fp64 C product "
+                        "on its OpenMP threads" % (per["fp8"]["rows"],
+                                                   per["fp4_blockscaled"]["rows"]),
+            "per_dtype": per, "host": _host_description()}
 
 
 if __name__ == "__main__":
