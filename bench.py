@@ -599,6 +599,234 @@ def _roofline(kernel, tflops, peak, basis):
             "clock_ghz": measured(kernel, "clock_ghz_estimate")}
 
 
+# Ablations of the dense kernels (page "ThunderKittens: Simple, Fast, and
+# Adorable AI Kernels", section 3.4, Tables 1-3 and its section 5 note on
+# the missing swizzle ablation; page "ThunderKittens reaches 22.4 PFLOPS on
+# NVIDIA Rubin" for the release timing and ring depth). Each group:
+# (group, dtype, M, N, K, [(setting label, tkg_gemm_ex options), ...]).
+# Every setting computes the same bits (the GPU tests check it).
+def ablation_groups():
+    ring = [("1 stage of 128 B (2 slots)", {"variant": 9}),
+            ("2 stages of 128 B (4 slots, default)", {"variant": 0}),
+            ("2.5 stages of 128 B (5 slots)", {"variant": 1})]
+    ring += [("%d stage%s of 64 B (32x32 blocks)" % (d, "s" if d > 1 else ""),
+              {"variant": 9 + d}) for d in range(1, 6)]
+    groups = [("ring_depth", "bf16", 4096, 4096, 4096, ring)]
+    for k in (64, 128, 256, 512, 1024):
+        groups.append(("persistent", "bf16", 4096, 4096, k, [
+            ("256x256 tiles, one workgroup per tile (256 = one per CU)", {"variant": 0}),
+            ("128x128 tiles, persistent (2 per CU, 2 tiles each)", {"variant": 4}),
+            ("128x128 tiles, one workgroup per tile (1024)", {"variant": 4, "grid": 1 << 20})]))
+    groups.append(("order", "bf16", 16384, 16384, 16384, [
+        ("grouped (GROUP_M 8) + XCD remap (default)", {}),
+        ("grouped (GROUP_M 8), no XCD remap", {"xcd_remap": 0}),
+        ("row-major tile order + XCD remap", {"group_m": 1}),
+        ("row-major tile order, no XCD remap (naive)", {"group_m": 1, "xcd_remap": 0})]))
+    for dt in ("bf16", "fp8"):
+        groups.append(("swizzle", dt, 8192, 8192, 8192, [
+            ("swizzled LDS (default)", {"variant": 0}),
+            ("plain LDS rows (no swizzle)", {"variant": 6})]))
+    groups.append(("schedule", "bf16", 8192, 8192, 8192, [
+        ("interleaved (default)", {"variant": 0}),
+        ("early B-slab release", {"variant": 7}),
+        ("ping-pong, 2 stages of 128 B", {"variant": 8}),
+        ("ping-pong, 4 stages of 64 B", {"variant": 15})]))
+    groups.append(("schedule", "fp8", 8192, 8192, 8192, [
+        ("interleaved (default)", {"variant": 0}),
+        ("early B-slab release", {"variant": 7}),
+        ("ping-pong, 2 stages of 128 B", {"variant": 8})]))
+    groups.append(("mfma_shape", "bf16", 8192, 8192, 8192, [
+        ("16x16x32, 8 waves (default)", {"variant": 0}),
+        ("32x32x16, 8 waves", {"variant": 2}),
+        ("16x16x32, 4 waves (one per SIMD)", {"variant": 3})]))
+    groups.append(("mfma_shape", "fp8", 8192, 8192, 8192, [
+        ("32x32x64, 8 waves (default)", {"variant": 0}),
+        ("16x16x128, 4 waves (one per SIMD)", {"variant": 2}),
+        ("32x32x64, 4 waves (one per SIMD)", {"variant": 3})]))
+    return groups
+
+
+def run_ablations(args):
+    """Every ablation setting as a block of warmup + timed launches (HIP
+    events), rounds alternating over a group's settings; prints one JSON
+    line with the results and the launch log, then the counter-calibration
+    copies."""
+    import numpy as np
+    import torch
+
+    import gemm_inputs.device as gdev
+    import tiled_dense_gemm_amd as tkg
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    log = LaunchLog(stream)
+    rows = []
+    for gi_, (group, dtype, M, N, K, settings) in enumerate(ablation_groups()):
+        ops = _operands(gdev, dtype, M, N, K, 1.0 if dtype == "fp8" else None, dev, 40)
+        if dtype == "bf16":
+            A, B, sa, sb, d = ops[0], ops[1], 1.0, 1.0, tkg.DTYPE_BF16
+        else:
+            A, sa, B, sb, d = ops[0], ops[1], ops[2], ops[3], tkg.DTYPE_FP8
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+        res = {lab: [] for lab, _ in settings}
+        for rnd in range(args.ablation_rounds):
+            for lab, opt in settings:
+                def fn(opt=opt):
+                    st = tkg.tkg_gemm_ex(d, M, N, K, A, None, sa, B, None, sb, C, stream=stream,
+                                         **opt)
+                    assert st == 0, (group, lab, st)
+                r = log.time("%d|%s|%s|%d" % (gi_, group, lab, rnd), "gemm_" + dtype, fn,
+                             args.warmup, args.steps)
+                res[lab].append(r["ms_mean"])
+        for lab, opt in settings:
+            ms = float(np.median(res[lab]))
+            rows.append({"gid": gi_, "group": group, "dtype": dtype, "M": M, "N": N, "K": K,
+                         "setting": lab, "options": opt, "ms_mean_per_round": res[lab],
+                         "tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)})
+        del ops, A, B, C
+        torch.cuda.empty_cache()
+    # calibration copies (1 GiB read + 1 GiB written each) for the byte counters
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"ablations": rows, "kernel_source_hash": kernel_source_hash(),
+                      "steps": args.steps, "warmup": args.warmup,
+                      "rounds": args.ablation_rounds, "launch_log": log.blocks}), flush=True)
+    return 0
+
+
+def summarize_ablations(run_dirs, out_md, out_json, command):
+    """profiles/ablations.md from rocprofv3 passes over `bench.py
+    --ablations`: each run dir holds one pass (a --kernel-trace run or a
+    --pmc run) and the log of the bench run it traced (run.log); every
+    dispatch is attributed to its setting through that run's launch log."""
+    import csv
+    import glob
+    import statistics
+
+    def rows(d, pattern):
+        out = []
+        for f in glob.glob(os.path.join(d, "**", pattern), recursive=True):
+            out += list(csv.DictReader(open(f)))
+        return out
+
+    def line_of(d):
+        for l in open(os.path.join(d, "run.log")):
+            if l.startswith("{") and '"ablations"' in l:
+                return json.loads(l)
+        raise SystemExit("no ablation line in %s/run.log" % d)
+
+    def split(seq, blocks):
+        """{block name: [rows of its timed launches]} by dispatch order."""
+        out, pos = {}, {}
+        for b in blocks:
+            i = pos.get(b["key"], 0)
+            out[b["name"]] = seq.get(b["key"], [])[i + b["warmup"]:i + b["warmup"] + b["timed"]]
+            pos[b["key"]] = i + b["warmup"] + b["timed"]
+        return out
+
+    trace = {}
+    counters = {}
+    calib = {}
+    ref = None
+    for d in run_dirs:
+        bl = line_of(d)
+        ref = ref or bl
+        tr = rows(d, "*kernel_trace.csv")
+        if tr:
+            seq = {}
+            for r in sorted(tr, key=lambda r: int(r["Start_Timestamp"])):
+                k = _kernel_key(r["Kernel_Name"])
+                if k:
+                    seq.setdefault(k, []).append(
+                        (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+            for name, ds in split(seq, bl["launch_log"]).items():
+                trace.setdefault(name.rsplit("|", 1)[0], []).extend(ds)
+        cc = rows(d, "*counter_collection.csv")
+        if cc:
+            by_disp = {}
+            for r in cc:
+                by_disp.setdefault(int(r["Dispatch_Id"]), []).append(r)
+            seq = {}
+            for disp in sorted(by_disp):
+                rs = by_disp[disp]
+                k = _kernel_key(rs[0]["Kernel_Name"])
+                vals = {r["Counter_Name"]: float(r["Counter_Value"]) for r in rs}
+                if k:
+                    seq.setdefault(k, []).append(vals)
+                elif "copy" in rs[0]["Kernel_Name"]:
+                    for c, v in vals.items():
+                        if v > 512 * 1024:
+                            calib.setdefault(c, []).append(v)
+            for name, vs in split(seq, bl["launch_log"]).items():
+                key = name.rsplit("|", 1)[0]
+                for vals in vs:
+                    for c, v in vals.items():
+                        counters.setdefault(key, {}).setdefault(c, []).append(v)
+    gib_kib = 1024.0 * 1024.0
+    fac = {c: gib_kib / statistics.mean(v) for c, v in calib.items()}
+    rec = {"kernel_source_hash": ref["kernel_source_hash"], "command": command,
+           "calibration": fac, "rows": []}
+    lines = ["# Ablations of the dense GEMM kernels on one MI355X (rocprofv3)", "",
+             "Every setting computes the same bits (the GPU tests compare all kernel "
+             "configurations and launch options bit for bit). Kernel source hash %s."
+             % ref["kernel_source_hash"], "", "Produced by:", "", "```", command, "```", "",
+             "Columns: TFLOP/s from the HIP-event mean of the traced run (median over %d "
+             "alternating rounds of %d launches after %d warmup launches) and from the "
+             "kernel trace's durations of the same launches; MFMA busy = "
+             "SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs over GRBM_GUI_ACTIVE / 8 XCDs; clock = "
+             "GRBM_GUI_ACTIVE / 8 over the traced duration; LDS conflict = "
+             "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; HBM bytes = FETCH_SIZE x %s + "
+             "WRITE_SIZE x %s (KiB, calibrated by 1 GiB copies); L2 hit = TCC_HIT / (HIT + "
+             "MISS)." % (ref["rounds"], ref["steps"], ref["warmup"],
+                         "%.3f" % fac.get("FETCH_SIZE", float("nan")),
+                         "%.3f" % fac.get("WRITE_SIZE", float("nan"))), ""]
+    cur = None
+    for row in ref["ablations"]:
+        gkey = "%d|%s|%s" % (row["gid"], row["group"], row["setting"])
+        head = (row["group"], row["dtype"], row["M"], row["N"], row["K"])
+        if head != cur:
+            cur = head
+            lines += ["", "## %s, %s, M=%d N=%d K=%d" % head, "",
+                      "| setting | TFLOP/s (events) | TFLOP/s (trace) | trace mean us | "
+                      "MFMA busy | clock GHz | LDS conflict | HBM bytes | L2 hit |",
+                      "|---|---|---|---|---|---|---|---|---|"]
+        ds = trace.get(gkey, [])
+        cs = counters.get(gkey, {})
+        flops = 2.0 * row["M"] * row["N"] * row["K"]
+        mean_us = statistics.mean(ds) if ds else None
+        g = lambda c: statistics.mean(cs[c]) if cs.get(c) else None
+        busy = (g("SQ_VALU_MFMA_BUSY_CYCLES") / 1024.0 / (g("GRBM_GUI_ACTIVE") / 8.0)
+                if g("SQ_VALU_MFMA_BUSY_CYCLES") and g("GRBM_GUI_ACTIVE") else None)
+        ghz = (g("GRBM_GUI_ACTIVE") / 8.0 / (mean_us * 1e3)
+               if g("GRBM_GUI_ACTIVE") and mean_us else None)
+        confl = (g("SQ_LDS_BANK_CONFLICT") / max(1.0, g("SQ_LDS_IDX_ACTIVE"))
+                 if g("SQ_LDS_BANK_CONFLICT") is not None and g("SQ_LDS_IDX_ACTIVE") else None)
+        hbm = (g("FETCH_SIZE") * 1024 * fac["FETCH_SIZE"] + g("WRITE_SIZE") * 1024 * fac["WRITE_SIZE"]
+               if g("FETCH_SIZE") and g("WRITE_SIZE") and "FETCH_SIZE" in fac and
+               "WRITE_SIZE" in fac else None)
+        l2 = (g("TCC_HIT_sum") / (g("TCC_HIT_sum") + g("TCC_MISS_sum"))
+              if g("TCC_HIT_sum") and g("TCC_MISS_sum") is not None else None)
+        out = dict(row, trace_mean_us=mean_us,
+                   trace_tflops=flops / (mean_us * 1e-6) / 1e12 if mean_us else None,
+                   mfma_busy=busy, clock_ghz=ghz, lds_conflict_over_active=confl,
+                   hbm_bytes=hbm, l2_hit_rate=l2)
+        rec["rows"].append(out)
+        f = lambda v, fmt: fmt % v if v is not None else "-"
+        lines.append("| %s | %.1f | %s | %s | %s | %s | %s | %s | %s |" % (
+            row["setting"], row["tflops"], f(out["trace_tflops"], "%.1f"), f(mean_us, "%.1f"),
+            f(busy, "%.3f"), f(ghz, "%.2f"), f(confl, "%.4f"),
+            f(hbm, "%.3g"), f(l2, "%.3f")))
+    lines.append("")
+    open(out_md, "w").write("\n".join(lines))
+    json.dump(rec, open(out_json, "w"), indent=1)
+    print("\n".join(lines))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -626,6 +854,13 @@ def main() -> int:
     ap.add_argument("--with-mx", action="store_true",
                     help="time the MX products under next_rows (the default; kept "
                          "for older command lines)")
+    ap.add_argument("--ablations", action="store_true",
+                    help="run the dense-kernel ablations instead of the step (one JSON "
+                         "line; for rocprofv3 passes)")
+    ap.add_argument("--ablation-rounds", type=int, default=2)
+    ap.add_argument("--summarize-ablations", nargs="+", metavar="RUN_DIR",
+                    help="rocprofv3 pass directories of --ablations runs (each with its "
+                         "run.log) -> profiles/ablations.md")
     ap.add_argument("--no-attn", action="store_true", help="skip the attention rows")
     ap.add_argument("--no-mx", action="store_true", help="skip the MX rows")
     args = ap.parse_args()
@@ -646,6 +881,12 @@ def main() -> int:
             os.path.join(ROOT, "profiles", "attention_fwd.md"), ATTN_TRAFFIC_FILE,
             args.profile_command, args.bench_log)
 
+    if args.summarize_ablations:
+        return summarize_ablations(args.summarize_ablations,
+                                   os.path.join(ROOT, "profiles", "ablations.md"),
+                                   os.path.join(ROOT, "profiles", "ablations.json"),
+                                   args.profile_command)
+
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU "
               "path (a GEMM shards by splitting N across GPUs with no "
@@ -659,6 +900,8 @@ def main() -> int:
     import tiled_dense_gemm_amd as tkg
 
     assert torch.cuda.is_available(), "bench.py needs the HIP device"
+    if args.ablations:
+        return run_ablations(args)
     dev = torch.device("cuda:0")
     n = args.size
     M = N = K = n
