@@ -387,6 +387,26 @@ def test_fp4_integers_bit_exact(dev):
     assert np.array_equal(_bf16_result(C), ref)
 
 
+def test_fp4_every_block_scale_code_bit_exact(dev):
+    # Every finite e4m3 code as a block scale (subnormals, negatives, +-0,
+    # 448) with every e2m1 code as a value, times the identity: value x
+    # block scale has at most 6 significant bits, so C is the dequantized A
+    # exactly (pins the in-register dequantization, scale byte selection
+    # per lane half and block included).
+    M, K = 256, 512
+    g = np.random.default_rng(23)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    As = np.resize(finite, M * (K // 16)).reshape(M, K // 16)
+    As = As[:, g.permutation(K // 16)]
+    Ac = g.integers(0, 16, (M, K)).astype(np.uint8)
+    Ap = gi.pack_nibbles(Ac)
+    Ip, Is = _fp4_identity(K)
+    C = tkg.gemm_fp4_blockscaled(_up(Ap, dev), _up(As, dev), 1.0,
+                                 _up(Ip, dev), _up(Is, dev), 1.0)
+    assert np.array_equal(_bf16_result(C), oracle.dequant_fp4_blockscaled(Ap, As))
+    assert len(np.unique(As)) == 254
+
+
 def test_fp4_signed_subnormal_and_zero_block_scales(dev):
     # Block scales of every kind the e4m3 format holds: negative (the sign
     # must reach the product), subnormal, +0 and -0, non-power-of-two

@@ -73,22 +73,13 @@ __device__ __forceinline__ TileState tile_state(const Fp4Args& p, int t) {
   return s;
 }
 
-// Block scale (byte BYTE of `word`, OCP e4m3) -> the scale operand of the
-// convert and the fp16 factor still to apply. The convert uses only the
-// magnitude of its scale's power of two (measured on gfx950: mantissa and
-// sign are ignored), so the scale is passed as decoded and the factor
-// carries the sign and the mantissa: +-(1 + m/8) for m in 0..7, exact in
-// fp16. Subnormal e4m3 scales decode to normal fp32 values, so they split
-// the same way; a zero scale gives a zero power of two (fp16 underflow).
-template <int BYTE>
-__device__ __forceinline__ void split_scale(uint32_t word, float& s,
-                                            f16x2_t& mant) {
-  s = __builtin_amdgcn_cvt_f32_fp8((int)word, BYTE);
-  const uint32_t u = __builtin_bit_cast(uint32_t, s);
-  const _Float16 m =
-      (_Float16)__builtin_bit_cast(float, (u & 0x807FFFFFu) | 0x3F800000u);
-  mant = f16x2_t{m, m};
-}
+// Dequantization in fp16, exactly: every OCP e4m3 value (subnormals and
+// 448 included) is an fp16 value, every e2m1 value is, and their product has
+// at most 6 significant bits and a magnitude in [2^-10, 2688] when nonzero
+// (0.5 x 2^-9 up to 6 x 448), inside fp16's normal range. So a value pair
+// is converted with unit scale and multiplied by its block scale in fp16
+// with no rounding; the two block scales a lane needs per 16-byte chunk
+// come from one fp8 -> fp16 convert of their two bytes.
 
 // Compile-time loop: f(integral_constant<int, I>) for I = B .. E-1.
 template <int B, int E, typename F>
@@ -243,15 +234,13 @@ void gemm_fp4_kernel(Fp4Args p) {
     }
   };
   // Half h of fragment f's conversion for k-step q of chunk s (f < FM: A
-  // fragment f, else B fragment f - FM): half 0 splits the block scale and
-  // converts values 0-3, half 1 values 4-7. Dword q of the chunk lies in
-  // block 2 (2s + khalf) + q/2 of the stage, i.e. byte 2 khalf + q/2 of
-  // scale word s.
-  struct Split {
-    float sc;
-    f16x2_t m;
-  };
-  auto conv_half = [&](const Raw& r, int s, auto qc, auto fc, auto hc, Split& sp, Deq& d) {
+  // fragment f, else B fragment f - FM): half 0 converts values 0-3, half 1
+  // values 4-7. Dword q of the chunk lies in block 2 (2s + khalf) + q/2 of
+  // the stage, i.e. byte 2 khalf + q/2 of scale word s: at q = 0 (the
+  // chunk's first k-step) both of the chunk's block scales go to fp16 into
+  // bscale[f], whose half q/2 later k-steps of the chunk use.
+  f16x2_t bscale[NF];
+  auto conv_half = [&](const Raw& r, int s, auto qc, auto fc, auto hc, Deq& d) {
     constexpr int q = decltype(qc)::value, f = decltype(fc)::value, h = decltype(hc)::value;
     constexpr bool IS_A = f < FM;
     constexpr int fi = IS_A ? f : f - FM;
@@ -268,9 +257,12 @@ void gemm_fp4_kernel(Fp4Args p) {
       else return d.b[fi];
     }();
     const uint32_t packed = (uint32_t)rv[q];
-    if constexpr (h == 0) split_scale<q / 2>(rs[s] >> (16 * khalf), sp.sc, sp.m);
-    const f16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, sp.sc, 2 * h) * sp.m;
-    const f16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, sp.sc, 2 * h + 1) * sp.m;
+    if constexpr (q == 0 && h == 0)
+      bscale[f] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(rs[s] >> (16 * khalf), 1.0f, false);
+    const _Float16 sc = bscale[f][q / 2];
+    const f16x2_t m = {sc, sc};
+    const f16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, 2 * h) * m;
+    const f16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(packed, 1.0f, 2 * h + 1) * m;
     v[4 * h + 0] = lo[0];
     v[4 * h + 1] = lo[1];
     v[4 * h + 2] = hi[0];
@@ -281,7 +273,6 @@ void gemm_fp4_kernel(Fp4Args p) {
   // conversion of the next k-step (from raw r, chunk s, dword q) is spread
   // evenly over this k-step's MFMAs.
   auto kstep = [&](const Deq& cur, Deq& nxt, const Raw& r, int s, auto qc, auto&& extra) {
-    Split sp[NF];
     static_for<0, NMMA>([&](auto slot_c) {
       constexpr int slot = decltype(slot_c)::value;
       constexpr int i = slot / FN, j = slot % FN;
@@ -289,7 +280,7 @@ void gemm_fp4_kernel(Fp4Args p) {
       static_for<slot * 2 * NF / NMMA, (slot + 1) * 2 * NF / NMMA>([&](auto hx_c) {
         constexpr int hx = decltype(hx_c)::value;
         conv_half(r, s, qc, std::integral_constant<int, hx / 2>{},
-                  std::integral_constant<int, hx % 2>{}, sp[hx / 2], nxt);
+                  std::integral_constant<int, hx % 2>{}, nxt);
       });
       extra(slot);
       __builtin_amdgcn_sched_barrier(0);
@@ -323,13 +314,10 @@ void gemm_fp4_kernel(Fp4Args p) {
     read_val(0, 0, f, raw[0]);
     read_scale(0, f, raw[0]);
   }
-  {
-    Split sp[NF];
-    static_for<0, NF>([&](auto fc) {
-      conv_half(raw[0], 0, Q0{}, fc, std::integral_constant<int, 0>{}, sp[decltype(fc)::value], deq[0]);
-      conv_half(raw[0], 0, Q0{}, fc, std::integral_constant<int, 1>{}, sp[decltype(fc)::value], deq[0]);
-    });
-  }
+  static_for<0, NF>([&](auto fc) {
+    conv_half(raw[0], 0, Q0{}, fc, std::integral_constant<int, 0>{}, deq[0]);
+    conv_half(raw[0], 0, Q0{}, fc, std::integral_constant<int, 1>{}, deq[0]);
+  });
 
   // Eight k-steps per stage (chunk s = u/4, k-step q = u%4). k-step u
   // multiplies deq[u&1] while deq[(u+1)&1] is filled with k-step u+1; the
@@ -361,15 +349,30 @@ void gemm_fp4_kernel(Fp4Args p) {
       fresh_tile = false;
       lds_barrier();
       const int nbuf = (buf + 1 == STAGES) ? 0 : buf + 1;
-      kstep(deq[0], deq[1], raw[1], 1, Q1{}, [&](int slot) {
-        if (slot < NDMA) issue_one(nl, buf, slot);
-        if (slot < NF) {
-          read_val(nbuf, 0, slot, raw[0]);
-          read_scale(nbuf, slot, raw[0]);
-        }
-      });
-      kstep(deq[1], deq[0], raw[1], 1, Q2{}, none);
-      kstep(deq[0], deq[1], raw[1], 1, Q3{}, none);
+      // The freed buffer's loads go out over k-steps 4-6, one every few
+      // MFMAs, and the next stage's chunk-0 and scale reads over k-steps 5
+      // and 6 (k-step 7 converts them; raw[0] is free since k-step 3).
+      // Bunched into k-step 4 they made it the stage's slowest (measured
+      // with s_memtime: 2550 cycles for k-steps 4-7 against 2280 for 0-3).
+      auto late = [&](int j) {
+        return [&, j](int slot) {
+          const int pos = j * NMMA + slot;
+#pragma unroll
+          for (int d = pos * NDMA / (3 * NMMA); d < (pos + 1) * NDMA / (3 * NMMA); ++d)
+            issue_one(nl, buf, d);
+          if (j >= 1) {
+            const int r = (j - 1) * NMMA + slot;
+#pragma unroll
+            for (int e = r * NF / NMMA; e < (r + 1) * NF / NMMA; ++e) {
+              if (e % 2 == 0) read_val(nbuf, 0, e / 2, raw[0]);
+              else read_scale(nbuf, e / 2, raw[0]);
+            }
+          }
+        };
+      };
+      kstep(deq[0], deq[1], raw[1], 1, Q1{}, late(0));
+      kstep(deq[1], deq[0], raw[1], 1, Q2{}, late(1));
+      kstep(deq[0], deq[1], raw[1], 1, Q3{}, late(2));
       kstep(deq[1], deq[0], raw[0], 0, Q0{}, none);
       pin(deq[0]);
       buf = nbuf;
