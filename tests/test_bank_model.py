@@ -1,11 +1,12 @@
 """LDS bank conflicts: the page's printed H100 model, and the MI355X
 measurements that choose and check the kernels' swizzled layouts.
 
-The gfx950 table (tests/golden/lds_probe_gfx950.json) was measured with
-tiled_dense_gemm_amd/probes/lds_bank_probe.hip and rocprofv3's
-SQ_LDS_BANK_CONFLICT counter (profiles/lds_bank_probe_gfx950.md gives the
-command); every fragment read the library reports must appear in it,
-address for address, as conflict-free."""
+The gfx950 table (tests/golden/lds_probe_gfx950.json) was measured with a
+probe kernel that issued each pattern and rocprofv3's SQ_LDS_BANK_CONFLICT
+counter (profiles/lds_bank_probe_gfx950.md describes the run); every
+fragment read the library reports must appear in it, address for address,
+as conflict-free. The model classes tried against the table are tested
+here too, each where it fails."""
 import json
 import os
 
@@ -208,3 +209,46 @@ def test_finish_strip_moves_every_element_once(mi, rj):
                 assert lds[offs[l] + 2 * k] == (row, col + k)
                 got.add((row, col + k))
     assert len(got) == mi * rj * mi
+
+
+def _search_addresses(A):
+    # the measured 16x16 row-swizzle search: lane l reads row l % 16 of
+    # 128-byte rows at chunk (l / 16) ^ mask(row), mask = A * bits(row)
+    out = []
+    for l in range(64):
+        r = l % 16
+        m = 0
+        for b in range(3):
+            m |= (bin(((A >> (4 * b)) & 15) & r).count("1") & 1) << b
+        out.append(r * 128 + (((l // 16) ^ m) << 4))
+    return out
+
+
+def test_gfx950_word_index_model_ruled_out():
+    # 64 banks by word index with the measured phase sizes predicts the
+    # geometry patterns and the kernels' reads, but not the unswizzled
+    # 16x16 reads of 128-byte rows: 8-way predicted, 4-way measured (the
+    # hardware spreads rows 128 bytes apart over more banks)
+    un = [p for p in PROBE["patterns"] if p["name"].startswith("bf16 16x16x32 unswizzled")]
+    assert un and all(p["degree"] == 4 for p in un)
+    assert all(bm.gfx950_degree(p["addresses"], 16, bm.gfx950_word_bank) == 8 for p in un)
+    for p in PROBE["patterns"]:
+        if p["op"] == "r" and (p["name"].startswith("b128 ") or " swizzled " in p["name"]) \
+                and "16x16x32 swizzled" not in p["name"] and p["bytes"] == 16:
+            assert bm.gfx950_degree(p["addresses"], 16, bm.gfx950_word_bank) == p["degree"], p["name"]
+
+
+def test_gfx950_linear_fold_ruled_out():
+    # Folding address bits 9 and 10 into bank bit 2 reproduces all 4096
+    # measured 16x16 row-swizzle reads (of the 4096 linear folds of bits
+    # 8..10 into the bank group, the only one that does) and the 4-way
+    # unswizzled reads, but predicts the 16x16 reads of the 64-byte-row
+    # layout conflict-free, which measure 2-way.
+    search = PROBE["search_16x16_degrees"]
+    for A in range(4096):
+        assert bm.gfx950_degree(_search_addresses(A), 16, bm.gfx950_fold_bank) == search[A], A
+    un = [p for p in PROBE["patterns"] if p["name"].startswith("bf16 16x16x32 unswizzled")]
+    assert all(bm.gfx950_degree(p["addresses"], 16, bm.gfx950_fold_bank) == 4 for p in un)
+    four_bit = by_name("4-bit values 16x16x32 swizzled step 0 part 0 frag 0")
+    assert four_bit["degree"] == 2
+    assert bm.gfx950_degree(four_bit["addresses"], 16, bm.gfx950_fold_bank) == 1

@@ -40,21 +40,14 @@ constexpr int BKB = 128;                  // value bytes per row per stage
 constexpr int SLOTS = 4;
 constexpr int SLAB = BM * BKB;            // 32 KiB
 constexpr int WM = BM / 2;               // wave tile rows (2 x WAVES_N waves)
-// Waves per workgroup row of the wide-scale kernel: 2 (4 waves, 128 x 128
-// wave tiles, one per SIMD) or 4 (8 waves, 128 x 64, two per SIMD; at
-// 8192^3, same process, bit-identical: MXFP4 4364 against 4029 TFLOP/s,
-// MXFP8 2622 against 2564). The other kernels run 2.
-#ifndef TKG_MX_WIDE_WAVES_N
-#define TKG_MX_WIDE_WAVES_N 4
-#endif
-// With 8 waves: 1 = only the first wave row (one wave per SIMD) issues the
-// global->LDS loads, as in the dense kernels; 0 = every wave loads. Same
-// process, bit-identical: MXFP4 4415 against 4319 TFLOP/s, MXFP8 2665
-// against 2630 (its loader copy keeps 60 bytes per lane in scratch, and is
-// still faster).
-#ifndef TKG_MX_LOADERS
-#define TKG_MX_LOADERS 1
-#endif
+// The wide-scale kernel runs 4 waves per workgroup row (8 waves, 128 x 64
+// wave tiles, two per SIMD; against 2, i.e. 4 waves of 128 x 128 at one per
+// SIMD, at 8192^3, same process, bit-identical: MXFP4 4364 against 4029
+// TFLOP/s, MXFP8 2622 against 2564), of which only the first wave row (one
+// wave per SIMD) issues the global->LDS loads, as in the dense kernels
+// (against all waves loading: MXFP4 4415 against 4319 TFLOP/s, MXFP8 2665
+// against 2630). The other kernels run 2 waves per row, all loading.
+constexpr int kWideWavesN = 4;
 
 template <int FMT, int WAVES>
 struct Mx {
@@ -121,7 +114,7 @@ void gemm_mx_kernel(MxArgs p) {
   constexpr int WAVES = 2 * WAVES_N;
   constexpr int WN = BN / WAVES_N;                // wave tile columns
   constexpr int FM = WM / 32, FN = WN / 32;       // 32x32 accumulators
-  constexpr bool LOADERS = WAVES == 8 && TKG_MX_LOADERS;
+  constexpr bool LOADERS = WAVES == 8;
   constexpr int LOAD_WAVES = LOADERS ? 4 : WAVES;   // waves that issue loads
   constexpr int DMA = SLAB / 1024 / LOAD_WAVES;   // value loads per loading wave per slab
   static_assert(WIDE || WAVES == 4, "eight waves stage their scales wide");
@@ -513,7 +506,7 @@ void launch_fmt(const MxArgs& a, int grid, hipStream_t stream) {
   // which the scalar part of an unmasked load's offset would reach outside
   // the bounds check), runs the masked instance. Scale rows that are whole
   // 16-byte pieces (K % 512 == 0) are staged wide.
-  constexpr int WW = TKG_MX_WIDE_WAVES_N;
+  constexpr int WW = kWideWavesN;
   if (mx_masked((MxType)FMT, a.M, a.N, a.vbytes, a.sbytes))
     hipLaunchKernelGGL((gemm_mx_kernel<FMT, true, false, 2>), dim3(grid), dim3(256), 0, stream, a);
   else if (a.sbytes % 16 == 0)
