@@ -156,6 +156,10 @@ def _kernel_key(name: str):
     for frag, key in KERNEL_KEYS.items():
         if frag in name:
             return key
+    if name.startswith("Cijk_") or "_Cijk_" in name:
+        # the vendor library's GEMM (hipBLASLt, through torch): a reference
+        # timed beside this library's kernels, never on the product path
+        return "vendor_fp8" if "F8" in name else "vendor_bf16"
     return None
 
 
@@ -604,45 +608,72 @@ def _roofline(kernel, tflops, peak, basis):
 # the missing swizzle ablation; page "ThunderKittens reaches 22.4 PFLOPS on
 # NVIDIA Rubin" for the release timing and ring depth). Each group:
 # (group, dtype, M, N, K, [(setting label, tkg_gemm_ex options), ...]).
-# Every setting computes the same bits (the GPU tests check it).
+# Every setting of this library computes the same bits (the GPU tests
+# check it); the vendor rows are timing references.
 def ablation_groups():
+    # bf16 17 is the default's configuration on the interleaved schedule:
+    # the ring-depth and MFMA-shape groups compare on that schedule
     ring = [("1 stage of 128 B (2 slots)", {"variant": 9}),
-            ("2 stages of 128 B (4 slots, default)", {"variant": 0}),
-            ("2.5 stages of 128 B (5 slots)", {"variant": 1})]
+            ("2 stages of 128 B (4 slots)", {"variant": 17}),
+            ("2.5 stages of 128 B (5 slots)", {"variant": 1}),
+            ("2 stages of 128 B, early reads (default)", {"variant": 0}),
+            ("2.5 stages of 128 B, early reads", {"variant": 18})]
     ring += [("%d stage%s of 64 B (32x32 blocks)" % (d, "s" if d > 1 else ""),
               {"variant": 9 + d}) for d in range(1, 6)]
     groups = [("ring_depth", "bf16", 4096, 4096, 4096, ring)]
+    # operands of 1 GiB, four times the last-level cache: loads come from HBM
+    groups.append(("ring_depth_large", "bf16", 16384, 16384, 16384, [
+        ("2 stages of 128 B, early reads", {"variant": 0}),
+        ("2.5 stages of 128 B, early reads (automatic)", {}),
+        ("2.5 stages of 128 B, interleaved", {"variant": 1})]))
     for k in (64, 128, 256, 512, 1024):
         groups.append(("persistent", "bf16", 4096, 4096, k, [
             ("256x256 tiles, one workgroup per tile (256 = one per CU)", {"variant": 0}),
             ("128x128 tiles, persistent (2 per CU, 2 tiles each)", {"variant": 4}),
             ("128x128 tiles, one workgroup per tile (1024)", {"variant": 4, "grid": 1 << 20})]))
     groups.append(("order", "bf16", 16384, 16384, 16384, [
-        ("grouped (GROUP_M 8) + XCD remap (default)", {}),
-        ("grouped (GROUP_M 8), no XCD remap", {"xcd_remap": 0}),
+        ("XCD blocks, bands of 16 rows (automatic)", {}),
+        ("grouped (GROUP_M 8) + XCD remap", {"group_m": 8, "xcd_remap": 1}),
+        ("grouped (GROUP_M 8), no XCD remap", {"group_m": 8, "xcd_remap": 0}),
         ("row-major tile order + XCD remap", {"group_m": 1}),
         ("row-major tile order, no XCD remap (naive)", {"group_m": 1, "xcd_remap": 0})]))
+    groups.append(("order", "fp8", 16384, 16384, 16384, [
+        ("XCD blocks, bands of 32 rows (automatic)", {}),
+        ("grouped (GROUP_M 8) + XCD remap", {"group_m": 8, "xcd_remap": 1}),
+        ("grouped (GROUP_M 32), no XCD remap", {"group_m": 32, "xcd_remap": 0})]))
     for dt in ("bf16", "fp8"):
         groups.append(("swizzle", dt, 8192, 8192, 8192, [
             ("swizzled LDS (default)", {"variant": 0}),
             ("plain LDS rows (no swizzle)", {"variant": 6})]))
     groups.append(("schedule", "bf16", 8192, 8192, 8192, [
-        ("interleaved (default)", {"variant": 0}),
+        ("early reads (default)", {"variant": 0}),
+        ("interleaved", {"variant": 17}),
         ("early B-slab release", {"variant": 7}),
         ("ping-pong, 2 stages of 128 B", {"variant": 8}),
         ("ping-pong, 4 stages of 64 B", {"variant": 15})]))
     groups.append(("schedule", "fp8", 8192, 8192, 8192, [
         ("interleaved (default)", {"variant": 0}),
+        ("early reads", {"variant": 11}),
         ("early B-slab release", {"variant": 7}),
         ("ping-pong, 2 stages of 128 B", {"variant": 8})]))
     groups.append(("mfma_shape", "bf16", 8192, 8192, 8192, [
-        ("16x16x32, 8 waves (default)", {"variant": 0}),
+        ("16x16x32, 8 waves", {"variant": 17}),
         ("32x32x16, 8 waves", {"variant": 2}),
-        ("16x16x32, 4 waves (one per SIMD)", {"variant": 3})]))
+        ("16x16x32, 4 waves (one per SIMD)", {"variant": 3}),
+        ("16x16x32, 4 waves (one per SIMD), early reads", {"variant": 16})]))
     groups.append(("mfma_shape", "fp8", 8192, 8192, 8192, [
         ("32x32x64, 8 waves (default)", {"variant": 0}),
         ("16x16x128, 4 waves (one per SIMD)", {"variant": 2}),
-        ("32x32x64, 4 waves (one per SIMD)", {"variant": 3})]))
+        ("32x32x64, 4 waves (one per SIMD)", {"variant": 3}),
+        ("32x32x64, 4 waves (one per SIMD), early reads", {"variant": 9})]))
+    # the vendor library on the same operands, in the same rounds: a
+    # reference for what the chip gives a tuned GEMM under the same power
+    # state (its results are not bit-compared)
+    for n in (8192, 16384):
+        for dt in ("bf16", "fp8"):
+            groups.append(("vendor", dt, n, n, n, [
+                ("this library (automatic)", {}),
+                ("hipBLASLt through torch", {"vendor": True})]))
     return groups
 
 
@@ -670,13 +701,27 @@ def run_ablations(args):
         C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         torch.cuda.synchronize()
         res = {lab: [] for lab, _ in settings}
+        vendor = None
+        if any(opt.get("vendor") for _, opt in settings):
+            if dtype == "bf16":
+                Bt = B.t()
+                vendor = lambda: torch.matmul(A, Bt, out=C)
+            else:
+                a8, b8t = A.view(torch.float8_e4m3fn), B.view(torch.float8_e4m3fn).t()
+                tsa = torch.tensor(float(sa), device=dev)
+                tsb = torch.tensor(float(sb), device=dev)
+                vendor = lambda: torch._scaled_mm(a8, b8t, scale_a=tsa, scale_b=tsb,
+                                                  out_dtype=torch.bfloat16)
         for rnd in range(args.ablation_rounds):
             for lab, opt in settings:
                 def fn(opt=opt):
                     st = tkg.tkg_gemm_ex(d, M, N, K, A, None, sa, B, None, sb, C, stream=stream,
                                          **opt)
                     assert st == 0, (group, lab, st)
-                r = log.time("%d|%s|%s|%d" % (gi_, group, lab, rnd), "gemm_" + dtype, fn,
+                key = "gemm_" + dtype
+                if opt.get("vendor"):
+                    fn, key = vendor, "vendor_" + dtype
+                r = log.time("%d|%s|%s|%d" % (gi_, group, lab, rnd), key, fn,
                              args.warmup, args.steps)
                 res[lab].append(r["ms_mean"])
         for lab, opt in settings:
@@ -771,8 +816,11 @@ def summarize_ablations(run_dirs, out_md, out_json, command):
     rec = {"kernel_source_hash": ref["kernel_source_hash"], "command": command,
            "calibration": fac, "rows": []}
     lines = ["# Ablations of the dense GEMM kernels on one MI355X (rocprofv3)", "",
-             "Every setting computes the same bits (the GPU tests compare all kernel "
-             "configurations and launch options bit for bit). Kernel source hash %s."
+             "Every setting of this library computes the same bits (the GPU tests "
+             "compare all kernel configurations and launch options bit for bit); the "
+             "\"vendor\" groups time hipBLASLt (through torch.matmul and torch._scaled_mm) "
+             "on the same operands in the same alternating rounds, as a reference. Kernel "
+             "source hash %s."
              % ref["kernel_source_hash"], "", "Produced by:", "", "```", command, "```", "",
              "Columns: TFLOP/s from the HIP-event mean of the traced run (median over %d "
              "alternating rounds of %d launches after %d warmup launches) and from the "

@@ -249,29 +249,43 @@ const char *tkg_status_string(int status);
  *   grid     -- workgroups to launch; 0 = one per compute unit (persistent),
  *               a value >= the number of output tiles gives one workgroup
  *               per tile (non-persistent).
- *   group_m  -- tile rows per band of the grouped tile order; 0 = default
- *               (8), 1 = plain row-major tile order.
+ *   group_m  -- tile rows per band of the grouped tile order; 1 = plain
+ *               row-major tile order; 0 = automatic: 8, except for bf16 and
+ *               fp8 products whose A and B together exceed the 256 MB
+ *               last-level cache, which take the most rows (up to 32, a
+ *               power of two) whose A panels fit in half of it, with the
+ *               XCD-block order (xcd_remap 1 becomes 2).
  *   xcd_remap -- 1 (default when grid is a multiple of 8) gives each XCD a
  *               contiguous range of tiles; 0 leaves the hardware's
- *               round-robin order.
+ *               round-robin order; 2 (XCD blocks) also re-deals each round
+ *               of grid tiles that fills a group_m x (grid / group_m)
+ *               rectangle so each XCD's tiles form a compact block of it
+ *               (split-K launches use 1 instead). Every setting computes
+ *               the same bits.
  *   variant  -- bf16/fp8: index of a kernel configuration, 0 .. n-1
  *               with n = tkg_variant_info(dtype, 0, NULL);
  *               tkg_variant_info() describes each (LDS ring shape, waves,
  *               MFMA block, tile, swizzle, schedule). 0 = automatic: the
  *               default configuration, or the 128 x 128 tile
  *               configuration 4 when the product has fewer 256 x 256
- *               output tiles than the device has compute units. The others
+ *               output tiles than the device has compute units, or for
+ *               bf16 products whose A and B exceed the 256 MB last-level
+ *               cache configuration 18 (5-slot ring). The others
  *               are the measured alternatives: bf16 1 = 5-slot ring,
  *               2 = 32x32x16 blocks, 3 = one wave per SIMD, 4 / 5 = 128 x
  *               128 tiles at two / one workgroups per compute unit, 6 =
  *               swizzle off (plain LDS rows), 7 = early release of the B
  *               slab, 8 = ping-pong, 9 = one-stage ring, 10 .. 14 = 64-byte
  *               stages (32x32x16 blocks) in a ring of 1 .. 5 stages,
- *               15 = ping-pong on four 64-byte stages; fp8 1 = 5-slot
+ *               15 = ping-pong on four 64-byte stages, 16 = one wave per
+ *               SIMD with early reads, 17 = the interleaved schedule,
+ *               18 = 5-slot ring with early reads; fp8 1 = 5-slot
  *               ring, 2 = one wave per SIMD
  *               on 16x16x128 blocks, 3 = one wave per SIMD on 32x32x64,
  *               4 / 5 as bf16, 6 = swizzle off, 7 = early B release,
- *               8 = ping-pong. TKG_ERR_SHAPE outside 0 .. n-1.
+ *               8 = ping-pong, 9 / 10 = one wave per SIMD on 32x32x64 /
+ *               16x16x128 with early reads, 11 = early reads, 12 = 5-slot
+ *               ring with early reads. TKG_ERR_SHAPE outside 0 .. n-1.
  *               4-bit product: 0 = 4 waves (default), 1 = 8 waves;
  *               TKG_ERR_SHAPE outside 0..1. Every variant of a product
  *               computes the same sums (the tests find them bit-identical).
@@ -323,7 +337,8 @@ typedef struct tkg_variant_desc {
   int32_t tile;         /* workgroup tile edge (tile x tile outputs)          */
   int32_t per_cu;       /* workgroups per compute unit of the default grid    */
   int32_t swizzle;      /* 1 = swizzled LDS rows, 0 = plain rows              */
-  int32_t schedule;     /* 0 interleaved, 1 early B release, 2 ping-pong      */
+  int32_t schedule;     /* 0 interleaved, 1 early B release, 2 ping-pong,
+                           3 early reads                                      */
 } tkg_variant_desc;
 int tkg_variant_info(int dtype, int variant, tkg_variant_desc *out);
 

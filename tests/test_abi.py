@@ -172,14 +172,16 @@ def test_splitk_count_rejects_oversized_k():
 def test_variant_table():
     # every dtype reports its configurations; the defaults are the measured
     # ones, and the ablation entries differ from the default in one field
-    assert tkg.num_variants(tkg.DTYPE_BF16) == 16
-    assert tkg.num_variants(tkg.DTYPE_FP8) == 9
+    assert tkg.num_variants(tkg.DTYPE_BF16) == 19
+    assert tkg.num_variants(tkg.DTYPE_FP8) == 13
     assert tkg.num_variants(tkg.DTYPE_FP4_BLOCKSCALED) == 2
     assert tkg.num_variants(tkg.DTYPE_MXFP4) == tkg.num_variants(tkg.DTYPE_MXFP8) == 1
     for d in (tkg.DTYPE_BF16, tkg.DTYPE_FP8):
         v0 = tkg.variant_info(d, 0)
         assert (v0["stage_kbytes"], v0["slots"], v0["waves"], v0["load_waves"], v0["tile"],
-                v0["swizzle"], v0["schedule"]) == (128, 4, 8, 4, 256, 1, 0)
+                v0["swizzle"]) == (128, 4, 8, 4, 256, 1)
+        # bf16 defaults to early reads, fp8 to the interleaved schedule
+        assert v0["schedule_name"] == ("early reads" if d == tkg.DTYPE_BF16 else "interleaved")
         small = tkg.variant_info(d, 4)
         assert small["tile"] == 128 and small["per_cu"] == 2
         swz = tkg.variant_info(d, 6)
@@ -187,9 +189,16 @@ def test_variant_table():
             {k: v for k, v in v0.items() if k != "swizzle"}
         assert tkg.variant_info(d, 7)["schedule_name"] == "early B release"
         assert tkg.variant_info(d, 8)["schedule_name"] == "ping-pong"
+        assert tkg.variant_info(d, tkg.num_variants(d) - 1)["schedule_name"] == "early reads"
+        assert tkg.variant_info(d, tkg.num_variants(d) - 1)["slots"] == 5
         n = tkg.num_variants(d)
         assert L.tkg_variant_info(d, n, None) == S["TKG_ERR_SHAPE"]
         assert L.tkg_variant_info(d, -1, None) == S["TKG_ERR_SHAPE"]
+    # bf16 17 is the interleaved schedule, otherwise the default
+    v17, v0 = tkg.variant_info(tkg.DTYPE_BF16, 17), tkg.variant_info(tkg.DTYPE_BF16, 0)
+    assert v17["schedule_name"] == "interleaved"
+    assert {k: v for k, v in v17.items() if not k.startswith("schedule")} == \
+        {k: v for k, v in v0.items() if not k.startswith("schedule")}
     # the ring-depth sweep: 64-byte stages in rings of 1 .. 5 stages
     depth = [tkg.variant_info(tkg.DTYPE_BF16, v) for v in range(10, 15)]
     assert [d["slots"] // 2 for d in depth] == [1, 2, 3, 4, 5]

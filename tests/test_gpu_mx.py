@@ -118,7 +118,7 @@ def test_mx_ex_output_scale_and_options(dev, elem):
     Bv, Bs = gi.mx_operand(76, N, K, elem)
     args = [_up(Av, dev), _up(As, dev), _up(Bv, dev), _up(Bs, dev)]
     outs = []
-    for grid, gm, xr in ((0, 0, 1), (100000, 0, 1), (0, 1, 0)):
+    for grid, gm, xr in ((0, 0, 1), (100000, 0, 1), (0, 1, 0), (16, 2, 2)):
         C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         st = tkg.tkg_gemm_ex(DTYPE[elem], M, N, K, args[0], args[1], 0.5, args[2], args[3],
                              0.25, C, grid=grid, group_m=gm, xcd_remap=xr)

@@ -189,12 +189,31 @@ def test_bf16_launch_options_agree(dev):
     A = gi.device.bf16_operand(7, M, K, std=K ** -0.5, device=dev)
     Bt = gi.device.bf16_operand(8, N, K, std=K ** -0.5, device=dev)
     ref = tkg.gemm_bf16(A, Bt)
-    for grid, gm, xr in [(10000, 0, 1), (0, 1, 1), (0, 3, 0), (64, 16, 1), (7, 8, 1)]:
-        C = torch.empty_like(ref)
+    for grid, gm, xr in [(10000, 0, 1), (0, 1, 1), (0, 3, 0), (64, 16, 1), (7, 8, 1),
+                         (0, 8, 2), (0, 4, 2), (0, 16, 2), (24, 8, 2)]:
+        C = torch.full_like(ref, float("nan"))
         st = tkg.tkg_gemm_ex(tkg.DTYPE_BF16, M, N, K, A, None, 1.0, Bt, None,
                              1.0, C, grid=grid, group_m=gm, xcd_remap=xr)
         assert st == 0
         assert torch.equal(C.view(torch.int16), ref.view(torch.int16)), (grid, gm, xr)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_xcd_block_order_covers_every_tile(dev, dtype):
+    # XCD-block order (xcd_remap 2) on full rounds: 16 x 16 tiles of 256 x 256
+    # over grids of 64 and 256 workgroups, group_m 4 .. 16, plus a ragged last
+    # band (M = 3000: 12 tile rows); a tile the map missed keeps its NaN fill,
+    # a tile dealt twice would still match, so coverage plus bit equality
+    # with the grouped order checks the map is a bijection.
+    for M, N, K in [(4096, 4096, 256), (3000, 4096, 256)]:
+        A, Bt, d, sa, sb = _dense_operands(dev, dtype, M, N, K, seed=41)
+        ref = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        assert tkg.tkg_gemm_ex(d, M, N, K, A, None, sa, Bt, None, sb, ref, xcd_remap=1) == 0
+        for grid, gm in [(64, 16), (64, 4), (256, 8), (256, 16), (0, 16), (128, 8)]:
+            C = torch.full_like(ref, float("nan"))
+            assert tkg.tkg_gemm_ex(d, M, N, K, A, None, sa, Bt, None, sb, C, grid=grid,
+                                   group_m=gm, xcd_remap=2) == 0
+            assert torch.equal(C.view(torch.int16), ref.view(torch.int16)), (M, grid, gm)
 
 
 def _dense_operands(dev, dtype, M, N, K, seed):
@@ -449,6 +468,23 @@ def test_fp4_variants_agree(dev):
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
     R = oracle.gemm_fp4_blockscaled(Ap, As, ta, Bp, Bs, tb)
     assert relfro(_bf16_result(outs[0]), R) <= LOWP_RELFRO
+
+
+def test_fp4_xcd_block_order_agrees(dev):
+    # 16 x 16 tiles of 256 x 256 over 64 workgroups in the XCD-block order
+    # (full rounds re-dealt) against the default order, NaN-filled output
+    M, N, K = 4096, 4096, 512
+    Ap, As, ta = gi.device.fp4_operand(62, M, K, device=dev)
+    Bp, Bs, tb = gi.device.fp4_operand(63, N, K, device=dev)
+    outs = []
+    for grid, gm, xr in ((0, 0, 1), (64, 16, 2), (64, 4, 2), (128, 8, 2)):
+        C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev)
+        st = tkg.tkg_gemm_ex(tkg.DTYPE_FP4_BLOCKSCALED, M, N, K, Ap, As, ta, Bp, Bs, tb, C,
+                             grid=grid, group_m=gm, xcd_remap=xr)
+        assert st == 0
+        outs.append(C)
+    for C in outs[1:]:
+        assert torch.equal(C.view(torch.int16), outs[0].view(torch.int16))
 
 
 @pytest.mark.parametrize("n", [16384, 65536])

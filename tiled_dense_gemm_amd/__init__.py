@@ -133,7 +133,7 @@ def tkg_status_string(status: int) -> str:
     return lib.tkg_status_string(int(status)).decode()
 
 
-SCHEDULES = {0: "interleaved", 1: "early B release", 2: "ping-pong"}
+SCHEDULES = {0: "interleaved", 1: "early B release", 2: "ping-pong", 3: "early reads"}
 
 
 def num_variants(dtype: int) -> int:

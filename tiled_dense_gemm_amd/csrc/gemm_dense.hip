@@ -56,7 +56,15 @@ static_assert(kBM == kBN, "A and B slabs share offsets");
 //   (the k-step's LDS reads and its share of the slab loads) and an MFMA
 //   phase, one barrier between phases; the second wave row starts one phase
 //   late, so on every SIMD one wave reads while the other multiplies.
-enum Sched { kInterleaved = 0, kEarlyB = 1, kPingPong = 2 };
+// * kEarlyReads: as kInterleaved, but the A fragments are double-buffered
+//   like the B fragments, and every fragment read of the next k-step goes
+//   out in the first half of the current k-step, in the order the next
+//   k-step first uses them. The reads then finish long before the stage-end
+//   barrier waits for them (with a single A set, the last A read is issued
+//   just before a k-step's last MFMA and its latency shows at the barrier
+//   and at the next k-step's first row). For one wave per SIMD, where no
+//   partner wave covers such a wait.
+enum Sched { kInterleaved = 0, kEarlyB = 1, kPingPong = 2, kEarlyReads = 3 };
 
 // Ring shapes. The LDS ring holds SLOTS operand slabs; a slab is one
 // operand's BT rows x BKB bytes of K, and a K stage is an A slab and a B
@@ -81,22 +89,25 @@ struct Ring {
 // One table per operand type (variant v selects entry v). Entry 0 is the
 // default, the fastest measured at 8192^3 on random operands: for bf16 two
 // waves per SIMD with 16x16x32 MFMAs (the 16x16 shape runs at a higher
-// clock on the power-limited chip); for fp8 two waves per SIMD with
-// 32x32x64 MFMAs (16x16x128 at two waves per SIMD spills). Entry
-// kDenseSmallTileVariant (4) is what variant 0 resolves to for products
-// with fewer 256 x 256 tiles than compute units. The others are the
-// measured alternatives: ring depth (2 and 5 slots; the 64-byte-stage
-// entries sweep 1 to 5 stages), MFMA shape, waves per SIMD, swizzle off,
-// early B release and ping-pong. The ring-depth sweep runs on 32x32x16
-// blocks (on 16x16 blocks its deeper rings spill registers).
+// clock on the power-limited chip) and early fragment reads; for fp8 two
+// waves per SIMD with 32x32x64 MFMAs (16x16x128 at two waves per SIMD
+// spills; early reads measure the same). Entry kDenseSmallTileVariant (4)
+// is what variant 0 resolves to for products with fewer 256 x 256 tiles
+// than compute units, and kDenseLargeVariantBf16 (18) what it resolves to
+// for bf16 products whose operands exceed the 256 MB last-level cache:
+// their loads then come from HBM, and the 5-slot ring keeps half a stage
+// more in flight. The others are the measured alternatives: ring depth (2
+// and 5 slots; the 64-byte-stage entries sweep 1 to 5 stages), MFMA shape,
+// waves per SIMD, swizzle off, the schedules. The ring-depth sweep runs on
+// 32x32x16 blocks (on 16x16 blocks its deeper rings spill registers).
 constexpr Ring kRingsBf16[] = {
-    {128, 4, 4, 1, 16, 256, 1, 1, kInterleaved},   // 0 default
+    {128, 4, 4, 1, 16, 256, 1, 1, kEarlyReads},    // 0 default
     {128, 5, 4, 1, 16, 256, 1, 1, kInterleaved},   // 1 5-slot ring (2.5 stages)
     {128, 4, 4, 1, 32, 256, 1, 1, kInterleaved},   // 2 32x32x16 blocks
     {128, 4, 2, 0, 16, 256, 1, 1, kInterleaved},   // 3 one wave per SIMD, 128x128
     {128, 4, 2, 0, 16, 128, 2, 1, kInterleaved},   // 4 128x128 tiles, 2 per CU
     {128, 4, 2, 0, 16, 128, 1, 1, kInterleaved},   // 5 128x128 tiles, 1 per CU
-    {128, 4, 4, 1, 16, 256, 1, 0, kInterleaved},   // 6 swizzle off
+    {128, 4, 4, 1, 16, 256, 1, 0, kEarlyReads},    // 6 swizzle off
     {128, 4, 4, 1, 16, 256, 1, 1, kEarlyB},        // 7 early B release
     {128, 4, 4, 0, 16, 256, 1, 1, kPingPong},      // 8 ping-pong
     {128, 2, 4, 1, 16, 256, 1, 1, kInterleaved},   // 9 one-stage ring
@@ -106,6 +117,9 @@ constexpr Ring kRingsBf16[] = {
     {64, 8, 4, 1, 32, 256, 1, 1, kInterleaved},    // 13 ... 4 stages
     {64, 10, 4, 1, 32, 256, 1, 1, kInterleaved},   // 14 ... 5 stages
     {64, 8, 4, 0, 16, 256, 1, 1, kPingPong},       // 15 ping-pong, 4 stages of 64 bytes
+    {128, 4, 2, 0, 16, 256, 1, 1, kEarlyReads},    // 16 one wave per SIMD, early reads
+    {128, 4, 4, 1, 16, 256, 1, 1, kInterleaved},   // 17 interleaved schedule
+    {128, 5, 4, 1, 16, 256, 1, 1, kEarlyReads},    // 18 5-slot ring, early reads
 };
 constexpr Ring kRingsFp8[] = {
     {128, 4, 4, 1, 32, 256, 1, 1, kInterleaved},   // 0 default
@@ -117,9 +131,16 @@ constexpr Ring kRingsFp8[] = {
     {128, 4, 4, 1, 32, 256, 1, 0, kInterleaved},   // 6 swizzle off
     {128, 4, 4, 1, 32, 256, 1, 1, kEarlyB},        // 7 early B release
     {128, 4, 4, 0, 32, 256, 1, 1, kPingPong},      // 8 ping-pong
+    {128, 4, 2, 0, 32, 256, 1, 1, kEarlyReads},    // 9 one wave per SIMD, 32x32x64, early reads
+    {128, 4, 2, 0, 16, 256, 1, 1, kEarlyReads},    // 10 one wave per SIMD, 16x16x128, early reads
+    {128, 4, 4, 1, 32, 256, 1, 1, kEarlyReads},    // 11 two waves per SIMD, early reads
+    {128, 5, 4, 1, 32, 256, 1, 1, kEarlyReads},    // 12 5-slot ring, early reads
 };
 constexpr int kNumBf16 = sizeof(kRingsBf16) / sizeof(kRingsBf16[0]);
 constexpr int kNumFp8 = sizeof(kRingsFp8) / sizeof(kRingsFp8[0]);
+static_assert(kRingsBf16[kDenseLargeVariantBf16].slots == 5 &&
+                  kRingsBf16[kDenseLargeVariantBf16].bt == 256,
+              "the large-product entry is the 5-slot ring");
 static_assert(kRingsBf16[kDenseSmallTileVariant].bt == 128 &&
                   kRingsFp8[kDenseSmallTileVariant].bt == 128,
               "the small-tile entry has 128 x 128 tiles");
@@ -160,7 +181,8 @@ __device__ __forceinline__ TileState tile_state(const DenseArgs& p, int u) {
   const uint32_t nk_raw = (klen + BKB - 1) / BKB;
   s.nk = (TRIP == 2) ? (nk_raw + (nk_raw & 1)) : nk_raw;
   int pm, pn;
-  grouped_tile(t, p.tiles_m, p.tiles_n, p.group_m, pm, pn);
+  // split-K launches use the grouped order (the reduction walks tiles in it)
+  order_tile(t, gridDim.x, SPLITK ? 0 : p.xcd_remap, p.tiles_m, p.tiles_n, p.group_m, pm, pn);
   s.m0 = pm * BT;
   s.n0 = pn * BT;
   // Resources cover only the rows of this tile that exist. A load reads
@@ -218,6 +240,7 @@ void gemm_dense_kernel(DenseArgs p) {
                 "early B release needs two k-steps per stage and a two-stage ring");
   static_assert(!PP || (WAVES_N == 4 && !LOADERS && SLOTS % 2 == 0 && SLOTS >= 4),
                 "ping-pong pairs the two wave rows, and every wave loads");
+  static_assert(SCHED != kEarlyReads || SLOTS >= 4, "early reads need a two-stage ring");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -414,11 +437,13 @@ void gemm_dense_kernel(DenseArgs p) {
   // registers are short (fp8 16x16 at two waves per SIMD: one set, each B
   // fragment re-read right after its last use, a few MFMAs before its next
   // one).
-  constexpr bool B_SINGLE = (DT == kFp8 && MI == 16 && WAVES_N == 4);
+  constexpr bool EARLY = SCHED == kEarlyReads;
+  constexpr bool B_SINGLE = (DT == kFp8 && MI == 16 && WAVES_N == 4) && !EARLY;
   constexpr int BSETS = B_SINGLE ? 1 : 2;
-  Frag fa[FM], fb[BSETS][FN];
-  auto read_a = [&](int aslot, int s, int i) {
-    read_one(smem + aslot * SLAB, a_base + i * MI * BKB, s, fa[i]);
+  constexpr int ASETS = EARLY ? 2 : 1;
+  Frag fa[ASETS][FM], fb[BSETS][FN];
+  auto read_a = [&](int aslot, int s, int i, Frag& v) {
+    read_one(smem + aslot * SLAB, a_base + i * MI * BKB, s, v);
   };
   auto read_b = [&](int bslot, int s, int j, Frag& v) {
     read_one(smem + bslot * SLAB, b_base + j * MI * BKB, s, v);
@@ -437,19 +462,35 @@ void gemm_dense_kernel(DenseArgs p) {
     constexpr bool READS = decltype(reads_tag)::value;
     Frag (&b)[FN] = fb[B_SINGLE ? 0 : c];
     Frag (&bn)[FN] = fb[B_SINGLE ? 0 : c ^ 1];
+    Frag (&a)[FM] = fa[EARLY ? c : 0];
+    Frag (&an)[FM] = fa[EARLY ? c ^ 1 : 0];
+    // early reads: read r (first-use order b0, a0, b1 .. b[FN-1], a1 ..
+    // a[FM-1]) follows MFMA slot r * RSTRIDE, within the k-step's first half
+    constexpr int NREAD = FM + FN;
+    constexpr int RSTRIDE = NMMA >= 2 * NREAD ? NMMA / (2 * NREAD) : 1;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        mma(b[j], fa[i], acc[i][j]);
+        mma(b[j], a[i], acc[i][j]);
         const int q = i * FN + j;
         if constexpr (READS) {
-          if constexpr (B_SINGLE) {
-            if (i == FM - 1) read_b(ns_b, ns, j, bn[j]);
+          if constexpr (EARLY) {
+            if (q % RSTRIDE == 0 && q / RSTRIDE < NREAD) {
+              const int r = q / RSTRIDE;
+              if (r == 0) read_b(ns_b, ns, 0, bn[0]);
+              else if (r == 1) read_a(ns_a, ns, 0, an[0]);
+              else if (r <= FN) read_b(ns_b, ns, r - 1, bn[r - 1]);
+              else read_a(ns_a, ns, r - FN, an[r - FN]);
+            }
           } else {
-            if (q < FN) read_b(ns_b, ns, q, bn[q]);
+            if constexpr (B_SINGLE) {
+              if (i == FM - 1) read_b(ns_b, ns, j, bn[j]);
+            } else {
+              if (q < FN) read_b(ns_b, ns, q, bn[q]);
+            }
+            if (j == FN - 1) read_a(ns_a, ns, i, fa[0][i]);
           }
-          if (j == FN - 1) read_a(ns_a, ns, i);
         }
         extra(q);
         __builtin_amdgcn_sched_barrier(0);
@@ -467,7 +508,7 @@ void gemm_dense_kernel(DenseArgs p) {
   __syncthreads();
   int aslot = 0, bslot = 1;         // slots of the stage being computed
 #pragma unroll
-  for (int i = 0; i < FM; ++i) read_a(aslot, 0, i);
+  for (int i = 0; i < FM; ++i) read_a(aslot, 0, i, fa[0][i]);
 #pragma unroll
   for (int j = 0; j < FN; ++j) read_b(bslot, 0, j, fb[0][j]);
 
@@ -530,7 +571,7 @@ void gemm_dense_kernel(DenseArgs p) {
       lds_barrier();
       Frag (&bn)[FN] = fb[B_SINGLE ? 0 : c ^ 1];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) read_a(aslot, 0, i);
+      for (int i = 0; i < FM; ++i) read_a(aslot, 0, i, fa[0][i]);
 #pragma unroll
       for (int j = 0; j < FN; ++j) read_b(bslot, 0, j, bn[j]);
     } else {

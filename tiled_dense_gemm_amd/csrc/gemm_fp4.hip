@@ -61,7 +61,7 @@ __device__ __forceinline__ TileState tile_state(const Fp4Args& p, int t) {
     return s;
   }
   int pm, pn;
-  grouped_tile(t, p.tiles_m, p.tiles_n, p.group_m, pm, pn);
+  order_tile(t, gridDim.x, p.xcd_remap, p.tiles_m, p.tiles_n, p.group_m, pm, pn);
   s.m0 = pm * BM;
   s.n0 = pn * BN;
   const uint32_t ra = (uint32_t)min(p.M - s.m0, BM);

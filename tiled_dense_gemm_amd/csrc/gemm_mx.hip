@@ -78,7 +78,7 @@ __device__ __forceinline__ TileState tile_state(const MxArgs& p, int t) {
     return s;
   }
   int pm, pn;
-  grouped_tile(t, p.tiles_m, p.tiles_n, p.group_m, pm, pn);
+  order_tile(t, gridDim.x, p.xcd_remap, p.tiles_m, p.tiles_n, p.group_m, pm, pn);
   s.m0 = pm * BM;
   s.n0 = pn * BN;
   const uint32_t rows_a = (uint32_t)min(p.M - s.m0, BM);

@@ -78,7 +78,13 @@ struct Plan {
   int32_t tiles_m, tiles_n, num_tiles, group_m, xcd_remap, grid;
 };
 
-int make_plan(int64_t M, int64_t N, int64_t bt, int occ, const tkg_opts* o, Plan* pl) {
+// panel_bytes > 0 (bf16/fp8 products whose operands exceed the last-level
+// cache): with group_m left automatic, the XCD-block order on bands of the
+// most tile rows (8 .. 32, a power of two) whose A panels of panel_bytes
+// each fit in half the cache, so a band's A panels stay cached while the
+// band's rounds stream B. Otherwise bands of 8 rows in the grouped order.
+int make_plan(int64_t M, int64_t N, int64_t bt, int occ, const tkg_opts* o, Plan* pl,
+              int64_t panel_bytes = 0) {
   pl->tiles_m = (int32_t)((M + bt - 1) / bt);
   pl->tiles_n = (int32_t)((N + bt - 1) / bt);
   const int64_t tiles = (int64_t)pl->tiles_m * pl->tiles_n;
@@ -91,9 +97,13 @@ int make_plan(int64_t M, int64_t N, int64_t bt, int occ, const tkg_opts* o, Plan
   if (grid > pl->num_tiles) grid = pl->num_tiles;
   pl->grid = grid;
   int gm = (o && o->group_m > 0) ? o->group_m : 8;
+  pl->xcd_remap = o == nullptr ? 1 : (o->xcd_remap == 2 ? 2 : (o->xcd_remap != 0 ? 1 : 0));
+  if (panel_bytes > 0 && !(o && o->group_m > 0)) {
+    while (gm < 32 && 2 * gm * panel_bytes <= tkg::kLastLevelCacheBytes / 2) gm *= 2;
+    if (pl->xcd_remap == 1) pl->xcd_remap = 2;
+  }
   if (gm > pl->tiles_m) gm = pl->tiles_m;
   pl->group_m = gm;
-  pl->xcd_remap = (o == nullptr || o->xcd_remap != 0) ? 1 : 0;
   return TKG_OK;
 }
 
@@ -126,16 +136,21 @@ int run_dense(tkg::DenseType dt, int64_t M, int64_t N, int64_t K,
   // product split over 8 GPUs, or K-heavy small products.
   int variant = opts ? opts->variant : 0;
   if (variant < 0 || variant >= tkg::dense_num_variants(dt)) return TKG_ERR_SHAPE;
+  // Operands beyond the last-level cache: the bf16 5-slot ring (variant 0)
+  // and the cache-sized XCD-block order (group_m 0).
+  const bool large = (M + N) * K * eb > tkg::kLastLevelCacheBytes;
   if (variant == 0) {
     int cus = 0;
     st = cu_count(&cus);
     if (st != TKG_OK) return st;
     const int64_t tiles256 = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
     if (tiles256 < cus) variant = tkg::kDenseSmallTileVariant;
+    else if (large && dt == tkg::kBf16) variant = tkg::kDenseLargeVariantBf16;
   }
   Plan pl;
-  st = make_plan(M, N, tkg::dense_tile(dt, variant), tkg::dense_occupancy(dt, variant), opts,
-                 &pl);
+  const int64_t bt = tkg::dense_tile(dt, variant);
+  st = make_plan(M, N, bt, tkg::dense_occupancy(dt, variant), opts, &pl,
+                 large ? bt * K * eb : 0);
   if (st != TKG_OK) return st;
   tkg::DenseArgs a;
   a.A = static_cast<const uint8_t*>(A);

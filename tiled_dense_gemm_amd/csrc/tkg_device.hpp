@@ -144,4 +144,45 @@ __device__ __forceinline__ void grouped_tile(int t, int tiles_m, int tiles_n,
   pn = r / rows;
 }
 
+// Tile t of the persistent order over a grid of G workgroups (workgroup w
+// runs tiles xcd_virtual_id(w) + k*G). remap 0 and 1: the grouped order.
+// remap 2 (XCD blocks): a round is the G consecutive tiles run at the same
+// time; when a round fills a group_m x (G / group_m) rectangle of one full
+// band, it is re-dealt so that the G/8 tiles of each XCD form an h x w block
+// of it (h + w operand panels per K stage in that XCD's L2, instead of up to
+// G/8 + 1 when group_m does not match the XCD's share). Any other round
+// keeps the grouped order, so the map stays a bijection.
+__device__ __forceinline__ void order_tile(int t, int G, int remap, int tiles_m,
+                                           int tiles_n, int group_m, int& pm,
+                                           int& pn) {
+  const int per_group = group_m * tiles_n;
+  const int g = t / per_group;
+  const int first = g * group_m;
+  if (remap == 2 && G % 8 == 0 && G % group_m == 0 && per_group % G == 0 &&
+      tiles_m - first >= group_m) {
+    const int cols = G / group_m;    // columns of the round's rectangle
+    const int per = G / 8;           // tiles per XCD per round
+    // split the rectangle into (8 / b) x b blocks, the most compact one
+    int b = 8, best = 1 << 30;
+#pragma unroll
+    for (int c = 8; c >= 1; c >>= 1) {
+      const int a = 8 / c;
+      if (group_m % a == 0 && cols % c == 0 && group_m / a + cols / c < best) {
+        best = group_m / a + cols / c;
+        b = c;
+      }
+    }
+    if (best < (1 << 30)) {
+      const int h = group_m / (8 / b), w = cols / b;
+      const int r = t - g * per_group;   // index in the band
+      const int i = r % G;               // index in the round = virtual id
+      const int x = i / per, s = i - (i / per) * per;
+      pm = first + (x / b) * h + s % h;
+      pn = (r - i) / group_m + (x % b) * w + s / h;
+      return;
+    }
+  }
+  grouped_tile(t, tiles_m, tiles_n, group_m, pm, pn);
+}
+
 }  // namespace tkg

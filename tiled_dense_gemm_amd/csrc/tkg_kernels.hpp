@@ -117,6 +117,11 @@ hipError_t launch_dense_reduce(DenseType dt, const DenseArgs& a, int variant,
 // the variant that variant 0 resolves to when the product has fewer
 // 256 x 256 output tiles than compute units
 constexpr int kDenseSmallTileVariant = 4;
+// the bf16 variant that variant 0 resolves to when the operands exceed the
+// last-level cache (kLastLevelCacheBytes): the 5-slot ring
+constexpr int kDenseLargeVariantBf16 = 18;
+// MI355X's memory-side last-level cache (the MALL), shared by the XCDs
+constexpr int64_t kLastLevelCacheBytes = 256ll << 20;
 hipError_t launch_fp4(const Fp4Args& a, int grid, int variant,
                       hipStream_t stream);
 int fp4_num_variants();
