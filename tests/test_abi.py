@@ -175,7 +175,8 @@ def test_variant_table():
     assert tkg.num_variants(tkg.DTYPE_BF16) == 19
     assert tkg.num_variants(tkg.DTYPE_FP8) == 13
     assert tkg.num_variants(tkg.DTYPE_FP4_BLOCKSCALED) == 2
-    assert tkg.num_variants(tkg.DTYPE_MXFP4) == tkg.num_variants(tkg.DTYPE_MXFP8) == 1
+    assert tkg.num_variants(tkg.DTYPE_MXFP4) == tkg.num_variants(tkg.DTYPE_MXFP8) == 2
+    assert tkg.variant_info(tkg.DTYPE_MXFP4, 1)["schedule_name"] == "early reads"
     for d in (tkg.DTYPE_BF16, tkg.DTYPE_FP8):
         v0 = tkg.variant_info(d, 0)
         assert (v0["stage_kbytes"], v0["slots"], v0["waves"], v0["load_waves"], v0["tile"],

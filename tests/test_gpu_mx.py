@@ -112,6 +112,27 @@ def test_mx_extreme_scales(dev, elem):
 
 
 @pytest.mark.parametrize("elem", ELEMS)
+def test_mx_variants_agree(dev, elem):
+    # the early-reads schedule (variant 1) reorders only LDS reads: the MFMA
+    # sequence per accumulator is the same, so the bits are; shapes take
+    # the wide-scale, narrow-scale and masked instances
+    for M, N, K, seed in [(512, 768, 1024, 80), (512, 512, 640, 82), (300, 700, 1152, 84)]:
+        Av, As = gi.mx_operand(seed, M, K, elem)
+        Bv, Bs = gi.mx_operand(seed + 1, N, K, elem)
+        args = [_up(Av, dev), _up(As, dev), _up(Bv, dev), _up(Bs, dev)]
+        outs = []
+        for v in (0, 1):
+            C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev)
+            assert tkg.tkg_gemm_ex(DTYPE[elem], M, N, K, args[0], args[1], 1.0, args[2],
+                                   args[3], 1.0, C, variant=v) == 0
+            outs.append(C)
+        assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), (M, N, K)
+        if M == 512 and N == 768:
+            R = oracle.gemm_mx(Av, As, Bv, Bs, elem)
+            assert relfro(_result(outs[1]), R) <= MX_RELFRO
+
+
+@pytest.mark.parametrize("elem", ELEMS)
 def test_mx_ex_output_scale_and_options(dev, elem):
     M, N, K = 700, 1300, 640
     Av, As = gi.mx_operand(75, M, K, elem)
@@ -130,7 +151,7 @@ def test_mx_ex_output_scale_and_options(dev, elem):
     assert relfro(_result(outs[0]), R) <= MX_RELFRO
     C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     assert tkg.tkg_gemm_ex(DTYPE[elem], M, N, K, args[0], args[1], 1.0, args[2], args[3],
-                           1.0, C, variant=1) == tkg.STATUS["TKG_ERR_SHAPE"]
+                           1.0, C, variant=2) == tkg.STATUS["TKG_ERR_SHAPE"]
 
 
 @pytest.mark.parametrize("elem", ELEMS)

@@ -107,7 +107,12 @@ __device__ __forceinline__ f32x16_t mfma_mx(i32x8_t b, int sb, i32x8_t a, int sa
 // stages (a superstage); superstages alternate between two LDS slots of
 // 256 rows x 16 bytes per operand, and a stage's scale word sits at byte
 // SB * (stage mod U) of its row.
-template <int FMT, bool KTAIL, bool WIDE, int WAVES_N>
+// EARLY: the A fragments are double-buffered like the B fragments and every
+// fragment read of the next k-step goes out over the current k-step's first
+// MFMAs, in the order the next k-step first uses them (the early-reads
+// schedule of gemm_dense.hip); otherwise each A fragment is re-read right
+// after its last MFMA of the k-step.
+template <int FMT, bool KTAIL, bool WIDE, int WAVES_N, bool EARLY>
 __global__ __launch_bounds__(128 * WAVES_N)
 __attribute__((amdgpu_waves_per_eu(WAVES_N / 2, WAVES_N / 2)))
 void gemm_mx_kernel(MxArgs p) {
@@ -271,10 +276,11 @@ void gemm_mx_kernel(MxArgs p) {
   auto main_loop = [&](auto loader_tag) {
   constexpr bool IS_LOADER = decltype(loader_tag)::value;
   // ---- registers ---------------------------------------------------------------
-  // A fragments single-buffered (re-read after their last MFMA), B double;
-  // scale words of the stage per fragment, read during the previous stage's
-  // last k-step and shifted so that this lane's block sits in bytes 0 and 2
-  i32x8_t fa[FM], fb[2][FN];
+  // A fragments single-buffered (re-read after their last MFMA) unless
+  // EARLY, B double; scale words of the stage per fragment, read during the
+  // previous stage's last k-step and shifted so that this lane's block sits
+  // in bytes 0 and 2
+  i32x8_t fa[EARLY ? 2 : 1][FM], fb[2][FN];
   using SW = typename std::conditional<S::FP4, u32x2_t, uint32_t>::type;
   SW sa[FM], sbs[FN];
   auto read_frag = [&](int slot, uint32_t row0, int s, i32x8_t& v) {
@@ -344,7 +350,7 @@ void gemm_mx_kernel(MxArgs p) {
     RW ra[FM], rb[FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      read_frag(aslot, a_base + i * 32 * BKB, 0, fa[i]);
+      read_frag(aslot, a_base + i * 32 * BKB, 0, fa[0][i]);
       read_scale(sa0 + as_base + i * SFRAG, ra[i]);
     }
 #pragma unroll
@@ -372,15 +378,30 @@ void gemm_mx_kernel(MxArgs p) {
     const uint32_t nsb = boundary ? scale_base(g, nb) : 0u;
     constexpr int SC = decltype(sc)::value;   // k-step index inside the stage
     constexpr int OPSEL = S::FP4 ? 2 * (SC % 2) : 2 * SC;
+    i32x8_t (&a)[FM] = fa[EARLY ? c : 0];
+    i32x8_t (&an)[FM] = fa[EARLY ? c ^ 1 : 0];
+    constexpr int NREAD = FM + FN, NMMA = FM * FN;
+    constexpr int RSTRIDE = NMMA >= 2 * NREAD ? NMMA / (2 * NREAD) : 1;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        acc[i][j] = mfma_mx<S::CB, OPSEL>(fb[c][j], sword(sbs[j], SC), fa[i],
+        acc[i][j] = mfma_mx<S::CB, OPSEL>(fb[c][j], sword(sbs[j], SC), a[i],
                                          sword(sa[i], SC), acc[i][j]);
         const int q = i * FN + j;
-        if (q < FN) read_frag(nb, b_base + q * 32 * BKB, ns, fb[c ^ 1][q]);
-        if (j == FN - 1) read_frag(na, a_base + i * 32 * BKB, ns, fa[i]);
+        if constexpr (EARLY) {
+          // read r (b0, a0, b1 .. b[FN-1], a1 .. a[FM-1]) after slot r * RSTRIDE
+          if (q % RSTRIDE == 0 && q / RSTRIDE < NREAD) {
+            const int r = q / RSTRIDE;
+            if (r == 0) read_frag(nb, b_base, ns, fb[c ^ 1][0]);
+            else if (r == 1) read_frag(na, a_base, ns, an[0]);
+            else if (r <= FN) read_frag(nb, b_base + (r - 1) * 32 * BKB, ns, fb[c ^ 1][r - 1]);
+            else read_frag(na, a_base + (r - FN) * 32 * BKB, ns, an[r - FN]);
+          }
+        } else {
+          if (q < FN) read_frag(nb, b_base + q * 32 * BKB, ns, fb[c ^ 1][q]);
+          if (j == FN - 1) read_frag(na, a_base + i * 32 * BKB, ns, an[i]);
+        }
         if (boundary) {
           if (q < FM) read_scale(nsa + as_base + q * SFRAG, sa_n[q]);
           else if (q < FM + FN) read_scale(nsb + bs_base + (q - FM) * SFRAG, sb_n[q - FM]);
@@ -500,7 +521,7 @@ void gemm_mx_kernel(MxArgs p) {
   wait_vmcnt<0>();
 }
 
-template <int FMT>
+template <int FMT, bool EARLY>
 void launch_fmt(const MxArgs& a, int grid, hipStream_t stream) {
   // A ragged last stage, or a ragged M or N tile (rows past the operand,
   // which the scalar part of an unmasked load's offset would reach outside
@@ -508,12 +529,14 @@ void launch_fmt(const MxArgs& a, int grid, hipStream_t stream) {
   // 16-byte pieces (K % 512 == 0) are staged wide.
   constexpr int WW = kWideWavesN;
   if (mx_masked((MxType)FMT, a.M, a.N, a.vbytes, a.sbytes))
-    hipLaunchKernelGGL((gemm_mx_kernel<FMT, true, false, 2>), dim3(grid), dim3(256), 0, stream, a);
-  else if (a.sbytes % 16 == 0)
-    hipLaunchKernelGGL((gemm_mx_kernel<FMT, false, true, WW>), dim3(grid), dim3(128 * WW), 0,
+    hipLaunchKernelGGL((gemm_mx_kernel<FMT, true, false, 2, EARLY>), dim3(grid), dim3(256), 0,
                        stream, a);
+  else if (a.sbytes % 16 == 0)
+    hipLaunchKernelGGL((gemm_mx_kernel<FMT, false, true, WW, EARLY>), dim3(grid), dim3(128 * WW),
+                       0, stream, a);
   else
-    hipLaunchKernelGGL((gemm_mx_kernel<FMT, false, false, 2>), dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((gemm_mx_kernel<FMT, false, false, 2, EARLY>), dim3(grid), dim3(256), 0,
+                       stream, a);
 }
 
 }  // namespace
@@ -524,9 +547,17 @@ bool mx_masked(MxType fmt, int64_t M, int64_t N, uint32_t vbytes, uint32_t sbyte
   return vbytes % BKB != 0 || M % BM != 0 || N % BN != 0;
 }
 
-hipError_t launch_mx(MxType fmt, const MxArgs& a, int grid, hipStream_t stream) {
-  if (fmt == kMxfp4) launch_fmt<kMxfp4>(a, grid, stream);
-  else launch_fmt<kMxfp8>(a, grid, stream);
+int mx_num_variants() { return 2; }
+
+hipError_t launch_mx(MxType fmt, const MxArgs& a, int grid, int variant, hipStream_t stream) {
+  const bool early = variant == 1;
+  if (fmt == kMxfp4) {
+    if (early) launch_fmt<kMxfp4, true>(a, grid, stream);
+    else launch_fmt<kMxfp4, false>(a, grid, stream);
+  } else {
+    if (early) launch_fmt<kMxfp8, true>(a, grid, stream);
+    else launch_fmt<kMxfp8, false>(a, grid, stream);
+  }
   return hipGetLastError();
 }
 

@@ -336,7 +336,7 @@ int run_mx(tkg::MxType fmt, int64_t M, int64_t N, int64_t K, const void* A,
   int st = check_common(M, N, K, 128, kmax);
   if (st != TKG_OK) return st;
   const int variant = opts ? opts->variant : 0;
-  if (variant != 0) return TKG_ERR_SHAPE;
+  if (variant < 0 || variant >= tkg::mx_num_variants()) return TKG_ERR_SHAPE;
   if (M == 0 || N == 0) return TKG_OK;
   if (C == nullptr ||
       (K > 0 && (A == nullptr || B == nullptr || As == nullptr || Bs == nullptr)))
@@ -366,7 +366,7 @@ int run_mx(tkg::MxType fmt, int64_t M, int64_t N, int64_t K, const void* A,
   if (K == 0) {
     a.A = a.B = a.As = a.Bs = static_cast<const uint8_t*>(C);
   }
-  const hipError_t e = tkg::launch_mx(fmt, a, pl.grid, static_cast<hipStream_t>(stream));
+  const hipError_t e = tkg::launch_mx(fmt, a, pl.grid, variant, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TKG_OK : TKG_ERR_LAUNCH;
 }
 
@@ -665,9 +665,9 @@ int tkg_variant_info(int dtype, int variant, tkg_variant_desc* out) {
     d = tkg_variant_desc{(int32_t)tkg::fp4_stage_vbytes(), 8, variant == 1 ? 8 : 4,
                          variant == 1 ? 8 : 4, 32, kBM, 1, 1, 0};
   } else if (dtype == TKG_DTYPE_MXFP4 || dtype == TKG_DTYPE_MXFP8) {
-    n = 1;
-    if (variant != 0) return TKG_ERR_SHAPE;
-    d = tkg_variant_desc{128, 4, 8, 4, 32, kBM, 1, 1, 0};
+    n = tkg::mx_num_variants();
+    if (variant < 0 || variant >= n) return TKG_ERR_SHAPE;
+    d = tkg_variant_desc{128, 4, 8, 4, 32, kBM, 1, 1, variant == 1 ? 3 : 0};
   } else {
     return TKG_ERR_SHAPE;
   }

@@ -125,7 +125,9 @@ constexpr int64_t kLastLevelCacheBytes = 256ll << 20;
 hipError_t launch_fp4(const Fp4Args& a, int grid, int variant,
                       hipStream_t stream);
 int fp4_num_variants();
-hipError_t launch_mx(MxType fmt, const MxArgs& a, int grid, hipStream_t stream);
+// variant 0: fragment reads after their last use; 1: early reads
+hipError_t launch_mx(MxType fmt, const MxArgs& a, int grid, int variant, hipStream_t stream);
+int mx_num_variants();
 // whether the MX launch runs the masked instance (ragged M or N tiles, or a
 // ragged last stage): every load's whole offset per lane, bounds-checked
 bool mx_masked(MxType fmt, int64_t M, int64_t N, uint32_t vbytes, uint32_t sbytes);
