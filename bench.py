@@ -128,6 +128,37 @@ def measured_traffic(kernel: str):
     return measured(kernel, "hbm_bytes_per_launch")
 
 
+ABLATIONS_FILE = os.path.join(ROOT, "profiles", "ablations.json")
+
+
+def vendor_reference():
+    """The committed ablation run's "vendor" groups: this library and the
+    vendor GEMM (hipBLASLt through torch) on the same operands in the same
+    alternating rounds, from the kernel trace of that run; None when the run
+    was taken on other kernel sources. Context for the roofline fractions,
+    not a measurement of this run."""
+    try:
+        rec = json.load(open(ABLATIONS_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    out = {}
+    for r in rec.get("rows", []):
+        if r.get("group") != "vendor":
+            continue
+        key = "%s_%dx%dx%d" % (r["dtype"], r["M"], r["N"], r["K"])
+        who = "vendor" if r.get("options", {}).get("vendor") else "this_library"
+        rnd = lambda v, d: None if v is None else round(v, d)
+        out.setdefault(key, {})[who] = {"tflops": rnd(r.get("trace_tflops"), 1),
+                                        "mfma_busy": rnd(r.get("mfma_busy"), 3),
+                                        "clock_ghz": rnd(r.get("clock_ghz"), 2)}
+    if not out:
+        return None
+    return {"source": "profiles/ablations.md (vendor groups)",
+            "vendor": "hipBLASLt through torch.matmul / torch._scaled_mm", "products": out}
+
+
 ATTN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
 
 
@@ -1123,6 +1154,7 @@ def main() -> int:
         "roofline": roofline,
         "rooflines": rooflines,
         "cpu_baseline": cpu,
+        "vendor_reference": vendor_reference(),
         "configs": configs,
         "wall_s_timed": round(wall, 3),
         "launch_log": log.blocks,
