@@ -1105,6 +1105,9 @@ def main() -> int:
     configs = None
     if not args.no_configs:
         configs = {}
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        DTYPE_CODES = {"bf16": tkg.DTYPE_BF16, "fp8": tkg.DTYPE_FP8,
+                       "fp4_blockscaled": tkg.DTYPE_FP4_BLOCKSCALED}
         for cname, dtype, cm, cn, ck, std, cw, cs in CONFIGS:
             ops = _operands(gdev, dtype, cm, cn, ck, std, dev, 30)
             Cc = torch.empty((cm, cn), dtype=torch.bfloat16, device=dev)
@@ -1116,6 +1119,9 @@ def main() -> int:
             row.update(_rate(cf, r["ms_mean"], PEAK_TFLOPS[dtype]))
             if dtype == "fp4_blockscaled":
                 row["frac_of_fp4_dense_peak"] = round(row["tflops"] / PEAK_FP4_DENSE, 4)
+            # the launch the automatic options made (configuration, grid,
+            # tile order), as the library plans it for this device
+            row["plan"] = tkg.plan_launch(DTYPE_CODES[dtype], cm, cn, ck, cus=cus)
             configs[cname] = row
             del ops, Cc
             torch.cuda.empty_cache()

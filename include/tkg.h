@@ -323,7 +323,7 @@ int tkg_gemm_ex(int dtype, int64_t M, int64_t N, int64_t K, const void *A,
 
 /*
  * Description of kernel configuration `variant` of dtype (TKG_DTYPE_BF16,
- * _FP8 or _FP4_BLOCKSCALED; the MX types have the one configuration 0),
+ * _FP8, _FP4_BLOCKSCALED, or the MX types' two: 0 and 1 = early reads),
  * written to *out when out is not NULL. Returns the number of
  * configurations of the dtype, or a negative tkg_status (TKG_ERR_SHAPE for
  * an unknown dtype or variant). No GPU work.
@@ -354,6 +354,29 @@ int tkg_variant_info(int dtype, int variant, tkg_variant_desc *out);
  * a negative tkg_status. No GPU work.
  */
 int tkg_launch_masked(int dtype, int64_t M, int64_t N, int64_t K, int variant);
+
+/*
+ * The launch tkg_gemm_ex(dtype, M, N, K, ..., opts) makes on a device with
+ * `cus` compute units (MI355X: 256), written to *out when out is not NULL:
+ * the configuration it runs (variant 0 resolved: 128 x 128 tiles for
+ * products with fewer 256 x 256 tiles than compute units, the bf16 5-slot
+ * ring for operands beyond the 256 MB last-level cache), its tile edge, the
+ * tile count, the grid, and the tile order applied (group_m, xcd_remap; see
+ * tkg_opts). opts may be NULL (the defaults). An empty product (M or N = 0)
+ * reports tiles = grid = 0. Returns TKG_OK, or the negative tkg_status that
+ * tkg_gemm_ex's shape checks return (TKG_ERR_SHAPE also for cus <= 0).
+ * Host logic only, no GPU work; the caller owns *out.
+ */
+typedef struct tkg_launch_plan {
+  int32_t variant;   /* configuration run (tkg_variant_info)               */
+  int32_t tile;      /* workgroup tile edge                                */
+  int32_t tiles;     /* output tiles                                       */
+  int32_t grid;      /* workgroups launched                                */
+  int32_t group_m;   /* tile rows per band of the tile order               */
+  int32_t xcd_remap; /* 0, 1 or 2 (XCD blocks) as applied                  */
+} tkg_launch_plan;
+int tkg_plan_launch(int dtype, int64_t M, int64_t N, int64_t K, const tkg_opts *opts,
+                    int cus, tkg_launch_plan *out);
 
 /*
  * LDS layout introspection for the CPU bank-conflict model (no GPU work).

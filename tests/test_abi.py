@@ -231,3 +231,53 @@ def test_masked_instance_choice(dtype):
     assert not tkg.launch_masked(tkg.DTYPE_MXFP8, 8192, 8192, 8320)
     assert L.tkg_launch_masked(0, -1, 8, 8, 0) == S["TKG_ERR_SHAPE"]
     assert L.tkg_launch_masked(0, 8, 8, 8, 99) == S["TKG_ERR_SHAPE"]
+
+
+def test_plan_launch_policy():
+    # the launch tkg_gemm_ex makes, on the host: variant 0 resolved by tile
+    # count and by operand size against the 256 MB last-level cache, and
+    # the tile order (cache-sized bands in the XCD-block order) for
+    # products whose A and B exceed that cache
+    P = tkg.plan_launch
+    bf, f8 = tkg.DTYPE_BF16, tkg.DTYPE_FP8
+    assert P(bf, 8192, 8192, 8192) == dict(variant=0, tile=256, tiles=1024, grid=256,
+                                           group_m=8, xcd_remap=1)
+    # 16384^3 bf16: 1 GiB of operands; 8 MiB A panels, 16 of them fit 128 MiB
+    assert P(bf, 16384, 16384, 16384) == dict(variant=18, tile=256, tiles=4096, grid=256,
+                                              group_m=16, xcd_remap=2)
+    # fp8: 4 MiB panels, 32 rows per band
+    assert P(f8, 16384, 16384, 16384) == dict(variant=0, tile=256, tiles=4096, grid=256,
+                                              group_m=32, xcd_remap=2)
+    assert P(f8, 8192, 8192, 8192)["group_m"] == 8
+    # exactly at the cache size (bf16 8192^3: 256 MiB) is not beyond it
+    assert P(bf, 8192, 8192, 8192)["variant"] == 0
+    # 8192 x 4096 x 14336: 336 MiB, 7 MiB panels -> 16 rows
+    p = P(bf, 8192, 4096, 14336)
+    assert (p["variant"], p["group_m"], p["xcd_remap"]) == (18, 16, 2)
+    # fewer 256 x 256 tiles than compute units: 128 x 128 tiles, 2 per CU
+    p = P(bf, 8192, 1024, 8192)
+    assert (p["variant"], p["tile"], p["tiles"], p["grid"]) == (4, 128, 512, 512)
+    p = P(bf, 8192, 1024, 8192, cus=64)          # a smaller device: 256-tiles fill it
+    assert (p["variant"], p["tile"], p["grid"]) == (0, 256, 64)
+    # explicit options are kept: band height, remap off, a chosen variant
+    assert P(bf, 16384, 16384, 16384, group_m=8)[("group_m")] == 8
+    assert P(bf, 16384, 16384, 16384, group_m=8)["xcd_remap"] == 1
+    p = P(bf, 16384, 16384, 16384, xcd_remap=0)
+    assert (p["group_m"], p["xcd_remap"]) == (16, 0)
+    assert P(bf, 16384, 16384, 16384, variant=3)["variant"] == 3
+    assert P(bf, 4096, 4096, 4096, xcd_remap=2)["xcd_remap"] == 2
+    # grid option, band height clipped to the tile rows
+    assert P(bf, 4096, 4096, 4096, grid=64)["grid"] == 64
+    assert P(bf, 512, 65536, 64)["group_m"] == 2     # 2 x 256 tiles: 256-tiles
+    assert P(bf, 512, 8192, 64)["group_m"] == 4      # 128-tiles: 4 tile rows
+    # the 4-bit and MX products keep the grouped order at every size
+    p = P(tkg.DTYPE_FP4_BLOCKSCALED, 16384, 16384, 16384)
+    assert (p["group_m"], p["xcd_remap"]) == (8, 1)
+    assert P(tkg.DTYPE_MXFP8, 16384, 16384, 16384)["xcd_remap"] == 1
+    # empty products launch nothing; bad shapes and devices are rejected
+    assert P(bf, 0, 64, 64)["grid"] == 0 and P(bf, 64, 64, 0)["grid"] > 0
+    for args, kw in [((bf, 64, 64, 12), {}), ((f8, 64, 64, 8), {}),
+                     ((bf, 64, 64, 64), {"cus": 0}), ((bf, 64, 64, 64), {"variant": 99}),
+                     ((tkg.DTYPE_MXFP4, 64, 64, 64), {}), ((9, 64, 64, 64), {})]:
+        with pytest.raises(tkg.TkgError):
+            P(*args, **kw)

@@ -25,7 +25,7 @@ __all__ = [
     "STATUS", "LIB_PATH", "tkg_attention_fwd", "attn_lds_offsets",
     "num_variants", "variant_info", "launch_masked", "gemm_splitk",
     "splitk_workspace_size", "splitk_count", "gemm_splitk_noalloc",
-    "NOALLOC_SCRATCH_BYTES",
+    "NOALLOC_SCRATCH_BYTES", "plan_launch",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtkg.so")
@@ -47,6 +47,11 @@ class TkgError(RuntimeError):
 class TkgOpts(ctypes.Structure):
     _fields_ = [("grid", ctypes.c_int32), ("group_m", ctypes.c_int32),
                 ("xcd_remap", ctypes.c_int32), ("variant", ctypes.c_int32)]
+
+
+class LaunchPlan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "variant", "tile", "tiles", "grid", "group_m", "xcd_remap")]
 
 
 class VariantDesc(ctypes.Structure):
@@ -113,6 +118,9 @@ def _load() -> ctypes.CDLL:
     L.tkg_variant_info.restype = i32
     L.tkg_launch_masked.argtypes = [i32, i64, i64, i64, i32]
     L.tkg_launch_masked.restype = i32
+    L.tkg_plan_launch.argtypes = [i32, i64, i64, i64, ctypes.POINTER(TkgOpts), i32,
+                                  ctypes.POINTER(LaunchPlan)]
+    L.tkg_plan_launch.restype = i32
     return L
 
 
@@ -162,6 +170,20 @@ def launch_masked(dtype: int, M: int, N: int, K: int, variant: int = 0) -> bool:
     if r < 0:
         raise TkgError(r, "tkg_launch_masked")
     return bool(r)
+
+
+def plan_launch(dtype: int, M: int, N: int, K: int, cus: int = 256, grid: int = 0,
+                group_m: int = 0, xcd_remap: int = 1, variant: int = 0) -> dict:
+    """The launch ``tkg_gemm_ex`` makes with these options on a device of
+    ``cus`` compute units (``tkg_plan_launch``): configuration, tile edge,
+    tile count, grid and tile order. No GPU work."""
+    o = TkgOpts(int(grid), int(group_m), int(xcd_remap), int(variant))
+    p = LaunchPlan()
+    r = lib.tkg_plan_launch(int(dtype), int(M), int(N), int(K), ctypes.byref(o), int(cus),
+                            ctypes.byref(p))
+    if r < 0:
+        raise TkgError(r, "tkg_plan_launch")
+    return {n: getattr(p, n) for n, _ in LaunchPlan._fields_}
 
 
 def lds_row_bytes(dtype: int) -> int:

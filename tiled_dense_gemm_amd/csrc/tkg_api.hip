@@ -83,16 +83,14 @@ struct Plan {
 // most tile rows (8 .. 32, a power of two) whose A panels of panel_bytes
 // each fit in half the cache, so a band's A panels stay cached while the
 // band's rounds stream B. Otherwise bands of 8 rows in the grouped order.
-int make_plan(int64_t M, int64_t N, int64_t bt, int occ, const tkg_opts* o, Plan* pl,
-              int64_t panel_bytes = 0) {
+// `cus`: the device's compute units (the default grid is cus x occ).
+int make_plan(int64_t M, int64_t N, int64_t bt, int occ, const tkg_opts* o, int cus,
+              Plan* pl, int64_t panel_bytes = 0) {
   pl->tiles_m = (int32_t)((M + bt - 1) / bt);
   pl->tiles_n = (int32_t)((N + bt - 1) / bt);
   const int64_t tiles = (int64_t)pl->tiles_m * pl->tiles_n;
   if (tiles > INT32_MAX / 2) return TKG_ERR_SHAPE;
   pl->num_tiles = (int32_t)tiles;
-  int cus = 0;
-  const int st = cu_count(&cus);
-  if (st != TKG_OK) return st;
   int grid = (o && o->grid > 0) ? o->grid : cus * occ;
   if (grid > pl->num_tiles) grid = pl->num_tiles;
   pl->grid = grid;
@@ -117,6 +115,29 @@ int check_common(int64_t M, int64_t N, int64_t K, int64_t kmult,
   return TKG_OK;
 }
 
+// The configuration and launch plan of a dense product on `cus` compute
+// units. Variant 0 takes 128 x 128 tiles when 256 x 256 ones would leave
+// compute units idle (fewer tiles than units), e.g. one GPU's N/8 shard of a
+// product split over 8 GPUs, or K-heavy small products; for operands beyond
+// the last-level cache, the bf16 5-slot ring. With group_m 0, such operands
+// also take the cache-sized XCD-block order (make_plan).
+int dense_plan(tkg::DenseType dt, int64_t M, int64_t N, int64_t K, const tkg_opts* opts,
+               int cus, int* variant_out, Plan* pl) {
+  const int64_t eb = 1 + (dt == tkg::kBf16);
+  int variant = opts ? opts->variant : 0;
+  if (variant < 0 || variant >= tkg::dense_num_variants(dt)) return TKG_ERR_SHAPE;
+  const bool large = (M + N) * K * eb > tkg::kLastLevelCacheBytes;
+  if (variant == 0) {
+    const int64_t tiles256 = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+    if (tiles256 < cus) variant = tkg::kDenseSmallTileVariant;
+    else if (large && dt == tkg::kBf16) variant = tkg::kDenseLargeVariantBf16;
+  }
+  const int64_t bt = tkg::dense_tile(dt, variant);
+  *variant_out = variant;
+  return make_plan(M, N, bt, tkg::dense_occupancy(dt, variant), opts, cus, pl,
+                   large ? bt * K * eb : 0);
+}
+
 int run_dense(tkg::DenseType dt, int64_t M, int64_t N, int64_t K,
               const void* A, const void* B, void* C, float scale,
               void* stream, const tkg_opts* opts) {
@@ -131,26 +152,12 @@ int run_dense(tkg::DenseType dt, int64_t M, int64_t N, int64_t K,
     return TKG_ERR_NULL;
   if (!aligned16(C) || (K > 0 && (!aligned16(A) || !aligned16(B))))
     return TKG_ERR_ALIGN;
-  // Variant 0 takes 128 x 128 tiles when 256 x 256 ones would leave compute
-  // units idle (fewer tiles than units), e.g. one GPU's N/8 shard of a
-  // product split over 8 GPUs, or K-heavy small products.
-  int variant = opts ? opts->variant : 0;
-  if (variant < 0 || variant >= tkg::dense_num_variants(dt)) return TKG_ERR_SHAPE;
-  // Operands beyond the last-level cache: the bf16 5-slot ring (variant 0)
-  // and the cache-sized XCD-block order (group_m 0).
-  const bool large = (M + N) * K * eb > tkg::kLastLevelCacheBytes;
-  if (variant == 0) {
-    int cus = 0;
-    st = cu_count(&cus);
-    if (st != TKG_OK) return st;
-    const int64_t tiles256 = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
-    if (tiles256 < cus) variant = tkg::kDenseSmallTileVariant;
-    else if (large && dt == tkg::kBf16) variant = tkg::kDenseLargeVariantBf16;
-  }
+  int cus = 0;
+  st = cu_count(&cus);
+  if (st != TKG_OK) return st;
+  int variant = 0;
   Plan pl;
-  const int64_t bt = tkg::dense_tile(dt, variant);
-  st = make_plan(M, N, bt, tkg::dense_occupancy(dt, variant), opts, &pl,
-                 large ? bt * K * eb : 0);
+  st = dense_plan(dt, M, N, K, opts, cus, &variant, &pl);
   if (st != TKG_OK) return st;
   tkg::DenseArgs a;
   a.A = static_cast<const uint8_t*>(A);
@@ -251,11 +258,11 @@ int run_dense_splitk(tkg::DenseType dt, int64_t M, int64_t N, int64_t K, const v
   if (ws == nullptr || ws_bytes < sp.ws_bytes) return TKG_ERR_WORKSPACE;
   if (!aligned16(ws)) return TKG_ERR_ALIGN;
   const int v = tkg::kDenseSmallTileVariant;
-  Plan pl;
-  st = make_plan(M, N, tkg::dense_tile(dt, v), tkg::dense_occupancy(dt, v), nullptr, &pl);
-  if (st != TKG_OK) return st;
   int cus = 0;
   st = cu_count(&cus);
+  if (st != TKG_OK) return st;
+  Plan pl;
+  st = make_plan(M, N, tkg::dense_tile(dt, v), tkg::dense_occupancy(dt, v), nullptr, cus, &pl);
   if (st != TKG_OK) return st;
   const int64_t units = (int64_t)pl.num_tiles * sp.splits;
   if (units > INT32_MAX / 2) return TKG_ERR_SHAPE;
@@ -298,8 +305,11 @@ int run_fp4(int64_t M, int64_t N, int64_t K, const void* A, const void* As,
   if (!aligned16(C) || (K > 0 && (!aligned16(A) || !aligned16(B) ||
                                   !aligned16(As) || !aligned16(Bs))))
     return TKG_ERR_ALIGN;
+  int cus = 0;
+  st = cu_count(&cus);
+  if (st != TKG_OK) return st;
   Plan pl;
-  st = make_plan(M, N, kBM, 1, opts, &pl);
+  st = make_plan(M, N, kBM, 1, opts, cus, &pl);
   if (st != TKG_OK) return st;
   tkg::Fp4Args a;
   a.A = static_cast<const uint8_t*>(A);
@@ -344,8 +354,11 @@ int run_mx(tkg::MxType fmt, int64_t M, int64_t N, int64_t K, const void* A,
   if (!aligned16(C) || (K > 0 && (!aligned16(A) || !aligned16(B) ||
                                   !aligned16(As) || !aligned16(Bs))))
     return TKG_ERR_ALIGN;
+  int cus = 0;
+  st = cu_count(&cus);
+  if (st != TKG_OK) return st;
   Plan pl;
-  st = make_plan(M, N, kBM, 1, opts, &pl);
+  st = make_plan(M, N, kBM, 1, opts, cus, &pl);
   if (st != TKG_OK) return st;
   tkg::MxArgs a;
   a.A = static_cast<const uint8_t*>(A);
@@ -646,6 +659,55 @@ int tkg_gemm_splitk_count(int dtype, int64_t M, int64_t N, int64_t K, int splits
   SplitPlan sp;
   st = splitk_plan(dt, M, N, K, splits, &sp);
   return st != TKG_OK ? st : sp.splits;
+}
+
+int tkg_plan_launch(int dtype, int64_t M, int64_t N, int64_t K, const tkg_opts* opts,
+                    int cus, tkg_launch_plan* out) {
+  if (cus <= 0) return TKG_ERR_SHAPE;
+  int variant = opts ? opts->variant : 0;
+  int64_t bt = kBM;
+  Plan pl{};
+  int st = TKG_OK;
+  bool empty = false;
+  switch (dtype) {
+    case TKG_DTYPE_BF16:
+    case TKG_DTYPE_FP8: {
+      const tkg::DenseType dt = dtype == TKG_DTYPE_BF16 ? tkg::kBf16 : tkg::kFp8;
+      st = check_common(M, N, K, dt == tkg::kBf16 ? 8 : 16,
+                        dt == tkg::kBf16 ? 4194303 : 8388607);
+      if (st != TKG_OK) return st;
+      if (variant < 0 || variant >= tkg::dense_num_variants(dt)) return TKG_ERR_SHAPE;
+      empty = M == 0 || N == 0;
+      if (!empty) {
+        st = dense_plan(dt, M, N, K, opts, cus, &variant, &pl);
+        bt = tkg::dense_tile(dt, variant);
+      }
+      break;
+    }
+    case TKG_DTYPE_FP4_BLOCKSCALED:
+      st = check_common(M, N, K, 64, 16777215);
+      if (st != TKG_OK) return st;
+      if (variant < 0 || variant >= tkg::fp4_num_variants()) return TKG_ERR_SHAPE;
+      empty = M == 0 || N == 0;
+      if (!empty) st = make_plan(M, N, kBM, 1, opts, cus, &pl);
+      break;
+    case TKG_DTYPE_MXFP4:
+    case TKG_DTYPE_MXFP8:
+      st = check_common(M, N, K, 128, dtype == TKG_DTYPE_MXFP4 ? 16777088 : 8388480);
+      if (st != TKG_OK) return st;
+      if (variant < 0 || variant >= tkg::mx_num_variants()) return TKG_ERR_SHAPE;
+      empty = M == 0 || N == 0;
+      if (!empty) st = make_plan(M, N, kBM, 1, opts, cus, &pl);
+      break;
+    default:
+      return TKG_ERR_SHAPE;
+  }
+  if (st != TKG_OK) return st;
+  if (out != nullptr) {
+    *out = tkg_launch_plan{variant, (int32_t)bt, empty ? 0 : pl.num_tiles, empty ? 0 : pl.grid,
+                           empty ? 0 : pl.group_m, empty ? 0 : pl.xcd_remap};
+  }
+  return TKG_OK;
 }
 
 int tkg_variant_info(int dtype, int variant, tkg_variant_desc* out) {
