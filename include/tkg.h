@@ -362,8 +362,13 @@ int tkg_launch_masked(int dtype, int64_t M, int64_t N, int64_t K, int variant);
  * products with fewer 256 x 256 tiles than compute units, the bf16 5-slot
  * ring for operands beyond the 256 MB last-level cache), its tile edge, the
  * tile count, the grid, and the tile order applied (group_m, xcd_remap; see
- * tkg_opts). opts may be NULL (the defaults). An empty product (M or N = 0)
- * reports tiles = grid = 0. Returns TKG_OK, or the negative tkg_status that
+ * tkg_opts); and, for whole-tile bf16/fp8 products with automatic variant
+ * and grid whose last round of 256 x 256 tiles is partial and small enough
+ * that its tiles' 128 x 128 quadrants fit one round of the small-tile
+ * configuration (two workgroups per compute unit), the second launch that
+ * runs those quadrants (the first launch then runs the full rounds' units
+ * only). opts may be NULL (the defaults). An empty product (M or N = 0)
+ * reports tiles = grid = units = 0. Returns TKG_OK, or the negative tkg_status that
  * tkg_gemm_ex's shape checks return (TKG_ERR_SHAPE also for cus <= 0).
  * Host logic only, no GPU work; the caller owns *out.
  */
@@ -374,6 +379,10 @@ typedef struct tkg_launch_plan {
   int32_t grid;      /* workgroups launched                                */
   int32_t group_m;   /* tile rows per band of the tile order               */
   int32_t xcd_remap; /* 0, 1 or 2 (XCD blocks) as applied                  */
+  int32_t units;     /* tiles the first launch runs                        */
+  int32_t tail_variant; /* configuration of the second launch, -1: none    */
+  int32_t tail_units;   /* 128 x 128 quadrants it runs (0: no second launch) */
+  int32_t tail_grid;    /* its workgroups                                  */
 } tkg_launch_plan;
 int tkg_plan_launch(int dtype, int64_t M, int64_t N, int64_t K, const tkg_opts *opts,
                     int cus, tkg_launch_plan *out);

@@ -240,14 +240,16 @@ def test_plan_launch_policy():
     # products whose A and B exceed that cache
     P = tkg.plan_launch
     bf, f8 = tkg.DTYPE_BF16, tkg.DTYPE_FP8
+    one = dict(units=1024, tail_variant=-1, tail_units=0, tail_grid=0)
     assert P(bf, 8192, 8192, 8192) == dict(variant=0, tile=256, tiles=1024, grid=256,
-                                           group_m=8, xcd_remap=1)
+                                           group_m=8, xcd_remap=1, **one)
     # 16384^3 bf16: 1 GiB of operands; 8 MiB A panels, 16 of them fit 128 MiB
+    one["units"] = 4096
     assert P(bf, 16384, 16384, 16384) == dict(variant=18, tile=256, tiles=4096, grid=256,
-                                              group_m=16, xcd_remap=2)
+                                              group_m=16, xcd_remap=2, **one)
     # fp8: 4 MiB panels, 32 rows per band
     assert P(f8, 16384, 16384, 16384) == dict(variant=0, tile=256, tiles=4096, grid=256,
-                                              group_m=32, xcd_remap=2)
+                                              group_m=32, xcd_remap=2, **one)
     assert P(f8, 8192, 8192, 8192)["group_m"] == 8
     # exactly at the cache size (bf16 8192^3: 256 MiB) is not beyond it
     assert P(bf, 8192, 8192, 8192)["variant"] == 0
@@ -281,3 +283,33 @@ def test_plan_launch_policy():
                      ((tkg.DTYPE_MXFP4, 64, 64, 64), {}), ((9, 64, 64, 64), {})]:
         with pytest.raises(tkg.TkgError):
             P(*args, **kw)
+
+
+def test_plan_launch_tail_quadrants():
+    # a partial last round of 256 x 256 tiles whose 128 x 128 quadrants fit
+    # one round of the small-tile slots (2 per CU) runs as a second launch
+    P = tkg.plan_launch
+    bf, f8 = tkg.DTYPE_BF16, tkg.DTYPE_FP8
+    p = P(bf, 6144, 6144, 6144)                 # 576 tiles: 2 rounds + 64
+    assert (p["units"], p["tail_variant"], p["tail_units"], p["tail_grid"]) == (512, 4, 256, 256)
+    p = P(f8, 4352, 4096, 1024)                 # 272 tiles: 1 round + 16
+    assert (p["units"], p["tail_units"], p["tail_grid"]) == (256, 64, 64)
+    p = P(bf, 6400, 6144, 512)                  # 600 tiles: 88 left, 352 <= 512
+    assert (p["units"], p["tail_units"]) == (512, 352)
+    # 400 tiles: 144 left, 576 quadrants > 512 slots: one launch
+    assert P(bf, 5120, 5120, 4096)["tail_units"] == 0
+    # 8448^2 x 8192 bf16: beyond the cache (5-slot ring, 32-row bands) and a tail
+    p = P(bf, 8448, 8448, 8192)
+    assert (p["variant"], p["group_m"], p["units"], p["tail_units"]) == (18, 32, 1024, 260)
+    # whole rounds, ragged tiles, explicit grid or variant, K = 0: one launch
+    for args, kw in [((bf, 8192, 8192, 8192), {}), ((bf, 6144, 6100, 1024), {}),
+                     ((bf, 6144, 6144, 1024), {"grid": 256}),
+                     ((bf, 6144, 6144, 1024), {"variant": 17}), ((bf, 6144, 6144, 0), {})]:
+        p = P(*args, **kw)
+        assert p["tail_units"] == 0 and p["tail_variant"] == -1 and p["units"] == p["tiles"], (args, kw)
+    # fewer tiles than CUs: the small-tile configuration, one launch
+    assert P(bf, 2048, 2048, 2048)["tail_units"] == 0
+    # a smaller device: 576 tiles on 128 CUs leave 64, whose 256 quadrants
+    # fill its 256 slots
+    p = P(bf, 6144, 6144, 1024, cus=128)
+    assert (p["grid"], p["units"], p["tail_units"], p["tail_grid"]) == (128, 512, 256, 256)

@@ -216,6 +216,31 @@ def test_xcd_block_order_covers_every_tile(dev, dtype):
             assert torch.equal(C.view(torch.int16), ref.view(torch.int16)), (M, grid, gm)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("M,N,K", [(6144, 6144, 512), (4352, 4096, 1024), (6400, 6144, 256),
+                                   (8448, 8448, 8192)])
+def test_tail_quadrant_launch_agrees(dev, dtype, M, N, K):
+    # a partial last round of 256 x 256 tiles runs as 128 x 128 quadrants in
+    # a second launch; against the single launch (an explicit grid turns the
+    # split off), bit for bit, every element written (NaN fill). 8448^2 x
+    # 8192 bf16 also takes the large-operand ring and order.
+    plan = tkg.plan_launch(tkg.DTYPE_BF16 if dtype == "bf16" else tkg.DTYPE_FP8, M, N, K)
+    assert plan["tail_units"] > 0 and plan["units"] % plan["grid"] == 0, plan
+    A, Bt, d, sa, sb = _dense_operands(dev, dtype, M, N, K, seed=43)
+    ref = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev)
+    assert tkg.tkg_gemm_ex(d, M, N, K, A, None, sa, Bt, None, sb, ref,
+                           grid=plan["grid"]) == 0
+    C = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device=dev)
+    assert tkg.tkg_gemm_ex(d, M, N, K, A, None, sa, Bt, None, sb, C) == 0
+    assert not torch.isnan(C.float()).any()
+    assert torch.equal(C.view(torch.int16), ref.view(torch.int16)), (M, N, K)
+    if M * N * K <= 6144 * 6144 * 512:
+        # the first tiles (first launch) and the last ones (quadrants)
+        _check_dense(dtype, A[:256], Bt[:512], sa, sb, C[:256, :512].contiguous(), (M, N, K))
+        _check_dense(dtype, A[-256:], Bt[-512:], sa, sb, C[-256:, -512:].contiguous(),
+                     (M, N, K, "tail"))
+
+
 def _dense_operands(dev, dtype, M, N, K, seed):
     if dtype == "bf16":
         A = gi.device.bf16_operand(seed, M, K, std=K ** -0.5, device=dev)

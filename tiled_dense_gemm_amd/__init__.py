@@ -51,7 +51,8 @@ class TkgOpts(ctypes.Structure):
 
 class LaunchPlan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
-        "variant", "tile", "tiles", "grid", "group_m", "xcd_remap")]
+        "variant", "tile", "tiles", "grid", "group_m", "xcd_remap", "units",
+        "tail_variant", "tail_units", "tail_grid")]
 
 
 class VariantDesc(ctypes.Structure):

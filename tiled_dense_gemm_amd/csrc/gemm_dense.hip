@@ -181,8 +181,17 @@ __device__ __forceinline__ TileState tile_state(const DenseArgs& p, int u) {
   const uint32_t nk_raw = (klen + BKB - 1) / BKB;
   s.nk = (TRIP == 2) ? (nk_raw + (nk_raw & 1)) : nk_raw;
   int pm, pn;
-  // split-K launches use the grouped order (the reduction walks tiles in it)
-  order_tile(t, gridDim.x, SPLITK ? 0 : p.xcd_remap, p.tiles_m, p.tiles_n, p.group_m, pm, pn);
+  if (!SPLITK && BT == 128 && p.quad_base >= 0) {
+    // a quadrant of a 256 x 256 tile the full-round launch left over
+    int PM, PN;
+    order_tile(p.quad_base + t / 4, p.quad_grid, p.quad_remap, p.quad_tiles_m,
+               p.quad_tiles_n, p.quad_group_m, PM, PN);
+    pm = 2 * PM + (t & 3) / 2;
+    pn = 2 * PN + (t & 1);
+  } else {
+    // split-K launches use the grouped order (the reduction walks tiles in it)
+    order_tile(t, gridDim.x, SPLITK ? 0 : p.xcd_remap, p.tiles_m, p.tiles_n, p.group_m, pm, pn);
+  }
   s.m0 = pm * BT;
   s.n0 = pn * BT;
   // Resources cover only the rows of this tile that exist. A load reads

@@ -76,6 +76,9 @@ int scratch_ptr(void** out) {
 
 struct Plan {
   int32_t tiles_m, tiles_n, num_tiles, group_m, xcd_remap, grid;
+  // two-launch dense products: the first launch runs units [0, full_units),
+  // the tail launch (tail_units > 0) the rest as 128 x 128 quadrants
+  int32_t full_units, tail_units, tail_grid;
 };
 
 // panel_bytes > 0 (bf16/fp8 products whose operands exceed the last-level
@@ -102,6 +105,9 @@ int make_plan(int64_t M, int64_t N, int64_t bt, int occ, const tkg_opts* o, int 
   }
   if (gm > pl->tiles_m) gm = pl->tiles_m;
   pl->group_m = gm;
+  pl->full_units = pl->num_tiles;
+  pl->tail_units = 0;
+  pl->tail_grid = 0;
   return TKG_OK;
 }
 
@@ -134,8 +140,29 @@ int dense_plan(tkg::DenseType dt, int64_t M, int64_t N, int64_t K, const tkg_opt
   }
   const int64_t bt = tkg::dense_tile(dt, variant);
   *variant_out = variant;
-  return make_plan(M, N, bt, tkg::dense_occupancy(dt, variant), opts, cus, pl,
-                   large ? bt * K * eb : 0);
+  const int st = make_plan(M, N, bt, tkg::dense_occupancy(dt, variant), opts, cus, pl,
+                           large ? bt * K * eb : 0);
+  if (st != TKG_OK) return st;
+  // Wave quantization: when the 256 x 256 tiles leave a partial last round
+  // whose tiles, split into 128 x 128 quadrants, fit one round of the
+  // small-tile configuration's workgroup slots (2 per CU), the full rounds
+  // run as usual and the leftover tiles' quadrants run in a second launch:
+  // a partial round of big tiles takes as long as a full one, its quadrants
+  // about 0.6 of it (measured: 6144^3). Whole tiles only; automatic variant
+  // and grid only. Both configurations compute the same bits.
+  const bool auto_variant = opts == nullptr || opts->variant == 0;
+  const bool auto_grid = opts == nullptr || opts->grid <= 0;
+  if (auto_variant && auto_grid && bt == kBM && K > 0 && M % kBM == 0 && N % kBN == 0) {
+    const int g = pl->grid;
+    const int full = (pl->num_tiles / g) * g, tail = pl->num_tiles - full;
+    const int slots = cus * tkg::dense_occupancy(dt, tkg::kDenseSmallTileVariant);
+    if (full > 0 && tail > 0 && 4 * tail <= slots) {
+      pl->full_units = full;
+      pl->tail_units = 4 * tail;
+      pl->tail_grid = 4 * tail;
+    }
+  }
+  return TKG_OK;
 }
 
 int run_dense(tkg::DenseType dt, int64_t M, int64_t N, int64_t K,
@@ -173,14 +200,31 @@ int run_dense(tkg::DenseType dt, int64_t M, int64_t N, int64_t K,
   a.group_m = pl.group_m;
   a.xcd_remap = pl.xcd_remap;
   a.splits = 1;
-  a.num_units = pl.num_tiles;
+  a.num_units = pl.full_units;
   a.ksplit = a.kbytes;
   a.ws = nullptr;
+  a.quad_base = -1;
+  a.quad_tiles_m = a.quad_tiles_n = a.quad_group_m = a.quad_grid = a.quad_remap = 0;
   if (K == 0) {  // empty reduction: the kernel's zero accumulators are C
     a.A = a.B = static_cast<const uint8_t*>(C);
   }
-  const hipError_t e = tkg::launch_dense(dt, a, pl.grid, variant,
-                                         static_cast<hipStream_t>(stream));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = tkg::launch_dense(dt, a, pl.grid, variant, s);
+  if (e != hipSuccess || pl.tail_units == 0) return e == hipSuccess ? TKG_OK : TKG_ERR_LAUNCH;
+  // the leftover tiles as 128 x 128 quadrants, in the first launch's order
+  tkg::DenseArgs q = a;
+  q.tiles_m = 2 * pl.tiles_m;
+  q.tiles_n = 2 * pl.tiles_n;
+  q.num_tiles = 4 * pl.num_tiles;
+  q.num_units = pl.tail_units;
+  q.xcd_remap = 1;
+  q.quad_base = pl.full_units;
+  q.quad_tiles_m = pl.tiles_m;
+  q.quad_tiles_n = pl.tiles_n;
+  q.quad_group_m = pl.group_m;
+  q.quad_grid = pl.grid;
+  q.quad_remap = pl.xcd_remap;
+  e = tkg::launch_dense(dt, q, pl.tail_grid, tkg::kDenseSmallTileVariant, s);
   return e == hipSuccess ? TKG_OK : TKG_ERR_LAUNCH;
 }
 
@@ -285,6 +329,8 @@ int run_dense_splitk(tkg::DenseType dt, int64_t M, int64_t N, int64_t K, const v
   a.num_units = (int32_t)units;
   a.ksplit = sp.ksplit;
   a.ws = static_cast<float*>(ws);
+  a.quad_base = -1;
+  a.quad_tiles_m = a.quad_tiles_n = a.quad_group_m = a.quad_grid = a.quad_remap = 0;
   hipError_t e = tkg::launch_dense(dt, a, grid, v, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return TKG_ERR_LAUNCH;
   e = tkg::launch_dense_reduce(dt, a, v, static_cast<hipStream_t>(stream));
@@ -704,8 +750,12 @@ int tkg_plan_launch(int dtype, int64_t M, int64_t N, int64_t K, const tkg_opts* 
   }
   if (st != TKG_OK) return st;
   if (out != nullptr) {
+    const bool tail = !empty && pl.tail_units > 0;
     *out = tkg_launch_plan{variant, (int32_t)bt, empty ? 0 : pl.num_tiles, empty ? 0 : pl.grid,
-                           empty ? 0 : pl.group_m, empty ? 0 : pl.xcd_remap};
+                           empty ? 0 : pl.group_m, empty ? 0 : pl.xcd_remap,
+                           empty ? 0 : pl.full_units,
+                           tail ? tkg::kDenseSmallTileVariant : -1,
+                           tail ? pl.tail_units : 0, tail ? pl.tail_grid : 0};
   }
   return TKG_OK;
 }

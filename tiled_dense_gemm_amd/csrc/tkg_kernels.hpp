@@ -26,6 +26,14 @@ struct DenseArgs {
   int32_t splits, num_units;
   uint32_t ksplit;
   float* ws;
+  // Tail launch of a two-launch product (quad_base >= 0; 128 x 128 tile
+  // configurations, whole tiles, one split): unit u is quadrant u % 4 (row
+  // half (u % 4) / 2, column half u % 2) of tile quad_base + u / 4 of the
+  // 256 x 256 launch that ran the full rounds, placed by that launch's tile
+  // order (quad_tiles_m x quad_tiles_n tiles, bands of quad_group_m rows,
+  // quad_grid workgroups, remap quad_remap). quad_base < 0: tiles_m,
+  // tiles_n, group_m and this launch's grid place the tiles.
+  int32_t quad_base, quad_tiles_m, quad_tiles_n, quad_group_m, quad_grid, quad_remap;
 };
 
 // Block-scaled 4-bit problem: values packed two per byte (K/2 bytes per row)
