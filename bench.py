@@ -128,37 +128,6 @@ def measured_traffic(kernel: str):
     return measured(kernel, "hbm_bytes_per_launch")
 
 
-ABLATIONS_FILE = os.path.join(ROOT, "profiles", "ablations.json")
-
-
-def vendor_reference():
-    """The committed ablation run's "vendor" groups: this library and the
-    vendor GEMM (hipBLASLt through torch) on the same operands in the same
-    alternating rounds, from the kernel trace of that run; None when the run
-    was taken on other kernel sources. Context for the roofline fractions,
-    not a measurement of this run."""
-    try:
-        rec = json.load(open(ABLATIONS_FILE))
-    except (OSError, ValueError):
-        return None
-    if rec.get("kernel_source_hash") != kernel_source_hash():
-        return None
-    out = {}
-    for r in rec.get("rows", []):
-        if r.get("group") != "vendor":
-            continue
-        key = "%s_%dx%dx%d" % (r["dtype"], r["M"], r["N"], r["K"])
-        who = "vendor" if r.get("options", {}).get("vendor") else "this_library"
-        rnd = lambda v, d: None if v is None else round(v, d)
-        out.setdefault(key, {})[who] = {"tflops": rnd(r.get("trace_tflops"), 1),
-                                        "mfma_busy": rnd(r.get("mfma_busy"), 3),
-                                        "clock_ghz": rnd(r.get("clock_ghz"), 2)}
-    if not out:
-        return None
-    return {"source": "profiles/ablations.md (vendor groups)",
-            "vendor": "hipBLASLt through torch.matmul / torch._scaled_mm", "products": out}
-
-
 ATTN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_traffic.json")
 
 
@@ -187,10 +156,6 @@ def _kernel_key(name: str):
     for frag, key in KERNEL_KEYS.items():
         if frag in name:
             return key
-    if name.startswith("Cijk_") or "_Cijk_" in name:
-        # the vendor library's GEMM (hipBLASLt, through torch): a reference
-        # timed beside this library's kernels, never on the product path
-        return "vendor_fp8" if "F8" in name else "vendor_bf16"
     return None
 
 
@@ -639,8 +604,7 @@ def _roofline(kernel, tflops, peak, basis):
 # the missing swizzle ablation; page "ThunderKittens reaches 22.4 PFLOPS on
 # NVIDIA Rubin" for the release timing and ring depth). Each group:
 # (group, dtype, M, N, K, [(setting label, tkg_gemm_ex options), ...]).
-# Every setting of this library computes the same bits (the GPU tests
-# check it); the vendor rows are timing references.
+# Every setting computes the same bits (the GPU tests check it).
 def ablation_groups():
     # bf16 17 is the default's configuration on the interleaved schedule:
     # the ring-depth and MFMA-shape groups compare on that schedule
@@ -697,14 +661,6 @@ def ablation_groups():
         ("16x16x128, 4 waves (one per SIMD)", {"variant": 2}),
         ("32x32x64, 4 waves (one per SIMD)", {"variant": 3}),
         ("32x32x64, 4 waves (one per SIMD), early reads", {"variant": 9})]))
-    # the vendor library on the same operands, in the same rounds: a
-    # reference for what the chip gives a tuned GEMM under the same power
-    # state (its results are not bit-compared)
-    for n in (8192, 16384):
-        for dt in ("bf16", "fp8"):
-            groups.append(("vendor", dt, n, n, n, [
-                ("this library (automatic)", {}),
-                ("hipBLASLt through torch", {"vendor": True})]))
     return groups
 
 
@@ -732,27 +688,13 @@ def run_ablations(args):
         C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         torch.cuda.synchronize()
         res = {lab: [] for lab, _ in settings}
-        vendor = None
-        if any(opt.get("vendor") for _, opt in settings):
-            if dtype == "bf16":
-                Bt = B.t()
-                vendor = lambda: torch.matmul(A, Bt, out=C)
-            else:
-                a8, b8t = A.view(torch.float8_e4m3fn), B.view(torch.float8_e4m3fn).t()
-                tsa = torch.tensor(float(sa), device=dev)
-                tsb = torch.tensor(float(sb), device=dev)
-                vendor = lambda: torch._scaled_mm(a8, b8t, scale_a=tsa, scale_b=tsb,
-                                                  out_dtype=torch.bfloat16)
         for rnd in range(args.ablation_rounds):
             for lab, opt in settings:
                 def fn(opt=opt):
                     st = tkg.tkg_gemm_ex(d, M, N, K, A, None, sa, B, None, sb, C, stream=stream,
                                          **opt)
                     assert st == 0, (group, lab, st)
-                key = "gemm_" + dtype
-                if opt.get("vendor"):
-                    fn, key = vendor, "vendor_" + dtype
-                r = log.time("%d|%s|%s|%d" % (gi_, group, lab, rnd), key, fn,
+                r = log.time("%d|%s|%s|%d" % (gi_, group, lab, rnd), "gemm_" + dtype, fn,
                              args.warmup, args.steps)
                 res[lab].append(r["ms_mean"])
         for lab, opt in settings:
@@ -847,11 +789,8 @@ def summarize_ablations(run_dirs, out_md, out_json, command):
     rec = {"kernel_source_hash": ref["kernel_source_hash"], "command": command,
            "calibration": fac, "rows": []}
     lines = ["# Ablations of the dense GEMM kernels on one MI355X (rocprofv3)", "",
-             "Every setting of this library computes the same bits (the GPU tests "
-             "compare all kernel configurations and launch options bit for bit); the "
-             "\"vendor\" groups time hipBLASLt (through torch.matmul and torch._scaled_mm) "
-             "on the same operands in the same alternating rounds, as a reference. Kernel "
-             "source hash %s."
+             "Every setting computes the same bits (the GPU tests compare all kernel "
+             "configurations and launch options bit for bit). Kernel source hash %s."
              % ref["kernel_source_hash"], "", "Produced by:", "", "```", command, "```", "",
              "Columns: TFLOP/s from the HIP-event mean of the traced run (median over %d "
              "alternating rounds of %d launches after %d warmup launches) and from the "
@@ -1160,7 +1099,6 @@ def main() -> int:
         "roofline": roofline,
         "rooflines": rooflines,
         "cpu_baseline": cpu,
-        "vendor_reference": vendor_reference(),
         "configs": configs,
         "wall_s_timed": round(wall, 3),
         "launch_log": log.blocks,
