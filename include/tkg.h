@@ -279,13 +279,15 @@ const char *tkg_status_string(int status);
  *               stages (32x32x16 blocks) in a ring of 1 .. 5 stages,
  *               15 = ping-pong on four 64-byte stages, 16 = one wave per
  *               SIMD with early reads, 17 = the interleaved schedule,
- *               18 = 5-slot ring with early reads; fp8 1 = 5-slot
+ *               18 = 5-slot ring with early reads, 19 = configuration 4
+ *               on the interleaved schedule; fp8 1 = 5-slot
  *               ring, 2 = one wave per SIMD
  *               on 16x16x128 blocks, 3 = one wave per SIMD on 32x32x64,
  *               4 / 5 as bf16, 6 = swizzle off, 7 = early B release,
  *               8 = ping-pong, 9 / 10 = one wave per SIMD on 32x32x64 /
  *               16x16x128 with early reads, 11 = early reads, 12 = 5-slot
- *               ring with early reads. TKG_ERR_SHAPE outside 0 .. n-1.
+ *               ring with early reads, 13 = configuration 4 on the
+ *               interleaved schedule. TKG_ERR_SHAPE outside 0 .. n-1.
  *               4-bit product: 0 = 4 waves (default), 1 = 8 waves;
  *               TKG_ERR_SHAPE outside 0..1. Every variant of a product
  *               computes the same sums (the tests find them bit-identical).

@@ -172,8 +172,8 @@ def test_splitk_count_rejects_oversized_k():
 def test_variant_table():
     # every dtype reports its configurations; the defaults are the measured
     # ones, and the ablation entries differ from the default in one field
-    assert tkg.num_variants(tkg.DTYPE_BF16) == 19
-    assert tkg.num_variants(tkg.DTYPE_FP8) == 13
+    assert tkg.num_variants(tkg.DTYPE_BF16) == 20
+    assert tkg.num_variants(tkg.DTYPE_FP8) == 14
     assert tkg.num_variants(tkg.DTYPE_FP4_BLOCKSCALED) == 2
     assert tkg.num_variants(tkg.DTYPE_MXFP4) == tkg.num_variants(tkg.DTYPE_MXFP8) == 2
     assert tkg.variant_info(tkg.DTYPE_MXFP4, 1)["schedule_name"] == "early reads"
@@ -190,8 +190,14 @@ def test_variant_table():
             {k: v for k, v in v0.items() if k != "swizzle"}
         assert tkg.variant_info(d, 7)["schedule_name"] == "early B release"
         assert tkg.variant_info(d, 8)["schedule_name"] == "ping-pong"
-        assert tkg.variant_info(d, tkg.num_variants(d) - 1)["schedule_name"] == "early reads"
-        assert tkg.variant_info(d, tkg.num_variants(d) - 1)["slots"] == 5
+        # the last entry: the small-tile configuration on the interleaved
+        # schedule, the one before it the 5-slot ring with early reads
+        last, small = tkg.variant_info(d, tkg.num_variants(d) - 1), tkg.variant_info(d, 4)
+        assert last["schedule_name"] == "interleaved" and small["schedule_name"] == "early reads"
+        assert {k: v for k, v in last.items() if not k.startswith("schedule")} == \
+            {k: v for k, v in small.items() if not k.startswith("schedule")}
+        five = tkg.variant_info(d, tkg.num_variants(d) - 2)
+        assert (five["schedule_name"], five["slots"]) == ("early reads", 5)
         n = tkg.num_variants(d)
         assert L.tkg_variant_info(d, n, None) == S["TKG_ERR_SHAPE"]
         assert L.tkg_variant_info(d, -1, None) == S["TKG_ERR_SHAPE"]

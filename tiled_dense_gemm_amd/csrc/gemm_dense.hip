@@ -105,7 +105,7 @@ constexpr Ring kRingsBf16[] = {
     {128, 5, 4, 1, 16, 256, 1, 1, kInterleaved},   // 1 5-slot ring (2.5 stages)
     {128, 4, 4, 1, 32, 256, 1, 1, kInterleaved},   // 2 32x32x16 blocks
     {128, 4, 2, 0, 16, 256, 1, 1, kInterleaved},   // 3 one wave per SIMD, 128x128
-    {128, 4, 2, 0, 16, 128, 2, 1, kInterleaved},   // 4 128x128 tiles, 2 per CU
+    {128, 4, 2, 0, 16, 128, 2, 1, kEarlyReads},    // 4 128x128 tiles, 2 per CU
     {128, 4, 2, 0, 16, 128, 1, 1, kInterleaved},   // 5 128x128 tiles, 1 per CU
     {128, 4, 4, 1, 16, 256, 1, 0, kEarlyReads},    // 6 swizzle off
     {128, 4, 4, 1, 16, 256, 1, 1, kEarlyB},        // 7 early B release
@@ -120,13 +120,14 @@ constexpr Ring kRingsBf16[] = {
     {128, 4, 2, 0, 16, 256, 1, 1, kEarlyReads},    // 16 one wave per SIMD, early reads
     {128, 4, 4, 1, 16, 256, 1, 1, kInterleaved},   // 17 interleaved schedule
     {128, 5, 4, 1, 16, 256, 1, 1, kEarlyReads},    // 18 5-slot ring, early reads
+    {128, 4, 2, 0, 16, 128, 2, 1, kInterleaved},   // 19 128x128 tiles, 2 per CU, interleaved
 };
 constexpr Ring kRingsFp8[] = {
     {128, 4, 4, 1, 32, 256, 1, 1, kInterleaved},   // 0 default
     {128, 5, 4, 1, 32, 256, 1, 1, kInterleaved},   // 1 5-slot ring
     {128, 4, 2, 0, 16, 256, 1, 1, kInterleaved},   // 2 one wave per SIMD, 16x16x128
     {128, 4, 2, 0, 32, 256, 1, 1, kInterleaved},   // 3 one wave per SIMD, 32x32x64
-    {128, 4, 2, 0, 16, 128, 2, 1, kInterleaved},   // 4 128x128 tiles, 2 per CU
+    {128, 4, 2, 0, 16, 128, 2, 1, kEarlyReads},    // 4 128x128 tiles, 2 per CU
     {128, 4, 2, 0, 16, 128, 1, 1, kInterleaved},   // 5 128x128 tiles, 1 per CU
     {128, 4, 4, 1, 32, 256, 1, 0, kInterleaved},   // 6 swizzle off
     {128, 4, 4, 1, 32, 256, 1, 1, kEarlyB},        // 7 early B release
@@ -135,6 +136,7 @@ constexpr Ring kRingsFp8[] = {
     {128, 4, 2, 0, 16, 256, 1, 1, kEarlyReads},    // 10 one wave per SIMD, 16x16x128, early reads
     {128, 4, 4, 1, 32, 256, 1, 1, kEarlyReads},    // 11 two waves per SIMD, early reads
     {128, 5, 4, 1, 32, 256, 1, 1, kEarlyReads},    // 12 5-slot ring, early reads
+    {128, 4, 2, 0, 16, 128, 2, 1, kInterleaved},   // 13 128x128 tiles, 2 per CU, interleaved
 };
 constexpr int kNumBf16 = sizeof(kRingsBf16) / sizeof(kRingsBf16[0]);
 constexpr int kNumFp8 = sizeof(kRingsFp8) / sizeof(kRingsFp8[0]);
