@@ -159,7 +159,10 @@ __device__ __forceinline__ void finish_staged(Acc (&acc)[FM][FN], float scale,
         if (m < M) {
           uint16_t* cp = C + (size_t)m * (size_t)N + n;
           if (vec8 && n + 7 < N) {
-            *reinterpret_cast<i32x4_t*>(cp) = v;
+            // non-temporal: the kernel never reads C, so its lines need not
+            // displace operand lines in L2 (measured 0.3-2% faster at
+            // 8192^3 and 16384^3, bf16 and fp8, same process)
+            __builtin_nontemporal_store(v, reinterpret_cast<i32x4_t*>(cp));
           } else {
 #pragma unroll
             for (int u = 0; u < 8; ++u)
