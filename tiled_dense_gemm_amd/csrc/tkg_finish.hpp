@@ -159,10 +159,16 @@ __device__ __forceinline__ void finish_staged(Acc (&acc)[FM][FN], float scale,
         if (m < M) {
           uint16_t* cp = C + (size_t)m * (size_t)N + n;
           if (vec8 && n + 7 < N) {
-            // non-temporal: the kernel never reads C, so its lines need not
-            // displace operand lines in L2 (measured 0.3-2% faster at
-            // 8192^3 and 16384^3, bf16 and fp8, same process)
-            __builtin_nontemporal_store(v, reinterpret_cast<i32x4_t*>(cp));
+            // Rows of whole 128-byte lines are stored non-temporally: the
+            // kernel never reads C, so its lines need not displace operand
+            // lines in L2 (0.3-2% at 8192^3 and 16384^3, bf16 and fp8, same
+            // process). 64-byte rows keep the default policy, under which
+            // L2 merges the two halves of a line into one write (streamed,
+            // the halves went out separately: 20-25% more bytes written).
+            if constexpr (F::RB >= 128)
+              __builtin_nontemporal_store(v, reinterpret_cast<i32x4_t*>(cp));
+            else
+              *reinterpret_cast<i32x4_t*>(cp) = v;
           } else {
 #pragma unroll
             for (int u = 0; u < 8; ++u)
