@@ -358,6 +358,13 @@ void gemm_mx_kernel(MxArgs p) {
       read_frag(bslot, b_base + j * 32 * BKB, 0, fb[0][j]);
       read_scale(sb0 + bs_base + j * SFRAG, rb[j]);
     }
+    if constexpr (WIDE) {
+      // whole rows, as at the stage boundary (a single-word read conflicts)
+#pragma unroll
+      for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(ra[i]));
+#pragma unroll
+      for (int j = 0; j < FN; ++j) asm volatile("" : "+v"(rb[j]));
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) sa[i] = lane_block(pick(ra[i], 0));
 #pragma unroll
