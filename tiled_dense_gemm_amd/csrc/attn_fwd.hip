@@ -403,12 +403,6 @@ void attn_fwd_kernel(AttnArgs p) {
 // plain) 860. Four waves per
 // workgroup (128 query rows) balance causal work better than eight; at
 // D = 64 the softmax outweighs the MFMAs and more resident waves win.
-#ifndef TKG_ATTN_CFG128
-#define TKG_ATTN_CFG128 4, 4, 2, true
-#endif
-#ifndef TKG_ATTN_CFG64
-#define TKG_ATTN_CFG64 4, 4, 4, false
-#endif
 template <int D, int W, int SL, int OCC, bool PIPE>
 struct AttnCfg {
   static constexpr int BQ = AttnShape<D, W, SL>::BQ;
@@ -419,8 +413,8 @@ struct AttnCfg {
     return hipGetLastError();
   }
 };
-using Cfg128 = AttnCfg<128, TKG_ATTN_CFG128>;
-using Cfg64 = AttnCfg<64, TKG_ATTN_CFG64>;
+using Cfg128 = AttnCfg<128, 4, 4, 2, true>;
+using Cfg64 = AttnCfg<64, 4, 4, 4, false>;
 
 }  // namespace
 
@@ -433,16 +427,14 @@ int attn_block_q(int D) { return D == 64 ? Cfg64::BQ : D == 128 ? Cfg128::BQ : 0
 // 1, 2, 4, 8 and 16 MiB gave 933, 937, 961, 968 and 948 there, and over
 // ten causal workloads (N 1024-16384, D 64 and 128) 8 MiB was best or
 // within 2% except D=128 N=1024 (4 MiB 750, 8 MiB 709).
-#ifndef TKG_ATTN_LPT_BYTES
-#define TKG_ATTN_LPT_BYTES (8 << 20)
-#endif
+constexpr int64_t kAttnLptBytes = 8 << 20;
 static int lpt_window(const AttnArgs& a, int D) {
   const int nbh = a.num_wg / a.qblocks;
   if (nbh % 8 != 0) return 1;
   const int hpx = nbh / 8;
   // K and V bytes per query head (a key/value head serves `group` of them)
   const int64_t share = std::max<int64_t>(1, (int64_t)a.Nk * D * 4 / a.group);
-  int w = (int)std::min<int64_t>(hpx, std::max<int64_t>(1, TKG_ATTN_LPT_BYTES / share));
+  int w = (int)std::min<int64_t>(hpx, std::max<int64_t>(1, kAttnLptBytes / share));
   while (hpx % w != 0) --w;
   return w;
 }
