@@ -390,6 +390,26 @@ int tkg_plan_launch(int dtype, int64_t M, int64_t N, int64_t K, const tkg_opts *
                     int cus, tkg_launch_plan *out);
 
 /*
+ * The persistent-grid tile order the kernels run (page "ThunderKittens:
+ * Simple, Fast, and Adorable AI Kernels", section 3.4, "Block Launch Order
+ * and L2 Cache Reuse"), computed by the same code: writes the tile row *pm
+ * and column *pn of work item `t` of a launch with `grid` workgroups over
+ * tiles_m x tiles_n tiles in bands of group_m tile rows, with xcd_remap
+ * 0, 1 or 2 as applied (tkg_launch_plan reports grid, group_m and
+ * xcd_remap). Workgroup w runs items v(w), v(w) + grid, ... where v(w) is
+ * its XCD-contiguous id. quad_base >= 0 describes the second launch of a
+ * two-launch product instead: item t is quadrant t % 4 of item
+ * quad_base + t / 4 of the first launch (whose grid, tile counts, group_m
+ * and remap the other arguments then are), and *pm, *pn index the
+ * half-edge tiles. Returns TKG_OK, or TKG_ERR_SHAPE for a non-positive
+ * grid, tile count or group_m, an xcd_remap outside 0..2, or t outside the
+ * items of the launch described. Host logic only, no GPU work.
+ */
+int tkg_tile_order(int32_t t, int32_t grid, int32_t xcd_remap, int32_t tiles_m,
+                   int32_t tiles_n, int32_t group_m, int32_t quad_base, int32_t *pm,
+                   int32_t *pn);
+
+/*
  * LDS layout introspection for the CPU bank-conflict model (no GPU work).
  * Writes the 64 per-lane LDS byte offsets (relative to the operand tile)
  * of one ds_read_b128 fragment read of the staged operand tiles:

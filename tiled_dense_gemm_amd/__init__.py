@@ -25,7 +25,7 @@ __all__ = [
     "STATUS", "LIB_PATH", "tkg_attention_fwd", "attn_lds_offsets",
     "num_variants", "variant_info", "launch_masked", "gemm_splitk",
     "splitk_workspace_size", "splitk_count", "gemm_splitk_noalloc",
-    "NOALLOC_SCRATCH_BYTES", "plan_launch",
+    "NOALLOC_SCRATCH_BYTES", "plan_launch", "tile_order",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtkg.so")
@@ -119,6 +119,9 @@ def _load() -> ctypes.CDLL:
     L.tkg_variant_info.restype = i32
     L.tkg_launch_masked.argtypes = [i32, i64, i64, i64, i32]
     L.tkg_launch_masked.restype = i32
+    L.tkg_tile_order.argtypes = [i32, i32, i32, i32, i32, i32, i32,
+                                 ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    L.tkg_tile_order.restype = i32
     L.tkg_plan_launch.argtypes = [i32, i64, i64, i64, ctypes.POINTER(TkgOpts), i32,
                                   ctypes.POINTER(LaunchPlan)]
     L.tkg_plan_launch.restype = i32
@@ -185,6 +188,19 @@ def plan_launch(dtype: int, M: int, N: int, K: int, cus: int = 256, grid: int = 
     if r < 0:
         raise TkgError(r, "tkg_plan_launch")
     return {n: getattr(p, n) for n, _ in LaunchPlan._fields_}
+
+
+def tile_order(t: int, grid: int, xcd_remap: int, tiles_m: int, tiles_n: int,
+               group_m: int, quad_base: int = -1):
+    """(tile row, tile column) of work item t in the kernels' persistent
+    order (``tkg_tile_order``; quad_base >= 0: a tail-launch quadrant). No
+    GPU work."""
+    pm, pn = ctypes.c_int32(), ctypes.c_int32()
+    r = lib.tkg_tile_order(int(t), int(grid), int(xcd_remap), int(tiles_m), int(tiles_n),
+                           int(group_m), int(quad_base), ctypes.byref(pm), ctypes.byref(pn))
+    if r < 0:
+        raise TkgError(r, "tkg_tile_order")
+    return pm.value, pn.value
 
 
 def lds_row_bytes(dtype: int) -> int:

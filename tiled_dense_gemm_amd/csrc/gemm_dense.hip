@@ -185,11 +185,8 @@ __device__ __forceinline__ TileState tile_state(const DenseArgs& p, int u) {
   int pm, pn;
   if (!SPLITK && BT == 128 && p.quad_base >= 0) {
     // a quadrant of a 256 x 256 tile the full-round launch left over
-    int PM, PN;
-    order_tile(p.quad_base + t / 4, p.quad_grid, p.quad_remap, p.quad_tiles_m,
-               p.quad_tiles_n, p.quad_group_m, PM, PN);
-    pm = 2 * PM + (t & 3) / 2;
-    pn = 2 * PN + (t & 1);
+    quadrant_tile(t, p.quad_base, p.quad_grid, p.quad_remap, p.quad_tiles_m, p.quad_tiles_n,
+                  p.quad_group_m, pm, pn);
   } else {
     // split-K launches use the grouped order (the reduction walks tiles in it)
     order_tile(t, gridDim.x, SPLITK ? 0 : p.xcd_remap, p.tiles_m, p.tiles_n, p.group_m, pm, pn);

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "tkg.h"
+#include "tkg_device.hpp"
 #include "tkg_kernels.hpp"
 #include "tkg_finish.hpp"
 #include "tkg_layout.hpp"
@@ -705,6 +706,28 @@ int tkg_gemm_splitk_count(int dtype, int64_t M, int64_t N, int64_t K, int splits
   SplitPlan sp;
   st = splitk_plan(dt, M, N, K, splits, &sp);
   return st != TKG_OK ? st : sp.splits;
+}
+
+int tkg_tile_order(int32_t t, int32_t grid, int32_t xcd_remap, int32_t tiles_m,
+                   int32_t tiles_n, int32_t group_m, int32_t quad_base, int32_t* pm,
+                   int32_t* pn) {
+  if (pm == nullptr || pn == nullptr) return TKG_ERR_NULL;
+  if (grid <= 0 || tiles_m <= 0 || tiles_n <= 0 || group_m <= 0 || xcd_remap < 0 ||
+      xcd_remap > 2)
+    return TKG_ERR_SHAPE;
+  const int64_t tiles = (int64_t)tiles_m * tiles_n;
+  if (tiles > INT32_MAX / 4) return TKG_ERR_SHAPE;
+  int r = 0, c = 0;
+  if (quad_base < 0) {
+    if (t < 0 || t >= tiles) return TKG_ERR_SHAPE;
+    tkg::order_tile(t, grid, xcd_remap, tiles_m, tiles_n, group_m, r, c);
+  } else {
+    if (quad_base > tiles || t < 0 || t >= 4 * (tiles - quad_base)) return TKG_ERR_SHAPE;
+    tkg::quadrant_tile(t, quad_base, grid, xcd_remap, tiles_m, tiles_n, group_m, r, c);
+  }
+  *pm = r;
+  *pn = c;
+  return TKG_OK;
 }
 
 int tkg_plan_launch(int dtype, int64_t M, int64_t N, int64_t K, const tkg_opts* opts,

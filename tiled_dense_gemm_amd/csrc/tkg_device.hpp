@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "tkg_layout.hpp"  // TKG_HD
+
 #define TKG_LDS __attribute__((address_space(3)))
 
 namespace tkg {
@@ -125,20 +127,21 @@ __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c,
 // 8 XCDs (workgroup w runs on XCD w % 8), each XCD with its own L2. The
 // virtual id gives every XCD a contiguous range of G/8 ids, so the tiles an
 // XCD runs at the same time are neighbours in the grouped order below and
-// share operand panels in that XCD's L2.
-__device__ __forceinline__ int xcd_virtual_id(int w, int G, int remap) {
+// share operand panels in that XCD's L2. (Host and device: the library
+// reports the order the kernels run, tkg_tile_order.)
+TKG_HD inline int xcd_virtual_id(int w, int G, int remap) {
   return (remap && G % 8 == 0) ? (w % 8) * (G / 8) + (w / 8) : w;
 }
 
 // Grouped order: tiles are walked in bands of `group_m` tile rows; inside a
 // band, column by column. Consecutive tiles then reuse the same few A row
 // panels and B column panels (the pages' {8, N, M/8} block order).
-__device__ __forceinline__ void grouped_tile(int t, int tiles_m, int tiles_n,
-                                             int group_m, int& pm, int& pn) {
+TKG_HD inline void grouped_tile(int t, int tiles_m, int tiles_n, int group_m, int& pm,
+                                int& pn) {
   const int per_group = group_m * tiles_n;
   const int g = t / per_group;
   const int first = g * group_m;
-  const int rows = min(tiles_m - first, group_m);
+  const int rows = tiles_m - first < group_m ? tiles_m - first : group_m;
   const int r = t - g * per_group;
   pm = first + r % rows;
   pn = r / rows;
@@ -152,9 +155,8 @@ __device__ __forceinline__ void grouped_tile(int t, int tiles_m, int tiles_n,
 // of it (h + w operand panels per K stage in that XCD's L2, instead of up to
 // G/8 + 1 when group_m does not match the XCD's share). Any other round
 // keeps the grouped order, so the map stays a bijection.
-__device__ __forceinline__ void order_tile(int t, int G, int remap, int tiles_m,
-                                           int tiles_n, int group_m, int& pm,
-                                           int& pn) {
+TKG_HD inline void order_tile(int t, int G, int remap, int tiles_m, int tiles_n,
+                              int group_m, int& pm, int& pn) {
   const int per_group = group_m * tiles_n;
   const int g = t / per_group;
   const int first = g * group_m;
@@ -183,6 +185,18 @@ __device__ __forceinline__ void order_tile(int t, int G, int remap, int tiles_m,
     }
   }
   grouped_tile(t, tiles_m, tiles_n, group_m, pm, pn);
+}
+
+// Tail launch of a two-launch product: unit u is quadrant u % 4 (row half
+// (u % 4) / 2, column half u % 2) of tile base + u / 4 in the first launch's
+// order (grid G, remap, tiles_m x tiles_n tiles, bands of group_m rows);
+// (pm, pn) indexes the half-edge tiles.
+TKG_HD inline void quadrant_tile(int u, int base, int G, int remap, int tiles_m, int tiles_n,
+                                 int group_m, int& pm, int& pn) {
+  int PM, PN;
+  order_tile(base + u / 4, G, remap, tiles_m, tiles_n, group_m, PM, PN);
+  pm = 2 * PM + (u & 3) / 2;
+  pn = 2 * PN + (u & 1);
 }
 
 }  // namespace tkg
