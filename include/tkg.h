@@ -401,9 +401,10 @@ int tkg_plan_launch(int dtype, int64_t M, int64_t N, int64_t K, const tkg_opts *
  * two-launch product instead: item t is quadrant t % 4 of item
  * quad_base + t / 4 of the first launch (whose grid, tile counts, group_m
  * and remap the other arguments then are), and *pm, *pn index the
- * half-edge tiles. Returns TKG_OK, or TKG_ERR_SHAPE for a non-positive
- * grid, tile count or group_m, an xcd_remap outside 0..2, or t outside the
- * items of the launch described. Host logic only, no GPU work.
+ * half-edge tiles. Returns TKG_OK, TKG_ERR_NULL for a null pm or pn, or
+ * TKG_ERR_SHAPE for a non-positive grid, tile count or group_m, a group_m
+ * above tiles_m, an xcd_remap outside 0..2, or t outside the items of the
+ * launch described. Host logic only, no GPU work.
  */
 int tkg_tile_order(int32_t t, int32_t grid, int32_t xcd_remap, int32_t tiles_m,
                    int32_t tiles_n, int32_t group_m, int32_t quad_base, int32_t *pm,

@@ -16,8 +16,9 @@ def _order(tiles_m, tiles_n, grid, remap, group_m):
 SHAPES = [
     # (tiles_m, tiles_n, grid, group_m): full bands, a partial last band,
     # grids below, at and above the tile count, group_m not dividing grid
+    # (group_m at most tiles_m, as the planner clamps it)
     (32, 32, 256, 8), (32, 32, 256, 16), (64, 64, 256, 16), (64, 64, 256, 32),
-    (24, 40, 256, 8), (30, 17, 256, 8), (7, 9, 256, 8), (5, 3, 16, 8),
+    (24, 40, 256, 8), (30, 17, 256, 8), (7, 9, 256, 7), (5, 3, 16, 5),
     (32, 56, 256, 8), (16, 16, 40, 3), (33, 31, 64, 4), (8, 8, 512, 8),
 ]
 
@@ -77,7 +78,7 @@ def test_tile_order_argument_errors():
     bad = tkg.STATUS["TKG_ERR_SHAPE"]
     for args in [(0, 0, 1, 4, 4, 2, -1), (0, 8, 3, 4, 4, 2, -1), (0, 8, 1, 0, 4, 2, -1),
                  (0, 8, 1, 4, 4, 0, -1), (16, 8, 1, 4, 4, 2, -1), (-1, 8, 1, 4, 4, 2, -1),
-                 (4, 8, 1, 4, 4, 2, 15), (0, 8, 1, 4, 4, 2, 17)]:
+                 (4, 8, 1, 4, 4, 2, 15), (0, 8, 1, 4, 4, 2, 17), (0, 8, 1, 4, 4, 5, -1)]:
         pm, pn = ctypes.c_int32(), ctypes.c_int32()
         assert tkg.lib.tkg_tile_order(*args, ctypes.byref(pm), ctypes.byref(pn)) == bad, args
     assert tkg.lib.tkg_tile_order(0, 8, 1, 4, 4, 2, -1, None, None) == tkg.STATUS["TKG_ERR_NULL"]

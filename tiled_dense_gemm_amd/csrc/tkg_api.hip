@@ -712,8 +712,8 @@ int tkg_tile_order(int32_t t, int32_t grid, int32_t xcd_remap, int32_t tiles_m,
                    int32_t tiles_n, int32_t group_m, int32_t quad_base, int32_t* pm,
                    int32_t* pn) {
   if (pm == nullptr || pn == nullptr) return TKG_ERR_NULL;
-  if (grid <= 0 || tiles_m <= 0 || tiles_n <= 0 || group_m <= 0 || xcd_remap < 0 ||
-      xcd_remap > 2)
+  if (grid <= 0 || tiles_m <= 0 || tiles_n <= 0 || group_m <= 0 || group_m > tiles_m ||
+      xcd_remap < 0 || xcd_remap > 2)
     return TKG_ERR_SHAPE;
   const int64_t tiles = (int64_t)tiles_m * tiles_n;
   if (tiles > INT32_MAX / 4) return TKG_ERR_SHAPE;
