@@ -33,8 +33,10 @@
  * - Return value: TKG_OK (0) once the kernel is enqueued, or a negative
  *   tkg_status. On any error nothing is enqueued and C is untouched.
  *   tkg_status_string() names every status.
- * - The library holds no mutable state besides a per-device cache of the
- *   compute-unit count; all entry points are thread-safe.
+ * - The library holds no mutable state besides per-device caches of the
+ *   compute-unit count and of the address of the allocation-free entry
+ *   point's scratch array (tkg_gemm_splitk_noalloc, whose calls on one GPU
+ *   share that array); all entry points are thread-safe.
  */
 #ifndef TKG_H
 #define TKG_H
@@ -93,9 +95,11 @@ int gemm_fp8(int64_t M, int64_t N, int64_t K, const void *A, float scale_a,
  *      a_scale * e4m3(A_scales[i][k/16]) * e2m1(A[i][k]).
  *   B, B_scales, b_scale: the same for B in column-major order (N x K/2
  *      values, N x K/16 scales).
- *   Each e2m1 value times its block scale is exact in bf16, so the product
- *   runs as an exact bf16 GEMM with fp32 accumulation; a_scale * b_scale
- *   (fp32) multiplies the accumulator before rounding to bf16.
+ *   Each e2m1 value times its block scale is exact in fp16 (at most 6
+ *   significant bits, magnitude within [2^-10, 2688]), so the product runs
+ *   on the fp16 matrix cores with fp32 accumulation and no rounding of the
+ *   operands; a_scale * b_scale (fp32) multiplies the accumulator before
+ *   rounding to bf16.
  *   Requires K % 64 == 0 and K <= 16777215. All five pointers 16-byte
  *   aligned.
  * The block-scaled 4-bit format with scale factors kept next to the
@@ -314,9 +318,10 @@ enum {
  * dtype: TKG_DTYPE_*. Arguments that a dtype does not use (A_scales,
  * B_scales for bf16/fp8; the scales for bf16) are ignored. For the MX
  * types a_scale * b_scale multiplies the result (the typed entry points
- * pass 1). opts may be NULL (defaults); the MX types have one kernel
- * configuration (variant 0). Same contract and errors as the typed entry
- * points.
+ * pass 1). opts may be NULL (defaults). The MX types have two kernel
+ * configurations: 0 (each fragment re-read after its last MFMA of the
+ * k-step) and 1 (early reads), bit-identical. Same contract and errors as
+ * the typed entry points.
  */
 int tkg_gemm_ex(int dtype, int64_t M, int64_t N, int64_t K, const void *A,
                 const void *A_scales, float a_scale, const void *B,
