@@ -150,6 +150,21 @@ KERNEL_KEYS = {"gemm_dense_kernel<0": "gemm_bf16", "gemm_dense_kernel<1": "gemm_
 # MX products (e2m1 / e4m3 values with an E8M0 scale per 32) run on the
 # scaled MFMAs at the 4-bit and 8-bit rates
 PEAK_MX_TFLOPS = {"mxfp4": 10100.0, "mxfp8": 5000.0}
+SHADER_ENGINES = 32     # 8 XCDs x 4 shader engines (arrays) on MI355X
+
+
+def _active_cycles(counters):
+    """Active shader cycles of one launch, per shader engine (None when not
+    collected). SQ_BUSY_CYCLES is summed over the chip's 32 shader engines
+    (8 XCDs x 4; the profiler's agent record lists 32 arrays), so its mean
+    per engine counts the cycles the kernel's waves occupied the arrays.
+    GRBM_GUI_ACTIVE also counts front-end activity around the launch: in a
+    counter run it has read up to 1.8x the shader engines' cycles for one
+    launch, which would inflate a clock and deflate a busy fraction."""
+    import statistics
+    if counters.get("SQ_BUSY_CYCLES"):
+        return statistics.mean(counters["SQ_BUSY_CYCLES"]) / SHADER_ENGINES
+    return None
 
 
 def _kernel_key(name: str):
@@ -341,21 +356,21 @@ def summarize_profile(trace_dir: str, fetch_dir: str, write_dir: str,
             e = extra[k]
             if k not in rec["kernels"]:
                 continue
-            if "SQ_VALU_MFMA_BUSY_CYCLES" in e and "GRBM_GUI_ACTIVE" in e:
-                # MFMA busy cycles per SIMD over GPU-active cycles per XCD
-                util = (statistics.mean(e["SQ_VALU_MFMA_BUSY_CYCLES"]) / 1024.0) / (
-                    statistics.mean(e["GRBM_GUI_ACTIVE"]) / 8.0)
+            act = _active_cycles(e)
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in e and act:
+                # MFMA busy cycles per SIMD over active cycles per shader engine
+                util = (statistics.mean(e["SQ_VALU_MFMA_BUSY_CYCLES"]) / 1024.0) / act
                 rec["kernels"][k]["mfma_busy_fraction"] = util
                 lines.append("")
-                lines.append("%s: MFMA busy %.1f%% of active cycles (1024 SIMDs, 8 XCDs)" % (k, 100 * util))
-            if "GRBM_GUI_ACTIVE" in e and rec["kernels"][k].get("mean_us"):
-                # GPU-active cycles per XCD over the traced launch duration: the
-                # average shader clock of the launch
-                ghz = statistics.mean(e["GRBM_GUI_ACTIVE"]) / 8.0 / (
-                    rec["kernels"][k]["mean_us"] * 1e3)
+                lines.append("%s: MFMA busy %.1f%% of active cycles (1024 SIMDs; SQ_BUSY_CYCLES "
+                             "over %d shader engines)" % (k, 100 * util, SHADER_ENGINES))
+            if act and rec["kernels"][k].get("mean_us"):
+                # active cycles per shader engine over the traced launch
+                # duration: the average shader clock of the launch
+                ghz = act / (rec["kernels"][k]["mean_us"] * 1e3)
                 rec["kernels"][k]["clock_ghz_estimate"] = ghz
-                lines.append("%s: about %.2f GHz over the launch (GRBM_GUI_ACTIVE per XCD / "
-                             "traced duration)" % (k, ghz))
+                lines.append("%s: about %.2f GHz over the launch (SQ_BUSY_CYCLES per shader "
+                             "engine / traced duration)" % (k, ghz))
             if "SQ_LDS_BANK_CONFLICT" in e and "SQ_LDS_IDX_ACTIVE" in e:
                 rec["kernels"][k]["lds_bank_conflict_over_active"] = (
                     statistics.mean(e["SQ_LDS_BANK_CONFLICT"]) /
@@ -501,12 +516,13 @@ def summarize_attention_profile(trace_dir, fetch_dir, write_dir, out_md, out_jso
                 rec["workloads"][k]["lds_bank_conflict_over_active"] = (
                     statistics.mean(e["SQ_LDS_BANK_CONFLICT"]) /
                     max(1.0, statistics.mean(e["SQ_LDS_IDX_ACTIVE"])))
-            if "GRBM_GUI_ACTIVE" in e and rec["workloads"][k]["mean_us"]:
-                # GPU-active cycles per XCD over the launch: the average clock
-                ghz = statistics.mean(e["GRBM_GUI_ACTIVE"]) / 8.0 / (rec["workloads"][k]["mean_us"] * 1e3)
+            act = _active_cycles(e)
+            if act and rec["workloads"][k]["mean_us"]:
+                # active cycles per shader engine over the launch: the average clock
+                ghz = act / (rec["workloads"][k]["mean_us"] * 1e3)
                 rec["workloads"][k]["clock_ghz_estimate"] = ghz
-                lines.append("%s: about %.2f GHz over the launch (GRBM_GUI_ACTIVE per XCD / "
-                             "traced duration)" % (k, ghz))
+                lines.append("%s: about %.2f GHz over the launch (SQ_BUSY_CYCLES per shader "
+                             "engine / traced duration)" % (k, ghz))
         lines.append("")
     open(out_md, "w").write("\n".join(lines))
     json.dump(rec, open(out_json, "w"), indent=1)
@@ -795,11 +811,11 @@ def summarize_ablations(run_dirs, out_md, out_json, command):
              "Columns: TFLOP/s from the HIP-event mean of the traced run (median over %d "
              "alternating rounds of %d launches after %d warmup launches) and from the "
              "kernel trace's durations of the same launches; MFMA busy = "
-             "SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs over GRBM_GUI_ACTIVE / 8 XCDs; clock = "
-             "GRBM_GUI_ACTIVE / 8 over the traced duration; LDS conflict = "
+             "SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs over SQ_BUSY_CYCLES / %d shader engines; "
+             "clock = SQ_BUSY_CYCLES / %d over the traced duration; LDS conflict = "
              "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; HBM bytes = FETCH_SIZE x %s + "
              "WRITE_SIZE x %s (KiB, calibrated by 1 GiB copies); L2 hit = TCC_HIT / (HIT + "
-             "MISS)." % (ref["rounds"], ref["steps"], ref["warmup"],
+             "MISS)." % (ref["rounds"], ref["steps"], ref["warmup"], SHADER_ENGINES, SHADER_ENGINES,
                          "%.3f" % fac.get("FETCH_SIZE", float("nan")),
                          "%.3f" % fac.get("WRITE_SIZE", float("nan"))), ""]
     cur = None
@@ -817,10 +833,10 @@ def summarize_ablations(run_dirs, out_md, out_json, command):
         flops = 2.0 * row["M"] * row["N"] * row["K"]
         mean_us = statistics.mean(ds) if ds else None
         g = lambda c: statistics.mean(cs[c]) if cs.get(c) else None
-        busy = (g("SQ_VALU_MFMA_BUSY_CYCLES") / 1024.0 / (g("GRBM_GUI_ACTIVE") / 8.0)
-                if g("SQ_VALU_MFMA_BUSY_CYCLES") and g("GRBM_GUI_ACTIVE") else None)
-        ghz = (g("GRBM_GUI_ACTIVE") / 8.0 / (mean_us * 1e3)
-               if g("GRBM_GUI_ACTIVE") and mean_us else None)
+        act = _active_cycles(cs)
+        busy = (g("SQ_VALU_MFMA_BUSY_CYCLES") / 1024.0 / act
+                if g("SQ_VALU_MFMA_BUSY_CYCLES") and act else None)
+        ghz = act / (mean_us * 1e3) if act and mean_us else None
         confl = (g("SQ_LDS_BANK_CONFLICT") / max(1.0, g("SQ_LDS_IDX_ACTIVE"))
                  if g("SQ_LDS_BANK_CONFLICT") is not None and g("SQ_LDS_IDX_ACTIVE") else None)
         hbm = (g("FETCH_SIZE") * 1024 * fac["FETCH_SIZE"] + g("WRITE_SIZE") * 1024 * fac["WRITE_SIZE"]
