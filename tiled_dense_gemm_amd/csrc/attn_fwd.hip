@@ -35,6 +35,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "tkg_attn_layout.hpp"
 #include "tkg_device.hpp"
@@ -45,6 +46,7 @@ namespace {
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // 4 bf16 pairs
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -78,6 +80,15 @@ __device__ __forceinline__ i32x4_t rsrc_words(const void* base, uint32_t nbytes)
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   return i32x4_t{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), (int)nbytes,
                  0x00020000};
+}
+
+// Compile-time loop: f(integral_constant<int, I>) for I = B .. E-1.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 __device__ __forceinline__ float max_with_partner(float x) {
@@ -147,10 +158,13 @@ void attn_fwd_kernel(AttnArgs p) {
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.Q + qoff, (uint32_t)p.Nq * S::ROWB);
   // the first half of the waves copies K tiles, the second half V tiles
   const bool loads_v = (int)wave * S::NPW >= S::NI / 2;
-  const i32x4_t rkv = rsrc_words((loads_v ? p.V : p.K) + kvoff, (uint32_t)p.Nk * S::ROWB);
+  const uint16_t* kv = (loads_v ? p.V : p.K) + kvoff;
+  const uint32_t kv_bytes = (uint32_t)p.Nk * S::ROWB;
 
   // ---- ring loads: piece i (1 KiB) of a slot is K (i < NI/2) or V. Lane
-  // offsets are relative to the block's first key; keys past Nk read zeros.
+  // offsets are relative to the block's first key, where each block's
+  // buffer starts (base and size in scalar registers, so the per-lane
+  // offsets stay fixed); keys past Nk read zeros.
   uint32_t dma_off[S::NPW];
 #pragma unroll
   for (int j = 0; j < S::NPW; ++j) {
@@ -160,11 +174,16 @@ void attn_fwd_kernel(AttnArgs p) {
     const uint32_t c = cs ^ (loads_v ? attn_v_swz(D, row) : attn_k_swz(D, row));
     dma_off[j] = row * S::ROWB + 16 * c;
   }
-  auto issue = [&](int blk, int slot) {
+  auto issue = [&](int blk, uint32_t slot_off) {
     const uint32_t k0b = (uint32_t)blk * (S::BK * S::ROWB);
-    const uint32_t dst = (uint32_t)(uintptr_t)smem + slot * S::STAGE + wave * S::NPW * 1024;
+    // bytes left from the block's first key (both below 2^31); uniform,
+    // and kept in a scalar register for the asm's resource operand
+    const int left = max((int)kv_bytes - (int)k0b, 0);
+    const i32x4_t r = rsrc_words(reinterpret_cast<const uint8_t*>(kv) + k0b,
+                                 (uint32_t)__builtin_amdgcn_readfirstlane(left));
+    const uint32_t dst = (uint32_t)(uintptr_t)smem + slot_off + wave * S::NPW * 1024;
 #pragma unroll
-    for (int j = 0; j < S::NPW; ++j) dma_b128_ring(rkv, dst + j * 1024, dma_off[j] + k0b);
+    for (int j = 0; j < S::NPW; ++j) dma_b128_ring(r, dst + j * 1024, dma_off[j]);
   };
 
   // ---- LDS read addresses: K fragment ks at (lane_k ^ 32 ks); V read (s, t,
@@ -178,6 +197,7 @@ void attn_fwd_kernel(AttnArgs p) {
 #pragma unroll
   for (int db = 0; db < S::DB; ++db) o[db] = f32x16_t{};
   float m = -INFINITY;  // reference max, log2 units (same in lanes l, l ^ 32)
+  float thr = -INFINITY;  // m + kRescaleSlack
   float l = 0.0f;       // this lane's part of the row sum
   const float c = p.c;
   const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
@@ -209,13 +229,16 @@ void attn_fwd_kernel(AttnArgs p) {
   };
   // the block's row max in log2 units (scores scale after: c > 0), both
   // halves of the row (lanes l, l ^ 32); raises the reference max m when
-  // it grows by more than the slack, rescaling O and the row sum
+  // it grows by more than the slack, rescaling O and the row sum. Whether
+  // any row grows that much is decided on each lane's half of its row
+  // (max(a, b) c = max(a c, b c) for c > 0, so the wave's decision is the
+  // same); the halves are combined only when some row does.
   auto update_max = [&](const f32x16_t& sa) {
     float mx = sa[0];
 #pragma unroll
     for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sa[e]);
-    const float mloc = max_with_partner(mx) * c;
-    if (__builtin_amdgcn_ballot_w64(mloc > m + kRescaleSlack)) {
+    if (__builtin_amdgcn_ballot_w64(mx * c > thr)) {
+      const float mloc = max_with_partner(mx) * c;
       const float mn = fmaxf(m, mloc);
       const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 on the first block
       l *= alpha;
@@ -224,16 +247,17 @@ void attn_fwd_kernel(AttnArgs p) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
       m = mn;
+      thr = m + kRescaleSlack;
     }
   };
   // probability pair t (scores 2t, 2t+1) in bf16, into the P^T operand of
   // k-step t / 4 (accumulator elements 8s .. 8s+7), added to the row sum
-  auto prob_pair = [&](const f32x16_t& sa, int t, bf16x8_t (&pk)[2]) {
+  // (a pair is kept as one 32-bit word, so it is converted once)
+  auto prob_pair = [&](const f32x16_t& sa, int t, u32x4_t (&pk)[2]) {
     const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[2 * t], c, -m));
     const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[2 * t + 1], c, -m));
     const bf16x2_t pr = {(__bf16)e0, (__bf16)e1};
-    pk[t / 4][2 * (t % 4)] = pr[0];
-    pk[t / 4][2 * (t % 4) + 1] = pr[1];
+    pk[t / 4][t % 4] = __builtin_bit_cast(uint32_t, pr);
     l = __builtin_amdgcn_fdot2_f32_bf16(pr, one, l, false);
     return pr;
   };
@@ -251,18 +275,19 @@ void attn_fwd_kernel(AttnArgs p) {
       }
   };
   // O^T += V^T P^T
-  auto pv_mma = [&](const bf16x8_t (&pk)[2], const bf16x8_t (&vf)[2][S::DB]) {
+  auto pv_mma = [&](const u32x4_t (&pk)[2], const bf16x8_t (&vf)[2][S::DB]) {
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int db = 0; db < S::DB; ++db) o[db] = mfma_bf16(vf[s][db], pk[s], o[db]);
+      for (int db = 0; db < S::DB; ++db)
+        o[db] = mfma_bf16(vf[s][db], __builtin_bit_cast(bf16x8_t, pk[s]), o[db]);
   };
   // Pipelined phase 1, in issue order: the K fragment reads of the next
   // block (four in flight) and the V^T fragment reads of the current one,
   // then per MFMA of the next block's S^T one or two pairs of the current
   // block's probabilities ahead of it; the fences keep this order.
   auto phase1 = [&](uint32_t cur, uint32_t nxt, f32x16_t& sn, const f32x16_t& sc,
-                    bf16x8_t (&pk)[2], bf16x8_t (&vf)[2][S::DB]) {
+                    u32x4_t (&pk)[2], bf16x8_t (&vf)[2][S::DB]) {
     constexpr int PPM = 8 / S::KS;              // probability pairs per MFMA
     constexpr int KA = S::KS < 4 ? S::KS : 4;   // K reads in flight
     bf16x8_t kf[S::KS];
@@ -310,52 +335,66 @@ void attn_fwd_kernel(AttnArgs p) {
 #pragma unroll
   for (int ks = 0; ks < S::KS; ++ks) asm volatile("" : "+v"(qf[ks]));
 #pragma unroll
-  for (int st = 1; st < S::SLOTS - 1; ++st) issue(st, st);
-  // blocks blk + AHEAD + 1 .. blk + SLOTS - 2 may still be in flight when
-  // iteration blk starts (the pipelined loop also reads block blk + 1)
+  for (int st = 1; st < S::SLOTS - 1; ++st) issue(st, st * S::STAGE);
+  // The loops below run SLOTS blocks per iteration, so the slot of every
+  // block (blk mod SLOTS) is a compile-time constant J and its LDS offsets
+  // fold into the LDS instructions. Blocks blk + AHEAD + 1 .. blk + SLOTS -
+  // 2 may still be in flight when block blk starts (the pipelined loop also
+  // reads block blk + 1).
   constexpr int AHEAD = PIPE ? 1 : 0;
-  auto top = [&](int blk) {
+  auto top = [&](auto J, int blk) {
+    constexpr int j = decltype(J)::value;
     if (blk + S::SLOTS - 2 < nblk)
       wait_vmcnt<(S::SLOTS - 2 - AHEAD) * S::NPW>();
     else
       wait_vmcnt<0>();
     lds_barrier();
     const int nx = blk + S::SLOTS - 1;
-    if (nx < nblk) issue(nx, nx % S::SLOTS);
+    if (nx < nblk) issue(nx, (uint32_t)((j + S::SLOTS - 1) % S::SLOTS) * S::STAGE);
   };
 
   if constexpr (!PIPE) {
-    // one block per iteration: scores, max, probabilities, P V; the other
-    // waves on the SIMD fill each wave's dependency waits
-    for (int blk = 0; blk < nblk; ++blk) {
-      top(blk);
-      if (blk < wblk) {
-        const uint32_t cur = (uint32_t)(blk % S::SLOTS) * S::STAGE;
-        f32x16_t sc;
-        bf16x8_t pk[2], vf[2][S::DB];
-        s_mma(cur, sc);
-        if (needs_mask(blk)) mask(sc, blk);
-        update_max(sc);
+    // one block per step: scores, max, probabilities, P V; the other waves
+    // on the SIMD fill each wave's dependency waits
+    for (int b0 = 0; b0 < nblk; b0 += S::SLOTS) {
+      static_for<0, S::SLOTS>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        const int blk = b0 + j;
+        if (blk >= nblk) return;
+        top(J, blk);
+        if (blk < wblk) {
+          constexpr uint32_t cur = (uint32_t)j * S::STAGE;
+          f32x16_t sc;
+          u32x4_t pk[2];
+          bf16x8_t vf[2][S::DB];
+          s_mma(cur, sc);
+          if (needs_mask(blk)) mask(sc, blk);
+          update_max(sc);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) prob_pair(sc, t, pk);
-        v_frags(cur, vf);
-        pv_mma(pk, vf);
-      }
+          for (int t = 0; t < 8; ++t) prob_pair(sc, t, pk);
+          v_frags(cur, vf);
+          pv_mma(pk, vf);
+        }
+      });
     }
   } else {
-    // Software pipeline: iteration blk computes block blk + 1's scores on
-    // the MFMAs while the VALUs turn block blk's scores into
-    // probabilities (phase1), then accumulates block blk's P V while the
-    // VALUs take block blk + 1's max. On a wave's last block, block
-    // blk + 1 lies wholly past its keys (past Nk, or after every query of
-    // the wave): its scores are masked to -inf, which leaves the max alone,
-    // so the last iteration needs no other path.
-    auto step = [&](int blk, f32x16_t& sc, f32x16_t& sn) {
-      top(blk);
+    // Software pipeline: step blk computes block blk + 1's scores on the
+    // MFMAs while the VALUs turn block blk's scores into probabilities
+    // (phase1), then accumulates block blk's P V while the VALUs take block
+    // blk + 1's max. On a wave's last block, block blk + 1 lies wholly past
+    // its keys (past Nk, or after every query of the wave): its scores are
+    // masked to -inf, which leaves the max alone, so the last step needs no
+    // other path. Scores alternate between two accumulators (even and odd
+    // blocks), so SLOTS is even.
+    static_assert(!PIPE || S::SLOTS % 2 == 0, "even and odd blocks alternate within a pass");
+    auto step = [&](auto J, int blk, f32x16_t& sc, f32x16_t& sn) {
+      constexpr int j = decltype(J)::value;
+      top(J, blk);
       if (blk < wblk) {
-        const uint32_t cur = (uint32_t)(blk % S::SLOTS) * S::STAGE;
-        const uint32_t nxt = (uint32_t)((blk + 1) % S::SLOTS) * S::STAGE;
-        bf16x8_t pk[2], vf[2][S::DB];
+        constexpr uint32_t cur = (uint32_t)j * S::STAGE;
+        constexpr uint32_t nxt = (uint32_t)((j + 1) % S::SLOTS) * S::STAGE;
+        u32x4_t pk[2];
+        bf16x8_t vf[2][S::DB];
         phase1(cur, nxt, sn, sc, pk, vf);
         if (needs_mask(blk + 1)) mask(sn, blk + 1);
         pv_mma(pk, vf);
@@ -369,9 +408,15 @@ void attn_fwd_kernel(AttnArgs p) {
       if (needs_mask(0)) mask(sa, 0);
       update_max(sa);
     }
-    for (int blk = 0; blk < nblk; blk += 2) {
-      step(blk, sa, sb);
-      if (blk + 1 < nblk) step(blk + 1, sb, sa);
+    for (int b0 = 0; b0 < nblk; b0 += S::SLOTS) {
+      static_for<0, S::SLOTS>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        if (b0 + j >= nblk) return;
+        if constexpr (j % 2 == 0)
+          step(J, b0 + j, sa, sb);
+        else
+          step(J, b0 + j, sb, sa);
+      });
     }
   }
 
