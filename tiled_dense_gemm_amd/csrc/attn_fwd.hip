@@ -236,7 +236,7 @@ void attn_fwd_kernel(AttnArgs p) {
   auto update_max = [&](const f32x16_t& sa) {
     float mx = sa[0];
 #pragma unroll
-    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sa[e]);
+    for (int e = 1; e < 16; ++e) mx = __builtin_elementwise_maximum(mx, sa[e]);
     if (__builtin_amdgcn_ballot_w64(mx * c > thr)) {
       const float mloc = max_with_partner(mx) * c;
       const float mn = fmaxf(m, mloc);
