@@ -60,6 +60,20 @@ L = tkg.lib
     (lambda: L.gemm_mxfp8(8, 8, 128, A16, A16, B16, None, C16, None), S["TKG_ERR_NULL"]),
     (lambda: L.gemm_mxfp4(8, 8, 128, A16, A16 + 4, B16, B16, C16, None), S["TKG_ERR_ALIGN"]),
     (lambda: L.gemm_mxfp8(0, 0, 128, None, None, None, None, None, None), S["TKG_OK"]),
+    # the largest K of each format passes the shape check (and stops at the
+    # null pointer); one K granule more is rejected
+    (lambda: L.gemm_bf16(8, 8, 4194296, None, B16, C16, None), S["TKG_ERR_NULL"]),
+    (lambda: L.gemm_bf16(8, 8, 4194304, None, B16, C16, None), S["TKG_ERR_SHAPE"]),
+    (lambda: L.gemm_fp8(8, 8, 8388592, None, 1.0, B16, 1.0, C16, None), S["TKG_ERR_NULL"]),
+    (lambda: L.gemm_fp8(8, 8, 8388608, None, 1.0, B16, 1.0, C16, None), S["TKG_ERR_SHAPE"]),
+    (lambda: L.gemm_fp4_blockscaled(8, 8, 16777152, None, A16, 1.0, B16, B16, 1.0, C16, None),
+     S["TKG_ERR_NULL"]),
+    (lambda: L.gemm_fp4_blockscaled(8, 8, 16777216, None, A16, 1.0, B16, B16, 1.0, C16, None),
+     S["TKG_ERR_SHAPE"]),
+    (lambda: L.gemm_mxfp4(8, 8, 16777088, None, A16, B16, B16, C16, None), S["TKG_ERR_NULL"]),
+    (lambda: L.gemm_mxfp4(8, 8, 16777216, None, A16, B16, B16, C16, None), S["TKG_ERR_SHAPE"]),
+    (lambda: L.gemm_mxfp8(8, 8, 8388480, None, A16, B16, B16, C16, None), S["TKG_ERR_NULL"]),
+    (lambda: L.gemm_mxfp8(8, 8, 8388608, None, A16, B16, B16, C16, None), S["TKG_ERR_SHAPE"]),
     # null pointers
     (lambda: L.gemm_bf16(8, 8, 8, None, B16, C16, None), S["TKG_ERR_NULL"]),
     (lambda: L.gemm_bf16(8, 8, 8, A16, None, C16, None), S["TKG_ERR_NULL"]),
