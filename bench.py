@@ -167,6 +167,36 @@ def _active_cycles(counters):
     return None
 
 
+def _issue_mix(counters):
+    """How a kernel's issue splits between the matrix cores and the other
+    vector ALU work (None when not collected), per SIMD as fractions of the
+    active cycles: MFMA busy; VALU busy (SQ_ACTIVE_INST_VALU, quad-cycles
+    summed over the SIMD's waves, MFMA issue included); both at once
+    (SQ_VALU_MFMA_COEXEC_CYCLES); and VALU instructions per MFMA
+    (SQ_INSTS_VALU counts the MFMAs too) and exp2 (transcendental)
+    instructions per MFMA."""
+    import statistics
+    act = _active_cycles(counters)
+    need = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_COEXEC_CYCLES",
+            "SQ_INSTS_VALU", "SQ_INSTS_MFMA")
+    if not act or any(not counters.get(c) for c in need):
+        return None
+    m = lambda c: statistics.mean(counters[c])
+    simds = 1024.0
+    out = {"mfma_busy": m("SQ_VALU_MFMA_BUSY_CYCLES") / simds / act,
+           "valu_busy": m("SQ_ACTIVE_INST_VALU") * 4 / simds / act,
+           "valu_mfma_coexec": m("SQ_VALU_MFMA_COEXEC_CYCLES") / simds / act,
+           "valu_per_mfma": m("SQ_INSTS_VALU") / m("SQ_INSTS_MFMA"),
+           "trans_per_mfma": (m("SQ_INSTS_VALU_TRANS_F32") / m("SQ_INSTS_MFMA")
+                              if counters.get("SQ_INSTS_VALU_TRANS_F32") else None)}
+    text = ("MFMA busy %.2f, VALU busy %.2f (MFMA issue included), both at once %.2f of the "
+            "active cycles; %.2f VALU instructions per MFMA (MFMAs counted)" % (
+                out["mfma_busy"], out["valu_busy"], out["valu_mfma_coexec"], out["valu_per_mfma"]))
+    if out["trans_per_mfma"] is not None:
+        text += ", %.2f exp2 per MFMA" % out["trans_per_mfma"]
+    return out, text
+
+
 def _kernel_key(name: str):
     for frag, key in KERNEL_KEYS.items():
         if frag in name:
@@ -371,6 +401,10 @@ def summarize_profile(trace_dir: str, fetch_dir: str, write_dir: str,
                 rec["kernels"][k]["clock_ghz_estimate"] = ghz
                 lines.append("%s: about %.2f GHz over the launch (SQ_BUSY_CYCLES per shader "
                              "engine / traced duration)" % (k, ghz))
+            mix = _issue_mix(e)
+            if mix:
+                rec["kernels"][k]["issue_mix"] = mix[0]
+                lines.append("%s: per SIMD, %s" % (k, mix[1]))
             if "SQ_LDS_BANK_CONFLICT" in e and "SQ_LDS_IDX_ACTIVE" in e:
                 rec["kernels"][k]["lds_bank_conflict_over_active"] = (
                     statistics.mean(e["SQ_LDS_BANK_CONFLICT"]) /
@@ -523,6 +557,10 @@ def summarize_attention_profile(trace_dir, fetch_dir, write_dir, out_md, out_jso
                 rec["workloads"][k]["clock_ghz_estimate"] = ghz
                 lines.append("%s: about %.2f GHz over the launch (SQ_BUSY_CYCLES per shader "
                              "engine / traced duration)" % (k, ghz))
+            mix = _issue_mix(e)
+            if mix:
+                rec["workloads"][k]["issue_mix"] = mix[0]
+                lines.append("%s: per SIMD, %s" % (k, mix[1]))
         lines.append("")
     open(out_md, "w").write("\n".join(lines))
     json.dump(rec, open(out_json, "w"), indent=1)
