@@ -176,11 +176,14 @@ void attn_fwd_kernel(AttnArgs p) {
   }
   auto issue = [&](int blk, uint32_t slot_off) {
     const uint32_t k0b = (uint32_t)blk * (S::BK * S::ROWB);
-    // bytes left from the block's first key (both below 2^31); uniform,
-    // and kept in a scalar register for the asm's resource operand
-    const int left = max((int)kv_bytes - (int)k0b, 0);
+    // bytes left from the block's first key: 0 for the prologue's blocks
+    // past the last key (k0b can then pass 2^31 while kv_bytes < 2^31, so
+    // the difference is taken in 64 bits); uniform, and kept in a scalar
+    // register for the asm's resource operand
+    const int64_t rest = (int64_t)kv_bytes - (int64_t)k0b;
+    const uint32_t left = rest > 0 ? (uint32_t)rest : 0u;
     const i32x4_t r = rsrc_words(reinterpret_cast<const uint8_t*>(kv) + k0b,
-                                 (uint32_t)__builtin_amdgcn_readfirstlane(left));
+                                 (uint32_t)__builtin_amdgcn_readfirstlane((int)left));
     const uint32_t dst = (uint32_t)(uintptr_t)smem + slot_off + wave * S::NPW * 1024;
 #pragma unroll
     for (int j = 0; j < S::NPW; ++j) dma_b128_ring(r, dst + j * 1024, dma_off[j]);
