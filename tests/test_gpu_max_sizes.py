@@ -15,7 +15,13 @@ both conditions select (5 and 7 are coprime): an integer below 2^24, so the
 fp32 accumulation is exact and every output must equal the count rounded
 to bf16, bit for bit. A row read at a wrong or wrapped offset, or zeros
 read past a bound, changes counts.
+
+Attention forward likewise at the most keys one head may hold (K and V
+each just below 2^31 bytes), on a pattern whose softmax has a closed form
+(below).
 """
+import math
+
 import numpy as np
 import pytest
 
@@ -136,4 +142,60 @@ def test_mx_largest_k(dev, elem):
     C = gemm(Av, As, Bv, Bs, out=C)
     _check(C, K, elem)
     del Av, Bv, As, Bs, C
+    _free()
+
+
+# ---------------------------------------------------------------- attention
+# One head whose keys fill the largest K and V the entry point accepts (Nk
+# rows of 2D bytes below 2^31): every query is e_0, K[j, 0] = +1 for even j
+# and -1 for odd j (0 elsewhere), V[j, d] = ((j + d) mod 5) - 2, scale 1.
+# The scores are +-1, so the softmax has a closed form built from residue
+# counts of j mod 10 (tests/test_max_size_counts.py checks it against the
+# oracle at small Nk). Nq = 40: two waves hold queries, two hold none.
+
+NQ_ATTN = 40
+
+
+def attention_closed_form(Nq, Nk, D):
+    """(O, sum_j p_j |v_j|, lse) of the pattern above, fp64: O is Nq x D."""
+    t = np.arange(10)
+    cnt = np.where(t < Nk, (Nk - t + 9) // 10, 0).astype(np.float64)   # j = t mod 10
+    w = np.where(t % 2 == 0, math.e, 1.0 / math.e)                      # exp(score)
+    r = (t[:, None] + np.arange(D)[None, :]) % 5 - 2                     # v of class t
+    Z = float(np.sum(cnt * w))
+    num = (cnt * w) @ r
+    mag = (cnt * w) @ np.abs(r)
+    O = np.broadcast_to(num / Z, (Nq, D))
+    A = np.broadcast_to(mag / Z, (Nq, D))
+    return O, A, math.log(Z)
+
+
+def _attn_pattern(Nq, Nk, D, dev):
+    Q = torch.zeros((1, 1, Nq, D), dtype=torch.bfloat16, device=dev)
+    Q[..., 0] = 1.0
+    K = torch.zeros((1, 1, Nk, D), dtype=torch.bfloat16, device=dev)
+    K[0, 0, 0::2, 0] = 1.0
+    K[0, 0, 1::2, 0] = -1.0
+    V = torch.empty((1, 1, Nk, D), dtype=torch.bfloat16, device=dev)
+    d = torch.arange(D, device=dev, dtype=torch.int32)
+    step = 1 << 20
+    for j0 in range(0, Nk, step):
+        j = torch.arange(j0, min(Nk, j0 + step), device=dev, dtype=torch.int32)
+        V[0, 0, j0:j0 + j.numel()] = ((j[:, None] + d[None, :]) % 5 - 2).to(torch.bfloat16)
+    return Q, K, V
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_attention_largest_kv(dev, D):
+    Nk = (2 ** 31 - 1) // (2 * D)          # the most keys one head may hold
+    Q, K, V = _attn_pattern(NQ_ATTN, Nk, D, dev)
+    O, lse = tkg.tkg_attention_fwd(Q, K, V, scale=1.0, lse=True)
+    torch.cuda.synchronize()
+    G = decode_bf16(to_numpy_u16(O))[0, 0]
+    Glse = lse.cpu().numpy().astype(np.float64)[0, 0]
+    R, A, Rlse = attention_closed_form(NQ_ATTN, Nk, D)
+    bound = 2.0 ** -8 * (A + np.abs(R)) + 1e-6        # test_gpu_attention's tolerance
+    assert np.all(np.abs(G - R) <= bound), (D, float(np.max(np.abs(G - R) - bound)))
+    assert np.all(np.abs(Glse - Rlse) <= 2.0 ** -8 + 1e-6 * abs(Rlse)), (D, Glse[:2], Rlse)
+    del Q, K, V, O, lse
     _free()

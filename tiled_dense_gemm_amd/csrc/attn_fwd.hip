@@ -31,7 +31,8 @@
 // raised when a block's row max exceeds it by more than 8 (in log2 units):
 // the probabilities then stay below 2^8, and most blocks skip the rescale
 // of O. The row sum adds the bf16-rounded probabilities that enter the P V
-// product, so numerator and denominator use the same weights.
+// product, so numerator and denominator use the same weights; it is kept
+// in fp32 per window of key blocks and totalled in fp64.
 #include <math.h>
 
 #include <algorithm>
@@ -49,6 +50,11 @@ typedef short s16x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // 4 bf16 pairs
 
 constexpr float kRescaleSlack = 8.0f;  // log2 units
+// The row sum is kept in fp32 over windows of this many key blocks and
+// folded into an fp64 total after each: one fp32 sum over a million keys
+// and more drifts by a part in a few hundred (a term of 1/8 beside a total
+// near 2^21, where the fp32 spacing is 1/4), the windowed one by < 1e-3.
+constexpr int kRowSumWindow = 64;
 constexpr float kLn2 = 0.69314718055994530942f;
 
 // 8-byte transposing LDS read (see attn_v_read in tkg_attn_layout.hpp).
@@ -201,7 +207,8 @@ void attn_fwd_kernel(AttnArgs p) {
   for (int db = 0; db < S::DB; ++db) o[db] = f32x16_t{};
   float m = -INFINITY;  // reference max, log2 units (same in lanes l, l ^ 32)
   float thr = -INFINITY;  // m + kRescaleSlack
-  float l = 0.0f;       // this lane's part of the row sum
+  float l = 0.0f;       // this lane's part of the row sum, current window
+  double lw = 0.0;      // ... over the finished windows
   const float c = p.c;
   const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -245,6 +252,7 @@ void attn_fwd_kernel(AttnArgs p) {
       const float mn = fmaxf(m, mloc);
       const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 on the first block
       l *= alpha;
+      lw *= (double)alpha;
 #pragma unroll
       for (int db = 0; db < S::DB; ++db)
 #pragma unroll
@@ -356,6 +364,16 @@ void attn_fwd_kernel(AttnArgs p) {
     if (nx < nblk) issue(nx, (uint32_t)((j + S::SLOTS - 1) % S::SLOTS) * S::STAGE);
   };
 
+  // after the pass starting at block b0: at a window's end, the window's
+  // row sum goes into the fp64 total (the branch is uniform)
+  static_assert(kRowSumWindow % S::SLOTS == 0, "whole passes per row-sum window");
+  auto fold_row_sum = [&](int b0) {
+    if ((b0 + S::SLOTS) % kRowSumWindow == 0) {
+      lw += (double)l;
+      l = 0.0f;
+    }
+  };
+
   if constexpr (!PIPE) {
     // one block per step: scores, max, probabilities, P V; the other waves
     // on the SIMD fill each wave's dependency waits
@@ -379,6 +397,7 @@ void attn_fwd_kernel(AttnArgs p) {
           pv_mma(pk, vf);
         }
       });
+      fold_row_sum(b0);
     }
   } else {
     // Software pipeline: step blk computes block blk + 1's scores on the
@@ -420,11 +439,12 @@ void attn_fwd_kernel(AttnArgs p) {
         else
           step(J, b0 + j, sb, sa);
       });
+      fold_row_sum(b0);
     }
   }
 
   // ---- finish: divide by the row sum, store bf16 rows and the log-sum-exp
-  const float lt = sum_with_partner(l);
+  const float lt = sum_with_partner((float)(lw + (double)l));
   const int q = q0w + (int)lr;
   if (wblk > 0 && q < p.Nq) {
     const float inv = 1.0f / lt;
