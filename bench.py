@@ -1149,6 +1149,7 @@ def main() -> int:
                                "A row-major, B column-major, bf16 C" % n,
                    "M": M, "N": N, "K": K, "global_batch": 1, "seq_len": None,
                    "parallelism": "single GPU"},
+        "device": _device_description(tkg, dev),
         "kernels": kernels,
         "roofline": roofline,
         "rooflines": rooflines,
@@ -1237,6 +1238,17 @@ def time_attention(args, dev, stream):
         del Q, K, V, O
         torch.cuda.empty_cache()
     return rows
+
+
+def _device_description(tkg, dev):
+    """The GPU the run used: name, architecture, compute units and the
+    runtime's peak shader clock (the clock the published dense peaks
+    assume; the kernels' measured clocks are in `rooflines`)."""
+    import torch
+    props = torch.cuda.get_device_properties(dev)
+    info = tkg.device_info()
+    return {"name": props.name, "arch": props.gcnArchName, "cus": info["cus"],
+            "peak_clock_mhz": info["peak_clock_mhz"]}
 
 
 def _host_description():

@@ -395,6 +395,17 @@ int tkg_plan_launch(int dtype, int64_t M, int64_t N, int64_t K, const tkg_opts *
                     int cus, tkg_launch_plan *out);
 
 /*
+ * The current HIP device as the launches see it: *cus its compute units
+ * (the default persistent grid is built on them; tkg_plan_launch's `cus`)
+ * and *peak_clock_khz the peak shader clock the runtime reports, the clock
+ * the published dense MFMA peaks assume (under the chip's power limit the
+ * kernels run below it). Returns TKG_OK, TKG_ERR_NULL for a null pointer,
+ * or TKG_ERR_DEVICE when no usable HIP device is current. Queries the
+ * runtime only, launches nothing; the caller owns both outputs.
+ */
+int tkg_device_info(int32_t *cus, int32_t *peak_clock_khz);
+
+/*
  * The persistent-grid tile order the kernels run (page "ThunderKittens:
  * Simple, Fast, and Adorable AI Kernels", section 3.4, "Block Launch Order
  * and L2 Cache Reuse"), computed by the same code: writes the tile row *pm

@@ -333,3 +333,15 @@ def test_plan_launch_tail_quadrants():
     # fill its 256 slots
     p = P(bf, 6144, 6144, 1024, cus=128)
     assert (p["grid"], p["units"], p["tail_units"], p["tail_grid"]) == (128, 512, 256, 256)
+
+
+def test_device_info_without_or_with_a_device():
+    # null outputs are rejected; without a usable device the call reports
+    # TKG_ERR_DEVICE (it only queries the runtime)
+    cus, clk = ctypes.c_int32(), ctypes.c_int32()
+    assert L.tkg_device_info(None, ctypes.byref(clk)) == S["TKG_ERR_NULL"]
+    assert L.tkg_device_info(ctypes.byref(cus), None) == S["TKG_ERR_NULL"]
+    st = L.tkg_device_info(ctypes.byref(cus), ctypes.byref(clk))
+    assert st in (S["TKG_OK"], S["TKG_ERR_DEVICE"])
+    if st == S["TKG_OK"]:
+        assert cus.value > 0 and clk.value > 0

@@ -531,3 +531,11 @@ def test_fp4_config_shapes_sampled(dev, n):
         bound = lowp_elem_bound(absprod, n)
         assert np.all(np.abs(G - R) <= bound), (n, i0, j0, float(np.max(np.abs(G - R) - bound)))
     del C
+
+
+def test_device_info_matches_the_device(dev):
+    # the CU count behind the default grid is the one torch reports, and the
+    # runtime's peak clock is set (MI355X: 2400 MHz)
+    info = tkg.device_info()
+    assert info["cus"] == torch.cuda.get_device_properties(dev).multi_processor_count
+    assert 500.0 <= info["peak_clock_mhz"] <= 5000.0

@@ -23,7 +23,7 @@ __all__ = [
     "TkgError", "DTYPE_BF16", "DTYPE_FP8", "DTYPE_FP4_BLOCKSCALED",
     "DTYPE_MXFP4", "DTYPE_MXFP8", "gemm_mxfp4", "gemm_mxfp8",
     "STATUS", "LIB_PATH", "tkg_attention_fwd", "attn_lds_offsets",
-    "num_variants", "variant_info", "launch_masked", "gemm_splitk",
+    "num_variants", "variant_info", "launch_masked", "gemm_splitk", "device_info",
     "splitk_workspace_size", "splitk_count", "gemm_splitk_noalloc",
     "NOALLOC_SCRATCH_BYTES", "plan_launch", "tile_order",
 ]
@@ -125,6 +125,8 @@ def _load() -> ctypes.CDLL:
     L.tkg_plan_launch.argtypes = [i32, i64, i64, i64, ctypes.POINTER(TkgOpts), i32,
                                   ctypes.POINTER(LaunchPlan)]
     L.tkg_plan_launch.restype = i32
+    L.tkg_device_info.argtypes = [ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    L.tkg_device_info.restype = i32
     return L
 
 
@@ -188,6 +190,16 @@ def plan_launch(dtype: int, M: int, N: int, K: int, cus: int = 256, grid: int = 
     if r < 0:
         raise TkgError(r, "tkg_plan_launch")
     return {n: getattr(p, n) for n, _ in LaunchPlan._fields_}
+
+
+def device_info() -> dict:
+    """The current device's compute units and peak shader clock
+    (``tkg_device_info``): {"cus": int, "peak_clock_mhz": float}."""
+    cus, clk = ctypes.c_int32(), ctypes.c_int32()
+    r = lib.tkg_device_info(ctypes.byref(cus), ctypes.byref(clk))
+    if r < 0:
+        raise TkgError(r, "tkg_device_info")
+    return {"cus": cus.value, "peak_clock_mhz": clk.value / 1000.0}
 
 
 def tile_order(t: int, grid: int, xcd_remap: int, tiles_m: int, tiles_n: int,

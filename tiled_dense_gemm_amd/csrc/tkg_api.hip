@@ -783,6 +783,20 @@ int tkg_plan_launch(int dtype, int64_t M, int64_t N, int64_t K, const tkg_opts* 
   return TKG_OK;
 }
 
+int tkg_device_info(int32_t* cus, int32_t* peak_clock_khz) {
+  if (cus == nullptr || peak_clock_khz == nullptr) return TKG_ERR_NULL;
+  int n = 0;
+  const int st = cu_count(&n);
+  if (st != TKG_OK) return st;
+  int dev = 0, clk = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&clk, hipDeviceAttributeClockRate, dev) != hipSuccess || clk <= 0)
+    return TKG_ERR_DEVICE;
+  *cus = n;
+  *peak_clock_khz = clk;
+  return TKG_OK;
+}
+
 int tkg_variant_info(int dtype, int variant, tkg_variant_desc* out) {
   tkg_variant_desc d{};
   int n = 0;
