@@ -217,6 +217,11 @@ int tkg_gemm_splitk_count(int dtype, int64_t M, int64_t N, int64_t K,
  *   (1/sqrt(D) is the usual choice). The caller owns every buffer; the
  *   call allocates nothing and is asynchronous on `stream` (a hipStream_t,
  *   NULL = default stream).
+ * Accuracy: scores are fp32 sums of exact bf16 products; each probability
+ * is rounded to bf16 before the P V product, and the row sum adds those
+ * same rounded values (in fp32 over windows of 2048 keys, totalled in
+ * fp64), so numerator and denominator use the same weights; O is rounded
+ * once to bf16.
  * Returns TKG_OK (nothing launched when B, Hq or Nq is 0), TKG_ERR_SHAPE
  * (unsupported D, negative or inconsistent sizes, Nk = 0 with queries, or
  * too large), TKG_ERR_VALUE (scale), TKG_ERR_NULL (Q, K, V or O NULL),
