@@ -199,3 +199,51 @@ def test_attention_largest_kv(dev, D):
     assert np.all(np.abs(Glse - Rlse) <= 2.0 ** -8 + 1e-6 * abs(Rlse)), (D, Glse[:2], Rlse)
     del Q, K, V, O, lse
     _free()
+
+
+# The most queries one head may hold (Q and O each just below 2^31 bytes),
+# over two key blocks: K[j, 0] = 1 (0 elsewhere), Q[i, 0] = (i mod 3) - 1,
+# so every score of row i is ((i mod 3) - 1) * scale, the softmax of every
+# row is uniform and O[i] is the mean of V's rows, while lse[i] =
+# ((i mod 3) - 1) * scale + ln Nk checks each row's own Q. O starts as NaN.
+
+NK_WIDE = 64
+
+
+def uniform_rows_closed_form(Nk, D, scale, rows):
+    """(O row, lse of the given row indices) of the pattern above, fp64."""
+    j, d = np.arange(Nk)[:, None], np.arange(D)[None, :]
+    O = ((j + d) % 5 - 2).mean(axis=0)
+    lse = ((np.asarray(rows) % 3) - 1) * scale + math.log(Nk)
+    return O, lse
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_attention_largest_q(dev, D):
+    Nq = (2 ** 31 - 1) // (2 * D)          # the most queries one head may hold
+    scale = 1.0 / math.sqrt(D)
+    Q = torch.zeros((1, 1, Nq, D), dtype=torch.bfloat16, device=dev)
+    Q[0, 0, :, 0] = ((torch.arange(Nq, device=dev) % 3) - 1).to(torch.bfloat16)
+    K = torch.zeros((1, 1, NK_WIDE, D), dtype=torch.bfloat16, device=dev)
+    K[..., 0] = 1.0
+    j = torch.arange(NK_WIDE, device=dev)[:, None]
+    d = torch.arange(D, device=dev)[None, :]
+    V = ((j + d) % 5 - 2).to(torch.bfloat16)[None, None]
+    O = torch.full((1, 1, Nq, D), float("nan"), dtype=torch.bfloat16, device=dev)
+    lse = torch.full((1, 1, Nq), float("nan"), dtype=torch.float32, device=dev)
+    tkg.tkg_attention_fwd(Q, K, V, scale=scale, out=O, lse=lse)
+    torch.cuda.synchronize()
+    Oref, _ = uniform_rows_closed_form(NK_WIDE, D, scale, [0])
+    # every row equals the mean of V's rows within one bf16 rounding
+    Of = O[0, 0].float()
+    assert bool(torch.isfinite(Of).all()), D
+    ref = torch.tensor(Oref, dtype=torch.float32, device=dev)
+    err = (Of - ref[None, :]).abs().max().item()
+    assert err <= 2.0 ** -8 * float(np.abs(Oref).max()) + 1e-6, (D, err)
+    # lse of every row: its own Q entry sets the score
+    rows = torch.arange(Nq, device=dev)
+    lref = ((rows % 3) - 1).double() * scale + math.log(NK_WIDE)
+    lerr = (lse[0, 0].double() - lref).abs().max().item()
+    assert lerr <= 2.0 ** -8 + 1e-6 * (abs(scale) + math.log(NK_WIDE)), (D, lerr)
+    del Q, K, V, O, lse, Of, rows, lref
+    _free()

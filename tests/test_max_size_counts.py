@@ -42,3 +42,19 @@ def test_attention_closed_form_matches_oracle(Nk, D):
     assert np.allclose(R[0, 0], O, rtol=1e-12, atol=1e-12)
     assert np.allclose(A[0, 0], Ac, rtol=1e-12, atol=1e-12)
     assert np.allclose(Rlse[0, 0], lse, rtol=1e-12, atol=0)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_uniform_rows_closed_form_matches_oracle(D):
+    from oracle.attention import attention_f64
+    Nq, Nk, scale = 7, mx.NK_WIDE, 1.0 / np.sqrt(D)
+    Q = np.zeros((1, 1, Nq, D))
+    Q[0, 0, :, 0] = (np.arange(Nq) % 3) - 1
+    K = np.zeros((1, 1, Nk, D))
+    K[..., 0] = 1.0
+    j, d = np.arange(Nk)[:, None], np.arange(D)[None, :]
+    V = ((j + d) % 5 - 2).astype(np.float64)[None, None]
+    R, Rlse = attention_f64(Q, K, V, scale=scale, causal=False)
+    O, lse = mx.uniform_rows_closed_form(Nk, D, scale, np.arange(Nq))
+    assert np.allclose(R[0, 0], O[None, :], rtol=1e-12, atol=1e-12)
+    assert np.allclose(Rlse[0, 0], lse, rtol=1e-12, atol=1e-12)
