@@ -960,7 +960,7 @@ def main() -> int:
                                    args.profile_command)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU "
+        print("bench.py measures one GPU only: the library has no multi-GPU "
               "path (a GEMM shards by splitting N across GPUs with no "
               "exchange; the per-GPU kernel is the one measured here).",
               file=sys.stderr)
