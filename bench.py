@@ -658,7 +658,9 @@ def _roofline(kernel, tflops, peak, basis):
 # the missing swizzle ablation; page "ThunderKittens reaches 22.4 PFLOPS on
 # NVIDIA Rubin" for the release timing and ring depth). Each group:
 # (group, dtype, M, N, K, [(setting label, tkg_gemm_ex options), ...]).
-# Every setting computes the same bits (the GPU tests check it).
+# Every setting computes the same bits at these sizes (the GPU tests check
+# it; fp8's 16x16x128 and 32x32x64 blocks can round a few elements to
+# neighbouring bf16 values once K reaches 16384).
 def ablation_groups():
     # bf16 17 is the default's configuration on the interleaved schedule:
     # the ring-depth and MFMA-shape groups compare on that schedule
@@ -843,8 +845,10 @@ def summarize_ablations(run_dirs, out_md, out_json, command):
     rec = {"kernel_source_hash": ref["kernel_source_hash"], "command": command,
            "calibration": fac, "rows": []}
     lines = ["# Ablations of the dense GEMM kernels on one MI355X (rocprofv3)", "",
-             "Every setting computes the same bits (the GPU tests compare all kernel "
-             "configurations and launch options bit for bit). Kernel source hash %s."
+             "Every setting computes the same bits at these sizes (the GPU tests compare "
+             "all kernel configurations and launch options bit for bit; fp8's 16x16x128 "
+             "and 32x32x64 blocks can round a few elements to neighbouring bf16 values "
+             "once K reaches 16384). Kernel source hash %s."
              % ref["kernel_source_hash"], "", "Produced by:", "", "```", command, "```", "",
              "Columns: TFLOP/s from the HIP-event mean of the traced run (median over %d "
              "alternating rounds of %d launches after %d warmup launches) and from the "

@@ -298,8 +298,17 @@ const char *tkg_status_string(int status);
  *               ring with early reads, 13 = configuration 4 on the
  *               interleaved schedule. TKG_ERR_SHAPE outside 0 .. n-1.
  *               4-bit product: 0 = 4 waves (default), 1 = 8 waves;
- *               TKG_ERR_SHAPE outside 0..1. Every variant of a product
- *               computes the same sums (the tests find them bit-identical).
+ *               TKG_ERR_SHAPE outside 0..1. Variants that issue the same
+ *               MFMA instruction compute the same bits. bf16's 16x16x32
+ *               and 32x32x16 blocks also agree bit for bit (16384^3
+ *               included). fp8's 16x16x128 configurations (2, 4, 5, 10,
+ *               13) round the fp32 accumulation at other points than the
+ *               32x32x64 ones once partial sums are inexact: an element
+ *               whose sum lies next to a bf16 rounding midpoint can round
+ *               to the neighbouring value (at 16384^3, 11 of 2^28 elements
+ *               on normal operands scaled by amax/448, each within the
+ *               fp8 error bound either way; none up to K = 8192 in the
+ *               tests and measurements).
  * Page "ThunderKittens: Simple, Fast, and Adorable AI Kernels", section
  * 3.4, "Persistent Grid Launch" (Table 2) and "Block Launch Order and L2
  * Cache Reuse" (Table 3), measure these choices.
