@@ -99,6 +99,12 @@ L = tkg.lib
     (lambda: L.tkg_attention_fwd(A16, B16, C16, A16, None, -1, 2, 2, 8, 8, 64, 0.1, 0, None), S["TKG_ERR_SHAPE"]),
     (lambda: L.tkg_attention_fwd(A16, B16, C16, A16, None, 1, 2, 2, 8, 0, 64, 0.1, 0, None), S["TKG_ERR_SHAPE"]),
     (lambda: L.tkg_attention_fwd(A16, B16, C16, A16, None, 1, 2, 2, 1 << 24, 8, 64, 0.1, 0, None), S["TKG_ERR_SHAPE"]),
+    # sizes whose byte counts overflow 64 bits are rejected, not wrapped
+    (lambda: L.tkg_attention_fwd(A16, B16, C16, A16, None, 1, 2, 2, 8, (1 << 62) + 8, 128, 0.1, 0, None), S["TKG_ERR_SHAPE"]),
+    (lambda: L.tkg_attention_fwd(A16, B16, C16, A16, None, 1, 2, 2, 1 << 62, 8, 64, 0.1, 0, None), S["TKG_ERR_SHAPE"]),
+    # the most keys one head may hold (Nk * 2D < 2^31) passes the size checks
+    (lambda: L.tkg_attention_fwd(None, None, None, None, None, 1, 2, 2, 8, (2**31 - 1) // 256, 128, 0.1, 0, None), S["TKG_ERR_NULL"]),
+    (lambda: L.tkg_attention_fwd(None, None, None, None, None, 1, 2, 2, 8, (2**31 - 1) // 256 + 1, 128, 0.1, 0, None), S["TKG_ERR_SHAPE"]),
     (lambda: L.tkg_attention_fwd(A16, B16, C16, A16, None, 1, 2, 2, 8, 8, 64, 0.0, 0, None), S["TKG_ERR_VALUE"]),
     (lambda: L.tkg_attention_fwd(A16, B16, C16, A16, None, 1, 2, 2, 8, 8, 64, -1.0, 0, None), S["TKG_ERR_VALUE"]),
     (lambda: L.tkg_attention_fwd(A16, B16, C16, A16, None, 1, 2, 2, 8, 8, 64, float("inf"), 0, None), S["TKG_ERR_VALUE"]),

@@ -438,7 +438,8 @@ int run_attention(const void* Q, const void* K, const void* V, void* O, float* l
   if (Hq > 0 && (Hkv <= 0 || Hq % Hkv != 0)) return TKG_ERR_SHAPE;
   if (causal && Nq != Nk) return TKG_ERR_SHAPE;
   // one buffer resource per head's Q (and K, V) rows: below 2^31 bytes
-  if (Nq * 2 * D > INT32_MAX || Nk * 2 * D > INT32_MAX) return TKG_ERR_SHAPE;
+  // (compared by division, so that no product of the sizes can overflow)
+  if (Nq > INT32_MAX / (2 * D) || Nk > INT32_MAX / (2 * D)) return TKG_ERR_SHAPE;
   const int64_t bq = tkg::attn_block_q((int)D);
   const int64_t qblocks = (Nq + bq - 1) / bq;
   if (B > INT32_MAX || Hq > INT32_MAX || (B > 0 && Hq * qblocks > INT32_MAX / B))
