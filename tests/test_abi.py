@@ -221,6 +221,10 @@ def test_variant_table():
         n = tkg.num_variants(d)
         assert L.tkg_variant_info(d, n, None) == S["TKG_ERR_SHAPE"]
         assert L.tkg_variant_info(d, -1, None) == S["TKG_ERR_SHAPE"]
+    # the fp8 configurations on 16x16x128 blocks, the ones whose sums can
+    # round differently from the default's 32x32x64 at long K
+    assert [v for v in range(tkg.num_variants(tkg.DTYPE_FP8))
+            if tkg.variant_info(tkg.DTYPE_FP8, v)["mfma_block"] == 16] == [2, 4, 5, 10, 13]
     # bf16 17 is the interleaved schedule, otherwise the default
     v17, v0 = tkg.variant_info(tkg.DTYPE_BF16, 17), tkg.variant_info(tkg.DTYPE_BF16, 0)
     assert v17["schedule_name"] == "interleaved"
